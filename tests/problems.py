@@ -1,0 +1,77 @@
+"""Test problems: seeded inputs (fp8_paged_kv_amd.inputs) packed into pools by
+the oracle's quantizer.  Used by the oracle pins and the GPU parity tests."""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+from fp8_paged_kv_amd import inputs
+from oracle import pool as opool
+
+POISON = 0xFF      # NaN E4M3 code, NaN fp32 scale bytes, NaN E8M0 scale
+
+
+def round16(n):
+    return (n + 15) // 16 * 16
+
+
+@dataclass
+class Problem:
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    P: int
+    kdesc: opool.PoolDesc
+    vdesc: opool.PoolDesc
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    table: np.ndarray
+    seq_lens: np.ndarray
+    q: np.ndarray                  # [B, Hq, D] float32, bf16-exact
+    sinks: Optional[np.ndarray]
+    window: int
+    sm_scale: Optional[float]
+    raw_k: list = field(default_factory=list)
+    raw_v: list = field(default_factory=list)
+
+    @property
+    def scale(self):
+        return self.D ** -0.5 if self.sm_scale is None else self.sm_scale
+
+
+def make_problem(seed, B, Hq, Hkv, D, P, lens, scale_kind="page_head", k_layout="heads",
+                 v_layout="heads_dmajor", window=0, sinks=False, sm_scale=None, row_pad=0,
+                 poison=True, cfg=99, spare_frac=0.1, k_gain=1.0):
+    lens = np.asarray(lens, dtype=np.int32)
+    assert len(lens) == B
+    table, rows = inputs.block_table(seed, cfg, lens, P, spare_frac=spare_frac)
+    kd = opool.natural_desc(Hkv, D, P, k_layout, scale_kind, rows)
+    vd = opool.natural_desc(Hkv, D, P, v_layout, scale_kind, rows)
+    from dataclasses import replace
+    kd = replace(kd, row_bytes=round16(kd.row_bytes) + row_pad)
+    vd = replace(vd, row_bytes=round16(vd.row_bytes) + row_pad)
+    fill = POISON if poison else 0
+    k_pool = np.full(rows * kd.row_bytes, fill, dtype=np.uint8)
+    v_pool = np.full(rows * vd.row_bytes, fill, dtype=np.uint8)
+    ks = [inputs.normal_bf16(seed, cfg, "k", b, (int(lens[b]), Hkv, D)) * np.float32(k_gain) for b in range(B)]
+    vs = [inputs.normal_bf16(seed, cfg, "v", b, (int(lens[b]), Hkv, D)) for b in range(B)]
+    k_pool = opool.pack_sequences(k_pool, kd, table, ks)
+    v_pool = opool.pack_sequences(v_pool, vd, table, vs)
+    q = inputs.normal_bf16(seed, cfg, "q", 0, (B, Hq, D))
+    s = inputs.sinks(seed, cfg, Hq) if sinks else None
+    return Problem(B, Hq, Hkv, D, P, kd, vd, k_pool, v_pool, table, lens, q, s, window, sm_scale, ks, vs)
+
+
+def permute_rows(prob: Problem, seed=1):
+    """Same logical data with the physical rows shuffled (table updated to match)."""
+    n = prob.kdesc.num_rows
+    perm = np.random.default_rng(seed).permutation(n)          # old row r -> new row perm[r]
+    def move(pool, desc):
+        old = pool.reshape(n, desc.row_bytes)
+        new = np.empty_like(old)
+        new[perm] = old
+        return new.reshape(-1)
+    table = np.where(prob.table >= 0, perm[np.maximum(prob.table, 0)], -1).astype(np.int32)
+    from dataclasses import replace
+    return replace(prob, k_pool=move(prob.k_pool, prob.kdesc), v_pool=move(prob.v_pool, prob.vdesc), table=table)

@@ -1,0 +1,230 @@
+"""Pins for the oracle's decode attention and split merge (CPU only): torch SDPA
+in float64, brute-force loops, closed forms and invariants."""
+import json
+import math
+import os
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt, fp8, pool as opool
+from tests.problems import make_problem, permute_rows
+
+
+def dense_kv(p, b):
+    L = int(p.seq_lens[b])
+    J = np.arange(L)
+    K = np.stack([opool.read_tokens(p.k_pool, p.kdesc, p.table[b], J, h) for h in range(p.Hkv)], 1)
+    V = np.stack([opool.read_tokens(p.v_pool, p.vdesc, p.table[b], J, h) for h in range(p.Hkv)], 1)
+    return K, V                                                        # [L, Hkv, D]
+
+
+def ref(p, **kw):
+    args = dict(window=p.window, sinks=p.sinks, sm_scale=p.sm_scale)
+    args.update(kw)
+    return oatt.decode_ref(p.q, p.k_pool, p.v_pool, p.kdesc, p.vdesc, p.table, p.seq_lens, **args)
+
+
+def sdpa(p, b, window, sinks, scale):
+    K, V = dense_kv(p, b)
+    L = K.shape[0]
+    G = p.Hq // p.Hkv
+    k = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, 0)   # [Hq, L, D]
+    v = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, 0)
+    q = torch.from_numpy(p.q[b].astype(np.float64))[:, None, :]         # [Hq, 1, D]
+    start = max(0, L - window) if window > 0 else 0
+    mask = torch.full((p.Hq, 1, L + 1), -math.inf, dtype=torch.float64)
+    mask[:, :, start:L] = 0.0
+    k = torch.cat([k, torch.zeros(p.Hq, 1, p.D, dtype=torch.float64)], 1)   # the sink: a zero key ...
+    v = torch.cat([v, torch.zeros(p.Hq, 1, p.D, dtype=torch.float64)], 1)   # ... with a zero value ...
+    mask[:, 0, L] = torch.from_numpy(np.asarray(sinks, np.float64)) if sinks is not None else -math.inf
+    if start == L and sinks is None:
+        return np.zeros((p.Hq, p.D))
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale)
+    return o[:, 0, :].numpy()                                          # ... and additive logit sigma
+
+
+@pytest.mark.parametrize("window,sinks,kind,scale", [
+    (0, False, "page_head", None), (0, True, "page_head", 0.3), (24, False, "token_head", None),
+    (7, True, "e8m0_32", 1.0), (200, True, "page_head", None)])
+def test_decode_matches_torch_sdpa_float64(window, sinks, kind, scale):
+    p = make_problem(21, B=3, Hq=8, Hkv=2, D=64, P=16, lens=[53, 16, 1], scale_kind=kind,
+                     window=window, sinks=sinks, sm_scale=scale)
+    got = ref(p)
+    for b in range(p.B):
+        want = sdpa(p, b, window, p.sinks, p.scale)
+        np.testing.assert_allclose(got[b], want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("window,sinks", [(0, False), (5, True), (100, False)])
+def test_decode_matches_brute_force_loops(window, sinks):
+    p = make_problem(22, B=2, Hq=4, Hkv=2, D=32, P=16, lens=[37, 9], window=window, sinks=sinks,
+                     sm_scale=0.2)
+    Ks, Vs = zip(*[dense_kv(p, b) for b in range(p.B)])
+    want = oatt.dense_loops_ref(p.q.astype(np.float64).tolist(), [k.tolist() for k in Ks],
+                                [v.tolist() for v in Vs], p.Hkv, 0.2, window, p.sinks)
+    np.testing.assert_allclose(ref(p), want, rtol=1e-12, atol=1e-14)
+
+
+def test_single_token_returns_v0():
+    p = make_problem(23, B=2, Hq=4, Hkv=2, D=64, P=16, lens=[1, 1])
+    out = ref(p)
+    for b in range(2):
+        K, V = dense_kv(p, b)
+        for h in range(4):
+            assert np.array_equal(out[b, h], V[0, h // 2])
+
+
+def test_single_token_with_sink_closed_form():
+    p = make_problem(24, B=1, Hq=4, Hkv=2, D=64, P=16, lens=[1], sinks=True)
+    out = ref(p)
+    K, V = dense_kv(p, 0)
+    for h in range(4):
+        s = p.scale * float(p.q[0, h].astype(np.float64) @ K[0, h // 2])
+        w = math.exp(s) / (math.exp(s) + math.exp(float(p.sinks[h])))
+        np.testing.assert_allclose(out[0, h], V[0, h // 2] * w, rtol=1e-13, atol=1e-16)
+
+
+def test_constant_v_returns_that_value():
+    p = make_problem(25, B=1, Hq=4, Hkv=2, D=64, P=16, lens=[45])
+    const = np.full((45, 2, 64), 0.75, np.float32)
+    vp = opool.pack_sequences(np.full_like(p.v_pool, 0xFF), p.vdesc, p.table, [const])
+    out = oatt.decode_ref(p.q, p.k_pool, vp, p.kdesc, p.vdesc, p.table, p.seq_lens)
+    vh = opool.read_tokens(vp, p.vdesc, p.table[0], np.arange(45), 0)
+    assert np.all(vh == vh[0, 0])                       # every token dequantizes to one value
+    np.testing.assert_allclose(out, vh[0, 0], rtol=1e-14)
+    assert abs(vh[0, 0] - 0.75) < 0.75 * 2 ** -20
+
+
+@pytest.mark.parametrize("W", [1, 15, 16, 17, 56, 57, 58, 0])
+def test_zero_scale_gives_mean_over_the_window(W):
+    L = 57
+    p = make_problem(26, B=1, Hq=4, Hkv=2, D=64, P=16, lens=[L], window=W, sm_scale=0.0)
+    out = ref(p)
+    _, V = dense_kv(p, 0)
+    n = L if W <= 0 else min(W, L)
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], V[L - n:, h // 2].mean(axis=0), rtol=1e-12, atol=1e-15)
+
+
+def test_zero_scale_with_sink_closed_form():
+    L = 20
+    p = make_problem(27, B=1, Hq=4, Hkv=2, D=64, P=16, lens=[L], sinks=True, sm_scale=0.0)
+    out = ref(p)
+    _, V = dense_kv(p, 0)
+    for h in range(4):
+        want = L * V[:, h // 2].mean(axis=0) / (L + math.exp(float(p.sinks[h])))
+        np.testing.assert_allclose(out[0, h], want, rtol=1e-12, atol=1e-15)
+
+
+def test_invariants():
+    p = make_problem(28, B=3, Hq=8, Hkv=2, D=64, P=16, lens=[70, 33, 5], sinks=True)
+    base = ref(p)
+    # physical row permutation
+    assert np.array_equal(ref(permute_rows(p, 3)), base)
+    # window >= L is full attention
+    assert np.array_equal(ref(p, window=70), base) and np.array_equal(ref(p, window=1000), base)
+    # sigma = -inf is no sink
+    nos = ref(p, sinks=None)
+    assert np.array_equal(ref(p, sinks=np.full(8, -np.inf)), nos)
+    # K scale x 2 with sm_scale / 2
+    kp = p.k_pool.copy().reshape(p.kdesc.num_rows, -1)
+    for h in range(p.Hkv):
+        at = opool.scale_offset(p.kdesc, h)
+        s = kp[:, at:at + 4].copy().view(np.float32)
+        ok = np.isfinite(s)
+        s[ok] *= 2
+        kp[:, at:at + 4] = s.view(np.uint8)
+    q2 = replace(p, k_pool=kp.reshape(-1), sm_scale=p.scale / 2)
+    np.testing.assert_allclose(ref(q2), base, rtol=1e-14, atol=1e-16)
+    # identical q rows in a group give identical outputs
+    q3 = p.q.copy(); q3[:, 1] = q3[:, 0]
+    o3 = ref(replace(p, q=q3, sinks=None))            # equal rows, equal (absent) sinks
+    assert np.array_equal(o3[:, 0], o3[:, 1])
+
+
+def test_positions_permuted_together_give_same_output():
+    p = make_problem(29, B=1, Hq=4, Hkv=2, D=64, P=16, lens=[32])
+    base = ref(p)
+    K, V = p.raw_k[0], p.raw_v[0]
+    perm = np.random.default_rng(0).permutation(32)
+    # pages are quantised per page: permute within each page so the scales are unchanged
+    perm = np.concatenate([np.random.default_rng(1).permutation(16), 16 + np.random.default_rng(2).permutation(16)])
+    kp = opool.pack_sequences(np.full_like(p.k_pool, 0xFF), p.kdesc, p.table, [K[perm]])
+    vp = opool.pack_sequences(np.full_like(p.v_pool, 0xFF), p.vdesc, p.table, [V[perm]])
+    np.testing.assert_allclose(ref(replace(p, k_pool=kp, v_pool=vp)), base, rtol=1e-13, atol=1e-15)
+
+
+def test_empty_sequence_gives_zero():
+    p = make_problem(30, B=2, Hq=4, Hkv=2, D=64, P=16, lens=[0, 3], sinks=True)
+    out = ref(p)
+    assert np.all(out[0] == 0)
+
+
+def _partials(p, b, g, cuts):
+    J = oatt.attended_positions(int(p.seq_lens[b]), p.window)
+    G = p.Hq // p.Hkv
+    K = opool.read_tokens(p.k_pool, p.kdesc, p.table[b], J, g)
+    V = opool.read_tokens(p.v_pool, p.vdesc, p.table[b], J, g)
+    parts = [oatt.partial_ref(p.q[b, g * G:(g + 1) * G], K[a:c], V[a:c], p.scale) for a, c in zip(cuts[:-1], cuts[1:])]
+    o = np.stack([x[0] for x in parts], 1)        # [G, S, D]
+    lse = np.stack([x[1] for x in parts], 1)      # [G, S]
+    return o, lse
+
+
+@pytest.mark.parametrize("sinks", [False, True])
+def test_merge_of_any_split_equals_unsplit(sinks):
+    p = make_problem(31, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[90, 40], sinks=sinks, window=75)
+    base = ref(p)
+    rng = np.random.default_rng(4)
+    for b in range(2):
+        n = len(oatt.attended_positions(int(p.seq_lens[b]), p.window))
+        for trial in range(4):
+            cuts = np.unique(np.concatenate([[0, n], rng.integers(0, n + 1, 3)]))
+            cuts = np.concatenate([cuts[:1], cuts, cuts[-1:]])          # empty splits at both ends too
+            for g in range(2):
+                o, lse = _partials(p, b, g, cuts)
+                sg = None if p.sinks is None else p.sinks[g * 4:(g + 1) * 4]
+                m = oatt.merge_ref(o[None], lse[None], sg)[0]
+                np.testing.assert_allclose(m, base[b, g * 4:(g + 1) * 4], rtol=1e-12, atol=1e-14)
+
+
+def test_merge_special_cases():
+    rng = np.random.default_rng(5)
+    o = rng.standard_normal((1, 2, 1, 8))
+    lse = rng.standard_normal((1, 2, 1))
+    assert np.array_equal(oatt.merge_ref(o, lse), o[:, :, 0])
+    empty = oatt.merge_ref(np.full((1, 2, 3, 8), np.nan), np.full((1, 2, 3), -np.inf))
+    assert np.all(empty == 0)
+    # one split plus a sink equal to its lse halves the output
+    half = oatt.merge_ref(o, lse, sinks=lse[0, :, 0])
+    np.testing.assert_allclose(half, o[:, :, 0] / 2, rtol=1e-15)
+
+
+def test_page_example_structure(golden_dir):
+    """The method page's CPU example: BT=16, H_KV=2, H_Q=4, D=64, 40 live tokens,
+    a permuted block table [[2, 0, 1]], default scale D**-0.5, checked against
+    dense softmax attention over the dequantized values at rtol = atol = 1e-2."""
+    ex = json.load(open(os.path.join(golden_dir, "p1_cpu_example.json")))
+    BT, H, HQ, D, T = ex["block_tokens"], ex["num_kv_heads"], ex["num_q_heads"], ex["head_dim"], ex["live_tokens"]
+    table = np.array(ex["block_table"], dtype=np.int32)
+    d = opool.natural_desc(H, D, BT, "tokens", "token_head", 3)
+    rng = np.random.default_rng(0)
+    kt = rng.standard_normal((48, H, D)).astype(np.float32)
+    vt = rng.standard_normal((48, H, D)).astype(np.float32)
+    kp = opool.pack_sequences(np.zeros(3 * d.row_bytes, np.uint8), d, table, [kt[:T]])
+    vp = opool.pack_sequences(np.zeros(3 * d.row_bytes, np.uint8), d, table, [vt[:T]])
+    q = rng.standard_normal((1, HQ, D)).astype(np.float32)
+    got = oatt.decode_ref(q, kp, vp, d, d, table, np.array([T]))
+    kd = np.stack([opool.read_tokens(kp, d, table[0], np.arange(T), h) for h in range(H)])   # [H, T, D]
+    vd = np.stack([opool.read_tokens(vp, d, table[0], np.arange(T), h) for h in range(H)])
+    qq = q[0].astype(np.float64).reshape(H, HQ // H, D)
+    w = np.einsum("hgd,htd->hgt", qq, kd) * D ** -0.5
+    w = np.exp(w - w.max(-1, keepdims=True)); w /= w.sum(-1, keepdims=True)
+    want = np.einsum("hgt,htd->hgd", w, vd).reshape(1, HQ, D)
+    np.testing.assert_allclose(got, want, rtol=ex["rtol"], atol=ex["atol"])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+    # and the dequantized K is the quantised input to within E4M3 precision
+    np.testing.assert_allclose(kd, kt[:T].transpose(1, 0, 2), rtol=2 ** -4, atol=2e-3)
