@@ -1,0 +1,393 @@
+// C-ABI of libfp8pa: argument validation, split planning, workspace carving,
+// launch counters and error reporting.  Every check runs on the host before
+// anything is enqueued; an invalid call launches nothing (the page's
+// convention: an explicit request is honoured or refused, never silently
+// replaced, and what ran is recorded).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/fp8pa.h"
+#include "fp8pa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+struct Counters {
+  std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0},
+      errors{0};
+};
+Counters g_cnt;
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  g_cnt.errors.fetch_add(1);
+  return code;
+}
+
+void ok() { g_err[0] = 0; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int ilog2(int64_t v) {
+  int r = 0;
+  while ((int64_t(1) << r) < v) ++r;
+  return r;
+}
+
+int64_t scale_bytes(const fp8pa_pool_desc& d) {
+  const int64_t H = d.num_kv_heads, P = d.page_size, D = d.head_dim;
+  switch (d.scale_kind) {
+    case FP8PA_SCALE_F32_PAGE_HEAD: return 4 * H;
+    case FP8PA_SCALE_F32_TOKEN_HEAD: return 4 * H * P;
+    default: return H * P * D / 32;
+  }
+}
+
+int64_t footer_offset(const fp8pa_pool_desc& d) {
+  return d.scale_offset < 0 ? (int64_t)d.page_size * d.num_kv_heads * d.head_dim : d.scale_offset;
+}
+
+// Checks one pool descriptor; returns 0 or an error code (message set).
+int check_desc(const fp8pa_pool_desc* d, const char* name) {
+  if (!d) return fail(FP8PA_EINVAL, "%s: descriptor is NULL", name);
+  if (d->reserved != 0) return fail(FP8PA_EINVAL, "%s: reserved field must be 0", name);
+  if (d->num_kv_heads < 1) return fail(FP8PA_EINVAL, "%s: num_kv_heads must be >= 1", name);
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256 && d->head_dim != 512)
+    return fail(FP8PA_EUNSUPPORTED, "%s: head_dim %d not in {64,128,256,512}", name, d->head_dim);
+  if (!pow2(d->page_size) || d->page_size < 16 || d->page_size > 1024)
+    return fail(FP8PA_EUNSUPPORTED, "%s: page_size %d is not a power of two in [16,1024]", name, d->page_size);
+  if (d->layout < FP8PA_LAYOUT_HEADS || d->layout > FP8PA_LAYOUT_HEADS_DMAJOR)
+    return fail(FP8PA_EINVAL, "%s: unknown layout %d", name, d->layout);
+  if (d->scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || d->scale_kind > FP8PA_SCALE_E8M0_G32)
+    return fail(FP8PA_EINVAL, "%s: unknown scale_kind %d", name, d->scale_kind);
+  const int64_t payload = (int64_t)d->page_size * d->num_kv_heads * d->head_dim;
+  const int64_t foot = footer_offset(*d);
+  if (d->row_bytes <= 0 || d->row_bytes % 16)
+    return fail(FP8PA_EINVAL, "%s: row_bytes %lld must be a positive multiple of 16", name, (long long)d->row_bytes);
+  if (foot < payload || foot % 16)
+    return fail(FP8PA_EINVAL, "%s: scale_offset %lld must be a multiple of 16 and >= the payload (%lld)", name,
+                (long long)foot, (long long)payload);
+  if (foot + scale_bytes(*d) > d->row_bytes)
+    return fail(FP8PA_EINVAL, "%s: payload + scales (%lld) exceed row_bytes %lld", name,
+                (long long)(foot + scale_bytes(*d)), (long long)d->row_bytes);
+  if (d->num_rows < 0) return fail(FP8PA_EINVAL, "%s: num_rows must be >= 0", name);
+  if (d->row_bytes > INT64_MAX / (d->num_rows > 0 ? d->num_rows : 1))
+    return fail(FP8PA_EINVAL, "%s: pool size overflows", name);
+  if (foot + scale_bytes(*d) > INT32_MAX) return fail(FP8PA_EUNSUPPORTED, "%s: row too large", name);
+  return 0;
+}
+
+fp8pa::PoolGeom geometry(const fp8pa_pool_desc& d) {
+  fp8pa::PoolGeom g{};
+  const int H = d.num_kv_heads, P = d.page_size, D = d.head_dim;
+  g.row_bytes = d.row_bytes;
+  g.sc_off = (int32_t)footer_offset(d);
+  const bool tok = d.layout == FP8PA_LAYOUT_TOKENS;
+  switch (d.layout) {
+    case FP8PA_LAYOUT_HEADS: g.head_stride = P * D; g.tok_stride = D; g.d_stride = 1; break;
+    case FP8PA_LAYOUT_TOKENS: g.head_stride = D; g.tok_stride = H * D; g.d_stride = 1; break;
+    default: g.head_stride = D * P; g.tok_stride = 1; g.d_stride = P; break;
+  }
+  switch (d.scale_kind) {
+    case FP8PA_SCALE_F32_PAGE_HEAD: g.sc_head_stride = 4; g.sc_tok_stride = 0; break;
+    case FP8PA_SCALE_F32_TOKEN_HEAD:
+      g.sc_head_stride = tok ? 4 : 4 * P;
+      g.sc_tok_stride = tok ? 4 * H : 4;
+      break;
+    default:
+      g.sc_head_stride = tok ? D / 32 : P * (D / 32);
+      g.sc_tok_stride = tok ? H * (D / 32) : D / 32;
+      break;
+  }
+  return g;
+}
+
+int target_workgroups() {
+  static int cached = 0;
+  if (cached) return cached;
+  int t = 1024;   // four per CU on a 256-CU part
+  if (const char* e = getenv("FP8PA_TARGET_WORKGROUPS")) {
+    const int v = atoi(e);
+    if (v > 0) t = v;
+  }
+  cached = t;
+  return t;
+}
+
+// Host-only split plan.  Returns 0 or an error code.
+int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int window, int num_splits,
+              int variant, fp8pa_plan* out) {
+  if (int rc = check_desc(kd, "kd")) return rc;
+  if (B < 0) return fail(FP8PA_EINVAL, "B must be >= 0");
+  if (Hq < 1 || Hq % kd->num_kv_heads) return fail(FP8PA_EINVAL, "Hq must be a positive multiple of num_kv_heads");
+  const int G = Hq / kd->num_kv_heads;
+  if (G > 16) return fail(FP8PA_EUNSUPPORTED, "query heads per KV head G=%d > 16", G);
+  if (max_seq_len < 0) return fail(FP8PA_EINVAL, "max_seq_len must be >= 0");
+  if (num_splits < 0) return fail(FP8PA_EINVAL, "num_splits must be >= 0");
+  if (variant != FP8PA_VARIANT_AUTO && variant != FP8PA_VARIANT_MFMA_BF16)
+    return fail(FP8PA_EUNSUPPORTED, "variant %d is not available", variant);
+  const int D = kd->head_dim;
+  if ((int64_t)2 * G * (D + 4) * 4 > 65536)
+    return fail(FP8PA_EUNSUPPORTED, "G=%d with head_dim %d exceeds the 64 KiB combine buffer", G, D);
+  const int TT = fp8pa::decode_tile_tokens(D);
+  const int64_t span = (window > 0 && window < max_seq_len) ? window : max_seq_len;
+  // Tiles a range of `span` positions may touch once aligned down to a tile.
+  const int64_t ntile = span > 0 ? (span - 1) / TT + 2 : 1;
+  int64_t S, tps;
+  if (num_splits > 0) {
+    S = num_splits < ntile ? num_splits : ntile;
+    tps = (ntile + S - 1) / S;
+  } else {
+    const int64_t units = (int64_t)(B > 0 ? B : 1) * kd->num_kv_heads;
+    S = (target_workgroups() + units - 1) / units;
+    const int64_t maxS = (ntile + 3) / 4;   // at least one tile per wave
+    if (S > maxS) S = maxS;
+    if (S < 1) S = 1;
+    tps = (ntile + S - 1) / S;
+    tps = (tps + 3) / 4 * 4;
+  }
+  S = (ntile + tps - 1) / tps;
+  if (S < 1) S = 1;
+  out->num_splits = (int32_t)S;
+  out->split_tokens = (int32_t)(tps * TT);
+  out->variant = FP8PA_VARIANT_MFMA_BF16;
+  out->reserved = 0;
+  if (S > 1) {
+    const int64_t po = (int64_t)B * Hq * S * D * 4;
+    const int64_t pl = (int64_t)B * Hq * S * 4;
+    out->workspace_bytes = (po + 255) / 256 * 256 + (pl + 255) / 256 * 256;
+  } else {
+    out->workspace_bytes = 0;
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8pa_version(void) { return "fp8pa 0.1.0 gfx950"; }
+
+const char* fp8pa_last_error(void) { return g_err; }
+
+int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int window, int num_splits,
+                      int variant, fp8pa_plan* out) {
+  if (!out) return fail(FP8PA_EINVAL, "plan output is NULL");
+  if (int rc = make_plan(B, Hq, kd, max_seq_len, window, num_splits, variant, out)) return rc;
+  ok();
+  return FP8PA_OK;
+}
+
+int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t* v_pool,
+                 const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, const int32_t* block_table,
+                 int64_t bt_stride, const int32_t* seq_lens, int B, int Hq, int window, const float* sinks,
+                 float sm_scale, int max_seq_len, int num_splits, int variant, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  fp8pa_plan plan;
+  if (int rc = make_plan(B, Hq, kd, max_seq_len, window, num_splits, variant, &plan)) return rc;
+  if (int rc = check_desc(vd, "vd")) return rc;
+  if (kd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
+    return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS or TOKENS layout");
+  if (vd->layout != FP8PA_LAYOUT_HEADS_DMAJOR)
+    return fail(FP8PA_EUNSUPPORTED, "vd: decode reads V in the HEADS_DMAJOR layout");
+  if (vd->num_kv_heads != kd->num_kv_heads || vd->head_dim != kd->head_dim || vd->page_size != kd->page_size ||
+      vd->scale_kind != kd->scale_kind)
+    return fail(FP8PA_EUNSUPPORTED, "K and V pools must share num_kv_heads, head_dim, page_size and scale_kind");
+  if (B == 0) {
+    ok();
+    g_cnt.decode_calls.fetch_add(1);
+    return FP8PA_OK;
+  }
+  if (!q || !out || !k_pool || !v_pool || !block_table || !seq_lens)
+    return fail(FP8PA_EINVAL, "a required device pointer is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(FP8PA_EINVAL, "q and out must be 16-byte aligned");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return fail(FP8PA_EINVAL, "pools must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4)) return fail(FP8PA_EINVAL, "block_table/seq_lens misaligned");
+  if (sinks && !aligned(sinks, 4)) return fail(FP8PA_EINVAL, "sinks misaligned");
+  if (bt_stride < 1) return fail(FP8PA_EINVAL, "bt_stride must be >= 1");
+  if (max_seq_len > 0 && bt_stride < (max_seq_len + kd->page_size - 1) / kd->page_size)
+    return fail(FP8PA_EINVAL, "bt_stride %lld is smaller than the pages of max_seq_len", (long long)bt_stride);
+  if (!std::isfinite(sm_scale)) return fail(FP8PA_EINVAL, "sm_scale must be finite");
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < (size_t)plan.workspace_bytes)
+      return fail(FP8PA_EWORKSPACE, "workspace of %lld bytes required (%zu given)", (long long)plan.workspace_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(FP8PA_EINVAL, "workspace must be 256-byte aligned");
+  }
+  const int D = kd->head_dim;
+  fp8pa::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = static_cast<uint16_t*>(out);
+  a.kp = k_pool;
+  a.vp = v_pool;
+  a.bt = block_table;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens;
+  a.sinks = sinks;
+  a.kg = geometry(*kd);
+  a.vg = geometry(*vd);
+  a.P = kd->page_size;
+  a.log2P = ilog2(kd->page_size);
+  a.Hq = Hq;
+  a.Hkv = kd->num_kv_heads;
+  a.G = Hq / kd->num_kv_heads;
+  a.window = window > 0 ? window : 0;
+  a.S = plan.num_splits;
+  a.split_tokens = plan.split_tokens;
+  a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
+  if (plan.num_splits > 1) {
+    const int64_t po = (int64_t)B * Hq * plan.num_splits * D * 4;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (po + 255) / 256 * 256);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = fp8pa::launch_decode(a, D, kd->scale_kind, B, st);
+  if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
+  g_cnt.decode_mfma.fetch_add(1);
+  if (plan.num_splits > 1) {
+    fp8pa::MergeArgs m{};
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.sinks = sinks;
+    m.out = a.out;
+    m.Hq = Hq;
+    m.S = plan.num_splits;
+    m.D = D;
+    m.seq_lens = seq_lens;
+    m.window = a.window;
+    m.split_tokens = plan.split_tokens;
+    m.tile_tokens = fp8pa::decode_tile_tokens(D);
+    e = fp8pa::launch_merge(m, B, st);
+    if (e != hipSuccess) return fail(FP8PA_EHIP, "merge launch: %s", hipGetErrorString(e));
+    g_cnt.merge.fetch_add(1);
+    g_cnt.decode_split.fetch_add(1);
+  }
+  g_cnt.decode_calls.fetch_add(1);
+  ok();
+  return FP8PA_OK;
+}
+
+int fp8pa_merge_splits(const float* part_o, const float* part_lse, const float* sinks, void* out, int B, int Hq,
+                       int S, int D, void* stream) {
+  if (B < 0 || Hq < 1 || S < 0) return fail(FP8PA_EINVAL, "bad B/Hq/S");
+  if (D != 64 && D != 128 && D != 256 && D != 512) return fail(FP8PA_EUNSUPPORTED, "D %d not in {64,128,256,512}", D);
+  if (B == 0) {
+    ok();
+    return FP8PA_OK;
+  }
+  if (!out || (S > 0 && (!part_o || !part_lse))) return fail(FP8PA_EINVAL, "a required device pointer is NULL");
+  if (!aligned(out, 4) || (part_o && !aligned(part_o, 4)) || (part_lse && !aligned(part_lse, 4)) ||
+      (sinks && !aligned(sinks, 4)))
+    return fail(FP8PA_EINVAL, "misaligned pointer");
+  fp8pa::MergeArgs m{};
+  m.part_o = part_o;
+  m.part_lse = part_lse;
+  m.sinks = sinks;
+  m.out = static_cast<uint16_t*>(out);
+  m.Hq = Hq;
+  m.S = S;
+  m.D = D;
+  hipError_t e = fp8pa::launch_merge(m, B, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP8PA_EHIP, "merge launch: %s", hipGetErrorString(e));
+  g_cnt.merge.fetch_add(1);
+  ok();
+  return FP8PA_OK;
+}
+
+int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, uint8_t* v_pool,
+                       const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, const int32_t* block_table,
+                       int64_t bt_stride, const int32_t* positions, const int32_t* counts, int B, int T,
+                       void* stream) {
+  if (int rc = check_desc(kd, "kd")) return rc;
+  if (int rc = check_desc(vd, "vd")) return rc;
+  if (vd->num_kv_heads != kd->num_kv_heads || vd->head_dim != kd->head_dim || vd->page_size != kd->page_size)
+    return fail(FP8PA_EUNSUPPORTED, "K and V pools must share num_kv_heads, head_dim and page_size");
+  if (B < 0 || T < 0) return fail(FP8PA_EINVAL, "B and T must be >= 0");
+  if (B == 0 || T == 0) {
+    ok();
+    return FP8PA_OK;
+  }
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !positions)
+    return fail(FP8PA_EINVAL, "a required device pointer is NULL");
+  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_table, 4) || !aligned(positions, 4) || (counts && !aligned(counts, 4)))
+    return fail(FP8PA_EINVAL, "misaligned pointer");
+  if (bt_stride < 1) return fail(FP8PA_EINVAL, "bt_stride must be >= 1");
+  fp8pa::AppendArgs a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.kp = k_pool;
+  a.vp = v_pool;
+  a.kg = geometry(*kd);
+  a.vg = geometry(*vd);
+  a.k_kind = kd->scale_kind;
+  a.v_kind = vd->scale_kind;
+  a.bt = block_table;
+  a.bt_stride = bt_stride;
+  a.positions = positions;
+  a.counts = counts;
+  a.T = T;
+  a.P = kd->page_size;
+  a.Hkv = kd->num_kv_heads;
+  a.D = kd->head_dim;
+  const int max_pages = (T + kd->page_size - 1) / kd->page_size + 1;
+  hipError_t e = fp8pa::launch_append(a, B, max_pages, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP8PA_EHIP, "append launch: %s", hipGetErrorString(e));
+  g_cnt.append.fetch_add(1);
+  ok();
+  return FP8PA_OK;
+}
+
+int fp8pa_debug_dequant(const uint8_t* codes, const void* scales, int scale_kind, int n, float* out,
+                        void* stream) {
+  if (n < 0) return fail(FP8PA_EINVAL, "n must be >= 0");
+  if (scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || scale_kind > FP8PA_SCALE_E8M0_G32)
+    return fail(FP8PA_EINVAL, "unknown scale_kind %d", scale_kind);
+  if (n == 0) {
+    ok();
+    return FP8PA_OK;
+  }
+  if (!codes || !scales || !out) return fail(FP8PA_EINVAL, "a required device pointer is NULL");
+  if (!aligned(out, 4) || (scale_kind != FP8PA_SCALE_E8M0_G32 && !aligned(scales, 4)))
+    return fail(FP8PA_EINVAL, "misaligned pointer");
+  hipError_t e = fp8pa::launch_debug_dequant(codes, scales, scale_kind, n, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP8PA_EHIP, "debug launch: %s", hipGetErrorString(e));
+  g_cnt.debug.fetch_add(1);
+  ok();
+  return FP8PA_OK;
+}
+
+int fp8pa_get_counters(fp8pa_counters* c) {
+  if (!c) return fail(FP8PA_EINVAL, "counters output is NULL");
+  c->decode_calls = g_cnt.decode_calls.load();
+  c->decode_mfma_bf16 = g_cnt.decode_mfma.load();
+  c->decode_split = g_cnt.decode_split.load();
+  c->merge_launches = g_cnt.merge.load();
+  c->append_launches = g_cnt.append.load();
+  c->debug_launches = g_cnt.debug.load();
+  c->errors = g_cnt.errors.load();
+  return FP8PA_OK;
+}
+
+int fp8pa_reset_counters(void) {
+  g_cnt.decode_calls = 0;
+  g_cnt.decode_mfma = 0;
+  g_cnt.decode_split = 0;
+  g_cnt.merge = 0;
+  g_cnt.append = 0;
+  g_cnt.debug = 0;
+  g_cnt.errors = 0;
+  return FP8PA_OK;
+}
+
+}  // extern "C"

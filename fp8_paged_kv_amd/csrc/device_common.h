@@ -1,0 +1,83 @@
+// Device helpers shared by the kernels: E4M3 conversion, E4M3 encoding,
+// vector types and wave64 reductions for gfx950.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Two E4M3 codes (bytes 0-1 of w, or bytes 2-3 when HI) to two packed bf16,
+// each exactly code value x 2**(exponent of `scale`) (the gfx950 scaled
+// conversion reads only the exponent field of its fp32 scale operand, which
+// is the E8M0 scale of the MXFP8 format).  E4M3 values are all exact in bf16.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, scale, HI));
+}
+
+// Eight codes held in two dwords to an MFMA operand of eight bf16 (element i
+// from byte i).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1, float scale) {
+  u32x4 r;
+  r[0] = e4m3x2_to_bf16x2<false>(w0, scale);
+  r[1] = e4m3x2_to_bf16x2<true>(w0, scale);
+  r[2] = e4m3x2_to_bf16x2<false>(w1, scale);
+  r[3] = e4m3x2_to_bf16x2<true>(w1, scale);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// fp32 operand carrying an E8M0 scale byte in its exponent field.
+__device__ __forceinline__ float e8m0_as_scale_operand(uint32_t u) {
+  return __builtin_bit_cast(float, u << 23);
+}
+
+// Exact fp32 value of one E4M3 code (byte 0 of w).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+}
+
+// Nearest E4M3 code of an fp32 value, ties to even, saturating at +-448 (the
+// hardware conversion rounds to nearest even and turns magnitudes >= 464
+// into NaN, so the value is clamped first; the clamp keeps the sign of zero).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  y = fminf(fmaxf(y, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xffu;
+}
+
+// Two fp32 to two packed bf16, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float a) {
+  return (uint16_t)(pack_bf16x2(a, 0.0f) & 0xffffu);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
+}  // namespace fp8pa

@@ -1,0 +1,74 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the HIP
+// kernels.  Not installed; the public interface is include/fp8pa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8pa {
+
+// Byte geometry of one pool, resolved on the host from fp8pa_pool_desc.
+struct PoolGeom {
+  int64_t row_bytes;
+  int32_t head_stride;     // payload bytes between KV heads of a row
+  int32_t tok_stride;      // payload bytes between tokens (heads/tokens layouts)
+  int32_t d_stride;        // payload bytes between dims (1, or P for HEADS_DMAJOR)
+  int32_t sc_off;          // scale footer offset in the row
+  int32_t sc_head_stride;  // footer bytes between heads
+  int32_t sc_tok_stride;   // footer bytes between tokens (0 for per-page scales)
+};
+
+struct DecodeArgs {
+  const uint16_t* q;       // bf16 [B, Hq, D]
+  uint16_t* out;           // bf16 [B, Hq, D]
+  const uint8_t* kp;
+  const uint8_t* vp;
+  const int32_t* bt;       // [B, bt_stride]
+  int64_t bt_stride;
+  const int32_t* seq_lens;
+  const float* sinks;      // [Hq] or null
+  float* part_o;           // [B, Hq, S, D] (S > 1 only)
+  float* part_lse;         // [B, Hq, S]
+  PoolGeom kg, vg;
+  int32_t P, log2P, Hq, Hkv, G, window;
+  int32_t S, split_tokens;
+  float qk_scale;          // sm_scale * log2(e)
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  const float* sinks;
+  uint16_t* out;
+  int32_t Hq, S, D;
+  // When seq_lens is set the per-sequence split count is recomputed exactly
+  // as the decode kernel does, and sequences with at most one split (whose
+  // output the decode kernel wrote itself) are skipped.
+  const int32_t* seq_lens;
+  int32_t window, split_tokens, tile_tokens;
+};
+
+struct AppendArgs {
+  const uint16_t* k_new;   // bf16 [B, T, Hkv, D]
+  const uint16_t* v_new;
+  uint8_t* kp;
+  uint8_t* vp;
+  PoolGeom kg, vg;
+  int32_t k_kind, v_kind;  // FP8PA_SCALE_*
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* positions;
+  const int32_t* counts;   // or null
+  int32_t T, P, Hkv, D;
+};
+
+// Tokens per decode tile (one tile = one MFMA round of one wave).
+inline int decode_tile_tokens(int D) { return D <= 128 ? 64 : 32; }
+
+hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, int B, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, int B, int max_pages, hipStream_t st);
+hipError_t launch_debug_dequant(const uint8_t* codes, const void* scales, int kind, int n,
+                                float* out, hipStream_t st);
+
+}  // namespace fp8pa

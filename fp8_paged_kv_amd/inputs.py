@@ -70,3 +70,28 @@ def block_table(seed, cfg, lens, page_size, spare_frac=0.05, min_rows=0, exclude
         table[b, :n] = rows[at:at + n]
         at += n
     return table, pool_rows
+
+
+def block_table_ranges(seed, cfg, ranges, page_size, spare_frac=0.05, pool_rows=None, tag=0, exclude=None):
+    """Random page table giving rows only to pages [first, end) of each sequence
+    (ranges[b] = (first, end)); other entries are -1.  Returns (table, rows used,
+    pool rows).  Rows come from a random permutation of the pool, skipping
+    ``exclude`` (rows another table of a shared pool already holds)."""
+    ranges = [(int(a), int(e)) for a, e in ranges]
+    need = sum(e - a for a, e in ranges)
+    width = max([e for _, e in ranges] + [1])
+    if pool_rows is None:
+        pool_rows = need + max(1, int(np.ceil(need * spare_frac)))
+    g = generator(seed, cfg, "rows", tag)
+    avail = np.arange(pool_rows, dtype=np.int64)
+    if exclude is not None and len(exclude):
+        avail = np.setdiff1d(avail, np.asarray(exclude, dtype=np.int64), assume_unique=True)
+    if len(avail) < need:
+        raise ValueError("pool too small for the table")
+    rows = g.permutation(avail)[:need]
+    table = np.full((len(ranges), width), -1, dtype=np.int32)
+    at = 0
+    for b, (a, e) in enumerate(ranges):
+        table[b, a:e] = rows[at:at + e - a]
+        at += e - a
+    return table, rows, pool_rows

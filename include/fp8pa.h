@@ -1,0 +1,207 @@
+/*
+ * fp8pa -- paged flash-decode attention over an FP8 (E4M3) KV cache, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "fp8 paged attention for MoE serving", sections
+ * "Smallest correct example", "Expected result" and "Supported scope"): one
+ * decode query token per sequence attends, through a per-sequence block
+ * table, to E4M3 keys and values stored in flat byte pools of packed rows;
+ * values are dequantized as code x scale; query head h reads KV head h / G
+ * (G = Hq / Hkv); an optional window keeps only the last W keys; an optional
+ * per-query-head sink adds one logit to the softmax denominator with no value;
+ * sm_scale replaces head_dim ** -0.5.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named "device" are HIP device pointers; the caller owns every
+ *    buffer (including the workspace).  The library allocates no device
+ *    memory, never synchronizes, and enqueues all work on `stream` (a
+ *    hipStream_t; NULL is the default stream).  Calls are asynchronous.
+ *  - Every entry point validates its host-visible arguments first.  On any
+ *    error it returns a negative status, records a message readable with
+ *    fp8pa_last_error(), and launches nothing.
+ *  - Values that live in device memory (seq_lens, block_table) are trusted:
+ *    they must describe rows inside the pools.  Table entries are read only
+ *    for pages that hold attended (or appended) positions; other entries may
+ *    hold anything, e.g. -1.
+ */
+#ifndef FP8PA_H
+#define FP8PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+enum {
+  FP8PA_OK = 0,
+  FP8PA_EINVAL = -1,        /* a bad argument (null, misaligned, out of range) */
+  FP8PA_EUNSUPPORTED = -2,  /* valid request this build does not implement     */
+  FP8PA_EWORKSPACE = -3,    /* workspace missing or smaller than required      */
+  FP8PA_EHIP = -4           /* a HIP launch reported an error                  */
+};
+
+/* ---- pool row payload layouts (byte offset of the code of KV head h,
+ *      in-page token t, dim d inside a row) --------------------------------
+ * The page names two orders, "tokens" and "heads" ("Supported scope").  The
+ * third keeps each (head, dim) row of a page token-contiguous: the value
+ * operand of the MFMA that contracts over tokens then loads straight from
+ * memory.  The decode kernel reads K in HEADS or TOKENS and V in
+ * HEADS_DMAJOR. */
+enum {
+  FP8PA_LAYOUT_HEADS = 0,        /* [Hkv][P][D]: (h*P + t)*D + d */
+  FP8PA_LAYOUT_TOKENS = 1,       /* [P][Hkv][D]: (t*Hkv + h)*D + d */
+  FP8PA_LAYOUT_HEADS_DMAJOR = 2  /* [Hkv][D][P]: (h*D + d)*P + t */
+};
+
+/* ---- scale kinds.  The scale footer starts at scale_offset inside the row
+ *      (the page's "fp8 payload + fp32 scales per block"); byte offsets from
+ *      there, with slot = t*Hkv + h for the TOKENS layout, else h*P + t:
+ *   F32_PAGE_HEAD   fp32 per (page, head):          4*h
+ *   F32_TOKEN_HEAD  fp32 per (token, head):         4*slot
+ *   E8M0_G32        E8M0 per (token, head, 32 dims along D), the MXFP8 scale
+ *                   of page "Attention MXFP8 TKG Kernel API Reference":
+ *                   slot*(D/32) + d/32.  Value 2**(u-127).                  */
+enum {
+  FP8PA_SCALE_F32_PAGE_HEAD = 0,
+  FP8PA_SCALE_F32_TOKEN_HEAD = 1,
+  FP8PA_SCALE_E8M0_G32 = 2
+};
+
+/* ---- decode variants.  An explicit request is honoured or refused with
+ *      FP8PA_EUNSUPPORTED, never replaced by another variant. */
+enum {
+  FP8PA_VARIANT_AUTO = 0,
+  FP8PA_VARIANT_MFMA_BF16 = 1   /* E4M3 -> bf16 exactly, bf16 MFMA, fp32 accumulate */
+};
+
+/* One pool (K or V) of one layer.  K and V pools may differ in layout and
+ * stride; several layers may share a pool through row_bytes. */
+typedef struct fp8pa_pool_desc {
+  int32_t num_kv_heads;  /* Hkv */
+  int32_t head_dim;      /* D: 64, 128, 256 or 512 */
+  int32_t page_size;     /* P tokens per row: a power of two in [16, 1024] */
+  int32_t layout;        /* FP8PA_LAYOUT_* */
+  int32_t scale_kind;    /* FP8PA_SCALE_* */
+  int32_t reserved;      /* must be 0 */
+  int64_t row_bytes;     /* stride between rows; multiple of 16, >= natural row */
+  int64_t scale_offset;  /* footer offset in the row; multiple of 16, >= P*Hkv*D;
+                            -1 selects the default P*Hkv*D */
+  int64_t num_rows;      /* rows in the pool (host-side sanity only) */
+} fp8pa_pool_desc;
+
+/* Split plan of one decode call (computed on the host from host values only,
+ * so a call can be captured in a HIP graph). */
+typedef struct fp8pa_plan {
+  int32_t num_splits;       /* S: partials per (sequence, query head) */
+  int32_t split_tokens;     /* positions per split */
+  int32_t variant;          /* FP8PA_VARIANT_* that will run */
+  int32_t reserved;
+  int64_t workspace_bytes;  /* needed by fp8pa_decode (0 when S == 1) */
+} fp8pa_plan;
+
+/* Library version string; never NULL. */
+const char* fp8pa_version(void);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* fp8pa_last_error(void);
+
+/* Plan a decode call.  B sequences, Hq query heads, K pool `kd`; every
+ * seq_lens[b] must be <= max_seq_len; window <= 0 means none; num_splits 0
+ * lets the library choose, else it is used as given (>= 1). */
+int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
+                      int window, int num_splits, int variant, fp8pa_plan* out);
+
+/*
+ * Decode attention (the hot path).
+ *   q           device bf16 [B, Hq, D], contiguous, 16-byte aligned.
+ *   out         device bf16 [B, Hq, D], contiguous, 16-byte aligned; written.
+ *   k_pool,
+ *   v_pool      device uint8 pools, 16-byte aligned, described by kd / vd.
+ *               kd: layout HEADS or TOKENS; vd: layout HEADS_DMAJOR.  Both:
+ *               same Hkv, D, P and scale kind.
+ *   block_table device int32 [B, bt_stride]: logical page -> row.
+ *   seq_lens    device int32 [B]: valid positions of each sequence, the token
+ *               being decoded included (append first, then decode); each
+ *               <= max_seq_len.
+ *   window      > 0: attend positions [L - window, L) only; <= 0: all.
+ *   sinks       device fp32 [Hq] sink logits (already in scaled-score units)
+ *               or NULL for none.
+ *   sm_scale    finite score scale (D ** -0.5 is the usual value).
+ *   max_seq_len, num_splits, variant: as for fp8pa_decode_plan.
+ *   workspace   device buffer of >= plan.workspace_bytes (256-byte aligned),
+ *               or NULL when that is 0.  Its contents need no initialisation.
+ * Output rows are bf16 (round to nearest even) of the fp32 result.
+ */
+int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t* v_pool,
+                 const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
+                 const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                 int B, int Hq, int window, const float* sinks, float sm_scale,
+                 int max_seq_len, int num_splits, int variant,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Log-sum-exp merge of split partials (page section "Why it happens": the
+ * grid splits each sequence; the partial results are combined afterwards).
+ *   part_o    device fp32 [B, Hq, S, D]: each split's normalised output.
+ *   part_lse  device fp32 [B, Hq, S]: each split's natural-log sum of
+ *             exp(score); -inf marks an empty split (its part_o is ignored).
+ *   sinks     device fp32 [Hq] or NULL; the sink enters the denominator once.
+ *   out       device bf16 [B, Hq, D].
+ *   D         64, 128, 256 or 512.
+ */
+int fp8pa_merge_splits(const float* part_o, const float* part_lse, const float* sinks,
+                       void* out, int B, int Hq, int S, int D, void* stream);
+
+/*
+ * Quantize and write new K and V tokens into the pools (page section
+ * "Supported scope": per-token-per-head E4M3 with an fp32 scale or sub-row
+ * groups, and a one-launch append).  Sequence b receives tokens
+ * k_new[b, 0:n_b] at positions positions[b] + t, n_b = counts ? counts[b] : T.
+ *   k_new, v_new  device bf16 [B, T, Hkv, D], contiguous.
+ *   kd, vd        any layout; same Hkv, D, P as each other.
+ *   positions     device int32 [B]; counts device int32 [B] or NULL.
+ * Encoding: y = fp32(x / s) correctly rounded, clamped to +-448, rounded to
+ * the nearest E4M3 (ties to even).  Scales:
+ *   F32_TOKEN_HEAD: s = fp32(amax / 448) per (token, head), 1 when amax = 0.
+ *   E8M0_G32: the smallest 2**k with amax <= 448 * 2**k per 32 dims.
+ *   F32_PAGE_HEAD: the page scale only grows: s = max(s_old, fp32(amax_new /
+ *     448)) (1 if that is 0), where s_old is 0 when the call writes the page's
+ *     first slot; if it grows, the page's earlier tokens are re-encoded from
+ *     their fp32 values.  Appends to one page must be ordered in time.
+ * Pages written must be distinct between sequences of one call.
+ */
+int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, uint8_t* v_pool,
+                       const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
+                       const int32_t* block_table, int64_t bt_stride,
+                       const int32_t* positions, const int32_t* counts,
+                       int B, int T, void* stream);
+
+/*
+ * Test hook: dequantize n codes with the device conversion the decode kernel
+ * uses.  scales: device fp32 [n] (F32 kinds) or uint8 E8M0 [n] (E8M0_G32).
+ * out: device fp32 [n].  Exact for all finite codes (E8M0 codes 10..245).
+ */
+int fp8pa_debug_dequant(const uint8_t* codes, const void* scales, int scale_kind, int n,
+                        float* out, void* stream);
+
+/* Launch counters: what actually ran, not what was requested. */
+typedef struct fp8pa_counters {
+  int64_t decode_calls;     /* successful fp8pa_decode calls */
+  int64_t decode_mfma_bf16; /* decode kernels launched, MFMA bf16 variant */
+  int64_t decode_split;     /* calls that used more than one split */
+  int64_t merge_launches;   /* merge kernels launched (decode + merge_splits) */
+  int64_t append_launches;
+  int64_t debug_launches;
+  int64_t errors;           /* calls refused or failed */
+} fp8pa_counters;
+
+int fp8pa_get_counters(fp8pa_counters* out);
+int fp8pa_reset_counters(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8PA_H */

@@ -220,14 +220,20 @@ def append_ref(pool, desc: PoolDesc, block_table, positions, x_new, counts=None)
     return pool
 
 
-def pack_sequences(pool, desc: PoolDesc, block_table, xs):
+def pack_sequences(pool, desc: PoolDesc, block_table, xs, heads=None):
     """Write whole sequences xs[b] ([L_b, H, D] floats) from position 0: one
     append per sequence, so every page scale is the plain amax of its tokens.
-    Vectorised over pages; equal to ``append_ref`` with positions 0 (pinned)."""
+    Vectorised over pages; equal to ``append_ref`` with positions 0 (pinned).
+    ``heads`` restricts the work to some KV heads (the others are not written)."""
     pool = np.array(pool, dtype=np.uint8, copy=True)
     H, P, D = desc.num_kv_heads, desc.page_size, desc.head_dim
+    heads = range(H) if heads is None else heads
+    tt = np.arange(P)[:, None]
+    dd = np.arange(D)[None, :]
     for b, x in enumerate(xs):
-        x = np.asarray(x, dtype=np.float64)
+        if x is None:
+            continue
+        x = np.asarray(x)
         L = x.shape[0]
         if L == 0:
             continue
@@ -235,41 +241,28 @@ def pack_sequences(pool, desc: PoolDesc, block_table, xs):
         rows = np.asarray(block_table[b][:n_pages], dtype=np.int64)
         if (rows < 0).any() or (rows >= desc.num_rows).any():
             raise IndexError("block table entry out of range for a written page")
-        xp = np.zeros((n_pages * P, H, D))
-        xp[:L] = x
-        xp = xp.reshape(n_pages, P, H, D)
         valid = (np.arange(n_pages * P) < L).reshape(n_pages, P)
-        if desc.scale_kind == "page_head":
-            amax = np.abs(xp).max(axis=(1, 3))                                # [n, H]
-            s = fp8.fp32_scale_from_amax(amax)
-            codes = fp8.encode_e4m3(fp8.to_fp32(xp / s[:, None, :, None]))
-            for h in range(H):
-                for i, r in enumerate(rows):
-                    _write_f32(pool, int(r) * desc.row_bytes + scale_offset(desc, h), s[i, h])
-        elif desc.scale_kind == "token_head":
-            amax = np.abs(xp).max(axis=3)                                     # [n, P, H]
-            s = fp8.fp32_scale_from_amax(amax)
-            codes = fp8.encode_e4m3(fp8.to_fp32(xp / s[..., None]))
-            for h in range(H):
-                for t in range(P):
-                    offs = rows * desc.row_bytes + scale_offset(desc, h, t)
-                    keep = valid[:, t]
-                    vals = s[:, t, h].astype(np.float32).view(np.uint8).reshape(-1, 4)
-                    idx = offs[:, None] + np.arange(4)[None, :]
-                    pool[idx[keep]] = vals[keep]
-        else:
-            codes, u = fp8.quantize_e8m0_g32(xp)                              # u [n, P, H, D/32]
-            for h in range(H):
-                for t in range(P):
-                    for g in range(D // 32):
-                        offs = rows * desc.row_bytes + scale_offset(desc, h, t, g)
-                        keep = valid[:, t]
-                        pool[offs[keep]] = u[keep, t, h, g]
-        tt = np.arange(P)[:, None]
-        dd = np.arange(D)[None, :]
-        for h in range(H):
-            off = code_offset(desc, h, tt, dd)                                # [P, D]
-            idx = rows[:, None, None] * desc.row_bytes + off[None]            # [n, P, D]
-            c = codes[:, :, h, :]
-            pool[idx[valid]] = c[valid]
+        for h in heads:
+            xp = np.zeros((n_pages * P, D))
+            xp[:L] = x[:, h, :]
+            xp = xp.reshape(n_pages, P, D)
+            if desc.scale_kind == "page_head":
+                s = fp8.fp32_scale_from_amax(np.abs(xp).max(axis=(1, 2)))             # [n]
+                codes = fp8.encode_e4m3(fp8.to_fp32(xp / s[:, None, None]))
+                at = rows * desc.row_bytes + scale_offset(desc, h)
+                pool[at[:, None] + np.arange(4)[None, :]] = s.astype(np.float32).view(np.uint8).reshape(-1, 4)
+            elif desc.scale_kind == "token_head":
+                s = fp8.fp32_scale_from_amax(np.abs(xp).max(axis=2))                  # [n, P]
+                codes = fp8.encode_e4m3(fp8.to_fp32(xp / s[..., None]))
+                offs = np.array([scale_offset(desc, h, t) for t in range(P)])
+                idx = rows[:, None, None] * desc.row_bytes + offs[None, :, None] + np.arange(4)[None, None, :]
+                vals = s.astype(np.float32).view(np.uint8).reshape(n_pages, P, 4)
+                pool[idx[valid]] = vals[valid]
+            else:
+                codes, u = fp8.quantize_e8m0_g32(xp)                                  # u [n, P, D/32]
+                offs = np.array([[scale_offset(desc, h, t, g) for g in range(D // 32)] for t in range(P)])
+                idx = rows[:, None, None] * desc.row_bytes + offs[None]
+                pool[idx[valid]] = u[valid]
+            idx = rows[:, None, None] * desc.row_bytes + code_offset(desc, h, tt, dd)[None]   # [n, P, D]
+            pool[idx[valid]] = codes[valid]
     return pool

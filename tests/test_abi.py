@@ -1,0 +1,174 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fp8pa.h declares, and refuses bad arguments before launching anything
+(the counters do not move).  Fake device addresses are used: validation never
+dereferences them and every case here fails before a launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_paged_kv_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8pa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ops.lib()
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ops.SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_struct_sizes():
+    assert b"gfx950" in ops.lib().fp8pa_version()
+    assert ctypes.sizeof(ops.PoolDesc) == 48
+    assert ctypes.sizeof(ops.Plan) == 24
+    assert ctypes.sizeof(ops.Counters) == 56
+
+
+def kd(**kw):
+    a = dict(num_kv_heads=8, head_dim=128, page_size=16, layout="heads", scale_kind="page_head",
+             row_bytes=16416, num_rows=100)
+    a.update(kw)
+    return ops.pool_desc(**a)
+
+
+def vd(**kw):
+    kw.setdefault("layout", "heads_dmajor")
+    return kd(**kw)
+
+
+F = 0x10000     # fake 16-byte aligned device address
+
+
+def call_decode(k=None, v=None, **kw):
+    a = dict(q=F, out=F, k_pool=F, v_pool=F, bt=F, bt_stride=512, seq_lens=F, B=2, Hq=32, window=0, sinks=None,
+             sm_scale=0.1, max_seq_len=8192, num_splits=0, variant=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    k = kd() if k is None else k
+    v = vd() if v is None else v
+    P = ctypes.c_void_p
+    return ops.lib().fp8pa_decode(P(a["q"]), P(a["out"]), P(a["k_pool"]), P(a["v_pool"]), ctypes.byref(k),
+                                  ctypes.byref(v), P(a["bt"]), a["bt_stride"], P(a["seq_lens"]), a["B"], a["Hq"],
+                                  a["window"], P(a["sinks"]) if a["sinks"] else None, a["sm_scale"],
+                                  a["max_seq_len"], a["num_splits"], a["variant"],
+                                  P(a["ws"]) if a["ws"] else None, a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(k=kd(head_dim=96), v=vd(head_dim=96)), ops.EUNSUPPORTED),
+    (dict(k=kd(page_size=24)), ops.EUNSUPPORTED),
+    (dict(k=kd(page_size=8)), ops.EUNSUPPORTED),
+    (dict(k=kd(row_bytes=16400)), ops.EINVAL),                  # payload + scales do not fit
+    (dict(k=kd(row_bytes=16424)), ops.EINVAL),                  # not a multiple of 16
+    (dict(k=kd(scale_offset=16392)), ops.EINVAL),               # footer not 16-aligned
+    (dict(k=kd(scale_offset=16000)), ops.EINVAL),               # footer inside the payload
+    (dict(k=kd(layout="heads_dmajor")), ops.EUNSUPPORTED),      # K must be token-major
+    (dict(v=vd(layout="heads")), ops.EUNSUPPORTED),             # V must be d-major
+    (dict(v=vd(num_kv_heads=4, row_bytes=8208)), ops.EUNSUPPORTED),
+    (dict(v=vd(scale_kind="token_head", row_bytes=16384 + 512)), ops.EUNSUPPORTED),
+    (dict(Hq=30), ops.EINVAL),
+    (dict(Hq=8 * 32), ops.EUNSUPPORTED),                        # G = 32
+    (dict(q=0), ops.EINVAL),
+    (dict(seq_lens=0), ops.EINVAL),
+    (dict(q=F + 8), ops.EINVAL),
+    (dict(k_pool=F + 4), ops.EINVAL),
+    (dict(bt_stride=0), ops.EINVAL),
+    (dict(bt_stride=100), ops.EINVAL),                          # fewer than ceil(8192 / 16) entries
+    (dict(sm_scale=float("nan")), ops.EINVAL),
+    (dict(sm_scale=float("inf")), ops.EINVAL),
+    (dict(variant=7), ops.EUNSUPPORTED),
+    (dict(max_seq_len=-1), ops.EINVAL),
+    (dict(num_splits=-2), ops.EINVAL),
+    (dict(num_splits=4), ops.EWORKSPACE),                       # splits need a workspace
+    (dict(num_splits=4, ws=F, ws_bytes=1024), ops.EWORKSPACE),
+    (dict(num_splits=4, ws=F + 16, ws_bytes=1 << 30), ops.EINVAL),   # workspace must be 256-aligned
+])
+def test_decode_refuses_before_launch(case, code):
+    ops.reset_counters()
+    case = dict(case)
+    rc = call_decode(**case)
+    assert rc == code, ops.last_error()
+    assert ops.last_error()
+    c = ops.counters()
+    assert c["decode_calls"] == 0 and c["decode_mfma_bf16"] == 0 and c["merge_launches"] == 0
+    assert c["errors"] == 1
+
+
+def test_reserved_field_must_be_zero():
+    k = kd()
+    k.reserved = 1
+    assert call_decode(k=k) == ops.EINVAL
+
+
+def test_empty_batch_is_a_no_op():
+    ops.reset_counters()
+    assert call_decode(B=0, q=0, out=0) == ops.OK
+    assert ops.counters()["decode_mfma_bf16"] == 0
+
+
+def test_plan_is_host_only_and_sane():
+    k = kd()
+    p = ops.decode_plan(32, 32, k, 8192)
+    assert p.num_splits >= 1 and p.split_tokens % 64 == 0
+    assert p.num_splits * p.split_tokens >= 8192
+    if p.num_splits > 1:
+        assert p.workspace_bytes >= 32 * 32 * p.num_splits * 129 * 4
+    # explicit split counts are honoured (clamped to the tiles available)
+    p1 = ops.decode_plan(32, 32, k, 8192, num_splits=1)
+    assert p1.num_splits == 1 and p1.workspace_bytes == 0 and p1.split_tokens >= 8192 + 63
+    p7 = ops.decode_plan(4, 32, k, 8192, num_splits=7)
+    assert p7.num_splits <= 7 and p7.num_splits * p7.split_tokens >= 8192 + 63
+    # a window bounds the span
+    pw = ops.decode_plan(64, 64, kd(head_dim=64, row_bytes=8224), 32768, window=128)
+    assert pw.num_splits == 1
+    # long context fills the machine
+    pl = ops.decode_plan(4, 64, kd(page_size=128, scale_kind="e8m0_32", row_bytes=135168), 131072)
+    assert pl.num_splits * 4 * 8 >= 512
+    with pytest.raises(ops.Fp8paError):
+        ops.decode_plan(1, 8, kd(head_dim=80), 100)
+
+
+def call_append(**kw):
+    a = dict(k_new=F, v_new=F, k_pool=F, v_pool=F, bt=F, bt_stride=8, positions=F, counts=None, B=2, T=1)
+    a.update(kw)
+    k, v = kw.get("k", kd()), kw.get("v", vd())
+    P = ctypes.c_void_p
+    return ops.lib().fp8pa_append_quant(P(a["k_new"]), P(a["v_new"]), P(a["k_pool"]), P(a["v_pool"]),
+                                        ctypes.byref(k), ctypes.byref(v), P(a["bt"]), a["bt_stride"],
+                                        P(a["positions"]), P(a["counts"]) if a["counts"] else None, a["B"], a["T"],
+                                        None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(k_new=0), ops.EINVAL), (dict(positions=0), ops.EINVAL), (dict(k_new=F + 1), ops.EINVAL),
+    (dict(bt_stride=0), ops.EINVAL), (dict(B=-1), ops.EINVAL),
+    (dict(v=vd(page_size=32, row_bytes=32800)), ops.EUNSUPPORTED),
+    (dict(k=kd(head_dim=48)), ops.EUNSUPPORTED),
+])
+def test_append_refuses_before_launch(case, code):
+    ops.reset_counters()
+    assert call_append(**case) == code
+    assert ops.counters()["append_launches"] == 0
+
+
+def test_merge_and_debug_refuse_before_launch():
+    P = ctypes.c_void_p
+    ops.reset_counters()
+    assert ops.lib().fp8pa_merge_splits(P(F), P(F), None, P(F), 2, 8, 4, 80, None) == ops.EUNSUPPORTED
+    assert ops.lib().fp8pa_merge_splits(None, P(F), None, P(F), 2, 8, 4, 64, None) == ops.EINVAL
+    assert ops.lib().fp8pa_merge_splits(P(F), P(F), None, P(F), 2, 0, 4, 64, None) == ops.EINVAL
+    assert ops.lib().fp8pa_debug_dequant(P(F), P(F), 5, 16, P(F), None) == ops.EINVAL
+    assert ops.lib().fp8pa_debug_dequant(None, P(F), 0, 16, P(F), None) == ops.EINVAL
+    c = ops.counters()
+    assert c["merge_launches"] == 0 and c["debug_launches"] == 0 and c["errors"] == 5

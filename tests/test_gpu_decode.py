@@ -1,0 +1,137 @@
+"""Decode parity on the GPU against the float64 oracle, on problems small
+enough for the oracle yet spanning several tiles and splits with ragged tails,
+plus the edge cases and invariants of the method."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_paged_kv_amd import ops
+from oracle import attention as oatt
+from tests.gpu_util import assert_parity, device_problem, gpu_decode, say, to_np
+from tests.problems import make_problem, permute_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle(p, **kw):
+    a = dict(window=p.window, sinks=p.sinks, sm_scale=p.sm_scale)
+    a.update(kw)
+    return oatt.decode_ref(p.q, p.k_pool, p.v_pool, p.kdesc, p.vdesc, p.table, p.seq_lens, **a)
+
+
+CASES = [
+    # (name, kwargs)
+    ("d64-g4", dict(B=3, Hq=8, Hkv=2, D=64, P=16, lens=[300, 17, 129])),
+    ("d128-g4", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[513, 64, 1])),
+    ("d128-g8-sinks", dict(B=2, Hq=16, Hkv=2, D=128, P=16, lens=[400, 77], sinks=True)),
+    ("d64-g8-window", dict(B=3, Hq=16, Hkv=2, D=64, P=16, lens=[500, 100, 20], window=128, sinks=True)),
+    ("d256-g2-window-scale1", dict(B=2, Hq=4, Hkv=2, D=256, P=32, lens=[700, 33], window=100, sm_scale=1.0)),
+    ("d512-g8-scale1", dict(B=2, Hq=8, Hkv=1, D=512, P=32, lens=[333, 64], sm_scale=1.0)),
+    ("d128-e8m0-p128", dict(B=2, Hq=16, Hkv=2, D=128, P=128, lens=[1000, 130], scale_kind="e8m0_32")),
+    ("d64-token-scale", dict(B=2, Hq=8, Hkv=2, D=64, P=16, lens=[250, 31], scale_kind="token_head")),
+    ("d128-ktokens", dict(B=2, Hq=8, Hkv=2, D=128, P=16, lens=[260, 5], k_layout="tokens")),
+    ("g1-mqa-like", dict(B=2, Hq=2, Hkv=2, D=64, P=16, lens=[90, 3])),
+    ("g16", dict(B=1, Hq=16, Hkv=1, D=64, P=64, lens=[450])),
+    ("wide-rows", dict(B=2, Hq=8, Hkv=2, D=64, P=16, lens=[100, 50], row_pad=4096)),
+    ("d256-e8m0", dict(B=1, Hq=8, Hkv=2, D=256, P=32, lens=[300], scale_kind="e8m0_32", sinks=True)),
+    ("d512-e8m0-window", dict(B=1, Hq=8, Hkv=1, D=512, P=16, lens=[260], scale_kind="e8m0_32", window=40)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("num_splits", [1, 0, 3])
+def test_decode_parity(name, kw, num_splits):
+    say("decode parity", name, "splits", num_splits)
+    p = make_problem(101, **kw)
+    got = to_np(gpu_decode(p, num_splits=num_splits))
+    assert_parity(got, oracle(p), name)
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 15, 16, 17, 63, 64, 65])
+def test_short_and_empty_sequences(L):
+    say("short", L)
+    p = make_problem(102, B=3, Hq=8, Hkv=2, D=128, P=16, lens=[L, 1, 70], sinks=(L % 2 == 1))
+    got = to_np(gpu_decode(p))
+    want = oracle(p)
+    assert_parity(got, want, f"L={L}")
+    if L == 0:
+        assert np.all(got[0] == 0)
+
+
+@pytest.mark.parametrize("W", [1, 15, 16, 17, 63, 64, 65, 299, 300, 301])
+def test_window_boundaries(W):
+    say("window", W)
+    p = make_problem(103, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[300, 40], window=W)
+    assert_parity(to_np(gpu_decode(p)), oracle(p), f"W={W}")
+
+
+def test_zero_scale_is_the_window_mean():
+    p = make_problem(104, B=1, Hq=8, Hkv=2, D=64, P=16, lens=[333], window=77, sm_scale=0.0)
+    assert_parity(to_np(gpu_decode(p)), oracle(p), "mean")
+
+
+def test_poison_outside_attended_positions_never_leaks():
+    """Slots past L, pages before the window and spare rows hold NaN codes and
+    NaN scales; table entries past the last page are -1 or out of range."""
+    p = make_problem(105, B=3, Hq=8, Hkv=2, D=64, P=16, lens=[37, 16, 250], window=50, sinks=True)
+    t = p.table.copy()
+    for b in range(3):
+        used = -(-int(p.seq_lens[b]) // 16)
+        t[b, used:] = 10 ** 8 if b == 0 else -1
+    # pages entirely before the window: point them at garbage rows too
+    t[2, : (250 - 50) // 16] = -7
+    p2 = replace(p, table=t)
+    got = to_np(gpu_decode(p2))
+    assert np.all(np.isfinite(got))
+    assert_parity(got, oracle(p), "poison")
+
+
+def test_invariants_bit_identical():
+    p = make_problem(106, B=3, Hq=16, Hkv=2, D=128, P=16, lens=[700, 130, 9], sinks=True)
+    base = gpu_decode(p).cpu()
+    # run twice: no races, no atomics in the result
+    assert torch.equal(gpu_decode(p).cpu(), base)
+    # physical rows permuted
+    assert torch.equal(gpu_decode(permute_rows(p, 5)).cpu(), base)
+    # window >= L is full attention
+    assert torch.equal(gpu_decode(p, window=700).cpu(), base)
+    assert torch.equal(gpu_decode(p, window=100000).cpu(), base)
+    # sink = -inf is no sink
+    dev = device_problem(p)
+    nos = gpu_decode(p, dev=dev, sinks=None).cpu()
+    neg = gpu_decode(p, dev=dev, sinks=torch.full((16,), -float("inf"), device="cuda:0")).cpu()
+    assert torch.equal(nos, neg)
+
+
+def test_split_counts_agree():
+    p = make_problem(107, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[1500, 700], sinks=True)
+    want = oracle(p)
+    outs = []
+    for s in [1, 2, 5, 8, 0]:
+        o = to_np(gpu_decode(p, num_splits=s))
+        assert_parity(o, want, f"splits={s}")
+        outs.append(o)
+    # different splits only change fp32 summation order
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 2e-2
+
+
+def test_seq_longer_than_the_plan_is_still_complete():
+    """max_seq_len is a contract; the last split absorbs any remainder so the
+    result stays exact even with a short hint."""
+    p = make_problem(108, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[900, 64])
+    assert_parity(to_np(gpu_decode(p, num_splits=2, max_seq_len=900)), oracle(p), "exact")
+
+
+def test_counters_record_what_ran():
+    ops.reset_counters()
+    p = make_problem(109, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[1000, 64])
+    gpu_decode(p, num_splits=4)
+    c = ops.counters()
+    assert c["decode_calls"] == 1 and c["decode_mfma_bf16"] == 1 and c["decode_split"] == 1
+    assert c["merge_launches"] == 1
+    gpu_decode(p, num_splits=1)
+    c = ops.counters()
+    assert c["decode_calls"] == 2 and c["merge_launches"] == 1

@@ -1,0 +1,113 @@
+"""The five workloads at full size, in the launch configuration the benchmark
+times.  Pools are built on the GPU by the append kernel; for sampled
+(sequence, KV head) panels the oracle re-quantizes the same seeded inputs, the
+GPU bytes must equal the oracle's, and the GPU decode output of those panels
+must match the oracle's decode within tolerance.  The tiny workload is checked
+on every panel."""
+import numpy as np
+import pytest
+import torch
+
+from fp8_paged_kv_amd import configs, workloads
+from oracle import attention as oatt, pool as opool
+from tests.gpu_util import assert_parity, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_panel(wl, layer, b, g, seed=configs.SEED):
+    """Host pools holding sequence b, KV head g of the layer, quantized by the oracle."""
+    kd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads", layer.scale_kind, layer.row_bytes, layer.pool_rows)
+    vd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads_dmajor", layer.scale_kind, layer.row_bytes,
+                        layer.pool_rows)
+    L, first = int(layer.lens[b]), int(layer.first_pos[b])
+    n = L - first
+    xk = workloads.raw_kv(seed, wl, layer.layer_index, b, "k", n, layer.Hkv, layer.D)
+    xv = workloads.raw_kv(seed, wl, layer.layer_index, b, "v", n, layer.Hkv, layer.D)
+    hk = np.zeros(layer.pool_rows * layer.row_bytes, np.uint8)
+    hv = np.zeros(layer.pool_rows * layer.row_bytes, np.uint8)
+    tb = layer.table_np
+    if first == 0:
+        xs_k = [None] * len(layer.lens); xs_k[b] = xk
+        xs_v = [None] * len(layer.lens); xs_v[b] = xv
+        hk = opool.pack_sequences(hk, kd, tb, xs_k, heads=[g])
+        hv = opool.pack_sequences(hv, vd, tb, xs_v, heads=[g])
+    else:
+        hk = opool.append_ref(hk, kd, tb[b:b + 1], [first], xk[None])
+        hv = opool.append_ref(hv, vd, tb[b:b + 1], [first], xv[None])
+    return kd, vd, hk, hv
+
+
+def panel_byte_index(desc, rows, g):
+    P, D = desc.page_size, desc.head_dim
+    t = np.arange(P)[:, None]
+    d = np.arange(D)[None, :]
+    code = opool.code_offset(desc, g, t, d).ravel()
+    if desc.scale_kind == "page_head":
+        sc = opool.scale_offset(desc, g) + np.arange(4)
+    elif desc.scale_kind == "token_head":
+        sc = np.array([opool.scale_offset(desc, g, tt) + i for tt in range(P) for i in range(4)])
+    else:
+        sc = np.array([opool.scale_offset(desc, g, tt, gg) for tt in range(P) for gg in range(D // 32)])
+    offs = np.concatenate([code, sc])
+    return (np.asarray(rows, np.int64)[:, None] * desc.row_bytes + offs[None, :]).ravel()
+
+
+def check_panel(wl, layer, out_np, b, g):
+    kd, vd, hk, hv = oracle_panel(wl, layer, b, g)
+    L = int(layer.lens[b])
+    start = max(0, L - layer.window) if layer.window > 0 else 0
+    pages = np.arange(start // layer.P, (L - 1) // layer.P + 1)
+    rows = layer.table_np[b, pages]
+    # bytes of every attended page: codes of the written slots and the scales
+    P = layer.P
+    written = np.zeros((len(pages), P), bool)
+    for i, p in enumerate(pages):
+        lo = max(int(layer.first_pos[b]), p * P)
+        written[i, lo - p * P:min(L, (p + 1) * P) - p * P] = True
+    for desc, host, dev in ((kd, hk, layer.k_pool), (vd, hv, layer.v_pool)):
+        idx = panel_byte_index(desc, rows, g)
+        got = dev[torch.from_numpy(idx).to(dev.device)].cpu().numpy()
+        want = host[idx]
+        # compare only written slots (the tail of the last page is poison on both sides only on the GPU)
+        n_code = P * desc.head_dim
+        per_row = len(idx) // len(rows)
+        gr = got.reshape(len(rows), per_row)
+        wr = want.reshape(len(rows), per_row)
+        tt = np.broadcast_to(np.arange(P)[:, None], (P, desc.head_dim))
+        if desc.layout == "heads_dmajor":
+            tt = np.broadcast_to(np.arange(P)[None, :], (desc.head_dim, P))
+        code_slot = tt.ravel()
+        keep_code = written[:, code_slot]
+        assert np.array_equal(gr[:, :n_code][keep_code], wr[:, :n_code][keep_code]), f"{layer.name} b={b} g={g} codes"
+        if desc.scale_kind == "page_head":
+            assert np.array_equal(gr[:, n_code:], wr[:, n_code:]), f"{layer.name} b={b} g={g} scales"
+        else:
+            per_tok = (per_row - n_code) // P
+            ks = np.repeat(written, per_tok, axis=1)
+            assert np.array_equal(gr[:, n_code:][ks], wr[:, n_code:][ks]), f"{layer.name} b={b} g={g} scales"
+    q = workloads.inputs.normal_bf16(configs.SEED, wl.index, "q", layer.layer_index, (len(layer.lens), layer.Hq, layer.D))
+    want = oatt.decode_ref(q, hk, hv, kd, vd, layer.table_np, layer.lens, window=layer.window,
+                           sinks=layer.sinks_np, sm_scale=layer.sm_scale, seqs=[b], heads=[g])
+    G = layer.Hq // layer.Hkv
+    return assert_parity(out_np[b, g * G:(g + 1) * G], want[b, g * G:(g + 1) * G], f"{layer.name} b={b} g={g}")
+
+
+@pytest.mark.parametrize("wl", configs.ALL, ids=[w.name for w in configs.ALL])
+def test_workload_full_size(wl):
+    say("workload", wl.name)
+    layers = workloads.build_workload(wl)
+    rng = np.random.default_rng(wl.index)
+    for layer in layers:
+        out = workloads.decode_layer(layer)
+        torch.cuda.synchronize()
+        out_np = to_np(out)
+        assert np.all(np.isfinite(out_np)), layer.name
+        if wl is configs.TINY:
+            pairs = [(b, g) for b in range(len(layer.lens)) for g in range(layer.Hkv)]
+        else:
+            pairs = [(int(np.argmax(layer.lens)), int(rng.integers(layer.Hkv))),
+                     (int(rng.integers(len(layer.lens))), int(rng.integers(layer.Hkv)))]
+        for b, g in pairs:
+            err, frac = check_panel(wl, layer, out_np, b, g)
+            say(f"  {layer.name} b={b} L={int(layer.lens[b])} g={g}: max err {err:.2e} ({frac:.2f} of bound)")
