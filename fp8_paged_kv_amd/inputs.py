@@ -72,14 +72,15 @@ def block_table(seed, cfg, lens, page_size, spare_frac=0.05, min_rows=0, exclude
     return table, pool_rows
 
 
-def block_table_ranges(seed, cfg, ranges, page_size, spare_frac=0.05, pool_rows=None, tag=0, exclude=None):
+def block_table_ranges(seed, cfg, ranges, page_size, spare_frac=0.05, pool_rows=None, tag=0, exclude=None,
+                       width=None):
     """Random page table giving rows only to pages [first, end) of each sequence
     (ranges[b] = (first, end)); other entries are -1.  Returns (table, rows used,
     pool rows).  Rows come from a random permutation of the pool, skipping
     ``exclude`` (rows another table of a shared pool already holds)."""
     ranges = [(int(a), int(e)) for a, e in ranges]
     need = sum(e - a for a, e in ranges)
-    width = max([e for _, e in ranges] + [1])
+    width = max([e for _, e in ranges] + [1] + ([width] if width else []))
     if pool_rows is None:
         pool_rows = need + max(1, int(np.ceil(need * spare_frac)))
     g = generator(seed, cfg, "rows", tag)

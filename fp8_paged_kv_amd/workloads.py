@@ -72,18 +72,19 @@ def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", lay
     for li, lay in enumerate(wl.layers):
         ranges[li] = [(first_attended_page(int(L), lay.window, P), -(-int(L) // P)) for L in lens]
     tables = {}
+    width = -(-int(wl.L_hi) // P)        # table width covers the longest sequence the workload allows
     if wl.shared_pool:
         need = sum(e - a for li in range(len(wl.layers)) for a, e in ranges[li])
         pool_rows = need + max(1, int(np.ceil(need * 0.05)))
         taken = np.zeros(0, dtype=np.int64)
         for li in range(len(wl.layers)):
             t, rows, _ = inputs.block_table_ranges(seed, wl.index, ranges[li], P, pool_rows=pool_rows, tag=li,
-                                                   exclude=taken)
+                                                   exclude=taken, width=width)
             taken = np.concatenate([taken, rows])
             tables[li] = (t, pool_rows)
     else:
         for li in range(len(wl.layers)):
-            t, _, pool_rows = inputs.block_table_ranges(seed, wl.index, ranges[li], P, tag=li)
+            t, _, pool_rows = inputs.block_table_ranges(seed, wl.index, ranges[li], P, tag=li, width=width)
             tables[li] = (t, pool_rows)
     sinks_np = inputs.sinks(seed, wl.index, wl.layers[0].Hq) if wl.sinks else None
     shared = {}

@@ -69,15 +69,13 @@ def check_panel(wl, layer, out_np, b, g):
         idx = panel_byte_index(desc, rows, g)
         got = dev[torch.from_numpy(idx).to(dev.device)].cpu().numpy()
         want = host[idx]
-        # compare only written slots (the tail of the last page is poison on both sides only on the GPU)
+        # compare written slots only: the GPU pool keeps poison in the unwritten tail of the last page
         n_code = P * desc.head_dim
         per_row = len(idx) // len(rows)
         gr = got.reshape(len(rows), per_row)
         wr = want.reshape(len(rows), per_row)
-        tt = np.broadcast_to(np.arange(P)[:, None], (P, desc.head_dim))
-        if desc.layout == "heads_dmajor":
-            tt = np.broadcast_to(np.arange(P)[None, :], (desc.head_dim, P))
-        code_slot = tt.ravel()
+        # panel_byte_index lists codes in (slot, dim) order for every layout
+        code_slot = np.broadcast_to(np.arange(P)[:, None], (P, desc.head_dim)).ravel()
         keep_code = written[:, code_slot]
         assert np.array_equal(gr[:, :n_code][keep_code], wr[:, :n_code][keep_code]), f"{layer.name} b={b} g={g} codes"
         if desc.scale_kind == "page_head":
