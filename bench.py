@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Decode benchmark: KV-read HBM GB/s (and % of the MI355X 8 TB/s peak) plus µs
+per decode call, on seeded synthetic workloads resident in HBM.
+
+Default workload: the Llama-3-8B-shaped decode (B=32, Hq=32, Hkv=8, D=128,
+page 16, seq_lens U[1024, 8192], E4M3 K/V with fp32 per-(page, head) scales,
+full attention).  One step = one decode call over the batch (plan, decode
+kernel, split merge).  Pools are built once by the library's append kernel;
+several copies are rotated so that consecutive steps never read a pool that
+could still sit in the 256 MB last-level cache.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--sweep] [--no-cpu-baseline] [--copy-probe]
+Prints one JSON line (rank 0, N=1).
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV-read HBM GB/s (% of MI355X peak) + µs per decode call, batch×context sweep"
+PEAK_GBPS = 8000.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "decode_llama3-8b-decode_pmc.json")
+KERNEL_SOURCES = ["fp8_paged_kv_amd/csrc/decode.hip", "fp8_paged_kv_amd/csrc/device_common.h",
+                  "fp8_paged_kv_amd/csrc/fp8pa_internal.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3-8b-decode")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough for 2 GiB)")
+    ap.add_argument("--sweep", action="store_true", help="batch x context sweep (CSV on stderr, JSON per point)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
+    ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB copy (PMC scale reference)")
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent API of the HIP runtime torch already loaded (one runtime per process)."""
+
+    def __init__(self):
+        path = None
+        for m in re.findall(r"/\S*libamdhip64\.so\S*", open("/proc/self/maps").read()):
+            path = m
+            break
+        self.lib = ctypes.CDLL(path or "libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(ctypes.c_void_p(b))
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per decode launch from the committed rocprofv3 PMC summary, if
+    it was taken on the current kernel sources; else None."""
+    try:
+        rec = json.load(open(PROFILE_PMC))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest() or rec.get("workload") != workload:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, num_splits):
+    """Runs `steps` timed steps; a step decodes every layer once (copy k % R).
+    Returns wall seconds, per-step GPU ms, and per-layer decode-kernel ms."""
+    R = len(layers_copies)
+    nl = len(layers_copies[0])
+    outs = [torch.empty_like(l.q) for l in layers_copies[0]]
+    ws = []
+    for l in layers_copies[0]:
+        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, num_splits)
+        ws.append(torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0"))
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(k, kev=None):
+        layers = layers_copies[k % R]
+        for j, l in enumerate(layers):
+            if kev is not None:
+                ops.set_decode_events(kev[2 * j], kev[2 * j + 1])
+            workloads.decode_layer(l, out=outs[j], workspace=ws[j], num_splits=num_splits)
+        ops.set_decode_events(None, None)
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    step_ev = hip.events(steps + 1)
+    kern_ev = [hip.events(2 * nl) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        hip.record(step_ev[k], stream)
+        step(k, kern_ev[k])
+    hip.record(step_ev[steps], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [hip.elapsed_ms(step_ev[k], step_ev[k + 1]) for k in range(steps)]
+    kern_ms = [[hip.elapsed_ms(kern_ev[k][2 * j], kern_ev[k][2 * j + 1]) for k in range(steps)] for j in range(nl)]
+    hip.destroy(step_ev)
+    for e in kern_ev:
+        hip.destroy(e)
+    return wall, step_ms, kern_ms, outs
+
+
+def clone_layer(l, torch):
+    import dataclasses
+    return dataclasses.replace(l, k_pool=l.k_pool.clone(), v_pool=l.v_pool.clone())
+
+
+def cpu_baseline(wl, layers, budget_s):
+    """The oracle (float64 numpy, one BLAS thread) timed on a bounded sample of
+    the same workload: whole sequences of the first layer, oracle-quantized
+    from the same seeded inputs, until about `budget_s` seconds of decode_ref."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from fp8_paged_kv_amd import configs, inputs, workloads
+    from oracle import attention as oatt, pool as opool
+
+    lay = layers[0]
+    kd = opool.PoolDesc(lay.Hkv, lay.D, lay.P, "heads", lay.scale_kind, lay.row_bytes, lay.pool_rows)
+    vd = opool.PoolDesc(lay.Hkv, lay.D, lay.P, "heads_dmajor", lay.scale_kind, lay.row_bytes, lay.pool_rows)
+    q = inputs.normal_bf16(configs.SEED, wl.index, "q", lay.layer_index, (len(lay.lens), lay.Hq, lay.D))
+    spent, nbytes, seqs = 0.0, 0, 0
+    with threadpool_limits(1):
+        for b in range(len(lay.lens)):
+            if spent >= budget_s:
+                break
+            L, first = int(lay.lens[b]), int(lay.first_pos[b])
+            xk = workloads.raw_kv(configs.SEED, wl, lay.layer_index, b, "k", L - first, lay.Hkv, lay.D)
+            xv = workloads.raw_kv(configs.SEED, wl, lay.layer_index, b, "v", L - first, lay.Hkv, lay.D)
+            hk = np.zeros(lay.pool_rows * lay.row_bytes, np.uint8)
+            hv = np.zeros(lay.pool_rows * lay.row_bytes, np.uint8)
+            if first == 0:
+                xs = [None] * len(lay.lens)
+                xs[b] = xk
+                hk = opool.pack_sequences(hk, kd, lay.table_np, xs)
+                xs[b] = xv
+                hv = opool.pack_sequences(hv, vd, lay.table_np, xs)
+            else:
+                hk = opool.append_ref(hk, kd, lay.table_np[b:b + 1], [first], xk[None])
+                hv = opool.append_ref(hv, vd, lay.table_np[b:b + 1], [first], xv[None])
+            t0 = time.perf_counter()
+            oatt.decode_ref(q, hk, hv, kd, vd, lay.table_np, lay.lens, window=lay.window, sinks=lay.sinks_np,
+                            sm_scale=lay.sm_scale, seqs=[b])
+            spent += time.perf_counter() - t0
+            start = max(0, L - lay.window) if lay.window > 0 else 0
+            n = L - start
+            sc = (2 * 4 * ((L - 1) // lay.P - start // lay.P + 1) * lay.Hkv if lay.scale_kind == "page_head"
+                  else 2 * n * (lay.D // 32) * lay.Hkv)
+            nbytes += 2 * n * lay.D * lay.Hkv + sc
+            seqs += 1
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{seqs} of {len(lay.lens)} sequences of {lay.name} (all KV heads), float64 numpy, "
+                      f"{spent:.1f} s of decode_ref, quantisation excluded",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def run_sweep(args, torch, ops, workloads, hip):
+    """C2 geometry at fixed L for B x L points; pools built on the GPU from a
+    seeded torch generator (timing only: content does not change the work)."""
+    import numpy as np
+    D, Hq, Hkv, P = 128, 32, 8, 16
+    rb = 16416
+    gen = torch.Generator(device="cuda:0")
+    print("B,L,us_per_call_median,kv_gbps,pct_peak", file=sys.stderr)
+    for L in (128, 1024, 4096, 16384, 32000, 131072):
+        for B in (1, 8, 32, 128):
+            pages = -(-L // P)
+            rows = B * pages
+            if rows * rb * 2 > 60e9:
+                continue
+            gen.manual_seed(L * 1000 + B)
+            k_pool = torch.full((rows * rb,), 0xFF, dtype=torch.uint8, device="cuda:0")
+            v_pool = torch.full((rows * rb,), 0xFF, dtype=torch.uint8, device="cuda:0")
+            kd = ops.pool_desc(Hkv, D, P, "heads", "page_head", rb, rows)
+            vd = ops.pool_desc(Hkv, D, P, "heads_dmajor", "page_head", rb, rows)
+            perm = torch.randperm(rows, generator=gen, device="cuda:0").to(torch.int32)
+            table = perm.view(B, pages).contiguous()
+            for b in range(B):
+                x = torch.randn((1, L, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+                y = torch.randn((1, L, Hkv, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+                ops.append_quant(x, y, k_pool, v_pool, kd, vd, table[b:b + 1],
+                                 torch.zeros(1, dtype=torch.int32, device="cuda:0"))
+            q = torch.randn((B, Hq, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+            lens = torch.full((B,), L, dtype=torch.int32, device="cuda:0")
+            layer = workloads.DeviceLayer(
+                name=f"sweep-B{B}-L{L}", Hq=Hq, Hkv=Hkv, D=D, P=P, window=0, sm_scale=D ** -0.5,
+                scale_kind="page_head", row_bytes=rb, pool_rows=rows, kd=kd, vd=vd, k_pool=k_pool, v_pool=v_pool,
+                block_table=table, table_np=None, seq_lens=lens, lens=np.full(B, L), first_pos=np.zeros(B),
+                q=q, sinks=None, sinks_np=None, max_seq_len=L)
+            nbytes = workloads.kv_bytes(layer)
+            R = max(1, min(8, int(np.ceil(2 * 2 ** 30 / (2 * rows * rb)))))
+            copies = [[layer]] + [[clone_layer(layer, torch)] for _ in range(R - 1)]
+            steps = max(20, min(args.steps, 200))
+            wall, step_ms, kern_ms, _ = time_layers(copies, steps, 5, hip, ops, workloads, torch, args.num_splits)
+            med = statistics.median(step_ms) * 1e3
+            gbps = nbytes / (statistics.median(kern_ms[0]) * 1e-3) / 1e9
+            print(f"{B},{L},{med:.2f},{gbps:.1f},{100 * gbps / PEAK_GBPS:.1f}", file=sys.stderr, flush=True)
+            print(json.dumps({"sweep_point": {"B": B, "L": L, "us_per_call_median": round(med, 2),
+                                              "kernel_gbps_median": round(gbps, 1),
+                                              "pct_peak": round(100 * gbps / PEAK_GBPS, 1)}}), flush=True)
+            del copies, layer, k_pool, v_pool
+            torch.cuda.empty_cache()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; the decode path shards by sequence or KV head with no "
+              "exchange, which needs no multi-GPU run to measure (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from fp8_paged_kv_amd import configs, ops, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ops.lib()
+    hip = Hip()
+    if args.sweep:
+        run_sweep(args, torch, ops, workloads, hip)
+        return
+    wl = {w.name: w for w in configs.ALL}[args.workload]
+    t_build = time.perf_counter()
+    layers = workloads.build_workload(wl)
+    build_s = time.perf_counter() - t_build
+    per_copy = sum(2 * l.k_pool.numel() for l in layers) if not wl.shared_pool else 2 * layers[0].k_pool.numel()
+    R = args.copies or max(2, min(16, int(np.ceil(2 * 2 ** 30 / per_copy))))
+    copies = [layers]
+    for _ in range(R - 1):
+        if wl.shared_pool:
+            import dataclasses
+            k2, v2 = layers[0].k_pool.clone(), layers[0].v_pool.clone()
+            copies.append([dataclasses.replace(l, k_pool=k2, v_pool=v2) for l in layers])
+        else:
+            copies.append([clone_layer(l, torch) for l in layers])
+    torch.cuda.synchronize()
+    # Copies hold identical bytes: every copy must give the same output bit for bit.
+    ref = [workloads.decode_layer(l).clone() for l in copies[0]]
+    for c in copies[1:]:
+        for j, l in enumerate(c):
+            assert torch.equal(workloads.decode_layer(l), ref[j]), "pool copies disagree"
+    torch.cuda.synchronize()
+
+    wall, step_ms, kern_ms, _ = time_layers(copies, args.steps, args.warmup, hip, ops, workloads, torch,
+                                            args.num_splits)
+    layer_bytes = [workloads.kv_bytes(l) for l in layers]
+    total_bytes = sum(layer_bytes)
+    ms_per_step = wall * 1e3 / args.steps
+    value = total_bytes / (wall / args.steps) / 1e9
+    dom = int(np.argmax(layer_bytes))
+    kern_avg_ms = statistics.mean(kern_ms[dom])
+    achieved = layer_bytes[dom] / (kern_avg_ms * 1e-3) / 1e9
+    traffic = stored_traffic(wl.name)
+    us = sorted(x * 1e3 for x in step_ms)
+    pct = lambda p: us[min(len(us) - 1, int(p * len(us)))]
+    plans = [ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, args.num_splits) for l in layers]
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "B": wl.B, "page": wl.P, "seq_lens": f"U[{wl.L_lo},{wl.L_hi}]",
+            "kv": "e4m3", "scales": wl.scale_kind,
+            "layers": [{"name": l.name, "Hq": l.Hq, "Hkv": l.Hkv, "D": l.D, "window": l.window,
+                        "sm_scale": round(l.sm_scale, 6), "kv_bytes": b, "splits": p.num_splits,
+                        "split_tokens": p.split_tokens, "kernel_us_mean": round(statistics.mean(km) * 1e3, 2),
+                        "kernel_gbps": round(b / (statistics.mean(km) * 1e-3) / 1e9, 1)}
+                       for l, b, p, km in zip(layers, layer_bytes, plans, kern_ms)],
+            "kv_bytes_per_step": total_bytes, "pool_copies_rotated": R, "parallelism": "single GPU",
+        },
+        "us_per_call": {"median": round(pct(0.5), 2), "p10": round(pct(0.1), 2), "p90": round(pct(0.9), 2),
+                        "note": "GPU time per step between hipEvents, decode kernel + split merge"},
+        "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": f"decode_kernel D={layers[dom].D} ({layers[dom].name})",
+                     "kernel_us_mean": round(kern_avg_ms * 1e3, 2), "bytes_per_launch": layer_bytes[dom]},
+        "build_s": round(build_s, 1),
+    }
+    if args.copy_probe:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        rec["copy_probe_bytes"] = n
+    rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, layers, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

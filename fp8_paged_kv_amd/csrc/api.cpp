@@ -18,6 +18,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 struct Counters {
   std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0},
@@ -251,8 +252,13 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (po + 255) / 256 * 256);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = fp8pa::launch_decode(a, D, kd->scale_kind, B, st);
+  hipError_t e = hipSuccess;
+  if (g_ev_start && (e = hipEventRecord(g_ev_start, st)) != hipSuccess)
+    return fail(FP8PA_EHIP, "event record: %s", hipGetErrorString(e));
+  e = fp8pa::launch_decode(a, D, kd->scale_kind, B, st);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
+  if (g_ev_stop && (e = hipEventRecord(g_ev_stop, st)) != hipSuccess)
+    return fail(FP8PA_EHIP, "event record: %s", hipGetErrorString(e));
   g_cnt.decode_mfma.fetch_add(1);
   if (plan.num_splits > 1) {
     fp8pa::MergeArgs m{};
@@ -376,6 +382,14 @@ int fp8pa_get_counters(fp8pa_counters* c) {
   c->append_launches = g_cnt.append.load();
   c->debug_launches = g_cnt.debug.load();
   c->errors = g_cnt.errors.load();
+  return FP8PA_OK;
+}
+
+int fp8pa_set_decode_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return fail(FP8PA_EINVAL, "set both events or neither");
+  g_ev_start = static_cast<hipEvent_t>(start);
+  g_ev_stop = static_cast<hipEvent_t>(stop);
+  ok();
   return FP8PA_OK;
 }
 

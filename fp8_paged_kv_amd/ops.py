@@ -53,6 +53,7 @@ SIGNATURES = {
     "fp8pa_debug_dequant": ([_P, _P, _I, _I, _P, _P], _I),
     "fp8pa_get_counters": ([ctypes.POINTER(Counters)], _I),
     "fp8pa_reset_counters": ([], _I),
+    "fp8pa_set_decode_events": ([_P, _P], _I),
 }
 
 
@@ -178,3 +179,9 @@ def counters():
 
 def reset_counters():
     lib().fp8pa_reset_counters()
+
+
+def set_decode_events(start, stop):
+    """Raw hipEvent_t handles (ints) that bracket the next decode kernels; None clears."""
+    _check(lib().fp8pa_set_decode_events(None if start is None else ctypes.c_void_p(start),
+                                         None if stop is None else ctypes.c_void_p(stop)))

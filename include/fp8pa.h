@@ -201,6 +201,12 @@ typedef struct fp8pa_counters {
 int fp8pa_get_counters(fp8pa_counters* out);
 int fp8pa_reset_counters(void);
 
+/* Profiling hook (calling thread only): while set, every fp8pa_decode records
+ * `start` on its stream just before the decode kernel and `stop` just after
+ * it, before any merge kernel, so the pair times the decode kernel alone.
+ * Both are hipEvent_t created by the caller; pass NULL, NULL to clear. */
+int fp8pa_set_decode_events(void* start, void* stop);
+
 #ifdef __cplusplus
 }
 #endif
