@@ -12,7 +12,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "../../include/fp8pa.h"
+#include "fp8pa.h"
 #include "fp8pa_internal.h"
 
 namespace {
@@ -25,6 +25,7 @@ struct Counters {
       errors{0};
 };
 Counters g_cnt;
+std::atomic<uint32_t> g_epoch{0};
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -67,7 +68,7 @@ int check_desc(const fp8pa_pool_desc* d, const char* name) {
     return fail(FP8PA_EUNSUPPORTED, "%s: head_dim %d not in {64,128,256,512}", name, d->head_dim);
   if (!pow2(d->page_size) || d->page_size < 16 || d->page_size > 1024)
     return fail(FP8PA_EUNSUPPORTED, "%s: page_size %d is not a power of two in [16,1024]", name, d->page_size);
-  if (d->layout < FP8PA_LAYOUT_HEADS || d->layout > FP8PA_LAYOUT_HEADS_DMAJOR)
+  if (d->layout < FP8PA_LAYOUT_HEADS || d->layout > FP8PA_LAYOUT_HEADS_D64)
     return fail(FP8PA_EINVAL, "%s: unknown layout %d", name, d->layout);
   if (d->scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || d->scale_kind > FP8PA_SCALE_E8M0_G32)
     return fail(FP8PA_EINVAL, "%s: unknown scale_kind %d", name, d->scale_kind);
@@ -94,10 +95,24 @@ fp8pa::PoolGeom geometry(const fp8pa_pool_desc& d) {
   g.row_bytes = d.row_bytes;
   g.sc_off = (int32_t)footer_offset(d);
   const bool tok = d.layout == FP8PA_LAYOUT_TOKENS;
+  g.tblk = P;
+  g.tblk_stride = 0;
+  g.d_stride = 1;
+  g.dchunk_stride = 64;
   switch (d.layout) {
-    case FP8PA_LAYOUT_HEADS: g.head_stride = P * D; g.tok_stride = D; g.d_stride = 1; break;
-    case FP8PA_LAYOUT_TOKENS: g.head_stride = D; g.tok_stride = H * D; g.d_stride = 1; break;
-    default: g.head_stride = D * P; g.tok_stride = 1; g.d_stride = P; break;
+    case FP8PA_LAYOUT_HEADS: g.head_stride = P * D; g.tok_stride = D; break;
+    case FP8PA_LAYOUT_TOKENS: g.head_stride = D; g.tok_stride = H * D; break;
+    case FP8PA_LAYOUT_HEADS_D64: g.head_stride = P * D; g.tok_stride = 64; g.dchunk_stride = 64 * P; break;
+    default: {
+      const int W = P < 64 ? P : 64;
+      g.head_stride = P * D;
+      g.tblk = W;
+      g.tblk_stride = D * W;
+      g.tok_stride = 1;
+      g.dchunk_stride = 64 * W;
+      g.d_stride = W;
+      break;
+    }
   }
   switch (d.scale_kind) {
     case FP8PA_SCALE_F32_PAGE_HEAD: g.sc_head_stride = 4; g.sc_tok_stride = 0; break;
@@ -113,10 +128,28 @@ fp8pa::PoolGeom geometry(const fp8pa_pool_desc& d) {
   return g;
 }
 
+int tile_variant() {
+  static int cached = -1;
+  if (cached < 0) {
+    const char* e = getenv("FP8PA_TILE_VARIANT");
+    cached = e ? atoi(e) : 0;
+  }
+  return cached;
+}
+
+int fused_merge() {
+  static int cached = -1;
+  if (cached < 0) {
+    const char* e = getenv("FP8PA_FUSED_MERGE");
+    cached = e ? (atoi(e) != 0) : 0;
+  }
+  return cached;
+}
+
 int target_workgroups() {
   static int cached = 0;
   if (cached) return cached;
-  int t = 1024;   // four per CU on a 256-CU part
+  int t = 2048;   // eight per CU on a 256-CU part (measured: evens out uneven sequence lengths)
   if (const char* e = getenv("FP8PA_TARGET_WORKGROUPS")) {
     const int v = atoi(e);
     if (v > 0) t = v;
@@ -140,7 +173,7 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   const int D = kd->head_dim;
   if ((int64_t)2 * G * (D + 4) * 4 > 65536)
     return fail(FP8PA_EUNSUPPORTED, "G=%d with head_dim %d exceeds the 64 KiB combine buffer", G, D);
-  const int TT = fp8pa::decode_tile_tokens(D);
+  const int TT = fp8pa::decode_tile_tokens(D, tile_variant());
   const int64_t span = (window > 0 && window < max_seq_len) ? window : max_seq_len;
   // Tiles a range of `span` positions may touch once aligned down to a tile.
   const int64_t ntile = span > 0 ? (span - 1) / TT + 2 : 1;
@@ -156,9 +189,16 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
     if (S < 1) S = 1;
     tps = (ntile + S - 1) / S;
     tps = (tps + 3) / 4 * 4;
+    if (tps * TT > fp8pa::kMaxSplitTokens) tps = fp8pa::kMaxSplitTokens / TT;
   }
   S = (ntile + tps - 1) / tps;
   if (S < 1) S = 1;
+  if ((int64_t)G * S * 4 > 65536)
+    return fail(FP8PA_EUNSUPPORTED, "%lld splits of %d query heads exceed the 64 KiB merge buffer", (long long)S, G);
+  // A workgroup stages the block-table rows of its split in LDS.
+  if ((tps * TT / kd->page_size + 2) * 4 > 65536)
+    return fail(FP8PA_EUNSUPPORTED, "a split of %lld positions needs more than 64 KiB of staged block table; "
+                "request more splits", (long long)(tps * TT));
   out->num_splits = (int32_t)S;
   out->split_tokens = (int32_t)(tps * TT);
   out->variant = FP8PA_VARIANT_MFMA_BF16;
@@ -166,7 +206,8 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   if (S > 1) {
     const int64_t po = (int64_t)B * Hq * S * D * 4;
     const int64_t pl = (int64_t)B * Hq * S * 4;
-    out->workspace_bytes = (po + 255) / 256 * 256 + (pl + 255) / 256 * 256;
+    const int64_t pc = (int64_t)B * kd->num_kv_heads * 8;
+    out->workspace_bytes = (po + 255) / 256 * 256 + (pl + 255) / 256 * 256 + (pc + 255) / 256 * 256;
   } else {
     out->workspace_bytes = 0;
   }
@@ -198,7 +239,7 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   if (int rc = make_plan(B, Hq, kd, max_seq_len, window, num_splits, variant, &plan)) return rc;
   if (int rc = check_desc(vd, "vd")) return rc;
   if (kd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
-    return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS or TOKENS layout");
+    return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS_D64, HEADS or TOKENS layout");
   if (vd->layout != FP8PA_LAYOUT_HEADS_DMAJOR)
     return fail(FP8PA_EUNSUPPORTED, "vd: decode reads V in the HEADS_DMAJOR layout");
   if (vd->num_kv_heads != kd->num_kv_heads || vd->head_dim != kd->head_dim || vd->page_size != kd->page_size ||
@@ -239,6 +280,7 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   a.vg = geometry(*vd);
   a.P = kd->page_size;
   a.log2P = ilog2(kd->page_size);
+  a.B = B;
   a.Hq = Hq;
   a.Hkv = kd->num_kv_heads;
   a.G = Hq / kd->num_kv_heads;
@@ -246,37 +288,45 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   a.S = plan.num_splits;
   a.split_tokens = plan.split_tokens;
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
+  a.max_staged = (int32_t)((int64_t)plan.split_tokens / kd->page_size + 2);
+  a.tile_variant = tile_variant();
+  a.fused_merge = fused_merge();
+  a.epoch = g_epoch.fetch_add(1) + 1;
   if (plan.num_splits > 1) {
     const int64_t po = (int64_t)B * Hq * plan.num_splits * D * 4;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (po + 255) / 256 * 256);
+    const int64_t pl = (int64_t)B * Hq * plan.num_splits * 4;
+    char* w = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(w);
+    a.part_lse = reinterpret_cast<float*>(w + (po + 255) / 256 * 256);
+    a.counters = reinterpret_cast<unsigned long long*>(w + (po + 255) / 256 * 256 + (pl + 255) / 256 * 256);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (g_ev_start && (e = hipEventRecord(g_ev_start, st)) != hipSuccess)
-    return fail(FP8PA_EHIP, "event record: %s", hipGetErrorString(e));
-  e = fp8pa::launch_decode(a, D, kd->scale_kind, B, st);
+  // A wave's 16-byte K loads cover 64 bytes of each of 16 tokens: whole lines
+  // when the 64-byte pieces of consecutive tokens are adjacent.
+  const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
+  hipError_t e = fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, B, st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
-  if (g_ev_stop && (e = hipEventRecord(g_ev_stop, st)) != hipSuccess)
-    return fail(FP8PA_EHIP, "event record: %s", hipGetErrorString(e));
   g_cnt.decode_mfma.fetch_add(1);
   if (plan.num_splits > 1) {
-    fp8pa::MergeArgs m{};
-    m.part_o = a.part_o;
-    m.part_lse = a.part_lse;
-    m.sinks = sinks;
-    m.out = a.out;
-    m.Hq = Hq;
-    m.S = plan.num_splits;
-    m.D = D;
-    m.seq_lens = seq_lens;
-    m.window = a.window;
-    m.split_tokens = plan.split_tokens;
-    m.tile_tokens = fp8pa::decode_tile_tokens(D);
-    e = fp8pa::launch_merge(m, B, st);
-    if (e != hipSuccess) return fail(FP8PA_EHIP, "merge launch: %s", hipGetErrorString(e));
-    g_cnt.merge.fetch_add(1);
     g_cnt.decode_split.fetch_add(1);
+    if (!a.fused_merge) {
+      fp8pa::MergeArgs m{};
+      m.part_o = a.part_o;
+      m.part_lse = a.part_lse;
+      m.sinks = sinks;
+      m.out = a.out;
+      m.Hq = Hq;
+      m.S = plan.num_splits;
+      m.D = D;
+      m.seq_lens = seq_lens;
+      m.window = a.window;
+      m.split_tokens = plan.split_tokens;
+      m.tile_tokens = fp8pa::decode_tile_tokens(D, a.tile_variant);
+      m.G = a.G;
+      e = fp8pa::launch_merge(m, B, st);
+      if (e != hipSuccess) return fail(FP8PA_EHIP, "merge launch: %s", hipGetErrorString(e));
+      g_cnt.merge.fetch_add(1);
+    }
   }
   g_cnt.decode_calls.fetch_add(1);
   ok();
@@ -303,6 +353,7 @@ int fp8pa_merge_splits(const float* part_o, const float* part_lse, const float* 
   m.Hq = Hq;
   m.S = S;
   m.D = D;
+  m.G = 1;
   hipError_t e = fp8pa::launch_merge(m, B, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8PA_EHIP, "merge launch: %s", hipGetErrorString(e));
   g_cnt.merge.fetch_add(1);
@@ -369,6 +420,19 @@ int fp8pa_debug_dequant(const uint8_t* codes, const void* scales, int scale_kind
   hipError_t e = fp8pa::launch_debug_dequant(codes, scales, scale_kind, n, out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8PA_EHIP, "debug launch: %s", hipGetErrorString(e));
   g_cnt.debug.fetch_add(1);
+  ok();
+  return FP8PA_OK;
+}
+
+int fp8pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(FP8PA_EINVAL, "a required device pointer is NULL");
+  if (bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4)) return fail(FP8PA_EINVAL, "misaligned buffer or size");
+  if (bytes == 0) {
+    ok();
+    return FP8PA_OK;
+  }
+  hipError_t e = fp8pa::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP8PA_EHIP, "probe launch: %s", hipGetErrorString(e));
   ok();
   return FP8PA_OK;
 }

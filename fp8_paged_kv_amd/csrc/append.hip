@@ -24,7 +24,8 @@ namespace {
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __builtin_bit_cast(float, (uint32_t)v << 16); }
 
 __device__ __forceinline__ int64_t code_at(const PoolGeom& g, int t, int d) {
-  return (int64_t)t * g.tok_stride + (int64_t)d * g.d_stride;
+  return (int64_t)(t / g.tblk) * g.tblk_stride + (int64_t)(t % g.tblk) * g.tok_stride +
+         (int64_t)(d >> 6) * g.dchunk_stride + (int64_t)(d & 63) * g.d_stride;
 }
 
 __device__ float block_max(float v, float* red) {

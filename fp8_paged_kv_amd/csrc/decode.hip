@@ -8,10 +8,19 @@
 //
 // Work decomposition.  The grid runs over (split, KV head, sequence) so the
 // GQA group shares every K/V read (page section "Why it happens").  A
-// workgroup is four wave64s; each wave walks its own tiles of the split with
-// an independent online softmax, and the four partial states are combined in
-// LDS at the end.  A split with more than one split per sequence writes a
-// normalised partial and its log-sum-exp for the merge kernel.
+// workgroup is four wave64s; each wave walks every fourth tile of the split
+// with an independent online softmax, and the four partial states are combined
+// in LDS at the end.  The block-table entries of the split are staged in LDS
+// once, and each wave double-buffers its tiles in registers: the loads of its
+// next tile are in flight while it computes the current one.
+//
+// Splits.  When a sequence spans more than one split, each split writes a
+// normalised partial and its log-sum-exp to the workspace, and the last split
+// of a (sequence, KV head) to arrive merges them and writes the output (the
+// standard log-sum-exp combination; the sink enters once).  Arrival counters
+// carry the call's epoch in their upper half, so a workspace needs no
+// initialisation, and the last arriver resets the count so a replayed graph
+// (same epoch) starts from zero again.
 //
 // Tile = 32*NS positions = four groups of 8*NS consecutive positions; a group
 // never crosses a page (P >= 16 and tiles are aligned to their size).
@@ -41,8 +50,11 @@
 // before the window) get a score of -inf by selection and their V bytes are
 // zeroed, so NaN codes or scales there never reach the output.  Pages with no
 // attended position are never looked up in the block table.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "fp8pa_internal.h"
+#include "merge_common.h"
 
 namespace fp8pa {
 namespace {
@@ -57,32 +69,62 @@ struct VRaw<1> { typedef u32x2 type; };
 template <>
 struct VRaw<2> { typedef u32x4 type; };
 
-// Split bookkeeping shared with the merge kernel: the first tile-aligned
-// position, the number of splits that hold attended positions.
-__device__ __forceinline__ void split_range(int L, int window, int tile, int split_tokens, int S,
-                                            int& start, int& tbeg, int& nsplit) {
-  start = (window > 0 && L > window) ? L - window : 0;
-  tbeg = start & ~(tile - 1);
-  int need = (L > start) ? (L - tbeg + split_tokens - 1) / split_tokens : 0;
-  nsplit = need < S ? need : S;
+// The D/32 E8M0 bytes of one position (one 32-dim group each), zero-extended
+// into a u32x4.
+template <int NG>
+__device__ __forceinline__ u32x4 load_e8_row(const uint8_t* p) {
+  if constexpr (NG == 2) return u32x4{(uint32_t)ld_global<uint16_t>(p), 0, 0, 0};
+  else if constexpr (NG == 4) return u32x4{ld_global<uint32_t>(p), 0, 0, 0};
+  else if constexpr (NG == 8) { const u32x2 v = ld_global<u32x2>(p); return u32x4{v[0], v[1], 0, 0}; }
+  else return ld_global<u32x4>(p);
 }
 
+__device__ __forceinline__ uint32_t byte_of(const u32x4& v, int i) { return (v[i >> 2] >> (8 * (i & 3))) & 0xffu; }
+
+// Registers of one tile for one lane.
 template <int D, int NS, int SK>
-__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
+struct Tile {
+  static constexpr int NM = D / 64, NC = D / 16, NG = D / 32, NE = (8 * NG) / 16;
+  typedef typename VRaw<NS>::type vraw_t;
+  u32x4 k[NS][2][NM];   // K codes of the lane's position rows
+  vraw_t v[NC];         // V codes of the lane's dims, GT positions each
+  float ks, vs;         // per-(page, head) scales of the lane's score group
+  float kst[NS][8];     // per-(token, head) scales of the lane's score positions
+  float vst[NS][8];
+  u32x4 ke8[NS][2];     // E8M0 bytes of the lane's K rows
+  u32x4 ve8[NS][NE];    // E8M0 bytes of the lane's 8 score positions, all groups
+};
+
+template <int D, int NS, int SK, bool PF, int OCC, bool KNT>
+__global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   constexpr int TT = 32 * NS;   // positions per tile
   constexpr int GT = 8 * NS;    // positions per group
   constexpr int NM = D / 64;    // 16-byte K pieces per position row per lane
   constexpr int NQ = D / 32;    // QK MFMAs per 16 positions
   constexpr int NC = D / 16;    // PV MFMAs per subtile (16 dims each)
   constexpr int NG = D / 32;    // E8M0 groups along D
-  typedef typename VRaw<NS>::type vraw_t;
+  typedef Tile<D, NS, SK> TileT;
+
+  extern __shared__ float s_dyn[];   // staged block table, later the wave-combine buffer
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;      // MFMA column: query head of the group
   const int quad = lane >> 4;   // MFMA k/row quad
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = a.G, P = a.P;
+  // Workgroup -> (KV head, sequence, split), KV head fastest and split
+  // slowest.  Workgroups are dispatched to the eight XCDs round-robin by id,
+  // so every XCD receives the same share of every sequence (grouping a
+  // sequence's heads on one XCD to share scale-footer lines in its L2 was
+  // measured slower: per-XCD work then follows a few sequence lengths), and
+  // the short last splits of long sequences are dispatched last.
+  const int id = blockIdx.x;
+  const int g = id % a.Hkv;
+  const int unit = id / a.Hkv;
+  const int split = unit / a.B, b = unit - split * a.B;
+  const int G = a.G, P = a.P, log2P = a.log2P;
 
   const int L = a.seq_lens[b];
   int start, tbeg, nsplit;
@@ -91,6 +133,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   const int r0 = tbeg + split * a.split_tokens;
   const int r1 = (split == nsplit - 1 || nsplit <= 1) ? L : min(L, r0 + a.split_tokens);
   const int ntiles = (r1 > r0) ? (r1 - r0 + TT - 1) / TT : 0;
+
+  // ---- stage the block-table rows of the split's attended pages in LDS.
+  const int32_t* btr = a.bt + (int64_t)b * a.bt_stride;
+  int* s_tab = reinterpret_cast<int*>(s_dyn);
+  const int p_first = (r0 > start ? r0 : start) >> log2P;
+  const int n_pages = ntiles > 0 ? ((r1 - 1) >> log2P) - p_first + 1 : 0;
+  const int nstaged = n_pages;   // the host sizes the stage for the longest split
+  for (int i = threadIdx.x; i < nstaged; i += 256) s_tab[i] = btr[p_first + i];
 
   // ---- Q operand (B of QK): lane (head n, quad) holds dims 64m + 16quad + 8h2 + i.
   bf16x8 qop[NQ];
@@ -105,12 +155,86 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
         qop[2 * m + h2] = __builtin_bit_cast(bf16x8, v);
       }
   }
+  __syncthreads();
 
-  const int32_t* btr = a.bt + (int64_t)b * a.bt_stride;
   const uint8_t* kpool = a.kp + (int64_t)g * a.kg.head_stride;
   const uint8_t* vpool = a.vp + (int64_t)g * a.vg.head_stride;
   const int kgrp = n >> 2;      // group of this lane's K row
   const int kslot = n & 3;
+
+  // Row of a page of this split.  A group with no attended position reads a
+  // clamped (attended) page instead: its scores are masked to -inf and its V
+  // bytes zeroed, so every lane issues the same loads and the compiler can
+  // count outstanding loads exactly across the prefetch.
+  auto row_of = [&](int page) -> int32_t {
+    int i = page - p_first;
+    i = i < 0 ? 0 : (i >= nstaged ? nstaged - 1 : i);
+    return s_tab[i];
+  };
+
+  // ---- issue the loads of one tile: scales first, then the K and V codes, so
+  // that the large code loads are the most recent ones in flight (a later
+  // wait for a scale, or for the reuse of a scale's register, then leaves
+  // them outstanding).
+  auto load_tile = [&](TileT& t, int T0) {
+    const int tk = T0 + GT * kgrp;   // first position of the lane's K group
+    const int tq = T0 + GT * quad;   // first position of the lane's score/V group
+    const int32_t row_k = row_of(tk >> log2P);
+    const int32_t row_q = row_of(tq >> log2P);
+    const int tpq = tq & (P - 1);
+    const uint8_t* ksc = a.kp + (int64_t)row_q * a.kg.row_bytes + a.kg.sc_off + g * a.kg.sc_head_stride;
+    const uint8_t* vsc = a.vp + (int64_t)row_q * a.vg.row_bytes + a.vg.sc_off + g * a.vg.sc_head_stride;
+    if constexpr (SK == 0) {
+      t.ks = ld_global<float>(ksc);
+      t.vs = ld_global<float>(vsc);
+    } else if constexpr (SK == 1) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tt = tpq + 8 * s + i;
+          t.kst[s][i] = ld_global<float>(ksc + tt * a.kg.sc_tok_stride);
+          t.vst[s][i] = ld_global<float>(vsc + tt * a.vg.sc_tok_stride);
+        }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint8_t* src = vsc + (tpq + 8 * s) * a.vg.sc_tok_stride;
+#pragma unroll
+        for (int k = 0; k < TileT::NE; ++k) t.ve8[s][k] = ld_global<u32x4>(src + 16 * k);
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
+          const uint8_t* kf = a.kp + (int64_t)row_k * a.kg.row_bytes + a.kg.sc_off + g * a.kg.sc_head_stride +
+                              tp * a.kg.sc_tok_stride;
+          t.ke8[s][aa] = load_e8_row<NG>(kf);
+        }
+    }
+    const uint8_t* krow = kpool + (int64_t)row_k * a.kg.row_bytes + 16 * quad;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa) {
+        const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const uint8_t* src = krow + tp * a.kg.tok_stride + m * a.kg.dchunk_stride;
+          t.k[s][aa][m] = KNT ? ld_stream<u32x4>(src) : ld_global<u32x4>(src);
+        }
+      }
+    // The lane's GT positions lie in one token block of the d-major V layout.
+    const uint8_t* vrow = vpool + (int64_t)row_q * a.vg.row_bytes + (int64_t)(tpq / a.vg.tblk) * a.vg.tblk_stride +
+                          (tpq % a.vg.tblk);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int d = 16 * c + n;
+      t.v[c] = ld_stream<typename TileT::vraw_t>(vrow + (int64_t)(d >> 6) * a.vg.dchunk_stride +
+                                                 (int64_t)(d & 63) * a.vg.d_stride);
+    }
+  };
 
   float m_run = kNegInf;        // running max (log2 units) of this lane's head column
   float l_run = 0.0f;           // this lane's share of the running sum
@@ -118,113 +242,34 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int it = wave; it < ntiles; it += kWaves) {
-    const int T0 = r0 + it * TT;
+  // ---- online-softmax update with one tile.
+  auto compute_tile = [&](TileT& t, int T0) {
     const bool interior = (T0 >= start) && (T0 + TT <= L);
-
-    // Rows of the four groups (wave-uniform); a group with no attended
-    // position is not looked up.
-    int32_t row[4];
-    bool gval[4];
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const int t0 = T0 + gi * GT;
-      gval[gi] = (t0 + GT > start) && (t0 < L);
-      row[gi] = gval[gi] ? btr[t0 >> a.log2P] : 0;
-    }
-    const int32_t row_k = kgrp == 0 ? row[0] : kgrp == 1 ? row[1] : kgrp == 2 ? row[2] : row[3];
-    const bool val_k = kgrp == 0 ? gval[0] : kgrp == 1 ? gval[1] : kgrp == 2 ? gval[2] : gval[3];
-    const int32_t row_q = quad == 0 ? row[0] : quad == 1 ? row[1] : quad == 2 ? row[2] : row[3];
-    const bool val_q = quad == 0 ? gval[0] : quad == 1 ? gval[1] : quad == 2 ? gval[2] : gval[3];
-
-    // ---- K loads: lane row = position GT*kgrp + 8s + 4aa + kslot of the tile.
-    u32x4 kraw[NS][2][NM];
-    const uint8_t* krow = kpool + (int64_t)row_k * a.kg.row_bytes + 16 * quad;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int aa = 0; aa < 2; ++aa) {
-        const int tp = (T0 + GT * kgrp + 8 * s + 4 * aa + kslot) & (P - 1);
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-          kraw[s][aa][m] = val_k ? ld_global<u32x4>(krow + tp * a.kg.tok_stride + 64 * m) : u32x4{0, 0, 0, 0};
-      }
-
-    // ---- V loads: lane (dim n of chunk c, quad) holds positions GT*quad + [0, GT).
-    vraw_t vraw[NC];
-    {
-      const int tp = (T0 + GT * quad) & (P - 1);
-      const uint8_t* vrow = vpool + (int64_t)row_q * a.vg.row_bytes + (int64_t)n * a.vg.d_stride + tp;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        vraw_t z = {};
-        vraw[c] = val_q ? ld_global<vraw_t>(vrow + (int64_t)16 * c * a.vg.d_stride) : z;
-      }
-    }
-
-    // ---- scales for this lane's score positions (group `quad`).
-    const uint8_t* ksc = a.kp + (int64_t)row_q * a.kg.row_bytes + a.kg.sc_off + g * a.kg.sc_head_stride;
-    const uint8_t* vsc = a.vp + (int64_t)row_q * a.vg.row_bytes + a.vg.sc_off + g * a.vg.sc_head_stride;
-    const int tq = (T0 + GT * quad) & (P - 1);   // in-page slot of the group's first position
-    float kscale[NS][2][4];
-    float vscale[NS][8];
-    if constexpr (SK == 0) {
-      const float ks = val_q ? ld_global<float>(ksc) : 0.0f;
-      const float vs = val_q ? ld_global<float>(vsc) : 0.0f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { kscale[s][0][i] = ks; kscale[s][1][i] = ks; }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vscale[s][i] = vs;
-      }
-    } else if constexpr (SK == 1) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int t = tq + 8 * s + i;
-          kscale[s][i >> 2][i & 3] = val_q ? ld_global<float>(ksc + t * a.kg.sc_tok_stride) : 0.0f;
-          vscale[s][i] = val_q ? ld_global<float>(vsc + t * a.vg.sc_tok_stride) : 0.0f;
-        }
-    } else {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { kscale[s][i >> 2][i & 3] = 1.0f; vscale[s][i] = 1.0f; }
-    }
-
-    // ---- S = K Q^T for the 16 position rows of each (subtile s, half aa).
     float sc[NS][2][4];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int aa = 0; aa < 2; ++aa) {
-        float cvt[NM];
-        if constexpr (SK == 2) {
-          // E8M0 scale of this lane's K row for the 32-dim group 2m + quad/2.
-          const int tp = (T0 + GT * kgrp + 8 * s + 4 * aa + kslot) & (P - 1);
-          const uint8_t* kfoot = a.kp + (int64_t)row_k * a.kg.row_bytes + a.kg.sc_off +
-                                 g * a.kg.sc_head_stride + tp * a.kg.sc_tok_stride;
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-            cvt[m] = e8m0_as_scale_operand(val_k ? (uint32_t)kfoot[2 * m + (quad >> 1)] : 127u);
-        } else {
-#pragma unroll
-          for (int m = 0; m < NM; ++m) cvt[m] = 1.0f;
-        }
         f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          const u32x4 w = kraw[s][aa][m];
-          s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[0], w[1], cvt[m]), qop[2 * m], s4);
-          s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[2], w[3], cvt[m]), qop[2 * m + 1], s4);
+          float cvt = 1.0f;
+          if constexpr (SK == 2) {
+            const uint32_t e = byte_of(t.ke8[s][aa], 2 * m + (quad >> 1));
+            cvt = e8m0_as_scale_operand(e);
+          }
+          const u32x4 w = t.k[s][aa][m];
+          s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[0], w[1], cvt), qop[2 * m], s4);
+          s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[2], w[3], cvt), qop[2 * m + 1], s4);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sc[s][aa][j] = s4[j] * (kscale[s][aa][j] * a.qk_scale);
+        for (int j = 0; j < 4; ++j) {
+          float f = a.qk_scale;
+          if constexpr (SK == 0) f *= t.ks;
+          if constexpr (SK == 1) f *= t.kst[s][4 * aa + j];
+          sc[s][aa][j] = s4[j] * f;
+        }
       }
-
-    // ---- mask positions outside [start, L) (boundary tiles only).
     if (!interior) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
@@ -236,8 +281,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
             if (pos < start || pos >= L) sc[s][aa][j] = kNegInf;
           }
     }
-
-    // ---- online softmax (log2 domain) for this lane's head column.
     float tmax = kNegInf;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -264,12 +307,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] *= alpha;
-
-    // ---- V bytes of masked positions are zeroed (boundary tiles only).
     if (!interior) {
       const int base = T0 + GT * quad;
       const int lo = start - base, hi = L - base;   // keep bytes in [lo, hi)
-      uint32_t keep[GT / 4];
 #pragma unroll
       for (int k = 0; k < GT / 4; ++k) {
         uint32_t mk = 0;
@@ -278,28 +318,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
           const int bi = 4 * k + byte;
           if (bi >= lo && bi < hi) mk |= 0xffu << (8 * byte);
         }
-        keep[k] = mk;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) t.v[c][k] &= mk;
       }
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int k = 0; k < GT / 4; ++k) vraw[c][k] &= keep[k];
     }
-
-    // ---- O^T += V^T P^T.
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if constexpr (SK == 2) {
-        // V scale per (position, 32-dim group): one B operand per group.
-        const uint8_t* vfoot = a.vp + (int64_t)row_q * a.vg.row_bytes + a.vg.sc_off + g * a.vg.sc_head_stride;
-        const int t8 = tq + 8 * s;
-        constexpr int NE = (8 * NG) / 16;
-        u32x4 e8[NE];      // byte i*NG + gq: position t8 + i, 32-dim group gq
-        {
-          const uint8_t* src = vfoot + t8 * a.vg.sc_tok_stride;
-#pragma unroll
-          for (int k = 0; k < NE; ++k) e8[k] = val_q ? ld_global<u32x4>(src + 16 * k) : u32x4{0, 0, 0, 0};
-        }
         bf16x8 pop[NG];
 #pragma unroll
         for (int gq = 0; gq < NG; ++gq) {
@@ -307,7 +332,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int bi = i * NG + gq;
-            const int ex = (int)((e8[bi >> 4][(bi >> 2) & 3] >> (8 * (bi & 3))) & 0xffu) - 127;
+            const int ex = (int)byte_of(t.ve8[s][bi >> 4], bi & 15) - 127;
             const float x = __builtin_amdgcn_ldexpf(p[s][i], ex);
             pv[i] = (p[s][i] == 0.0f) ? 0.0f : x;
           }
@@ -317,21 +342,54 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const bf16x8 vop = e4m3x8_to_bf16x8(vraw[c][2 * s], vraw[c][2 * s + 1], 1.0f);
+          const bf16x8 vop = e4m3x8_to_bf16x8(t.v[c][2 * s], t.v[c][2 * s + 1], 1.0f);
           acc[c] = mfma_16x16x32_bf16(vop, pop[c >> 1], acc[c]);
         }
       } else {
         float pv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * vscale[s][i];
+        for (int i = 0; i < 8; ++i) {
+          float vsc = 1.0f;
+          if constexpr (SK == 0) vsc = t.vs;
+          if constexpr (SK == 1) vsc = t.vst[s][i];
+          pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * vsc;
+        }
         u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
                     pack_bf16x2(pv[6], pv[7])};
         const bf16x8 pop = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const bf16x8 vop = e4m3x8_to_bf16x8(vraw[c][2 * s], vraw[c][2 * s + 1], 1.0f);
+          const bf16x8 vop = e4m3x8_to_bf16x8(t.v[c][2 * s], t.v[c][2 * s + 1], 1.0f);
           acc[c] = mfma_16x16x32_bf16(vop, pop, acc[c]);
         }
+      }
+    }
+  };
+
+  // ---- tile loop: wave w takes tiles w, w+4, ...
+  {
+    const int nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+    auto tile_pos = [&](int k) { return r0 + (wave + kWaves * k) * TT; };
+    if constexpr (PF) {
+      // Loads run one tile ahead, ping-ponging two register buffers.  The trip
+      // count is fixed and loads are unconditional (a prefetch past the last
+      // tile re-reads a cache-hot tile), so the waits before each compute
+      // cover only that tile's loads.
+      TileT A, B;
+      if (nmine > 0) load_tile(A, tile_pos(0));
+      const int npairs = nmine / 2;
+      for (int k = 0; k < npairs; ++k) {
+        load_tile(B, tile_pos(2 * k + 1));
+        compute_tile(A, tile_pos(2 * k));
+        load_tile(A, tile_pos(2 * k + 2 < nmine ? 2 * k + 2 : 2 * k + 1));
+        compute_tile(B, tile_pos(2 * k + 1));
+      }
+      if (nmine & 1) compute_tile(A, tile_pos(nmine - 1));
+    } else {
+      TileT A;
+      for (int k = 0; k < nmine; ++k) {
+        load_tile(A, tile_pos(k));
+        compute_tile(A, tile_pos(k));
       }
     }
   }
@@ -339,9 +397,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   // ---- combine the four waves' states in LDS.
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-  extern __shared__ float s_o[];   // [2][G][D + 4]
+  float* s_o = s_dyn;   // [2][G][D + 4]; the staged table is no longer read after the barrier
   constexpr int OS = D + 4;
   if (quad == 0) {
     s_m[wave][n] = m_run;
@@ -379,8 +435,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
   }
   __syncthreads();
-  if (wave != 0 || !col) return;
-  {
+  if (wave == 0 && col) {
     const float* src = s_o + n * OS + 4 * quad;
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
@@ -388,6 +443,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 
   const int h = g * G + n;
   if (nsplit <= 1) {
+    if (wave != 0 || !col) return;
     // Final output: o = acc / (sum + e^(sink - max)), sink in log2 units.
     float den = Ltot;
     if (a.sinks) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - M_ref);
@@ -398,38 +454,97 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       u32x2 pk = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv), pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
       *reinterpret_cast<u32x2*>(orow + 16 * c) = pk;
     }
-  } else {
+    return;
+  }
+
+  // ---- partial of this split, then arrival; the last split merges.
+  // Partials are written and read with agent-scope atomic accesses, which on
+  // this multi-XCD part are coherent across the per-XCD L2 caches without a
+  // cache write-back or invalidate; the barrier waits for the stores to
+  // complete before the arrival is counted.
+  if (wave == 0 && col) {
     const size_t ph = ((size_t)b * a.Hq + h) * a.S + split;
     const float inv = (Ltot > 0.0f) ? 1.0f / Ltot : 0.0f;
     float* orow = a.part_o + ph * D + 4 * quad;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(orow + 16 * c) = acc[c] * inv;
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __hip_atomic_store(orow + 16 * c + j, acc[c][j] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (quad == 0)
-      a.part_lse[ph] = (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : (M + __builtin_amdgcn_logf(Ltot)) * kLn2;
+      __hip_atomic_store(a.part_lse + ph,
+                         (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : (M + __builtin_amdgcn_logf(Ltot)) * kLn2,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (!a.fused_merge) return;   // a separate merge kernel combines the partials
+  if (threadIdx.x == 0) {
+    // Wave 0 wrote the partials; wait until its stores have completed at the
+    // coherence point before counting this split as arrived.
+    __builtin_amdgcn_s_waitcnt(0);
+    unsigned long long* cnt = a.counters + ((size_t)b * a.Hkv + g);
+    const unsigned long long tag = (unsigned long long)a.epoch << 32;
+    unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned int arrived;
+    while (true) {
+      arrived = ((old >> 32) == a.epoch) ? (unsigned int)(old & 0xffffffffu) : 0u;
+      unsigned long long want = tag | (unsigned long long)(arrived + 1);
+      if (__hip_atomic_compare_exchange_strong(cnt, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        break;
+    }
+    const bool last = (int)(arrived + 1) == nsplit;
+    if (last) __hip_atomic_store(cnt, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __shared__ float s_inv[16];
+  merge_heads<D, true>(a.part_o, a.part_lse, a.sinks, a.out, b, a.Hq, a.S, g * G, G, nsplit, s_dyn, s_inv);
 }
 
-template <int D, int NS>
-hipError_t launch_d(const DecodeArgs& a, int sk, int B, hipStream_t st) {
-  dim3 grid(a.S, a.Hkv, B), block(256);
-  const size_t lds = (size_t)2 * a.G * (D + 4) * sizeof(float);
+template <int D, int NS, bool PF, int OCC, bool KNT>
+hipError_t launch_d(const DecodeArgs& a, int sk, int B, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  dim3 grid(a.S * B * a.Hkv), block(256);
+  size_t lds = (size_t)2 * a.G * (D + 4) * sizeof(float);                                     // wave combine
+  lds = lds > (size_t)a.max_staged * sizeof(int) ? lds : (size_t)a.max_staged * sizeof(int);   // table
+  lds = lds > (size_t)a.G * a.S * sizeof(float) ? lds : (size_t)a.G * a.S * sizeof(float);     // merge
   switch (sk) {
-    case 0: hipLaunchKernelGGL((decode_kernel<D, NS, 0>), grid, block, lds, st, a); break;
-    case 1: hipLaunchKernelGGL((decode_kernel<D, NS, 1>), grid, block, lds, st, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, NS, 2>), grid, block, lds, st, a); break;
+    case 0: hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT>), grid, block, lds, st, e0, e1, 0, a); break;
+    case 1: hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT>), grid, block, lds, st, e0, e1, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT>), grid, block, lds, st, e0, e1, 0, a); break;
   }
   return hipGetLastError();
 }
 
+template <bool KNT>
+hipError_t launch_k(const DecodeArgs& a, int D, int sk, int B, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  // tile_variant (tuning): 0 default, 1 prefetch at one wave per SIMD,
+  // 2 prefetch with 32-position tiles (D = 128), 3 no prefetch, 4 prefetch.
+  const int v = a.tile_variant;
+  switch (D) {
+    case 64:
+      return v == 4 ? launch_d<64, 2, true, 2, KNT>(a, sk, B, st, e0, e1)
+                    : launch_d<64, 2, false, 2, KNT>(a, sk, B, st, e0, e1);
+    case 128:
+      switch (v) {
+        case 1: return launch_d<128, 2, true, 1, KNT>(a, sk, B, st, e0, e1);
+        case 2: return launch_d<128, 1, true, 2, KNT>(a, sk, B, st, e0, e1);
+        case 4: return launch_d<128, 2, true, 2, KNT>(a, sk, B, st, e0, e1);
+        default: return launch_d<128, 2, false, 2, KNT>(a, sk, B, st, e0, e1);
+      }
+    case 256:
+      return v == 4 ? launch_d<256, 1, true, 1, KNT>(a, sk, B, st, e0, e1)
+                    : launch_d<256, 1, false, 1, KNT>(a, sk, B, st, e0, e1);
+    default: return launch_d<512, 1, false, 1, KNT>(a, sk, B, st, e0, e1);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, int B, hipStream_t st) {
-  switch (D) {
-    case 64: return launch_d<64, 2>(a, scale_kind, B, st);
-    case 128: return launch_d<128, 2>(a, scale_kind, B, st);
-    case 256: return launch_d<256, 1>(a, scale_kind, B, st);
-    default: return launch_d<512, 1>(a, scale_kind, B, st);
-  }
+hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int B, hipStream_t st,
+                         hipEvent_t e0, hipEvent_t e1) {
+  return k_whole_lines ? launch_k<true>(a, D, scale_kind, B, st, e0, e1)
+                       : launch_k<false>(a, D, scale_kind, B, st, e0, e1);
 }
 
 }  // namespace fp8pa

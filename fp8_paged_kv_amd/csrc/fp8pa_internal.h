@@ -8,11 +8,17 @@
 namespace fp8pa {
 
 // Byte geometry of one pool, resolved on the host from fp8pa_pool_desc.
+// Code of (KV head h, in-page token t, dim d) sits at
+//   h*head_stride + (t / tblk)*tblk_stride + (t % tblk)*tok_stride
+//     + (d / 64)*dchunk_stride + (d % 64)*d_stride
 struct PoolGeom {
   int64_t row_bytes;
   int32_t head_stride;     // payload bytes between KV heads of a row
-  int32_t tok_stride;      // payload bytes between tokens (heads/tokens layouts)
-  int32_t d_stride;        // payload bytes between dims (1, or P for HEADS_DMAJOR)
+  int32_t tblk;            // tokens per token block (a power of two; P if unblocked)
+  int32_t tblk_stride;     // bytes between token blocks
+  int32_t tok_stride;      // bytes between tokens inside a block
+  int32_t dchunk_stride;   // bytes between 64-dim chunks
+  int32_t d_stride;        // bytes between dims inside a chunk
   int32_t sc_off;          // scale footer offset in the row
   int32_t sc_head_stride;  // footer bytes between heads
   int32_t sc_tok_stride;   // footer bytes between tokens (0 for per-page scales)
@@ -29,8 +35,13 @@ struct DecodeArgs {
   const float* sinks;      // [Hq] or null
   float* part_o;           // [B, Hq, S, D] (S > 1 only)
   float* part_lse;         // [B, Hq, S]
+  unsigned long long* counters;  // [B, Hkv] split arrivals: (epoch << 32) | count
+  uint32_t epoch;          // distinct per call
+  int32_t max_staged;      // block-table entries a workgroup stages in LDS (split / P + 2)
+  int32_t tile_variant;    // D=128 kernel shape (tuning; 0 = default)
+  int32_t fused_merge;     // 1: the last split merges; 0: launch_merge runs after the kernel
   PoolGeom kg, vg;
-  int32_t P, log2P, Hq, Hkv, G, window;
+  int32_t P, log2P, B, Hq, Hkv, G, window;
   int32_t S, split_tokens;
   float qk_scale;          // sm_scale * log2(e)
 };
@@ -41,6 +52,7 @@ struct MergeArgs {
   const float* sinks;
   uint16_t* out;
   int32_t Hq, S, D;
+  int32_t G;               // query heads merged per workgroup (divides Hq, <= 16)
   // When seq_lens is set the per-sequence split count is recomputed exactly
   // as the decode kernel does, and sequences with at most one split (whose
   // output the decode kernel wrote itself) are skipped.
@@ -63,11 +75,22 @@ struct AppendArgs {
 };
 
 // Tokens per decode tile (one tile = one MFMA round of one wave).
-inline int decode_tile_tokens(int D) { return D <= 128 ? 64 : 32; }
+inline int decode_tile_tokens(int D, int tile_variant = 0) {
+  return (D <= 128 && !(D == 128 && tile_variant == 2)) ? 64 : 32;
+}
 
-hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, int B, hipStream_t st);
+// Longest split the automatic planner makes.  A workgroup stages the
+// block-table rows of its split in LDS (split / P + 2 entries).
+constexpr int kMaxSplitTokens = 16384;
+
+// start/stop: optional events that time the decode kernel alone.  k_whole_lines:
+// the K layout lets every 16-byte K load of a wave cover whole 128-byte lines
+// (non-temporal loads are used then).
+hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int B, hipStream_t st,
+                         hipEvent_t start, hipEvent_t stop);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int B, int max_pages, hipStream_t st);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_debug_dequant(const uint8_t* codes, const void* scales, int kind, int n,
                                 float* out, hipStream_t st);
 

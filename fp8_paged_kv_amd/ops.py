@@ -9,7 +9,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8pa.so")
 
-LAYOUTS = {"heads": 0, "tokens": 1, "heads_dmajor": 2}
+LAYOUTS = {"heads": 0, "tokens": 1, "heads_dmajor": 2, "heads_d64": 3}
 SCALE_KINDS = {"page_head": 0, "token_head": 1, "e8m0_32": 2}
 VARIANTS = {"auto": 0, "mfma_bf16": 1}
 
@@ -54,6 +54,7 @@ SIGNATURES = {
     "fp8pa_get_counters": ([ctypes.POINTER(Counters)], _I),
     "fp8pa_reset_counters": ([], _I),
     "fp8pa_set_decode_events": ([_P, _P], _I),
+    "fp8pa_stream_read": ([_P, _SZ, _P, _P], _I),
 }
 
 
@@ -179,6 +180,11 @@ def counters():
 
 def reset_counters():
     lib().fp8pa_reset_counters()
+
+
+def stream_read(buf, sink, stream=None):
+    """Measurement helper: one streaming read of the whole of `buf`."""
+    _check(lib().fp8pa_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def set_decode_events(start, stop):

@@ -1,7 +1,7 @@
 """Device-resident synthetic decode workloads (the shapes in ``configs``),
 built with the library's own append kernel from seeded bf16 inputs.
 
-Per layer: K pool in the "heads" layout, V pool in "heads_dmajor", both with
+Per layer: K pool in the "heads_d64" layout, V pool in "heads_dmajor", both with
 the workload's scale kind and row stride; pages that hold no attended position
 (before a window) get no row (their table entries are -1); unused slots and
 spare rows hold 0xFF (NaN codes and scales).  Raw K/V of sequence b in layer l
@@ -93,7 +93,7 @@ def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", lay
         lay = wl.layers[li]
         table, pool_rows = tables[li]
         rb = lay.row_bytes
-        kd = ops.pool_desc(lay.Hkv, lay.D, P, "heads", wl.scale_kind, rb, pool_rows)
+        kd = ops.pool_desc(lay.Hkv, lay.D, P, "heads_d64", wl.scale_kind, rb, pool_rows)
         vd = ops.pool_desc(lay.Hkv, lay.D, P, "heads_dmajor", wl.scale_kind, rb, pool_rows)
         if wl.shared_pool and "k" in shared:
             k_pool, v_pool = shared["k"], shared["v"]

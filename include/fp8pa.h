@@ -46,14 +46,20 @@ enum {
 /* ---- pool row payload layouts (byte offset of the code of KV head h,
  *      in-page token t, dim d inside a row) --------------------------------
  * The page names two orders, "tokens" and "heads" ("Supported scope").  The
- * third keeps each (head, dim) row of a page token-contiguous: the value
- * operand of the MFMA that contracts over tokens then loads straight from
- * memory.  The decode kernel reads K in HEADS or TOKENS and V in
- * HEADS_DMAJOR. */
+ * other two are this library's own, chosen so that one wave-wide 16-byte load
+ * of the decode kernel covers whole 128-byte lines: HEADS_D64 for keys (the
+ * 64-byte pieces of consecutive tokens side by side), HEADS_DMAJOR for values
+ * (token-contiguous per dim, which the value operand of the MFMA that
+ * contracts over tokens needs).  The decode kernel reads K in HEADS, TOKENS or
+ * HEADS_D64 (fastest) and V in HEADS_DMAJOR. */
 enum {
-  FP8PA_LAYOUT_HEADS = 0,        /* [Hkv][P][D]: (h*P + t)*D + d */
-  FP8PA_LAYOUT_TOKENS = 1,       /* [P][Hkv][D]: (t*Hkv + h)*D + d */
-  FP8PA_LAYOUT_HEADS_DMAJOR = 2  /* [Hkv][D][P]: (h*D + d)*P + t */
+  FP8PA_LAYOUT_HEADS = 0,         /* [Hkv][P][D]: (h*P + t)*D + d */
+  FP8PA_LAYOUT_TOKENS = 1,        /* [P][Hkv][D]: (t*Hkv + h)*D + d */
+  FP8PA_LAYOUT_HEADS_DMAJOR = 2,  /* [Hkv][P/W][D][W], W = min(P, 64):
+                                     h*P*D + (t/W)*D*W + d*W + t%W
+                                     (for P <= 64: [Hkv][D][P]) */
+  FP8PA_LAYOUT_HEADS_D64 = 3      /* [Hkv][D/64][P][64]:
+                                     ((h*(D/64) + d/64)*P + t)*64 + d%64 */
 };
 
 /* ---- scale kinds.  The scale footer starts at scale_offset inside the row
@@ -120,8 +126,8 @@ int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
  *   out         device bf16 [B, Hq, D], contiguous, 16-byte aligned; written.
  *   k_pool,
  *   v_pool      device uint8 pools, 16-byte aligned, described by kd / vd.
- *               kd: layout HEADS or TOKENS; vd: layout HEADS_DMAJOR.  Both:
- *               same Hkv, D, P and scale kind.
+ *               kd: layout HEADS_D64, HEADS or TOKENS; vd: layout
+ *               HEADS_DMAJOR.  Both: same Hkv, D, P and scale kind.
  *   block_table device int32 [B, bt_stride]: logical page -> row.
  *   seq_lens    device int32 [B]: valid positions of each sequence, the token
  *               being decoded included (append first, then decode); each
@@ -186,6 +192,12 @@ int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, ui
  */
 int fp8pa_debug_dequant(const uint8_t* codes, const void* scales, int scale_kind, int n,
                         float* out, void* stream);
+
+/* Measurement helper: reads `bytes` (a multiple of 16) of device memory at
+ * `buf` (16-byte aligned) once with a plain streaming kernel and nothing
+ * else, so that its rate gives this machine's HBM read ceiling.  `sink` is a
+ * device uint32 that the kernel may write. */
+int fp8pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Launch counters: what actually ran, not what was requested. */
 typedef struct fp8pa_counters {

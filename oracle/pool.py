@@ -11,11 +11,17 @@ the payload).  Rows are ``row_bytes`` apart, which may be wider than the natural
 row so that layers of different geometry can share a pool.  A per-sequence
 block table maps logical page p to a physical row.
 
-Payload layouts (byte offset of the code for head h, in-page token t, dim d):
-  "heads"        [H][P][D]: (h*P + t)*D + d
-  "tokens"       [P][H][D]: (t*H + h)*D + d
-  "heads_dmajor" [H][D][P]: (h*D + d)*P + t    (token-minor; the page names
-                 "tokens" and "heads"; this third order is this library's own)
+Payload layouts (byte offset of the code for head h, in-page token t, dim d).
+The page names "tokens" and "heads"; the other two are this library's own
+orders, chosen so that a wave-wide 16-byte load covers whole 128-byte lines:
+  "heads"        [H][P][D]:        (h*P + t)*D + d
+  "tokens"       [P][H][D]:        (t*H + h)*D + d
+  "heads_d64"    [H][D/64][P][64]: ((h*(D/64) + d//64)*P + t)*64 + d%64
+                 (keys: 64-byte pieces of consecutive tokens side by side)
+  "heads_dmajor" [H][P/W][D][W], W = min(P, 64):
+                 h*P*D + (t//W)*D*W + d*W + t%W
+                 (values: token-contiguous per dim, in blocks of W tokens;
+                 for P <= 64 this is [H][D][P])
 Scale footer (byte offset from ``scale_offset``):
   "page_head"  fp32 per (page, head):  4*h
   "token_head" fp32 per (token, head): 4*(h*P + t), or 4*(t*H + h) for "tokens"
@@ -29,7 +35,7 @@ import numpy as np
 
 from . import fp8
 
-LAYOUTS = ("heads", "tokens", "heads_dmajor")
+LAYOUTS = ("heads", "tokens", "heads_d64", "heads_dmajor")
 SCALE_KINDS = ("page_head", "token_head", "e8m0_32")
 
 
@@ -66,6 +72,10 @@ class PoolDesc:
         assert self.footer >= self.payload_bytes
         if self.scale_kind == "e8m0_32":
             assert self.head_dim % 32 == 0
+        if self.layout == "heads_d64":
+            assert self.head_dim % 64 == 0
+        if self.layout == "heads_dmajor":
+            assert self.page_size <= 64 or self.page_size % 64 == 0
 
 
 def natural_desc(num_kv_heads, head_dim, page_size, layout, scale_kind, num_rows, row_bytes=None):
@@ -81,7 +91,10 @@ def code_offset(desc: PoolDesc, h, t, d):
         return (h * P + t) * D + d
     if desc.layout == "tokens":
         return (t * H + h) * D + d
-    return (h * D + d) * P + t
+    if desc.layout == "heads_d64":
+        return ((h * (D // 64) + d // 64) * P + t) * 64 + d % 64
+    W = min(P, 64)
+    return h * P * D + (t // W) * D * W + d * W + t % W
 
 
 def scale_offset(desc: PoolDesc, h, t=0, g=0):

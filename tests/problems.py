@@ -40,7 +40,7 @@ class Problem:
         return self.D ** -0.5 if self.sm_scale is None else self.sm_scale
 
 
-def make_problem(seed, B, Hq, Hkv, D, P, lens, scale_kind="page_head", k_layout="heads",
+def make_problem(seed, B, Hq, Hkv, D, P, lens, scale_kind="page_head", k_layout="heads_d64",
                  v_layout="heads_dmajor", window=0, sinks=False, sm_scale=None, row_pad=0,
                  poison=True, cfg=99, spare_frac=0.1, k_gain=1.0):
     lens = np.asarray(lens, dtype=np.int32)

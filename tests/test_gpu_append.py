@@ -33,7 +33,8 @@ def run_gpu(pool_k, pool_v, kd, vd, table, positions, xk, xv, counts=None):
 
 
 @pytest.mark.parametrize("kind", opool.SCALE_KINDS)
-@pytest.mark.parametrize("klayout,vlayout", [("heads", "heads_dmajor"), ("tokens", "heads_dmajor"), ("heads", "tokens")])
+@pytest.mark.parametrize("klayout,vlayout", [("heads", "heads_dmajor"), ("tokens", "heads_dmajor"), ("heads", "tokens"),
+                                             ("heads_d64", "heads_dmajor")])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_bulk_append_bit_exact(kind, klayout, vlayout, D):
     say("bulk append", kind, klayout, vlayout, D)
@@ -107,3 +108,21 @@ def test_chunked_append_from_unaligned_positions_bit_exact():
     assert np.array_equal(dk.cpu().numpy(), wk)
     assert np.array_equal(dv.cpu().numpy(), wv)
     assert ops.counters()["append_launches"] >= 5
+
+
+@pytest.mark.parametrize("kind", opool.SCALE_KINDS)
+@pytest.mark.parametrize("P", [64, 128, 256])
+def test_bulk_append_large_pages_bit_exact(kind, P):
+    """Pages of 64+ tokens: blocked d-major values and 64-byte-chunked keys."""
+    say("large-page append", kind, P)
+    lens = [300, 129]
+    table, kd = make(kind, "heads_d64", D=128, P=P, lens=lens)
+    _, vd = make(kind, "heads_dmajor", D=128, P=P, lens=lens)
+    T = max(lens)
+    xk = np.stack([inputs.normal_bf16(4, 0, "k", b, (T, 2, 128)) for b in range(2)])
+    xv = np.stack([inputs.normal_bf16(4, 0, "v", b, (T, 2, 128)) for b in range(2)])
+    empty_k = np.full(kd.num_rows * kd.row_bytes, 0xFF, np.uint8)
+    empty_v = np.full(vd.num_rows * vd.row_bytes, 0xFF, np.uint8)
+    gk, gv = run_gpu(empty_k, empty_v, kd, vd, table, [0, 0], xk, xv, counts=lens)
+    assert np.array_equal(gk, opool.append_ref(empty_k, kd, table, [0, 0], xk, counts=lens))
+    assert np.array_equal(gv, opool.append_ref(empty_v, vd, table, [0, 0], xv, counts=lens))

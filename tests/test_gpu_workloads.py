@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 def oracle_panel(wl, layer, b, g, seed=configs.SEED):
     """Host pools holding sequence b, KV head g of the layer, quantized by the oracle."""
-    kd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads", layer.scale_kind, layer.row_bytes, layer.pool_rows)
+    kd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads_d64", layer.scale_kind, layer.row_bytes, layer.pool_rows)
     vd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads_dmajor", layer.scale_kind, layer.row_bytes,
                         layer.pool_rows)
     L, first = int(layer.lens[b]), int(layer.first_pos[b])

@@ -11,8 +11,9 @@ from tests.problems import make_problem, permute_rows
 
 @pytest.mark.parametrize("layout", opool.LAYOUTS)
 @pytest.mark.parametrize("kind", opool.SCALE_KINDS)
-def test_offsets_are_a_bijection_inside_the_row(layout, kind):
-    H, D, P = 3, 64, 16
+@pytest.mark.parametrize("P,D", [(16, 64), (32, 128), (128, 128)])
+def test_offsets_are_a_bijection_inside_the_row(layout, kind, P, D):
+    H = 3
     d = opool.natural_desc(H, D, P, layout, kind, 1)
     h, t, dd = np.meshgrid(np.arange(H), np.arange(P), np.arange(D), indexing="ij")
     off = opool.code_offset(d, h, t, dd).ravel()
@@ -69,7 +70,7 @@ def test_row_permutation_leaves_values_unchanged():
 
 
 @pytest.mark.parametrize("kind", opool.SCALE_KINDS)
-@pytest.mark.parametrize("layout", ["heads", "heads_dmajor"])
+@pytest.mark.parametrize("layout", ["heads", "heads_d64", "heads_dmajor"])
 def test_bulk_append_equals_pack(kind, layout):
     p = make_problem(4, B=2, Hq=2, Hkv=2, D=64, P=16, lens=[35, 35], scale_kind=kind,
                      k_layout=layout, v_layout=layout)
@@ -159,19 +160,31 @@ def test_append_respects_counts_and_leaves_other_rows():
         assert np.all(g2[r] == 0xFF)
 
 
-@pytest.mark.parametrize("layout,shape,axes", [
-    ("heads", "HPD", (0, 1, 2)), ("tokens", "PHD", (1, 0, 2)), ("heads_dmajor", "HDP", (0, 2, 1))])
+def _payload_as_hpd(payload, layout, H, P, D):
+    """The payload stated as a C-order array whose axes the layout names,
+    brought to [H, P, D] by reshapes and transposes only."""
+    if layout == "heads":
+        return payload.reshape(H, P, D)
+    if layout == "tokens":
+        return payload.reshape(P, H, D).transpose(1, 0, 2)
+    if layout == "heads_d64":
+        return payload.reshape(H, D // 64, P, 64).transpose(0, 2, 1, 3).reshape(H, P, D)
+    W = min(P, 64)
+    return payload.reshape(H, P // W, D, W).transpose(0, 1, 3, 2).reshape(H, P, D)
+
+
+@pytest.mark.parametrize("layout", opool.LAYOUTS)
 @pytest.mark.parametrize("kind", opool.SCALE_KINDS)
-def test_row_layout_matches_reshape_views(layout, shape, axes, kind):
+@pytest.mark.parametrize("P,D", [(16, 64), (16, 128), (128, 128), (256, 64)])
+def test_row_layout_matches_reshape_views(layout, kind, P, D):
     """The row format stated a second way: the payload is a C-order array whose
     axes are named by the layout, the footer a C-order array of scales."""
-    H, P, D = 2, 16, 64
+    H = 2
     p = make_problem(9, B=1, Hq=2, Hkv=H, D=D, P=P, lens=[P], scale_kind=kind, k_layout=layout, v_layout=layout)
     d = p.kdesc
     row = int(p.table[0, 0])
     r = p.k_pool[row * d.row_bytes:(row + 1) * d.row_bytes]
-    dims = {"H": H, "P": P, "D": D}
-    codes = r[:d.payload_bytes].reshape([dims[c] for c in shape]).transpose(np.argsort(axes))   # -> [H, P, D]
+    codes = _payload_as_hpd(r[:d.payload_bytes], layout, H, P, D)
     foot = r[d.footer:d.footer + d.scale_bytes]
     if kind == "page_head":
         sc = foot.copy().view(np.float32).astype(np.float64)[:, None, None]
@@ -185,3 +198,4 @@ def test_row_layout_matches_reshape_views(layout, shape, axes, kind):
     for h in range(H):
         got = opool.read_tokens(p.k_pool, d, p.table[0], np.arange(P), h)
         assert np.array_equal(got, want[h])
+    assert np.array_equal(np.sort(r[:d.payload_bytes]), np.sort(codes.ravel()))
