@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3-8b-decode")
-    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--workgroups", type=int, default=0, help="0: one resident generation (auto)")
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough for 2 GiB)")
     ap.add_argument("--sweep", action="store_true", help="batch x context sweep (CSV on stderr, JSON per point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -107,7 +107,7 @@ def stored_traffic(workload):
     return rec.get("traffic_bytes_per_launch")
 
 
-def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, num_splits):
+def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgroups):
     """Runs `steps` timed steps; a step decodes every layer once (copy k % R).
     Returns wall seconds, per-step GPU ms, and per-layer decode-kernel ms."""
     R = len(layers_copies)
@@ -115,7 +115,7 @@ def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, num_sp
     outs = [torch.empty_like(l.q) for l in layers_copies[0]]
     ws = []
     for l in layers_copies[0]:
-        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, num_splits)
+        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, workgroups)
         ws.append(torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0"))
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -124,7 +124,7 @@ def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, num_sp
         for j, l in enumerate(layers):
             if kev is not None:
                 ops.set_decode_events(kev[2 * j], kev[2 * j + 1])
-            workloads.decode_layer(l, out=outs[j], workspace=ws[j], num_splits=num_splits)
+            workloads.decode_layer(l, out=outs[j], workspace=ws[j], workgroups=workgroups)
         ops.set_decode_events(None, None)
 
     for k in range(warmup):
@@ -245,7 +245,7 @@ def run_sweep(args, torch, ops, workloads, hip):
             R = max(1, min(8, int(np.ceil(2 * 2 ** 30 / (2 * rows * rb)))))
             copies = [[layer]] + [[clone_layer(layer, torch)] for _ in range(R - 1)]
             steps = max(20, min(args.steps, 200))
-            wall, step_ms, kern_ms, _ = time_layers(copies, steps, 5, hip, ops, workloads, torch, args.num_splits)
+            wall, step_ms, kern_ms, _ = time_layers(copies, steps, 5, hip, ops, workloads, torch, args.workgroups)
             med = statistics.median(step_ms) * 1e3
             gbps = nbytes / (statistics.median(kern_ms[0]) * 1e-3) / 1e9
             print(f"{B},{L},{med:.2f},{gbps:.1f},{100 * gbps / PEAK_GBPS:.1f}", file=sys.stderr, flush=True)
@@ -296,7 +296,7 @@ def main():
     torch.cuda.synchronize()
 
     wall, step_ms, kern_ms, _ = time_layers(copies, args.steps, args.warmup, hip, ops, workloads, torch,
-                                            args.num_splits)
+                                            args.workgroups)
     layer_bytes = [workloads.kv_bytes(l) for l in layers]
     total_bytes = sum(layer_bytes)
     ms_per_step = wall * 1e3 / args.steps
@@ -307,7 +307,7 @@ def main():
     traffic = stored_traffic(wl.name)
     us = sorted(x * 1e3 for x in step_ms)
     pct = lambda p: us[min(len(us) - 1, int(p * len(us)))]
-    plans = [ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, args.num_splits) for l in layers]
+    plans = [ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, args.workgroups) for l in layers]
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -325,8 +325,8 @@ def main():
             "workload": wl.name, "B": wl.B, "page": wl.P, "seq_lens": f"U[{wl.L_lo},{wl.L_hi}]",
             "kv": "e4m3", "scales": wl.scale_kind,
             "layers": [{"name": l.name, "Hq": l.Hq, "Hkv": l.Hkv, "D": l.D, "window": l.window,
-                        "sm_scale": round(l.sm_scale, 6), "kv_bytes": b, "splits": p.num_splits,
-                        "split_tokens": p.split_tokens, "kernel_us_mean": round(statistics.mean(km) * 1e3, 2),
+                        "sm_scale": round(l.sm_scale, 6), "kv_bytes": b, "workgroups": p.workgroups,
+                        "tile_tokens": p.tile_tokens, "kernel_us_mean": round(statistics.mean(km) * 1e3, 2),
                         "kernel_gbps": round(b / (statistics.mean(km) * 1e-3) / 1e9, 1)}
                        for l, b, p, km in zip(layers, layer_bytes, plans, kern_ms)],
             "kv_bytes_per_step": total_bytes, "pool_copies_rotated": R, "parallelism": "single GPU",

@@ -20,7 +20,7 @@ SOURCES = ["decode.hip", "merge.hip", "append.hip", "probe.hip", "api.cpp"]
 # Packed fp32 VALU instructions are kept out of generated code (the device
 # pass honours the feature flag; the host pass warns that it does not know it).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
+COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

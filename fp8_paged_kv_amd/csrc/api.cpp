@@ -137,80 +137,55 @@ int tile_variant() {
   return cached;
 }
 
-int fused_merge() {
-  static int cached = -1;
-  if (cached < 0) {
-    const char* e = getenv("FP8PA_FUSED_MERGE");
-    cached = e ? (atoi(e) != 0) : 0;
-  }
-  return cached;
+// Compute units of the current device (0 when no device can be queried).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
 }
 
-int target_workgroups() {
-  static int cached = 0;
-  if (cached) return cached;
-  int t = 2048;   // eight per CU on a 256-CU part (measured: evens out uneven sequence lengths)
-  if (const char* e = getenv("FP8PA_TARGET_WORKGROUPS")) {
-    const int v = atoi(e);
-    if (v > 0) t = v;
-  }
-  cached = t;
-  return t;
-}
-
-// Host-only split plan.  Returns 0 or an error code.
-int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int window, int num_splits,
-              int variant, fp8pa_plan* out) {
+// Host-only decode plan.  Returns 0 or an error code.
+int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int window, int workgroups, int variant,
+              fp8pa_plan* out, size_t* lds_out) {
   if (int rc = check_desc(kd, "kd")) return rc;
   if (B < 0) return fail(FP8PA_EINVAL, "B must be >= 0");
   if (Hq < 1 || Hq % kd->num_kv_heads) return fail(FP8PA_EINVAL, "Hq must be a positive multiple of num_kv_heads");
   const int G = Hq / kd->num_kv_heads;
   if (G > 16) return fail(FP8PA_EUNSUPPORTED, "query heads per KV head G=%d > 16", G);
   if (max_seq_len < 0) return fail(FP8PA_EINVAL, "max_seq_len must be >= 0");
-  if (num_splits < 0) return fail(FP8PA_EINVAL, "num_splits must be >= 0");
+  if (workgroups < 0) return fail(FP8PA_EINVAL, "workgroups must be >= 0");
   if (variant != FP8PA_VARIANT_AUTO && variant != FP8PA_VARIANT_MFMA_BF16)
     return fail(FP8PA_EUNSUPPORTED, "variant %d is not available", variant);
   const int D = kd->head_dim;
-  if ((int64_t)2 * G * (D + 4) * 4 > 65536)
-    return fail(FP8PA_EUNSUPPORTED, "G=%d with head_dim %d exceeds the 64 KiB combine buffer", G, D);
-  const int TT = fp8pa::decode_tile_tokens(D, tile_variant());
-  const int64_t span = (window > 0 && window < max_seq_len) ? window : max_seq_len;
-  // Tiles a range of `span` positions may touch once aligned down to a tile.
-  const int64_t ntile = span > 0 ? (span - 1) / TT + 2 : 1;
-  int64_t S, tps;
-  if (num_splits > 0) {
-    S = num_splits < ntile ? num_splits : ntile;
-    tps = (ntile + S - 1) / S;
-  } else {
-    const int64_t units = (int64_t)(B > 0 ? B : 1) * kd->num_kv_heads;
-    S = (target_workgroups() + units - 1) / units;
-    const int64_t maxS = (ntile + 3) / 4;   // at least one tile per wave
-    if (S > maxS) S = maxS;
-    if (S < 1) S = 1;
-    tps = (ntile + S - 1) / S;
-    tps = (tps + 3) / 4 * 4;
-    if (tps * TT > fp8pa::kMaxSplitTokens) tps = fp8pa::kMaxSplitTokens / TT;
+  const int tv = tile_variant();
+  const size_t lds = fp8pa::decode_lds_bytes(D, tv, B, G, kd->page_size);
+  if (lds > 65536)
+    return fail(FP8PA_EUNSUPPORTED, "B=%d, G=%d, head_dim %d need %zu bytes of LDS (> 64 KiB)", B, G, D, lds);
+  int W = workgroups;
+  if (W == 0) {
+    // One resident generation: every workgroup gets an equal share of the
+    // tiles and all of them run at once.
+    const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
+    const int cus = device_cus();
+    const int per_cu = cus > 0 ? fp8pa::decode_blocks_per_cu(D, kd->scale_kind, k_whole, tv, lds) : 0;
+    W = (cus > 0 && per_cu > 0) ? cus * per_cu : 1024;
   }
-  S = (ntile + tps - 1) / tps;
-  if (S < 1) S = 1;
-  if ((int64_t)G * S * 4 > 65536)
-    return fail(FP8PA_EUNSUPPORTED, "%lld splits of %d query heads exceed the 64 KiB merge buffer", (long long)S, G);
-  // A workgroup stages the block-table rows of its split in LDS.
-  if ((tps * TT / kd->page_size + 2) * 4 > 65536)
-    return fail(FP8PA_EUNSUPPORTED, "a split of %lld positions needs more than 64 KiB of staged block table; "
-                "request more splits", (long long)(tps * TT));
-  out->num_splits = (int32_t)S;
-  out->split_tokens = (int32_t)(tps * TT);
+  out->workgroups = W;
+  out->tile_tokens = fp8pa::decode_tile_tokens(D, tv);
   out->variant = FP8PA_VARIANT_MFMA_BF16;
   out->reserved = 0;
-  if (S > 1) {
-    const int64_t po = (int64_t)B * Hq * S * D * 4;
-    const int64_t pl = (int64_t)B * Hq * S * 4;
+  if (W > 1) {
+    const int64_t po = (int64_t)W * 2 * G * D * 4;
+    const int64_t pl = (int64_t)W * 2 * G * 4;
     const int64_t pc = (int64_t)B * kd->num_kv_heads * 8;
     out->workspace_bytes = (po + 255) / 256 * 256 + (pl + 255) / 256 * 256 + (pc + 255) / 256 * 256;
   } else {
     out->workspace_bytes = 0;
   }
+  if (lds_out) *lds_out = lds;
+  (void)max_seq_len;
+  (void)window;
   return 0;
 }
 
@@ -222,10 +197,10 @@ const char* fp8pa_version(void) { return "fp8pa 0.1.0 gfx950"; }
 
 const char* fp8pa_last_error(void) { return g_err; }
 
-int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int window, int num_splits,
+int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int window, int workgroups,
                       int variant, fp8pa_plan* out) {
   if (!out) return fail(FP8PA_EINVAL, "plan output is NULL");
-  if (int rc = make_plan(B, Hq, kd, max_seq_len, window, num_splits, variant, out)) return rc;
+  if (int rc = make_plan(B, Hq, kd, max_seq_len, window, workgroups, variant, out, nullptr)) return rc;
   ok();
   return FP8PA_OK;
 }
@@ -233,10 +208,11 @@ int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
 int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t* v_pool,
                  const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, const int32_t* block_table,
                  int64_t bt_stride, const int32_t* seq_lens, int B, int Hq, int window, const float* sinks,
-                 float sm_scale, int max_seq_len, int num_splits, int variant, void* workspace,
+                 float sm_scale, int max_seq_len, int workgroups, int variant, void* workspace,
                  size_t workspace_bytes, void* stream) {
   fp8pa_plan plan;
-  if (int rc = make_plan(B, Hq, kd, max_seq_len, window, num_splits, variant, &plan)) return rc;
+  size_t lds = 0;
+  if (int rc = make_plan(B, Hq, kd, max_seq_len, window, workgroups, variant, &plan, &lds)) return rc;
   if (int rc = check_desc(vd, "vd")) return rc;
   if (kd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
     return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS_D64, HEADS or TOKENS layout");
@@ -267,6 +243,8 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
     if (!aligned(workspace, 256)) return fail(FP8PA_EINVAL, "workspace must be 256-byte aligned");
   }
   const int D = kd->head_dim;
+  const int G = Hq / kd->num_kv_heads;
+  const int W = plan.workgroups;
   fp8pa::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.out = static_cast<uint16_t*>(out);
@@ -283,51 +261,27 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   a.B = B;
   a.Hq = Hq;
   a.Hkv = kd->num_kv_heads;
-  a.G = Hq / kd->num_kv_heads;
+  a.G = G;
   a.window = window > 0 ? window : 0;
-  a.S = plan.num_splits;
-  a.split_tokens = plan.split_tokens;
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
-  a.max_staged = (int32_t)((int64_t)plan.split_tokens / kd->page_size + 2);
   a.tile_variant = tile_variant();
-  a.fused_merge = fused_merge();
   a.epoch = g_epoch.fetch_add(1) + 1;
-  if (plan.num_splits > 1) {
-    const int64_t po = (int64_t)B * Hq * plan.num_splits * D * 4;
-    const int64_t pl = (int64_t)B * Hq * plan.num_splits * 4;
-    char* w = static_cast<char*>(workspace);
-    a.part_o = reinterpret_cast<float*>(w);
-    a.part_lse = reinterpret_cast<float*>(w + (po + 255) / 256 * 256);
-    a.counters = reinterpret_cast<unsigned long long*>(w + (po + 255) / 256 * 256 + (pl + 255) / 256 * 256);
+  if (W > 1) {
+    const int64_t po = (int64_t)W * 2 * G * D * 4;
+    const int64_t pl = (int64_t)W * 2 * G * 4;
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(ws + (po + 255) / 256 * 256);
+    a.counters = reinterpret_cast<unsigned long long*>(ws + (po + 255) / 256 * 256 + (pl + 255) / 256 * 256);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   // A wave's 16-byte K loads cover 64 bytes of each of 16 tokens: whole lines
   // when the 64-byte pieces of consecutive tokens are adjacent.
   const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
-  hipError_t e = fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, B, st, g_ev_start, g_ev_stop);
+  hipError_t e = fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
   g_cnt.decode_mfma.fetch_add(1);
-  if (plan.num_splits > 1) {
-    g_cnt.decode_split.fetch_add(1);
-    if (!a.fused_merge) {
-      fp8pa::MergeArgs m{};
-      m.part_o = a.part_o;
-      m.part_lse = a.part_lse;
-      m.sinks = sinks;
-      m.out = a.out;
-      m.Hq = Hq;
-      m.S = plan.num_splits;
-      m.D = D;
-      m.seq_lens = seq_lens;
-      m.window = a.window;
-      m.split_tokens = plan.split_tokens;
-      m.tile_tokens = fp8pa::decode_tile_tokens(D, a.tile_variant);
-      m.G = a.G;
-      e = fp8pa::launch_merge(m, B, st);
-      if (e != hipSuccess) return fail(FP8PA_EHIP, "merge launch: %s", hipGetErrorString(e));
-      g_cnt.merge.fetch_add(1);
-    }
-  }
+  if (W > 1) g_cnt.decode_split.fetch_add(1);
   g_cnt.decode_calls.fetch_add(1);
   ok();
   return FP8PA_OK;

@@ -6,21 +6,27 @@
 // through its block table, with E4M3 K/V dequantized as code x scale, a custom
 // sm_scale, and an optional per-head sink logit in the denominator.
 //
-// Work decomposition.  The grid runs over (split, KV head, sequence) so the
-// GQA group shares every K/V read (page section "Why it happens").  A
-// workgroup is four wave64s; each wave walks every fourth tile of the split
-// with an independent online softmax, and the four partial states are combined
-// in LDS at the end.  The block-table entries of the split are staged in LDS
-// once, and each wave double-buffers its tiles in registers: the loads of its
-// next tile are in flight while it computes the current one.
+// Work decomposition.  A unit is one (sequence, KV head): the G query heads
+// of the unit share every K/V read (page section "Why it happens": the grid
+// runs over sequence, KV head and split).  A unit's attended positions form a
+// run of tiles; the tiles of all units, sequence by sequence, make one global
+// list, and workgroup w of W takes the w-th equal share of it, so every
+// workgroup streams the same number of bytes however uneven the sequence
+// lengths are, and W is chosen so that all workgroups are resident at once.
+// Every workgroup builds the list itself from seq_lens (a prefix sum in LDS),
+// so the grid depends on host values only.  A workgroup's share cuts units
+// into segments; a workgroup is four wave64s, each wave walks every fourth
+// tile of a segment with its own online softmax, and the four states are
+// combined in LDS.  The block-table rows of a segment are staged in LDS.
 //
-// Splits.  When a sequence spans more than one split, each split writes a
-// normalised partial and its log-sum-exp to the workspace, and the last split
-// of a (sequence, KV head) to arrive merges them and writes the output (the
-// standard log-sum-exp combination; the sink enters once).  Arrival counters
-// carry the call's epoch in their upper half, so a workspace needs no
-// initialisation, and the last arriver resets the count so a replayed graph
-// (same epoch) starts from zero again.
+// Merging.  A segment that covers a whole unit writes the output.  Otherwise
+// it writes a normalised partial and its log-sum-exp (only a workgroup's first
+// and last segments can be partial: two slots per workgroup), and the last of
+// the unit's workgroups to arrive merges them (the standard log-sum-exp
+// combination; the sink enters once).  Arrival counters carry the call's
+// epoch in their upper half, so a workspace needs no initialisation, and the
+// last arriver resets the count so a replayed graph (same epoch) starts from
+// zero again.
 //
 // Tile = 32*NS positions = four groups of 8*NS consecutive positions; a group
 // never crosses a page (P >= 16 and tiles are aligned to their size).
@@ -103,69 +109,86 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   constexpr int NQ = D / 32;    // QK MFMAs per 16 positions
   constexpr int NC = D / 16;    // PV MFMAs per subtile (16 dims each)
   constexpr int NG = D / 32;    // E8M0 groups along D
+  constexpr int CH = kMaxSplitTokens / TT;   // tiles whose page rows are staged at once
   typedef Tile<D, NS, SK> TileT;
 
-  extern __shared__ float s_dyn[];   // staged block table, later the wave-combine buffer
+  extern __shared__ int s_dyn[];   // [B + 1] tile prefix, then the page-row stage / wave-combine buffer
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
+  __shared__ float s_M[16], s_inv[16];
+  __shared__ int s_wsum[kWaves];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;      // MFMA column: query head of the group
   const int quad = lane >> 4;   // MFMA k/row quad
-  // Workgroup -> (KV head, sequence, split), KV head fastest and split
-  // slowest.  Workgroups are dispatched to the eight XCDs round-robin by id,
-  // so every XCD receives the same share of every sequence (grouping a
-  // sequence's heads on one XCD to share scale-footer lines in its L2 was
-  // measured slower: per-XCD work then follows a few sequence lengths), and
-  // the short last splits of long sequences are dispatched last.
-  const int id = blockIdx.x;
-  const int g = id % a.Hkv;
-  const int unit = id / a.Hkv;
-  const int split = unit / a.B, b = unit - split * a.B;
-  const int G = a.G, P = a.P, log2P = a.log2P;
+  const int G = a.G, P = a.P, log2P = a.log2P, B = a.B, Hkv = a.Hkv;
+  const int W = gridDim.x, w = blockIdx.x;
+  const bool col = n < G;
 
-  const int L = a.seq_lens[b];
-  int start, tbeg, nsplit;
-  split_range(L, a.window, TT, a.split_tokens, a.S, start, tbeg, nsplit);
-  if (split >= (nsplit > 1 ? nsplit : 1)) return;
-  const int r0 = tbeg + split * a.split_tokens;
-  const int r1 = (split == nsplit - 1 || nsplit <= 1) ? L : min(L, r0 + a.split_tokens);
-  const int ntiles = (r1 > r0) ? (r1 - r0 + TT - 1) / TT : 0;
-
-  // ---- stage the block-table rows of the split's attended pages in LDS.
-  const int32_t* btr = a.bt + (int64_t)b * a.bt_stride;
-  int* s_tab = reinterpret_cast<int*>(s_dyn);
-  const int p_first = (r0 > start ? r0 : start) >> log2P;
-  const int n_pages = ntiles > 0 ? ((r1 - 1) >> log2P) - p_first + 1 : 0;
-  const int nstaged = n_pages;   // the host sizes the stage for the longest split
-  for (int i = threadIdx.x; i < nstaged; i += 256) s_tab[i] = btr[p_first + i];
-
-  // ---- Q operand (B of QK): lane (head n, quad) holds dims 64m + 16quad + 8h2 + i.
-  bf16x8 qop[NQ];
+  // ---- tiles per sequence and their prefix sums.
+  auto tiles_of = [&](int L) {
+    const int st = (a.window > 0 && L > a.window) ? L - a.window : 0;
+    const int tb = st & ~(TT - 1);
+    return L > st ? (L - tb + TT - 1) / TT : 0;
+  };
+  int* s_pre = s_dyn;
+  int* s_work_i = s_dyn + ((B + 4) & ~3);
+  float* s_work = reinterpret_cast<float*>(s_work_i);
   {
-    const bool has = n < G;
-    const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)g * G + (has ? n : 0)) * D;
+    const int per = (B + 255) / 256;
+    const int bb0 = threadIdx.x * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+      if (bb0 + i < B) local += tiles_of(a.seq_lens[bb0 + i]);
+    int incl = local;
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        u32x4 v = has ? ld_global<u32x4>(qrow + 64 * m + 16 * quad + 8 * h2) : u32x4{0, 0, 0, 0};
-        qop[2 * m + h2] = __builtin_bit_cast(bf16x8, v);
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int excl = incl - local;
+    for (int i = 0; i < wave; ++i) excl += s_wsum[i];
+    for (int i = 0; i < per; ++i)
+      if (bb0 + i < B) {
+        s_pre[bb0 + i] = excl;
+        excl += tiles_of(a.seq_lens[bb0 + i]);
       }
+    if (threadIdx.x == 0) s_pre[B] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    __syncthreads();
   }
-  __syncthreads();
+  const int64_t T = (int64_t)s_pre[B] * Hkv;
 
-  const uint8_t* kpool = a.kp + (int64_t)g * a.kg.head_stride;
-  const uint8_t* vpool = a.vp + (int64_t)g * a.vg.head_stride;
+  // Sequences with nothing to attend get a zero output.
+  for (int bb = w; bb < B; bb += W) {
+    if (s_pre[bb + 1] != s_pre[bb]) continue;
+    uint16_t* o = a.out + (size_t)bb * a.Hq * D;
+    for (int i = threadIdx.x; i < a.Hq * D; i += 256) o[i] = 0;
+  }
+
+  // Workgroup holding global tile t: the largest w with floor(w*T/W) <= t.
+  // When T < W some workgroups get an empty share; they hold no tile.
+  auto wg_of = [&](int64_t t) -> int { return (int)(((t + 1) * W + T - 1) / T - 1); };
+  auto share_lo = [&](int wi) -> int64_t { return (int64_t)wi * T / W; };
+  auto nonempty = [&](int wi) -> bool { return share_lo(wi) < share_lo(wi + 1); };
+
+  // Per-segment state (captured by the tile helpers below).
+  int b = 0, g = 0, L = 0, start = 0, tbeg = 0, p_first = 0, nstaged = 1;
+  const int32_t* btr = a.bt;
+  const uint8_t* kpool = a.kp;
+  const uint8_t* vpool = a.vp;
+  int* s_tab = s_work_i;
   const int kgrp = n >> 2;      // group of this lane's K row
   const int kslot = n & 3;
+  bf16x8 qop[NQ];
 
-  // Row of a page of this split.  A group with no attended position reads a
-  // clamped (attended) page instead: its scores are masked to -inf and its V
-  // bytes zeroed, so every lane issues the same loads and the compiler can
-  // count outstanding loads exactly across the prefetch.
+  // Row of a page of the current chunk.  A group with no attended position
+  // reads a clamped (attended) page instead: its scores are masked to -inf and
+  // its V bytes zeroed, so every lane issues the same loads and the compiler
+  // can count outstanding loads exactly across the prefetch.
   auto row_of = [&](int page) -> int32_t {
     int i = page - p_first;
     i = i < 0 ? 0 : (i >= nstaged ? nstaged - 1 : i);
@@ -239,8 +262,6 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   float m_run = kNegInf;        // running max (log2 units) of this lane's head column
   float l_run = 0.0f;           // this lane's share of the running sum
   f32x4 acc[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- online-softmax update with one tile.
   auto compute_tile = [&](TileT& t, int T0) {
@@ -366,148 +387,235 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     }
   };
 
-  // ---- tile loop: wave w takes tiles w, w+4, ...
-  {
-    const int nmine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-    auto tile_pos = [&](int k) { return r0 + (wave + kWaves * k) * TT; };
-    if constexpr (PF) {
-      // Loads run one tile ahead, ping-ponging two register buffers.  The trip
-      // count is fixed and loads are unconditional (a prefetch past the last
-      // tile re-reads a cache-hot tile), so the waits before each compute
-      // cover only that tile's loads.
-      TileT A, B;
-      if (nmine > 0) load_tile(A, tile_pos(0));
-      const int npairs = nmine / 2;
-      for (int k = 0; k < npairs; ++k) {
-        load_tile(B, tile_pos(2 * k + 1));
-        compute_tile(A, tile_pos(2 * k));
-        load_tile(A, tile_pos(2 * k + 2 < nmine ? 2 * k + 2 : 2 * k + 1));
-        compute_tile(B, tile_pos(2 * k + 1));
+  int64_t cur = (int64_t)w * T / W;
+  const int64_t hi = (int64_t)(w + 1) * T / W;
+  int slot = 0;
+  while (cur < hi) {
+    // ---- the segment: unit (b, g), tiles [ta, tc) of the unit.
+    {
+      int lo_b = 0, hi_b = B - 1;   // largest b with s_pre[b] * Hkv <= cur (a non-empty sequence)
+      while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if ((int64_t)s_pre[mid] * Hkv <= cur) lo_b = mid;
+        else hi_b = mid - 1;
       }
-      if (nmine & 1) compute_tile(A, tile_pos(nmine - 1));
+      b = lo_b;
+    }
+    const int nb = s_pre[b + 1] - s_pre[b];
+    const int64_t ubase = (int64_t)s_pre[b] * Hkv;
+    g = (int)((cur - ubase) / nb);
+    const int64_t ustart = ubase + (int64_t)g * nb;
+    const int64_t uend = ustart + nb;
+    const int64_t send = hi < uend ? hi : uend;
+    const int ta = (int)(cur - ustart), tc = (int)(send - ustart);
+    L = a.seq_lens[b];
+    start = (a.window > 0 && L > a.window) ? L - a.window : 0;
+    tbeg = start & ~(TT - 1);
+    btr = a.bt + (int64_t)b * a.bt_stride;
+    kpool = a.kp + (int64_t)g * a.kg.head_stride;
+    vpool = a.vp + (int64_t)g * a.vg.head_stride;
+    {
+      // Q operand (B of QK): lane (head n, quad) holds dims 64m + 16quad + 8h2 + i.
+      const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)g * G + (col ? n : 0)) * D;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          u32x4 v = col ? ld_global<u32x4>(qrow + 64 * m + 16 * quad + 8 * h2) : u32x4{0, 0, 0, 0};
+          qop[2 * m + h2] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    m_run = kNegInf;
+    l_run = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int ca = ta; ca < tc; ca += CH) {
+      const int cb = tc < ca + CH ? tc : ca + CH;
+      const int pos0 = tbeg + ca * TT > start ? tbeg + ca * TT : start;
+      const int pos1 = tbeg + cb * TT < L ? tbeg + cb * TT : L;
+      p_first = pos0 >> log2P;
+      nstaged = ((pos1 - 1) >> log2P) - p_first + 1;
+      __syncthreads();   // earlier readers of the stage are done
+      for (int i = threadIdx.x; i < nstaged; i += 256) s_tab[i] = btr[p_first + i];
+      __syncthreads();
+      // ---- tile loop: wave w takes tiles ca + w, ca + w + 4, ...
+      const int nmine = cb - ca > wave ? (cb - ca - wave + kWaves - 1) / kWaves : 0;
+      auto tile_pos = [&](int k) { return tbeg + (ca + wave + kWaves * k) * TT; };
+      if constexpr (PF) {
+        // Loads run one tile ahead, ping-ponging two register buffers.  The
+        // trip count is fixed and loads are unconditional (a prefetch past
+        // the last tile re-reads a cache-hot tile), so the waits before each
+        // compute cover only that tile's loads.
+        TileT A, Bt;
+        if (nmine > 0) load_tile(A, tile_pos(0));
+        const int npairs = nmine / 2;
+        for (int k = 0; k < npairs; ++k) {
+          load_tile(Bt, tile_pos(2 * k + 1));
+          compute_tile(A, tile_pos(2 * k));
+          load_tile(A, tile_pos(2 * k + 2 < nmine ? 2 * k + 2 : 2 * k + 1));
+          compute_tile(Bt, tile_pos(2 * k + 1));
+        }
+        if (nmine & 1) compute_tile(A, tile_pos(nmine - 1));
+      } else {
+        TileT A;
+        for (int k = 0; k < nmine; ++k) {
+          load_tile(A, tile_pos(k));
+          compute_tile(A, tile_pos(k));
+        }
+      }
+    }
+
+    // ---- combine the four waves' states in LDS.
+    float lsum = l_run;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    float* s_o = s_work;   // [2][G][D + 4]
+    constexpr int OS = D + 4;
+    if (quad == 0) {
+      s_m[wave][n] = m_run;
+      s_l[wave][n] = lsum;
+    }
+    __syncthreads();   // also: every wave is past its last read of the page-row stage
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i][n]);
+    const float M_ref = (M == kNegInf) ? 0.0f : M;
+    float Ltot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) Ltot += s_l[i][n] * __builtin_amdgcn_exp2f(s_m[i][n] - M_ref);
+    {
+      const float f = __builtin_amdgcn_exp2f(m_run - M_ref);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] *= f;
+    }
+    if (wave >= 2 && col) {
+      float* dst = s_o + ((wave - 2) * G + n) * OS + 4 * quad;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
+    }
+    __syncthreads();
+    if (wave < 2 && col) {
+      const float* src = s_o + (wave * G + n) * OS + 4 * quad;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
+    }
+    __syncthreads();
+    if (wave == 1 && col) {
+      float* dst = s_o + n * OS + 4 * quad;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
+    }
+    __syncthreads();
+    if (wave == 0 && col) {
+      const float* src = s_o + n * OS + 4 * quad;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
+    }
+
+    const int h = g * G + n;
+    if (ta == 0 && tc == nb) {
+      // The segment is the whole unit: o = acc / (sum + e^(sink - max)).
+      if (wave == 0 && col) {
+        float den = Ltot;
+        if (a.sinks) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - M_ref);
+        const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
+        uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * D + 4 * quad;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          u32x2 pk = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv), pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + 16 * c) = pk;
+        }
+      }
     } else {
-      TileT A;
-      for (int k = 0; k < nmine; ++k) {
-        load_tile(A, tile_pos(k));
-        compute_tile(A, tile_pos(k));
+      // ---- partial of this segment, then arrival; the unit's last arriver merges.
+      // Partials are written and read with agent-scope atomic accesses, which
+      // on this multi-XCD part are coherent across the per-XCD L2 caches
+      // without a cache write-back or invalidate.
+      const size_t pbase = ((size_t)w * 2 + slot) * G;
+      if (wave == 0 && col) {
+        const float inv = (Ltot > 0.0f) ? 1.0f / Ltot : 0.0f;
+        float* orow = a.part_o + (pbase + n) * D + 4 * quad;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            __hip_atomic_store(orow + 16 * c + j, acc[c][j] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (quad == 0)
+          __hip_atomic_store(a.part_lse + pbase + n,
+                             (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : (M + __builtin_amdgcn_logf(Ltot)) * kLn2,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const int w_a = wg_of(ustart), w_b = wg_of(uend - 1);
+      if (threadIdx.x == 0) {
+        // Wave 0 wrote the partial; wait until its stores have completed at
+        // the coherence point before counting this segment as arrived.
+        __builtin_amdgcn_s_waitcnt(0);
+        unsigned long long* cntp = a.counters + ((size_t)b * Hkv + g);
+        const unsigned long long tag = (unsigned long long)a.epoch << 32;
+        unsigned long long old = __hip_atomic_load(cntp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned int arrived;
+        while (true) {
+          arrived = ((old >> 32) == a.epoch) ? (unsigned int)(old & 0xffffffffu) : 0u;
+          unsigned long long want = tag | (unsigned long long)(arrived + 1);
+          if (__hip_atomic_compare_exchange_strong(cntp, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT))
+            break;
+        }
+        int expected = 0;
+        for (int wi = w_a; wi <= w_b; ++wi) expected += nonempty(wi) ? 1 : 0;
+        const bool last = (int)(arrived + 1) == expected;
+        if (last) __hip_atomic_store(cntp, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last ? 1 : 0;
+      }
+      __syncthreads();
+      if (s_last) {
+        // Partials of the unit: workgroups w_a..w_b; w_a holds it in its last
+        // slot when its share began before the unit, every other one in its
+        // first slot.
+        const int first_slot_a = (share_lo(w_a) < ustart) ? 1 : 0;
+        auto part = [&](int wi) -> size_t { return ((size_t)wi * 2 + (wi == w_a ? first_slot_a : 0)) * G; };
+        if (threadIdx.x < G) {
+          const int hh = threadIdx.x;
+          const float sink = a.sinks ? a.sinks[g * G + hh] : kNegInf;
+          float Mx = sink;
+          for (int wi = w_a; wi <= w_b; ++wi)
+            if (nonempty(wi))
+              Mx = fmaxf(Mx, __hip_atomic_load(a.part_lse + part(wi) + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          float den = (a.sinks && Mx != kNegInf) ? __builtin_expf(sink - Mx) : 0.0f;
+          for (int wi = w_a; wi <= w_b; ++wi) {
+            if (!nonempty(wi)) continue;
+            const float lse = __hip_atomic_load(a.part_lse + part(wi) + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            den += (lse == kNegInf || Mx == kNegInf) ? 0.0f : __builtin_expf(lse - Mx);
+          }
+          s_M[hh] = Mx;
+          s_inv[hh] = (Mx == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+          const int hh = idx / D, d = idx - hh * D;
+          const float Mx = s_M[hh];
+          float num = 0.0f;
+          for (int wi = w_a; wi <= w_b; ++wi) {
+            if (!nonempty(wi)) continue;
+            const size_t pb = part(wi) + hh;
+            const float lse = __hip_atomic_load(a.part_lse + pb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float ov = __hip_atomic_load(a.part_o + pb * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lse != kNegInf && Mx != kNegInf) num += __builtin_expf(lse - Mx) * ov;
+          }
+          a.out[((size_t)b * a.Hq + g * G + hh) * D + d] = f32_to_bf16_bits(num * s_inv[hh]);
+        }
       }
     }
+    __syncthreads();   // LDS and s_last are reused by the next segment
+    cur = send;
+    slot = 1;
   }
-
-  // ---- combine the four waves' states in LDS.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  float* s_o = s_dyn;   // [2][G][D + 4]; the staged table is no longer read after the barrier
-  constexpr int OS = D + 4;
-  if (quad == 0) {
-    s_m[wave][n] = m_run;
-    s_l[wave][n] = l_run;
-  }
-  __syncthreads();
-  float M = kNegInf;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][n]);
-  const float M_ref = (M == kNegInf) ? 0.0f : M;
-  float Ltot = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) Ltot += s_l[w][n] * __builtin_amdgcn_exp2f(s_m[w][n] - M_ref);
-  {
-    const float f = __builtin_amdgcn_exp2f(m_run - M_ref);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] *= f;
-  }
-  const bool col = n < G;
-  if (wave >= 2 && col) {
-    float* dst = s_o + ((wave - 2) * G + n) * OS + 4 * quad;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
-  }
-  __syncthreads();
-  if (wave < 2 && col) {
-    const float* src = s_o + (wave * G + n) * OS + 4 * quad;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
-  }
-  __syncthreads();
-  if (wave == 1 && col) {
-    float* dst = s_o + n * OS + 4 * quad;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
-  }
-  __syncthreads();
-  if (wave == 0 && col) {
-    const float* src = s_o + n * OS + 4 * quad;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
-  }
-
-  const int h = g * G + n;
-  if (nsplit <= 1) {
-    if (wave != 0 || !col) return;
-    // Final output: o = acc / (sum + e^(sink - max)), sink in log2 units.
-    float den = Ltot;
-    if (a.sinks) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - M_ref);
-    const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
-    uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * D + 4 * quad;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x2 pk = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv), pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + 16 * c) = pk;
-    }
-    return;
-  }
-
-  // ---- partial of this split, then arrival; the last split merges.
-  // Partials are written and read with agent-scope atomic accesses, which on
-  // this multi-XCD part are coherent across the per-XCD L2 caches without a
-  // cache write-back or invalidate; the barrier waits for the stores to
-  // complete before the arrival is counted.
-  if (wave == 0 && col) {
-    const size_t ph = ((size_t)b * a.Hq + h) * a.S + split;
-    const float inv = (Ltot > 0.0f) ? 1.0f / Ltot : 0.0f;
-    float* orow = a.part_o + ph * D + 4 * quad;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __hip_atomic_store(orow + 16 * c + j, acc[c][j] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (quad == 0)
-      __hip_atomic_store(a.part_lse + ph,
-                         (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : (M + __builtin_amdgcn_logf(Ltot)) * kLn2,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (!a.fused_merge) return;   // a separate merge kernel combines the partials
-  if (threadIdx.x == 0) {
-    // Wave 0 wrote the partials; wait until its stores have completed at the
-    // coherence point before counting this split as arrived.
-    __builtin_amdgcn_s_waitcnt(0);
-    unsigned long long* cnt = a.counters + ((size_t)b * a.Hkv + g);
-    const unsigned long long tag = (unsigned long long)a.epoch << 32;
-    unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned int arrived;
-    while (true) {
-      arrived = ((old >> 32) == a.epoch) ? (unsigned int)(old & 0xffffffffu) : 0u;
-      unsigned long long want = tag | (unsigned long long)(arrived + 1);
-      if (__hip_atomic_compare_exchange_strong(cnt, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        break;
-    }
-    const bool last = (int)(arrived + 1) == nsplit;
-    if (last) __hip_atomic_store(cnt, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __shared__ float s_inv[16];
-  merge_heads<D, true>(a.part_o, a.part_lse, a.sinks, a.out, b, a.Hq, a.S, g * G, G, nsplit, s_dyn, s_inv);
 }
 
 template <int D, int NS, bool PF, int OCC, bool KNT>
-hipError_t launch_d(const DecodeArgs& a, int sk, int B, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  dim3 grid(a.S * B * a.Hkv), block(256);
-  size_t lds = (size_t)2 * a.G * (D + 4) * sizeof(float);                                     // wave combine
-  lds = lds > (size_t)a.max_staged * sizeof(int) ? lds : (size_t)a.max_staged * sizeof(int);   // table
-  lds = lds > (size_t)a.G * a.S * sizeof(float) ? lds : (size_t)a.G * a.S * sizeof(float);     // merge
+hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  dim3 grid(W), block(256);
   switch (sk) {
     case 0: hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT>), grid, block, lds, st, e0, e1, 0, a); break;
     case 1: hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT>), grid, block, lds, st, e0, e1, 0, a); break;
@@ -516,35 +624,59 @@ hipError_t launch_d(const DecodeArgs& a, int sk, int B, hipStream_t st, hipEvent
   return hipGetLastError();
 }
 
-template <bool KNT>
-hipError_t launch_k(const DecodeArgs& a, int D, int sk, int B, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  // tile_variant (tuning): 0 default, 1 prefetch at one wave per SIMD,
-  // 2 prefetch with 32-position tiles (D = 128), 3 no prefetch, 4 prefetch.
-  const int v = a.tile_variant;
+template <int D, int NS, bool PF, int OCC, bool KNT>
+int occupancy_d(int sk, size_t lds) {
+  int nb = 0;
+  hipError_t e;
+  switch (sk) {
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 0, PF, OCC, KNT>, 256, lds); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 1, PF, OCC, KNT>, 256, lds); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 2, PF, OCC, KNT>, 256, lds); break;
+  }
+  return e == hipSuccess ? nb : -1;
+}
+
+// Dispatch on head dim and kernel shape.  tile_variant (tuning): 0 default,
+// 1 prefetch at one wave per SIMD, 2 prefetch with 32-position tiles
+// (D = 128), 3 no prefetch, 4 prefetch.
+template <bool KNT, typename F>
+auto by_shape(int D, int v, F&& f) {
   switch (D) {
-    case 64:
-      return v == 4 ? launch_d<64, 2, true, 2, KNT>(a, sk, B, st, e0, e1)
-                    : launch_d<64, 2, false, 2, KNT>(a, sk, B, st, e0, e1);
+    case 64: return v == 4 ? f.template operator()<64, 2, true, 2, KNT>() : f.template operator()<64, 2, false, 2, KNT>();
     case 128:
       switch (v) {
-        case 1: return launch_d<128, 2, true, 1, KNT>(a, sk, B, st, e0, e1);
-        case 2: return launch_d<128, 1, true, 2, KNT>(a, sk, B, st, e0, e1);
-        case 4: return launch_d<128, 2, true, 2, KNT>(a, sk, B, st, e0, e1);
-        default: return launch_d<128, 2, false, 2, KNT>(a, sk, B, st, e0, e1);
+        case 1: return f.template operator()<128, 2, true, 1, KNT>();
+        case 2: return f.template operator()<128, 1, true, 2, KNT>();
+        case 4: return f.template operator()<128, 2, true, 2, KNT>();
+        default: return f.template operator()<128, 2, false, 2, KNT>();
       }
     case 256:
-      return v == 4 ? launch_d<256, 1, true, 1, KNT>(a, sk, B, st, e0, e1)
-                    : launch_d<256, 1, false, 1, KNT>(a, sk, B, st, e0, e1);
-    default: return launch_d<512, 1, false, 1, KNT>(a, sk, B, st, e0, e1);
+      return v == 4 ? f.template operator()<256, 1, true, 1, KNT>() : f.template operator()<256, 1, false, 1, KNT>();
+    default: return f.template operator()<512, 1, false, 1, KNT>();
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int B, hipStream_t st,
-                         hipEvent_t e0, hipEvent_t e1) {
-  return k_whole_lines ? launch_k<true>(a, D, scale_kind, B, st, e0, e1)
-                       : launch_k<false>(a, D, scale_kind, B, st, e0, e1);
+size_t decode_lds_bytes(int D, int tile_variant, int B, int G, int P) {
+  const int TT = decode_tile_tokens(D, tile_variant);
+  const size_t pre = (size_t)((B + 4) & ~3) * 4;
+  const size_t stage = (size_t)(kMaxSplitTokens / TT * TT / P + 2) * 4;
+  const size_t combine = (size_t)2 * G * (D + 4) * 4;
+  return pre + (stage > combine ? stage : combine);
+}
+
+int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, int tile_variant, size_t lds) {
+  auto q = [&]<int DD, int NS, bool PF, int OCC, bool KNT>() { return occupancy_d<DD, NS, PF, OCC, KNT>(scale_kind, lds); };
+  return k_whole_lines ? by_shape<true>(D, tile_variant, q) : by_shape<false>(D, tile_variant, q);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                         hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  auto l = [&]<int DD, int NS, bool PF, int OCC, bool KNT>() {
+    return launch_d<DD, NS, PF, OCC, KNT>(a, scale_kind, W, lds, st, e0, e1);
+  };
+  return k_whole_lines ? by_shape<true>(D, a.tile_variant, l) : by_shape<false>(D, a.tile_variant, l);
 }
 
 }  // namespace fp8pa

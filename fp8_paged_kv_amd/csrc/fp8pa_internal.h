@@ -33,31 +33,23 @@ struct DecodeArgs {
   int64_t bt_stride;
   const int32_t* seq_lens;
   const float* sinks;      // [Hq] or null
-  float* part_o;           // [B, Hq, S, D] (S > 1 only)
-  float* part_lse;         // [B, Hq, S]
-  unsigned long long* counters;  // [B, Hkv] split arrivals: (epoch << 32) | count
+  float* part_o;           // [W][2][G][D] partial outputs (first / last segment of a workgroup)
+  float* part_lse;         // [W][2][G]
+  unsigned long long* counters;  // [B * Hkv] arrivals per unit: (epoch << 32) | count
   uint32_t epoch;          // distinct per call
-  int32_t max_staged;      // block-table entries a workgroup stages in LDS (split / P + 2)
-  int32_t tile_variant;    // D=128 kernel shape (tuning; 0 = default)
-  int32_t fused_merge;     // 1: the last split merges; 0: launch_merge runs after the kernel
+  int32_t tile_variant;    // kernel shape (tuning; 0 = default)
   PoolGeom kg, vg;
   int32_t P, log2P, B, Hq, Hkv, G, window;
-  int32_t S, split_tokens;
   float qk_scale;          // sm_scale * log2(e)
 };
 
 struct MergeArgs {
-  const float* part_o;
-  const float* part_lse;
+  const float* part_o;     // [B, Hq, S, D]
+  const float* part_lse;   // [B, Hq, S]
   const float* sinks;
   uint16_t* out;
   int32_t Hq, S, D;
   int32_t G;               // query heads merged per workgroup (divides Hq, <= 16)
-  // When seq_lens is set the per-sequence split count is recomputed exactly
-  // as the decode kernel does, and sequences with at most one split (whose
-  // output the decode kernel wrote itself) are skipped.
-  const int32_t* seq_lens;
-  int32_t window, split_tokens, tile_tokens;
 };
 
 struct AppendArgs {
@@ -79,15 +71,17 @@ inline int decode_tile_tokens(int D, int tile_variant = 0) {
   return (D <= 128 && !(D == 128 && tile_variant == 2)) ? 64 : 32;
 }
 
-// Longest split the automatic planner makes.  A workgroup stages the
-// block-table rows of its split in LDS (split / P + 2 entries).
+// Positions whose page rows a workgroup stages in LDS at once.
 constexpr int kMaxSplitTokens = 16384;
 
-// start/stop: optional events that time the decode kernel alone.  k_whole_lines:
-// the K layout lets every 16-byte K load of a wave cover whole 128-byte lines
-// (non-temporal loads are used then).
-hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int B, hipStream_t st,
-                         hipEvent_t start, hipEvent_t stop);
+// Dynamic LDS of a decode launch, resident workgroups per CU, and the launch
+// itself (start/stop: optional events that time the decode kernel alone;
+// k_whole_lines: the K layout lets every 16-byte K load of a wave cover whole
+// 128-byte lines, so non-temporal loads are used).
+size_t decode_lds_bytes(int D, int tile_variant, int B, int G, int P);
+int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, int tile_variant, size_t lds);
+hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                         hipStream_t st, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int B, int max_pages, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);

@@ -11,15 +11,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   extern __shared__ float s_w[];
   __shared__ float s_inv[16];
   const int grp = blockIdx.x, b = blockIdx.y;
-  int ns = a.S;
-  if (a.seq_lens) {
-    // Same split count as the decode kernel; with at most one split the
-    // decode kernel wrote the output itself.
-    int start, tbeg;
-    split_range(a.seq_lens[b], a.window, a.tile_tokens, a.split_tokens, a.S, start, tbeg, ns);
-    if (ns <= 1) return;
-  }
-  merge_heads<D, false>(a.part_o, a.part_lse, a.sinks, a.out, b, a.Hq, a.S, grp * a.G, a.G, ns, s_w, s_inv);
+  merge_heads<D, false>(a.part_o, a.part_lse, a.sinks, a.out, b, a.Hq, a.S, grp * a.G, a.G, a.S, s_w, s_inv);
 }
 
 }  // namespace

@@ -1,5 +1,4 @@
-// Split bookkeeping and the log-sum-exp merge, shared by the decode kernel
-// (where the last split to arrive may merge) and the standalone merge kernel.
+// The log-sum-exp merge of split partials (standalone merge kernel).
 //
 // The pages split each sequence so the whole chip is busy (page "fp8 paged
 // attention for MoE serving", section "Why it happens") but do not print how
@@ -13,16 +12,6 @@
 #include "device_common.h"
 
 namespace fp8pa {
-
-// First attended position, first tile-aligned position and the number of
-// splits holding attended positions of a sequence of L positions.
-__device__ __forceinline__ void split_range(int L, int window, int tile, int split_tokens, int S, int& start,
-                                            int& tbeg, int& nsplit) {
-  start = (window > 0 && L > window) ? L - window : 0;
-  tbeg = start & ~(tile - 1);
-  const int need = (L > start) ? (L - tbeg + split_tokens - 1) / split_tokens : 0;
-  nsplit = need < S ? need : S;
-}
 
 template <bool COHERENT>
 __device__ __forceinline__ float ld_part(const float* p) {

@@ -29,7 +29,7 @@ class PoolDesc(ctypes.Structure):
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("num_splits", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
+    _fields_ = [("workgroups", ctypes.c_int32), ("tile_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
 
 
@@ -107,15 +107,15 @@ def _need(t, name, dtype=None, device=True):
         raise ValueError(f"{name} must be contiguous")
 
 
-def decode_plan(B, Hq, kd, max_seq_len, window=0, num_splits=0, variant="auto"):
+def decode_plan(B, Hq, kd, max_seq_len, window=0, workgroups=0, variant="auto"):
     p = Plan()
-    _check(lib().fp8pa_decode_plan(B, Hq, ctypes.byref(kd), max_seq_len, window, num_splits,
+    _check(lib().fp8pa_decode_plan(B, Hq, ctypes.byref(kd), max_seq_len, window, workgroups,
                                    VARIANTS.get(variant, variant), ctypes.byref(p)))
     return p
 
 
 def decode(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window=0, sinks=None, sm_scale=None,
-           num_splits=0, variant="auto", out=None, workspace=None, stream=None):
+           workgroups=0, variant="auto", out=None, workspace=None, stream=None):
     """Decode attention.  q bf16 [B, Hq, D]; returns bf16 [B, Hq, D]."""
     _need(q, "q", torch.bfloat16)
     _need(k_pool, "k_pool", torch.uint8)
@@ -129,13 +129,13 @@ def decode(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window
         out = torch.empty_like(q)
     _need(out, "out", torch.bfloat16)
     scale = D ** -0.5 if sm_scale is None else float(sm_scale)
-    plan = decode_plan(B, Hq, kd, max_seq_len, window, num_splits, variant)
+    plan = decode_plan(B, Hq, kd, max_seq_len, window, workgroups, variant)
     if plan.workspace_bytes > 0 and workspace is None:
         workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8pa_decode(_ptr(q), _ptr(out), _ptr(k_pool), _ptr(v_pool), ctypes.byref(kd), ctypes.byref(vd),
                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, Hq, window, _ptr(sinks),
-                              scale, max_seq_len, num_splits, VARIANTS.get(variant, variant), _ptr(workspace),
+                              scale, max_seq_len, workgroups, VARIANTS.get(variant, variant), _ptr(workspace),
                               ws_bytes, _stream(stream)))
     return out
 

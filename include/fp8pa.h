@@ -98,14 +98,18 @@ typedef struct fp8pa_pool_desc {
   int64_t num_rows;      /* rows in the pool (host-side sanity only) */
 } fp8pa_pool_desc;
 
-/* Split plan of one decode call (computed on the host from host values only,
- * so a call can be captured in a HIP graph). */
+/* Plan of one decode call (computed on the host from host values only, so a
+ * call can be captured in a HIP graph).  The attended positions of every
+ * (sequence, KV head) are cut into tiles; the tiles of all of them form one
+ * list, and each of `workgroups` workgroups takes an equal share, so the work
+ * is balanced however uneven the sequence lengths are.  Units cut between
+ * workgroups are merged by log-sum-exp inside the same launch. */
 typedef struct fp8pa_plan {
-  int32_t num_splits;       /* S: partials per (sequence, query head) */
-  int32_t split_tokens;     /* positions per split */
+  int32_t workgroups;       /* W (auto: all resident at once on this device) */
+  int32_t tile_tokens;      /* positions per tile */
   int32_t variant;          /* FP8PA_VARIANT_* that will run */
   int32_t reserved;
-  int64_t workspace_bytes;  /* needed by fp8pa_decode (0 when S == 1) */
+  int64_t workspace_bytes;  /* needed by fp8pa_decode (0 when W == 1) */
 } fp8pa_plan;
 
 /* Library version string; never NULL. */
@@ -115,10 +119,11 @@ const char* fp8pa_version(void);
 const char* fp8pa_last_error(void);
 
 /* Plan a decode call.  B sequences, Hq query heads, K pool `kd`; every
- * seq_lens[b] must be <= max_seq_len; window <= 0 means none; num_splits 0
- * lets the library choose, else it is used as given (>= 1). */
+ * seq_lens[b] must be <= max_seq_len; window <= 0 means none; workgroups 0
+ * lets the library choose, else it is used as given (>= 1).  Refuses
+ * (FP8PA_EUNSUPPORTED) shapes whose LDS needs exceed 64 KiB (B above ~15000). */
 int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
-                      int window, int num_splits, int variant, fp8pa_plan* out);
+                      int window, int workgroups, int variant, fp8pa_plan* out);
 
 /*
  * Decode attention (the hot path).
@@ -136,7 +141,7 @@ int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
  *   sinks       device fp32 [Hq] sink logits (already in scaled-score units)
  *               or NULL for none.
  *   sm_scale    finite score scale (D ** -0.5 is the usual value).
- *   max_seq_len, num_splits, variant: as for fp8pa_decode_plan.
+ *   max_seq_len, workgroups, variant: as for fp8pa_decode_plan.
  *   workspace   device buffer of >= plan.workspace_bytes (256-byte aligned),
  *               or NULL when that is 0.  Its contents need no initialisation.
  * Output rows are bf16 (round to nearest even) of the fp32 result.
@@ -145,7 +150,7 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
                  const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
                  const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                  int B, int Hq, int window, const float* sinks, float sm_scale,
-                 int max_seq_len, int num_splits, int variant,
+                 int max_seq_len, int workgroups, int variant,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -203,8 +208,8 @@ int fp8pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* strea
 typedef struct fp8pa_counters {
   int64_t decode_calls;     /* successful fp8pa_decode calls */
   int64_t decode_mfma_bf16; /* decode kernels launched, MFMA bf16 variant */
-  int64_t decode_split;     /* calls that used more than one split */
-  int64_t merge_launches;   /* merge kernels launched (decode + merge_splits) */
+  int64_t decode_split;     /* calls run with more than one workgroup */
+  int64_t merge_launches;   /* fp8pa_merge_splits kernels launched */
   int64_t append_launches;
   int64_t debug_launches;
   int64_t errors;           /* calls refused or failed */

@@ -36,13 +36,13 @@ def device_problem(p):
     )
 
 
-def gpu_decode(p, dev=None, num_splits=0, max_seq_len=None, window=None, sinks="same", **kw):
+def gpu_decode(p, dev=None, workgroups=0, max_seq_len=None, window=None, sinks="same", **kw):
     dev = device_problem(p) if dev is None else dev
     msl = int(p.seq_lens.max()) if max_seq_len is None else max_seq_len
     s = dev["sinks"] if isinstance(sinks, str) else sinks
     out = ops.decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["kd"], dev["vd"], dev["block_table"],
                      dev["seq_lens"], msl, window=p.window if window is None else window, sinks=s,
-                     sm_scale=p.sm_scale, num_splits=num_splits, **kw)
+                     sm_scale=p.sm_scale, workgroups=workgroups, **kw)
     torch.cuda.synchronize()
     return out
 

@@ -53,7 +53,7 @@ F = 0x10000     # fake 16-byte aligned device address
 
 def call_decode(k=None, v=None, **kw):
     a = dict(q=F, out=F, k_pool=F, v_pool=F, bt=F, bt_stride=512, seq_lens=F, B=2, Hq=32, window=0, sinks=None,
-             sm_scale=0.1, max_seq_len=8192, num_splits=0, variant=0, ws=None, ws_bytes=0)
+             sm_scale=0.1, max_seq_len=8192, workgroups=1, variant=0, ws=None, ws_bytes=0)
     a.update(kw)
     k = kd() if k is None else k
     v = vd() if v is None else v
@@ -61,7 +61,7 @@ def call_decode(k=None, v=None, **kw):
     return ops.lib().fp8pa_decode(P(a["q"]), P(a["out"]), P(a["k_pool"]), P(a["v_pool"]), ctypes.byref(k),
                                   ctypes.byref(v), P(a["bt"]), a["bt_stride"], P(a["seq_lens"]), a["B"], a["Hq"],
                                   a["window"], P(a["sinks"]) if a["sinks"] else None, a["sm_scale"],
-                                  a["max_seq_len"], a["num_splits"], a["variant"],
+                                  a["max_seq_len"], a["workgroups"], a["variant"],
                                   P(a["ws"]) if a["ws"] else None, a["ws_bytes"], None)
 
 
@@ -89,10 +89,11 @@ def call_decode(k=None, v=None, **kw):
     (dict(sm_scale=float("inf")), ops.EINVAL),
     (dict(variant=7), ops.EUNSUPPORTED),
     (dict(max_seq_len=-1), ops.EINVAL),
-    (dict(num_splits=-2), ops.EINVAL),
-    (dict(num_splits=4), ops.EWORKSPACE),                       # splits need a workspace
-    (dict(num_splits=4, ws=F, ws_bytes=1024), ops.EWORKSPACE),
-    (dict(num_splits=4, ws=F + 16, ws_bytes=1 << 30), ops.EINVAL),   # workspace must be 256-aligned
+    (dict(workgroups=-2), ops.EINVAL),
+    (dict(workgroups=4), ops.EWORKSPACE),                       # cut units need a workspace
+    (dict(workgroups=4, ws=F, ws_bytes=1024), ops.EWORKSPACE),
+    (dict(workgroups=4, ws=F + 16, ws_bytes=1 << 30), ops.EINVAL),   # workspace must be 256-aligned
+    (dict(B=20000), ops.EUNSUPPORTED),                          # the tile prefix would not fit in LDS
 ])
 def test_decode_refuses_before_launch(case, code):
     ops.reset_counters()
@@ -120,21 +121,19 @@ def test_empty_batch_is_a_no_op():
 def test_plan_is_host_only_and_sane():
     k = kd()
     p = ops.decode_plan(32, 32, k, 8192)
-    assert p.num_splits >= 1 and p.split_tokens % 64 == 0
-    assert p.num_splits * p.split_tokens >= 8192
-    if p.num_splits > 1:
-        assert p.workspace_bytes >= 32 * 32 * p.num_splits * 129 * 4
-    # explicit split counts are honoured (clamped to the tiles available)
-    p1 = ops.decode_plan(32, 32, k, 8192, num_splits=1)
-    assert p1.num_splits == 1 and p1.workspace_bytes == 0 and p1.split_tokens >= 8192 + 63
-    p7 = ops.decode_plan(4, 32, k, 8192, num_splits=7)
-    assert p7.num_splits <= 7 and p7.num_splits * p7.split_tokens >= 8192 + 63
-    # a window bounds the span
-    pw = ops.decode_plan(64, 64, kd(head_dim=64, row_bytes=8224), 32768, window=128)
-    assert pw.num_splits == 1
-    # long context fills the machine
-    pl = ops.decode_plan(4, 64, kd(page_size=128, scale_kind="e8m0_32", row_bytes=135168), 131072)
-    assert pl.num_splits * 4 * 8 >= 512
+    assert p.workgroups >= 1 and p.tile_tokens == 64
+    G, D = 4, 128
+    if p.workgroups > 1:
+        assert p.workspace_bytes >= p.workgroups * 2 * G * (D + 1) * 4 + 32 * 8 * 8
+    # explicit workgroup counts are honoured
+    p1 = ops.decode_plan(32, 32, k, 8192, workgroups=1)
+    assert p1.workgroups == 1 and p1.workspace_bytes == 0
+    p7 = ops.decode_plan(4, 32, k, 8192, workgroups=7)
+    assert p7.workgroups == 7 and p7.workspace_bytes >= 7 * 2 * G * (D + 1) * 4
+    # the plan depends on host values only: same answer twice, any seq_lens
+    assert ops.decode_plan(32, 32, k, 8192).workgroups == p.workgroups
+    # head dims 256 and 512 use 32-position tiles
+    assert ops.decode_plan(16, 16, kd(head_dim=512, num_kv_heads=2, page_size=32, row_bytes=65568), 16384).tile_tokens == 32
     with pytest.raises(ops.Fp8paError):
         ops.decode_plan(1, 8, kd(head_dim=80), 100)
 

@@ -45,11 +45,11 @@ CASES = [
 
 
 @pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("num_splits", [1, 0, 3])
-def test_decode_parity(name, kw, num_splits):
-    say("decode parity", name, "splits", num_splits)
+@pytest.mark.parametrize("workgroups", [1, 0, 3])
+def test_decode_parity(name, kw, workgroups):
+    say("decode parity", name, "workgroups", workgroups)
     p = make_problem(101, **kw)
-    got = to_np(gpu_decode(p, num_splits=num_splits))
+    got = to_np(gpu_decode(p, workgroups=workgroups))
     assert_parity(got, oracle(p), name)
 
 
@@ -109,37 +109,35 @@ def test_invariants_bit_identical():
     assert torch.equal(nos, neg)
 
 
-def test_split_counts_agree():
+def test_workgroup_counts_agree():
     p = make_problem(107, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[1500, 700], sinks=True)
     want = oracle(p)
     outs = []
-    for s in [1, 2, 5, 8, 0]:
-        o = to_np(gpu_decode(p, num_splits=s))
-        assert_parity(o, want, f"splits={s}")
+    for s in [1, 2, 5, 8, 13, 40, 0]:
+        o = to_np(gpu_decode(p, workgroups=s))
+        assert_parity(o, want, f"workgroups={s}")
         outs.append(o)
     # different splits only change fp32 summation order
     for o in outs[1:]:
         assert np.max(np.abs(o - outs[0])) < 2e-2
 
 
-def test_seq_longer_than_the_plan_is_still_complete():
-    """max_seq_len is a contract; the last split absorbs any remainder so the
-    result stays exact even with a short hint."""
-    p = make_problem(108, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[900, 64])
-    assert_parity(to_np(gpu_decode(p, num_splits=2, max_seq_len=900)), oracle(p), "exact")
+def test_more_workgroups_than_tiles():
+    """Workgroups with an empty share exit; units are still complete."""
+    p = make_problem(108, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[130, 64])
+    assert_parity(to_np(gpu_decode(p, workgroups=97)), oracle(p), "many workgroups")
 
 
 def test_counters_record_what_ran():
     ops.reset_counters()
     p = make_problem(109, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[1000, 64])
-    gpu_decode(p, num_splits=4)
+    gpu_decode(p, workgroups=4)
     c = ops.counters()
     assert c["decode_calls"] == 1 and c["decode_mfma_bf16"] == 1 and c["decode_split"] == 1
-    fused = os.environ.get("FP8PA_FUSED_MERGE", "0") != "0"
-    assert c["merge_launches"] == (0 if fused else 1)   # fused: the last split to arrive merges
-    gpu_decode(p, num_splits=1)
+    assert c["merge_launches"] == 0          # cut units are merged inside the decode kernel
+    gpu_decode(p, workgroups=1)
     c = ops.counters()
-    assert c["decode_calls"] == 2 and c["decode_split"] == 1 and c["merge_launches"] == (0 if fused else 1)
+    assert c["decode_calls"] == 2 and c["decode_split"] == 1 and c["merge_launches"] == 0
 
 
 def test_split_merge_many_calls_one_workspace():
@@ -149,8 +147,8 @@ def test_split_merge_many_calls_one_workspace():
     p = make_problem(110, B=4, Hq=16, Hkv=2, D=128, P=16, lens=[3000, 1500, 64, 2500], sinks=True)
     dev = device_problem(p)
     msl = int(p.seq_lens.max())
-    plan = ops.decode_plan(p.B, p.Hq, dev["kd"], msl, num_splits=8)
-    assert plan.num_splits == 8
+    plan = ops.decode_plan(p.B, p.Hq, dev["kd"], msl, workgroups=8)
+    assert plan.workgroups == 8
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda:0")
     rng = np.random.default_rng(0)
     outs = []
@@ -160,7 +158,7 @@ def test_split_merge_many_calls_one_workspace():
         qs.append(q)
         dev["q"] = torch.from_numpy(q).to(torch.bfloat16).to("cuda:0")
         outs.append(ops.decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["kd"], dev["vd"], dev["block_table"],
-                               dev["seq_lens"], msl, sinks=dev["sinks"], num_splits=8, workspace=ws))
+                               dev["seq_lens"], msl, sinks=dev["sinks"], workgroups=8, workspace=ws))
     torch.cuda.synchronize()
     for i in (0, 1, 2, 11, 22, 23):
         assert_parity(to_np(outs[i]), oracle(replace(p, q=qs[i])), f"call {i}")
