@@ -137,6 +137,18 @@ int tile_variant() {
   return cached;
 }
 
+// Fewest tiles a workgroup takes: one per wave, so short calls use fewer,
+// fuller workgroups (tunable through FP8PA_MIN_TILES).
+int min_tiles() {
+  static int cached = -1;
+  if (cached < 0) {
+    const char* e = getenv("FP8PA_MIN_TILES");
+    cached = e ? atoi(e) : 4;
+    if (cached < 1) cached = 1;
+  }
+  return cached;
+}
+
 // Compute units of the current device (0 when no device can be queried).
 int device_cus() {
   int dev = 0, n = 0;
@@ -265,6 +277,7 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   a.window = window > 0 ? window : 0;
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
   a.tile_variant = tile_variant();
+  a.min_tiles = min_tiles();
   a.epoch = g_epoch.fetch_add(1) + 1;
   if (W > 1) {
     const int64_t po = (int64_t)W * 2 * G * D * 4;

@@ -13,6 +13,9 @@
 // list, and workgroup w of W takes the w-th equal share of it, so every
 // workgroup streams the same number of bytes however uneven the sequence
 // lengths are, and W is chosen so that all workgroups are resident at once.
+// A call with few tiles uses only the first ceil(T / min_tiles) workgroups
+// (at least one tile per wave), so every active workgroup's share is
+// non-empty.
 // Every workgroup builds the list itself from seq_lens (a prefix sum in LDS),
 // so the grid depends on host values only.  A workgroup's share cuts units
 // into segments; a workgroup is four wave64s, each wave walks every fourth
@@ -124,7 +127,8 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   const int n = lane & 15;      // MFMA column: query head of the group
   const int quad = lane >> 4;   // MFMA k/row quad
   const int G = a.G, P = a.P, log2P = a.log2P, B = a.B, Hkv = a.Hkv;
-  const int W = gridDim.x, w = blockIdx.x;
+  int W = gridDim.x;
+  const int w = blockIdx.x;
   const bool col = n < G;
 
   // ---- tiles per sequence and their prefix sums.
@@ -163,17 +167,22 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   const int64_t T = (int64_t)s_pre[B] * Hkv;
 
   // Sequences with nothing to attend get a zero output.
-  for (int bb = w; bb < B; bb += W) {
+  for (int bb = w; bb < B; bb += (int)gridDim.x) {
     if (s_pre[bb + 1] != s_pre[bb]) continue;
     uint16_t* o = a.out + (size_t)bb * a.Hq * D;
     for (int i = threadIdx.x; i < a.Hq * D; i += 256) o[i] = 0;
   }
 
+  // Active workgroups: W <= T, so every share holds at least one tile.
+  {
+    const int64_t want = (T + a.min_tiles - 1) / a.min_tiles;
+    if (want < W) W = (int)want;
+  }
+  if (w >= W) return;
+
   // Workgroup holding global tile t: the largest w with floor(w*T/W) <= t.
-  // When T < W some workgroups get an empty share; they hold no tile.
   auto wg_of = [&](int64_t t) -> int { return (int)(((t + 1) * W + T - 1) / T - 1); };
   auto share_lo = [&](int wi) -> int64_t { return (int64_t)wi * T / W; };
-  auto nonempty = [&](int wi) -> bool { return share_lo(wi) < share_lo(wi + 1); };
 
   // Per-segment state (captured by the tile helpers below).
   int b = 0, g = 0, L = 0, start = 0, tbeg = 0, p_first = 0, nstaged = 1;
@@ -562,9 +571,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
                                                    __HIP_MEMORY_SCOPE_AGENT))
             break;
         }
-        int expected = 0;
-        for (int wi = w_a; wi <= w_b; ++wi) expected += nonempty(wi) ? 1 : 0;
-        const bool last = (int)(arrived + 1) == expected;
+        const bool last = (int)(arrived + 1) == w_b - w_a + 1;
         if (last) __hip_atomic_store(cntp, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = last ? 1 : 0;
       }
@@ -580,11 +587,9 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
           const float sink = a.sinks ? a.sinks[g * G + hh] : kNegInf;
           float Mx = sink;
           for (int wi = w_a; wi <= w_b; ++wi)
-            if (nonempty(wi))
-              Mx = fmaxf(Mx, __hip_atomic_load(a.part_lse + part(wi) + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            Mx = fmaxf(Mx, __hip_atomic_load(a.part_lse + part(wi) + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
           float den = (a.sinks && Mx != kNegInf) ? __builtin_expf(sink - Mx) : 0.0f;
           for (int wi = w_a; wi <= w_b; ++wi) {
-            if (!nonempty(wi)) continue;
             const float lse = __hip_atomic_load(a.part_lse + part(wi) + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             den += (lse == kNegInf || Mx == kNegInf) ? 0.0f : __builtin_expf(lse - Mx);
           }
@@ -597,7 +602,6 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
           const float Mx = s_M[hh];
           float num = 0.0f;
           for (int wi = w_a; wi <= w_b; ++wi) {
-            if (!nonempty(wi)) continue;
             const size_t pb = part(wi) + hh;
             const float lse = __hip_atomic_load(a.part_lse + pb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const float ov = __hip_atomic_load(a.part_o + pb * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -38,6 +38,7 @@ struct DecodeArgs {
   unsigned long long* counters;  // [B * Hkv] arrivals per unit: (epoch << 32) | count
   uint32_t epoch;          // distinct per call
   int32_t tile_variant;    // kernel shape (tuning; 0 = default)
+  int32_t min_tiles;       // fewest tiles per active workgroup (>= 1)
   PoolGeom kg, vg;
   int32_t P, log2P, B, Hq, Hkv, G, window;
   float qk_scale;          // sm_scale * log2(e)
