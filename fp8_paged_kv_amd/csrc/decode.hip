@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   extern __shared__ int s_dyn[];   // [B + 1] tile prefix, then the page-row stage / wave-combine buffer
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
-  __shared__ float s_M[16], s_inv[16];
+  __shared__ float s_M[16], s_den[16], s_sc[16];
   __shared__ int s_wsum[kWaves];
   __shared__ int s_last;
 
@@ -542,14 +542,13 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
       // on this multi-XCD part are coherent across the per-XCD L2 caches
       // without a cache write-back or invalidate.
       const size_t pbase = ((size_t)w * 2 + slot) * G;
+      const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
       if (wave == 0 && col) {
+        // Lane (head n, quad) holds dims 16c + 4quad .. +3: one 16-byte store per c.
         const float inv = (Ltot > 0.0f) ? 1.0f / Ltot : 0.0f;
-        float* orow = a.part_o + (pbase + n) * D + 4 * quad;
+        const uint32_t row = (uint32_t)((pbase + n) * D * 4) + 16 * quad;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            __hip_atomic_store(orow + 16 * c + j, acc[c][j] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int c = 0; c < NC; ++c) st_coherent4(prs, row + 64 * c, acc[c] * inv);
         if (quad == 0)
           __hip_atomic_store(a.part_lse + pbase + n,
                              (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : (M + __builtin_amdgcn_logf(Ltot)) * kLn2,
@@ -577,37 +576,88 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
       }
       __syncthreads();
       if (s_last) {
-        // Partials of the unit: workgroups w_a..w_b; w_a holds it in its last
+        // The unit's partials: workgroups w_a..w_b; w_a holds it in its last
         // slot when its share began before the unit, every other one in its
-        // first slot.
+        // first slot.  Merged 64 partials at a time with a running maximum
+        // (log-sum-exp combination; the sink enters once, as the initial
+        // maximum with weight 1): per chunk the weights go to LDS and every
+        // thread accumulates float4 groups of the G x D outputs in registers.
+        const int nseg = w_b - w_a + 1;
         const int first_slot_a = (share_lo(w_a) < ustart) ? 1 : 0;
-        auto part = [&](int wi) -> size_t { return ((size_t)wi * 2 + (wi == w_a ? first_slot_a : 0)) * G; };
-        if (threadIdx.x < G) {
-          const int hh = threadIdx.x;
-          const float sink = a.sinks ? a.sinks[g * G + hh] : kNegInf;
-          float Mx = sink;
-          for (int wi = w_a; wi <= w_b; ++wi)
-            Mx = fmaxf(Mx, __hip_atomic_load(a.part_lse + part(wi) + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          float den = (a.sinks && Mx != kNegInf) ? __builtin_expf(sink - Mx) : 0.0f;
-          for (int wi = w_a; wi <= w_b; ++wi) {
-            const float lse = __hip_atomic_load(a.part_lse + part(wi) + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            den += (lse == kNegInf || Mx == kNegInf) ? 0.0f : __builtin_expf(lse - Mx);
+        auto part_row = [&](int wi) -> uint32_t {
+          return (uint32_t)(((size_t)wi * 2 + (wi == w_a ? first_slot_a : 0)) * G);
+        };
+        constexpr int CHS = 64;   // partials per chunk
+        constexpr int NJ = 2;     // float4 groups per thread per pass
+        const int ngrp = G * D / 4;
+        float* s_wt = s_work;     // [G][CHS]
+        for (int pass0 = 0; pass0 < ngrp; pass0 += 256 * NJ) {
+          f32x4 num[NJ];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) num[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (threadIdx.x < G) {
+            const float sk = a.sinks ? a.sinks[g * G + threadIdx.x] : kNegInf;
+            s_M[threadIdx.x] = sk;
+            s_den[threadIdx.x] = (sk != kNegInf) ? 1.0f : 0.0f;
           }
-          s_M[hh] = Mx;
-          s_inv[hh] = (Mx == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
-        }
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-          const int hh = idx / D, d = idx - hh * D;
-          const float Mx = s_M[hh];
-          float num = 0.0f;
-          for (int wi = w_a; wi <= w_b; ++wi) {
-            const size_t pb = part(wi) + hh;
-            const float lse = __hip_atomic_load(a.part_lse + pb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float ov = __hip_atomic_load(a.part_o + pb * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (lse != kNegInf && Mx != kNegInf) num += __builtin_expf(lse - Mx) * ov;
+          for (int c0 = 0; c0 < nseg; c0 += CHS) {
+            const int nc = nseg - c0 < CHS ? nseg - c0 : CHS;
+            for (int i = threadIdx.x; i < G * CHS; i += 256) {
+              const int hh = i / CHS, k = i - hh * CHS;
+              s_wt[i] = k < nc ? __hip_atomic_load(a.part_lse + part_row(w_a + c0 + k) + hh, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : kNegInf;
+            }
+            __syncthreads();
+            if (threadIdx.x < G) {
+              const int hh = threadIdx.x;
+              const float Mo = s_M[hh];
+              float Mn = Mo;
+              for (int k = 0; k < nc; ++k) Mn = fmaxf(Mn, s_wt[hh * CHS + k]);
+              const float sc = (Mo == kNegInf) ? 0.0f : __builtin_expf(Mo - Mn);
+              float den = s_den[hh] * sc;
+              for (int k = 0; k < nc; ++k) {
+                const float l = s_wt[hh * CHS + k];
+                const float wv = (l == kNegInf) ? 0.0f : __builtin_expf(l - Mn);
+                s_wt[hh * CHS + k] = wv;
+                den += wv;
+              }
+              s_M[hh] = Mn;
+              s_den[hh] = den;
+              s_sc[hh] = sc;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const int gi = pass0 + threadIdx.x + 256 * j;
+              if (gi < ngrp) {
+                const int hh = (4 * gi) / D;
+                f32x4 acc4 = num[j] * s_sc[hh];
+                const float* wrow = s_wt + hh * CHS;
+#pragma unroll 8
+                for (int k = 0; k < nc; ++k) {
+                  const f32x4 o4 = ld_coherent4(prs, (part_row(w_a + c0 + k) * D + 4 * gi) * 4);
+                  const float wv = wrow[k];
+                  acc4 += (wv > 0.0f) ? o4 * wv : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+                num[j] = acc4;
+              }
+            }
+            __syncthreads();   // s_wt, s_M, s_den are rewritten next
           }
-          a.out[((size_t)b * a.Hq + g * G + hh) * D + d] = f32_to_bf16_bits(num * s_inv[hh]);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int gi = pass0 + threadIdx.x + 256 * j;
+            if (gi < ngrp) {
+              const int hh = (4 * gi) / D, d = 4 * gi - hh * D;
+              const float den = s_den[hh];
+              const float inv = (s_M[hh] == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
+              const f32x4 o = num[j] * inv;
+              u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+              *reinterpret_cast<u32x2*>(a.out + ((size_t)b * a.Hq + g * G + hh) * D + d) = pk;
+            }
+          }
+          __syncthreads();   // every thread has read s_M / s_den before the next pass resets them
         }
       }
     }

@@ -87,4 +87,23 @@ __device__ __forceinline__ T ld_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
 
+// 16-byte loads and stores for data exchanged between workgroups of one
+// launch: they carry the sc1 cache policy, as agent-scope atomic accesses do
+// on this part, so they are coherent across the per-XCD L2 caches.  The
+// buffer resource covers `bytes` bytes from `base` (accesses beyond it read
+// zero and write nothing).
+constexpr int kCachePolicySC1 = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ f32x4 ld_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicySC1));
+}
+
+__device__ __forceinline__ void st_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCachePolicySC1);
+}
+
 }  // namespace fp8pa
