@@ -190,7 +190,7 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   if (W > 1) {
     const int64_t po = (int64_t)W * 2 * G * D * 4;
     const int64_t pl = (int64_t)W * 2 * G * 4;
-    const int64_t pc = (int64_t)B * kd->num_kv_heads * 8;
+    const int64_t pc = (int64_t)W * 2 * 4;
     out->workspace_bytes = (po + 255) / 256 * 256 + (pl + 255) / 256 * 256 + (pc + 255) / 256 * 256;
   } else {
     out->workspace_bytes = 0;
@@ -285,7 +285,7 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
     char* ws = static_cast<char*>(workspace);
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_lse = reinterpret_cast<float*>(ws + (po + 255) / 256 * 256);
-    a.counters = reinterpret_cast<unsigned long long*>(ws + (po + 255) / 256 * 256 + (pl + 255) / 256 * 256);
+    a.flags = reinterpret_cast<uint32_t*>(ws + (po + 255) / 256 * 256 + (pl + 255) / 256 * 256);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   // A wave's 16-byte K loads cover 64 bytes of each of 16 tokens: whole lines

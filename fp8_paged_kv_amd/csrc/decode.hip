@@ -24,12 +24,14 @@
 //
 // Merging.  A segment that covers a whole unit writes the output.  Otherwise
 // it writes a normalised partial and its log-sum-exp (only a workgroup's first
-// and last segments can be partial: two slots per workgroup), and the last of
-// the unit's workgroups to arrive merges them (the standard log-sum-exp
-// combination; the sink enters once).  Arrival counters carry the call's
-// epoch in their upper half, so a workspace needs no initialisation, and the
-// last arriver resets the count so a replayed graph (same epoch) starts from
-// zero again.
+// and last segments can be partial: two slots per workgroup) and then a flag
+// holding the call's epoch.  The workgroup holding a unit's last piece (its
+// first segment) merges the unit's partials at the end of its own share, when
+// the other holders, all of lower index, are finishing too: it waits for
+// their flags, combines (the standard log-sum-exp combination; the sink
+// enters once) and clears the flags, so a replayed graph (same epoch) starts
+// clean.  Flags need no initialisation: stale ones hold another call's
+// epoch.  No read-modify-write atomics are involved.
 //
 // Tile = 32*NS positions = four groups of 8*NS consecutive positions; a group
 // never crosses a page (P >= 16 and tiles are aligned to their size).
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   __shared__ float s_l[kWaves][16];
   __shared__ float s_M[16], s_den[16], s_sc[16];
   __shared__ int s_wsum[kWaves];
-  __shared__ int s_last;
+  __shared__ int s_timeout;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -399,6 +401,9 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   int64_t cur = (int64_t)w * T / W;
   const int64_t hi = (int64_t)(w + 1) * T / W;
   int slot = 0;
+  // Unit to merge at the end of the share (uniform across the workgroup).
+  int pend = 0, pend_b = 0, pend_g = 0, pend_wa = 0;
+  int64_t pend_ustart = 0;
   while (cur < hi) {
     // ---- the segment: unit (b, g), tiles [ta, tc) of the unit.
     {
@@ -537,10 +542,11 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
         }
       }
     } else {
-      // ---- partial of this segment, then arrival; the unit's last arriver merges.
-      // Partials are written and read with agent-scope atomic accesses, which
-      // on this multi-XCD part are coherent across the per-XCD L2 caches
-      // without a cache write-back or invalidate.
+      // ---- partial of this segment, then its flag (or, for the unit's last
+      // piece, a merge at the end of the share).  Partials are written and
+      // read with sc1 (agent-coherent) accesses, which on this multi-XCD part
+      // are coherent across the per-XCD L2 caches without a cache write-back
+      // or invalidate.
       const size_t pbase = ((size_t)w * 2 + slot) * G;
       const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
       if (wave == 0 && col) {
@@ -555,115 +561,136 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       const int w_a = wg_of(ustart), w_b = wg_of(uend - 1);
-      if (threadIdx.x == 0) {
-        // Wave 0 wrote the partial; wait until its stores have completed at
-        // the coherence point before counting this segment as arrived.
+      if (w == w_b) {
+        // This is the unit's last piece: merge the unit at the end of the share.
+        pend = 1;
+        pend_b = b;
+        pend_g = g;
+        pend_ustart = ustart;
+        pend_wa = w_a;
+      } else if (threadIdx.x == 0) {
+        // Wave 0 wrote the partial; once its stores have completed at the
+        // coherence point, publish the slot.
         __builtin_amdgcn_s_waitcnt(0);
-        unsigned long long* cntp = a.counters + ((size_t)b * Hkv + g);
-        const unsigned long long tag = (unsigned long long)a.epoch << 32;
-        unsigned long long old = __hip_atomic_load(cntp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        unsigned int arrived;
-        while (true) {
-          arrived = ((old >> 32) == a.epoch) ? (unsigned int)(old & 0xffffffffu) : 0u;
-          unsigned long long want = tag | (unsigned long long)(arrived + 1);
-          if (__hip_atomic_compare_exchange_strong(cntp, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT))
-            break;
-        }
-        const bool last = (int)(arrived + 1) == w_b - w_a + 1;
-        if (last) __hip_atomic_store(cntp, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last ? 1 : 0;
-      }
-      __syncthreads();
-      if (s_last) {
-        // The unit's partials: workgroups w_a..w_b; w_a holds it in its last
-        // slot when its share began before the unit, every other one in its
-        // first slot.  Merged 64 partials at a time with a running maximum
-        // (log-sum-exp combination; the sink enters once, as the initial
-        // maximum with weight 1): per chunk the weights go to LDS and every
-        // thread accumulates float4 groups of the G x D outputs in registers.
-        const int nseg = w_b - w_a + 1;
-        const int first_slot_a = (share_lo(w_a) < ustart) ? 1 : 0;
-        auto part_row = [&](int wi) -> uint32_t {
-          return (uint32_t)(((size_t)wi * 2 + (wi == w_a ? first_slot_a : 0)) * G);
-        };
-        constexpr int CHS = 64;   // partials per chunk
-        constexpr int NJ = 2;     // float4 groups per thread per pass
-        const int ngrp = G * D / 4;
-        float* s_wt = s_work;     // [G][CHS]
-        for (int pass0 = 0; pass0 < ngrp; pass0 += 256 * NJ) {
-          f32x4 num[NJ];
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) num[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (threadIdx.x < G) {
-            const float sk = a.sinks ? a.sinks[g * G + threadIdx.x] : kNegInf;
-            s_M[threadIdx.x] = sk;
-            s_den[threadIdx.x] = (sk != kNegInf) ? 1.0f : 0.0f;
-          }
-          for (int c0 = 0; c0 < nseg; c0 += CHS) {
-            const int nc = nseg - c0 < CHS ? nseg - c0 : CHS;
-            for (int i = threadIdx.x; i < G * CHS; i += 256) {
-              const int hh = i / CHS, k = i - hh * CHS;
-              s_wt[i] = k < nc ? __hip_atomic_load(a.part_lse + part_row(w_a + c0 + k) + hh, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)
-                               : kNegInf;
-            }
-            __syncthreads();
-            if (threadIdx.x < G) {
-              const int hh = threadIdx.x;
-              const float Mo = s_M[hh];
-              float Mn = Mo;
-              for (int k = 0; k < nc; ++k) Mn = fmaxf(Mn, s_wt[hh * CHS + k]);
-              const float sc = (Mo == kNegInf) ? 0.0f : __builtin_expf(Mo - Mn);
-              float den = s_den[hh] * sc;
-              for (int k = 0; k < nc; ++k) {
-                const float l = s_wt[hh * CHS + k];
-                const float wv = (l == kNegInf) ? 0.0f : __builtin_expf(l - Mn);
-                s_wt[hh * CHS + k] = wv;
-                den += wv;
-              }
-              s_M[hh] = Mn;
-              s_den[hh] = den;
-              s_sc[hh] = sc;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-              const int gi = pass0 + threadIdx.x + 256 * j;
-              if (gi < ngrp) {
-                const int hh = (4 * gi) / D;
-                f32x4 acc4 = num[j] * s_sc[hh];
-                const float* wrow = s_wt + hh * CHS;
-#pragma unroll 8
-                for (int k = 0; k < nc; ++k) {
-                  const f32x4 o4 = ld_coherent4(prs, (part_row(w_a + c0 + k) * D + 4 * gi) * 4);
-                  const float wv = wrow[k];
-                  acc4 += (wv > 0.0f) ? o4 * wv : f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-                num[j] = acc4;
-              }
-            }
-            __syncthreads();   // s_wt, s_M, s_den are rewritten next
-          }
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const int gi = pass0 + threadIdx.x + 256 * j;
-            if (gi < ngrp) {
-              const int hh = (4 * gi) / D, d = 4 * gi - hh * D;
-              const float den = s_den[hh];
-              const float inv = (s_M[hh] == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
-              const f32x4 o = num[j] * inv;
-              u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-              *reinterpret_cast<u32x2*>(a.out + ((size_t)b * a.Hq + g * G + hh) * D + d) = pk;
-            }
-          }
-          __syncthreads();   // every thread has read s_M / s_den before the next pass resets them
-        }
+        __hip_atomic_store(a.flags + 2 * w + slot, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    __syncthreads();   // LDS and s_last are reused by the next segment
+    __syncthreads();   // LDS is reused by the next segment
     cur = send;
     slot = 1;
+  }
+
+  if (pend) {
+    // ---- merge the unit whose last piece was this share's first segment.
+    // Its pieces are held by workgroups w_a..w; w_a holds it in its last
+    // slot when its share began before the unit, every other one in its
+    // first slot.
+    const int w_a = pend_wa;
+    const int nseg = w - w_a + 1;
+    const int first_slot_a = (share_lo(w_a) < pend_ustart) ? 1 : 0;
+    auto slot_of = [&](int wi) -> int { return wi == w_a ? first_slot_a : 0; };
+    auto part_row = [&](int wi) -> uint32_t { return (uint32_t)(((size_t)wi * 2 + slot_of(wi)) * G); };
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_s_waitcnt(0);   // this workgroup's own partial (wave 0) is complete
+      s_timeout = 0;
+    }
+    // Wait for the other holders' flags.  They have lower indices, so they
+    // were dispatched first and never wait on this workgroup; the wait is
+    // bounded all the same (a timeout yields NaN outputs).
+    for (int i = threadIdx.x; i < nseg - 1; i += 256) {
+      const uint32_t* f = a.flags + 2 * (w_a + i) + slot_of(w_a + i);
+      int spins = 0;
+      while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
+        if (++spins > (1 << 22)) {
+          s_timeout = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    const int bq = pend_b, gq = pend_g;
+    const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
+    // Merged 64 partials at a time with a running maximum per head (the sink
+    // is the initial maximum, with weight 1): per chunk the weights go to LDS
+    // and every thread accumulates float4 groups of the G x D outputs in
+    // registers.
+    constexpr int CHS = 64;   // partials per chunk
+    constexpr int NJ = 2;     // float4 groups per thread per pass
+    const int ngrp = G * D / 4;
+    float* s_wt = s_work;     // [G][CHS]
+    for (int pass0 = 0; pass0 < ngrp; pass0 += 256 * NJ) {
+      f32x4 num[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) num[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (threadIdx.x < G) {
+        const float sk = a.sinks ? a.sinks[gq * G + threadIdx.x] : kNegInf;
+        s_M[threadIdx.x] = sk;
+        s_den[threadIdx.x] = (sk != kNegInf) ? 1.0f : 0.0f;
+      }
+      for (int c0 = 0; c0 < nseg; c0 += CHS) {
+        const int nc = nseg - c0 < CHS ? nseg - c0 : CHS;
+        for (int i = threadIdx.x; i < G * CHS; i += 256) {
+          const int hh = i / CHS, k = i - hh * CHS;
+          s_wt[i] = k < nc ? __hip_atomic_load(a.part_lse + part_row(w_a + c0 + k) + hh, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : kNegInf;
+        }
+        __syncthreads();
+        if (threadIdx.x < G) {
+          const int hh = threadIdx.x;
+          const float Mo = s_M[hh];
+          float Mn = Mo;
+          for (int k = 0; k < nc; ++k) Mn = fmaxf(Mn, s_wt[hh * CHS + k]);
+          const float sc = (Mo == kNegInf) ? 0.0f : __builtin_expf(Mo - Mn);
+          float den = s_den[hh] * sc;
+          for (int k = 0; k < nc; ++k) {
+            const float l = s_wt[hh * CHS + k];
+            const float wv = (l == kNegInf) ? 0.0f : __builtin_expf(l - Mn);
+            s_wt[hh * CHS + k] = wv;
+            den += wv;
+          }
+          s_M[hh] = Mn;
+          s_den[hh] = den;
+          s_sc[hh] = sc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int gi = pass0 + threadIdx.x + 256 * j;
+          if (gi < ngrp) {
+            const int hh = (4 * gi) / D;
+            f32x4 acc4 = num[j] * s_sc[hh];
+            const float* wrow = s_wt + hh * CHS;
+#pragma unroll 8
+            for (int k = 0; k < nc; ++k) {
+              const f32x4 o4 = ld_coherent4(prs, (part_row(w_a + c0 + k) * D + 4 * gi) * 4);
+              const float wv = wrow[k];
+              acc4 += (wv > 0.0f) ? o4 * wv : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            num[j] = acc4;
+          }
+        }
+        __syncthreads();   // s_wt, s_M, s_den are rewritten next
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int gi = pass0 + threadIdx.x + 256 * j;
+        if (gi < ngrp) {
+          const int hh = (4 * gi) / D, d = 4 * gi - hh * D;
+          const float den = s_den[hh];
+          const float inv = (s_M[hh] == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
+          const f32x4 o = num[j] * inv;
+          u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+          *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
+        }
+      }
+      __syncthreads();   // every thread has read s_M / s_den before the next pass resets them
+    }
+    // Clear the consumed flags (a replayed graph reuses the epoch).
+    for (int i = threadIdx.x; i < nseg - 1; i += 256)
+      __hip_atomic_store(a.flags + 2 * (w_a + i) + slot_of(w_a + i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -35,7 +35,7 @@ struct DecodeArgs {
   const float* sinks;      // [Hq] or null
   float* part_o;           // [W][2][G][D] partial outputs (first / last segment of a workgroup)
   float* part_lse;         // [W][2][G]
-  unsigned long long* counters;  // [B * Hkv] arrivals per unit: (epoch << 32) | count
+  uint32_t* flags;         // [W][2] a slot's flag holds the call's epoch once its partial is complete
   uint32_t epoch;          // distinct per call
   int32_t tile_variant;    // kernel shape (tuning; 0 = default)
   int32_t min_tiles;       // fewest tiles per active workgroup (>= 1)
