@@ -149,6 +149,18 @@ int min_tiles() {
   return cached;
 }
 
+// Fixed cost of a unit (setup, combine, partial) in the share balance, in
+// quarter tiles (tunable through FP8PA_SEG_COST).
+int seg_cost() {
+  static int cached = -1;
+  if (cached < 0) {
+    const char* e = getenv("FP8PA_SEG_COST");
+    cached = e ? atoi(e) : 24;
+    if (cached < 0) cached = 0;
+  }
+  return cached;
+}
+
 // Compute units of the current device (0 when no device can be queried).
 int device_cus() {
   int dev = 0, n = 0;
@@ -278,6 +290,7 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
   a.tile_variant = tile_variant();
   a.min_tiles = min_tiles();
+  a.seg_cost = seg_cost();
   a.epoch = g_epoch.fetch_add(1) + 1;
   if (W > 1) {
     const int64_t po = (int64_t)W * 2 * G * D * 4;

@@ -90,6 +90,15 @@ __device__ __forceinline__ u32x4 load_e8_row(const uint8_t* p) {
   else return ld_global<u32x4>(p);
 }
 
+// floor(a / b) for 0 <= a < 2^53, 0 < b: a double-precision quotient
+// corrected by one step either way (much shorter than 64-bit integer division).
+__device__ __forceinline__ int64_t floordiv(int64_t a, int64_t b) {
+  int64_t q = (int64_t)((double)a / (double)b);
+  if (q * b > a) --q;
+  else if ((q + 1) * b <= a) ++q;
+  return q;
+}
+
 __device__ __forceinline__ uint32_t byte_of(const u32x4& v, int i) { return (v[i >> 2] >> (8 * (i & 3))) & 0xffu; }
 
 // Registers of one tile for one lane.
@@ -121,8 +130,9 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_M[16], s_den[16], s_sc[16];
-  __shared__ int s_wsum[kWaves];
+  __shared__ int s_wsum[kWaves], s_wsum_ne[kWaves];
   __shared__ int s_timeout;
+  __shared__ int64_t s_bnd[2];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -139,31 +149,51 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     const int tb = st & ~(TT - 1);
     return L > st ? (L - tb + TT - 1) / TT : 0;
   };
-  int* s_pre = s_dyn;
-  int* s_work_i = s_dyn + ((B + 4) & ~3);
+  int* s_pre = s_dyn;                       // [B + 1] tiles before sequence b
+  int* s_nep = s_dyn + ((B + 4) & ~3);      // [B + 1] non-empty sequences before b
+  int* s_work_i = s_nep + ((B + 4) & ~3);
   float* s_work = reinterpret_cast<float*>(s_work_i);
   {
     const int per = (B + 255) / 256;
     const int bb0 = threadIdx.x * per;
-    int local = 0;
-    for (int i = 0; i < per; ++i)
-      if (bb0 + i < B) local += tiles_of(a.seq_lens[bb0 + i]);
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    if (lane == 63) s_wsum[wave] = incl;
-    __syncthreads();
-    int excl = incl - local;
-    for (int i = 0; i < wave; ++i) excl += s_wsum[i];
+    int local = 0, lne = 0;
     for (int i = 0; i < per; ++i)
       if (bb0 + i < B) {
-        s_pre[bb0 + i] = excl;
-        excl += tiles_of(a.seq_lens[bb0 + i]);
+        const int nt = tiles_of(a.seq_lens[bb0 + i]);
+        local += nt;
+        lne += nt > 0;
       }
-    if (threadIdx.x == 0) s_pre[B] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    int incl = local, incl_ne = lne;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off), v2 = __shfl_up(incl_ne, off);
+      if (lane >= off) {
+        incl += v;
+        incl_ne += v2;
+      }
+    }
+    if (lane == 63) {
+      s_wsum[wave] = incl;
+      s_wsum_ne[wave] = incl_ne;
+    }
+    __syncthreads();
+    int excl = incl - local, excl_ne = incl_ne - lne;
+    for (int i = 0; i < wave; ++i) {
+      excl += s_wsum[i];
+      excl_ne += s_wsum_ne[i];
+    }
+    for (int i = 0; i < per; ++i)
+      if (bb0 + i < B) {
+        const int nt = tiles_of(a.seq_lens[bb0 + i]);
+        s_pre[bb0 + i] = excl;
+        s_nep[bb0 + i] = excl_ne;
+        excl += nt;
+        excl_ne += nt > 0;
+      }
+    if (threadIdx.x == 0) {
+      s_pre[B] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+      s_nep[B] = s_wsum_ne[0] + s_wsum_ne[1] + s_wsum_ne[2] + s_wsum_ne[3];
+    }
     __syncthreads();
   }
   const int64_t T = (int64_t)s_pre[B] * Hkv;
@@ -175,16 +205,65 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     for (int i = threadIdx.x; i < a.Hq * D; i += 256) o[i] = 0;
   }
 
-  // Active workgroups: W <= T, so every share holds at least one tile.
+  // Shares are balanced in cost: a tile costs TC = 4 and every (non-empty)
+  // unit a fixed SC more (its setup, wave combine and partial), laid out
+  // before its tiles.  Workgroup w takes the tiles whose cost start lies in
+  // [floor(w*Ct/W), floor((w+1)*Ct/W)).  Any cost window of SC + TC holds a
+  // tile start, so capping W at Ct / (SC + TC*min_tiles) keeps every share
+  // non-empty (at least min_tiles tiles' worth).  When units average at most
+  // one tile per wave, a split would only add merges: tiles then cost 0 and a
+  // unit 1, so shares are whole units (unit-aligned mode).
+  const int64_t U = (int64_t)Hkv * s_nep[B];
+  const bool unit_mode = T <= (int64_t)kWaves * U;
+  const int64_t TC = unit_mode ? 0 : 4;
+  const int64_t SC = unit_mode ? 1 : a.seg_cost;
+  const int64_t Ct = SC * U + TC * T;
   {
-    const int64_t want = (T + a.min_tiles - 1) / a.min_tiles;
+    int64_t want = Ct / (SC + TC * a.min_tiles);
+    if (want < 1) want = 1;
+    if (T == 0) want = 0;
     if (want < W) W = (int)want;
   }
   if (w >= W) return;
-
-  // Workgroup holding global tile t: the largest w with floor(w*T/W) <= t.
-  auto wg_of = [&](int64_t t) -> int { return (int)(((t + 1) * W + T - 1) / T - 1); };
-  auto share_lo = [&](int wi) -> int64_t { return (int64_t)wi * T / W; };
+  auto cpre = [&](int bb) -> int64_t { return SC * Hkv * s_nep[bb] + TC * (int64_t)Hkv * s_pre[bb]; };
+  // Cost start of tile i of unit (bb, gg).
+  auto tile_cost = [&](int bb, int gg, int i) -> int64_t {
+    const int nbb = s_pre[bb + 1] - s_pre[bb];
+    return cpre(bb) + (int64_t)gg * (SC + TC * nbb) + SC + TC * i;
+  };
+  // Workgroup holding a tile of cost start c: the largest w with floor(w*Ct/W) <= c.
+  auto wg_of_cost = [&](int64_t c) -> int { return (int)(floordiv((c + 1) * W + Ct - 1, Ct) - 1); };
+  // The share's first and end tiles: the first tile whose cost start is >=
+  // floor(w*Ct/W), resp. floor((w+1)*Ct/W), found by the thread whose
+  // sequence's cost range holds that point (T past the end).
+  {
+    const int64_t cb[2] = {floordiv((int64_t)w * Ct, W), floordiv((int64_t)(w + 1) * Ct, W)};
+    if (threadIdx.x < 2) s_bnd[threadIdx.x] = T;
+    __syncthreads();
+    const int per = (B + 255) / 256;
+    for (int i = 0; i < per; ++i) {
+      const int bb = threadIdx.x * per + i;
+      if (bb >= B) break;
+      const int64_t lo = cpre(bb), hiw = cpre(bb + 1);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int64_t c = cb[e];
+        if (c >= lo && c < hiw) {
+          const int nbb = s_pre[bb + 1] - s_pre[bb];
+          const int64_t span = SC + TC * nbb;
+          int64_t gg = floordiv(c - lo, span);
+          const int64_t r = c - lo - gg * span;
+          int64_t t = r <= SC ? 0 : (TC > 0 ? (r - SC + 3) >> 2 : nbb);
+          if (t >= nbb) {
+            t = 0;
+            ++gg;
+          }
+          s_bnd[e] = (int64_t)Hkv * s_pre[bb] + gg * nbb + t;
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   // Per-segment state (captured by the tile helpers below).
   int b = 0, g = 0, L = 0, start = 0, tbeg = 0, p_first = 0, nstaged = 1;
@@ -398,12 +477,11 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     }
   };
 
-  int64_t cur = (int64_t)w * T / W;
-  const int64_t hi = (int64_t)(w + 1) * T / W;
+  int64_t cur = s_bnd[0];
+  const int64_t hi = s_bnd[1];
   int slot = 0;
   // Unit to merge at the end of the share (uniform across the workgroup).
-  int pend = 0, pend_b = 0, pend_g = 0, pend_wa = 0;
-  int64_t pend_ustart = 0;
+  int pend = 0, pend_b = 0, pend_g = 0, pend_wa = 0, pend_first_slot_a = 0;
   while (cur < hi) {
     // ---- the segment: unit (b, g), tiles [ta, tc) of the unit.
     {
@@ -417,7 +495,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     }
     const int nb = s_pre[b + 1] - s_pre[b];
     const int64_t ubase = (int64_t)s_pre[b] * Hkv;
-    g = (int)((cur - ubase) / nb);
+    g = (int)floordiv(cur - ubase, nb);
     const int64_t ustart = ubase + (int64_t)g * nb;
     const int64_t uend = ustart + nb;
     const int64_t send = hi < uend ? hi : uend;
@@ -560,13 +638,16 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
                              (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : (M + __builtin_amdgcn_logf(Ltot)) * kLn2,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      const int w_a = wg_of(ustart), w_b = wg_of(uend - 1);
+      const int w_a = wg_of_cost(tile_cost(b, g, 0)), w_b = wg_of_cost(tile_cost(b, g, nb - 1));
       if (w == w_b) {
         // This is the unit's last piece: merge the unit at the end of the share.
         pend = 1;
         pend_b = b;
         pend_g = g;
-        pend_ustart = ustart;
+        // w_a's share holds an earlier segment (so this unit sits in its
+        // last slot) iff it starts at or before the previous unit's last
+        // tile, whose cost start is 4 below this unit's.
+        pend_first_slot_a = floordiv((int64_t)w_a * Ct, W) <= tile_cost(b, g, 0) - SC - TC ? 1 : 0;
         pend_wa = w_a;
       } else if (threadIdx.x == 0) {
         // Wave 0 wrote the partial; once its stores have completed at the
@@ -587,7 +668,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     // first slot.
     const int w_a = pend_wa;
     const int nseg = w - w_a + 1;
-    const int first_slot_a = (share_lo(w_a) < pend_ustart) ? 1 : 0;
+    const int first_slot_a = pend_first_slot_a;
     auto slot_of = [&](int wi) -> int { return wi == w_a ? first_slot_a : 0; };
     auto part_row = [&](int wi) -> uint32_t { return (uint32_t)(((size_t)wi * 2 + slot_of(wi)) * G); };
     if (threadIdx.x == 0) {
@@ -616,7 +697,8 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     // and every thread accumulates float4 groups of the G x D outputs in
     // registers.
     constexpr int CHS = 64;   // partials per chunk
-    constexpr int NJ = 2;     // float4 groups per thread per pass
+    constexpr int NJ = D >= 512 ? 4 : (D >= 256 ? 2 : 1);   // float4 groups per thread per pass
+    constexpr int KB = 8;     // partials whose loads are in flight together
     const int ngrp = G * D / 4;
     float* s_wt = s_work;     // [G][CHS]
     for (int pass0 = 0; pass0 < ngrp; pass0 += 256 * NJ) {
@@ -655,20 +737,37 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
           s_sc[hh] = sc;
         }
         __syncthreads();
+        {
+          // Loads of KB partials x NJ groups are issued together; absent
+          // ones use an offset past the buffer's range, which reads zero.
+          constexpr uint32_t kNone = 0xFFFFFFF0u;
+          int hhj[NJ];
+          uint32_t offj[NJ];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int gi = pass0 + threadIdx.x + 256 * j;
-          if (gi < ngrp) {
-            const int hh = (4 * gi) / D;
-            f32x4 acc4 = num[j] * s_sc[hh];
-            const float* wrow = s_wt + hh * CHS;
-#pragma unroll 8
-            for (int k = 0; k < nc; ++k) {
-              const f32x4 o4 = ld_coherent4(prs, (part_row(w_a + c0 + k) * D + 4 * gi) * 4);
-              const float wv = wrow[k];
-              acc4 += (wv > 0.0f) ? o4 * wv : f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < NJ; ++j) {
+            const int gi = pass0 + threadIdx.x + 256 * j;
+            hhj[j] = gi < ngrp ? (4 * gi) / D : 0;
+            offj[j] = gi < ngrp ? (uint32_t)(16 * gi) : kNone;
+            num[j] *= s_sc[hhj[j]];
+          }
+          for (int k0 = 0; k0 < nc; k0 += KB) {
+            f32x4 ov[NJ][KB];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+              const bool ok = k0 + kk < nc;
+              const uint32_t rb = ok ? part_row(w_a + c0 + k0 + kk) * (uint32_t)D * 4u : 0u;
+#pragma unroll
+              for (int j = 0; j < NJ; ++j) ov[j][kk] = ld_coherent4(prs, (ok && offj[j] != kNone) ? rb + offj[j] : kNone);
             }
-            num[j] = acc4;
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+              const int kx = k0 + kk < CHS ? k0 + kk : CHS - 1;
+#pragma unroll
+              for (int j = 0; j < NJ; ++j) {
+                const float wv = (k0 + kk < nc) ? s_wt[hhj[j] * CHS + kx] : 0.0f;
+                num[j] += (wv > 0.0f) ? ov[j][kk] * wv : f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+            }
           }
         }
         __syncthreads();   // s_wt, s_M, s_den are rewritten next
@@ -741,7 +840,7 @@ auto by_shape(int D, int v, F&& f) {
 
 size_t decode_lds_bytes(int D, int tile_variant, int B, int G, int P) {
   const int TT = decode_tile_tokens(D, tile_variant);
-  const size_t pre = (size_t)((B + 4) & ~3) * 4;
+  const size_t pre = (size_t)2 * ((B + 4) & ~3) * 4;
   const size_t stage = (size_t)(kMaxSplitTokens / TT * TT / P + 2) * 4;
   const size_t combine = (size_t)2 * G * (D + 4) * 4;
   return pre + (stage > combine ? stage : combine);

@@ -39,6 +39,7 @@ struct DecodeArgs {
   uint32_t epoch;          // distinct per call
   int32_t tile_variant;    // kernel shape (tuning; 0 = default)
   int32_t min_tiles;       // fewest tiles per active workgroup (>= 1)
+  int32_t seg_cost;        // fixed cost of a unit in the share balance, in quarter tiles (>= 0)
   PoolGeom kg, vg;
   int32_t P, log2P, B, Hq, Hkv, G, window;
   float qk_scale;          // sm_scale * log2(e)

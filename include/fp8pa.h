@@ -121,7 +121,7 @@ const char* fp8pa_last_error(void);
 /* Plan a decode call.  B sequences, Hq query heads, K pool `kd`; every
  * seq_lens[b] must be <= max_seq_len; window <= 0 means none; workgroups 0
  * lets the library choose, else it is used as given (>= 1).  Refuses
- * (FP8PA_EUNSUPPORTED) shapes whose LDS needs exceed 64 KiB (B above ~15000). */
+ * (FP8PA_EUNSUPPORTED) shapes whose LDS needs exceed 64 KiB (B above ~7500). */
 int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
                       int window, int workgroups, int variant, fp8pa_plan* out);
 
