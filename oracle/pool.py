@@ -22,7 +22,14 @@ orders, chosen so that a wave-wide 16-byte load covers whole 128-byte lines:
                  h*P*D + (t//W)*D*W + d*W + t%W
                  (values: token-contiguous per dim, in blocks of W tokens;
                  for P <= 64 this is [H][D][P])
-Scale footer (byte offset from ``scale_offset``):
+Row placement.  By default a row's payload starts at the row start and its
+scales at ``scale_offset``.  With ``align64`` (this library's option, for rows
+whose width is not a multiple of 64 bytes) the payload of row r starts at the
+first 64-byte boundary of the row, r*row_bytes + ((-r*row_bytes) mod 64) from
+the pool start, and the scale block sits in the gap before the payload when it
+fits there, else right after the payload.
+
+Scale footer (byte offset from the scale block's start):
   "page_head"  fp32 per (page, head):  4*h
   "token_head" fp32 per (token, head): 4*(h*P + t), or 4*(t*H + h) for "tokens"
   "e8m0_32"    one E8M0 byte per (token, head, 32 dims along D):
@@ -49,6 +56,7 @@ class PoolDesc:
     row_bytes: int
     num_rows: int
     scale_offset: Optional[int] = None
+    align64: bool = False
 
     @property
     def payload_bytes(self) -> int:
@@ -66,10 +74,21 @@ class PoolDesc:
     def natural_row_bytes(self) -> int:
         return self.payload_bytes + self.scale_bytes
 
+    def shifts(self):
+        """Payload shifts (bytes) that rows of this pool take."""
+        if not self.align64:
+            return [0]
+        return sorted({(-r * self.row_bytes) % 64 for r in range(64)})
+
     def check(self):
         assert self.layout in LAYOUTS and self.scale_kind in SCALE_KINDS
         assert self.footer + self.scale_bytes <= self.row_bytes
         assert self.footer >= self.payload_bytes
+        if self.align64:
+            assert self.scale_offset is None
+            for sh in self.shifts():
+                end = sh + self.payload_bytes if sh >= self.scale_bytes else sh + self.payload_bytes + self.scale_bytes
+                assert end <= self.row_bytes
         if self.scale_kind == "e8m0_32":
             assert self.head_dim % 32 == 0
         if self.layout == "heads_d64":
@@ -85,6 +104,23 @@ def natural_desc(num_kv_heads, head_dim, page_size, layout, scale_kind, num_rows
 
 
 # ---------------------------------------------------------------- addressing
+def row_code_base(desc: PoolDesc, rows):
+    """Byte offset of the payload of physical row(s) from the pool start."""
+    base = np.asarray(rows, dtype=np.int64) * desc.row_bytes
+    if not desc.align64:
+        return base
+    return base + (-base) % 64
+
+
+def row_scale_base(desc: PoolDesc, rows):
+    """Byte offset of the scale block of physical row(s) from the pool start."""
+    base = np.asarray(rows, dtype=np.int64) * desc.row_bytes
+    if not desc.align64:
+        return base + desc.footer
+    sh = (-base) % 64
+    return np.where(sh >= desc.scale_bytes, base, base + sh + desc.payload_bytes)
+
+
 def code_offset(desc: PoolDesc, h, t, d):
     H, P, D = desc.num_kv_heads, desc.page_size, desc.head_dim
     if desc.layout == "heads":
@@ -97,14 +133,21 @@ def code_offset(desc: PoolDesc, h, t, d):
     return h * P * D + (t // W) * D * W + d * W + t % W
 
 
-def scale_offset(desc: PoolDesc, h, t=0, g=0):
+def scale_rel(desc: PoolDesc, h, t=0, g=0):
+    """Offset of a scale inside the scale block."""
     H, P, D = desc.num_kv_heads, desc.page_size, desc.head_dim
     slot = (t * H + h) if desc.layout == "tokens" else (h * P + t)
     if desc.scale_kind == "page_head":
-        return desc.footer + 4 * h
+        return 4 * h
     if desc.scale_kind == "token_head":
-        return desc.footer + 4 * slot
-    return desc.footer + slot * (D // 32) + g
+        return 4 * slot
+    return slot * (D // 32) + g
+
+
+def scale_offset(desc: PoolDesc, h, t=0, g=0):
+    """Offset of a scale from the row start (pools without ``align64``)."""
+    assert not desc.align64
+    return desc.footer + scale_rel(desc, h, t, g)
 
 
 def _page_codes(pool, desc, rows, h):
@@ -113,22 +156,22 @@ def _page_codes(pool, desc, rows, h):
     t = np.arange(P)[:, None]
     d = np.arange(D)[None, :]
     off = code_offset(desc, h, t, d)                                   # [P, D]
-    base = np.asarray(rows, dtype=np.int64)[:, None, None] * desc.row_bytes
+    base = row_code_base(desc, rows)[:, None, None]
     return pool[base + off[None]]
 
 
 def _page_scales(pool, desc, rows, h):
     """Scales of head h for the rows, broadcastable against [n, P, D] (float64)."""
     P, D = desc.page_size, desc.head_dim
-    base = np.asarray(rows, dtype=np.int64) * desc.row_bytes
+    base = row_scale_base(desc, rows)
     if desc.scale_kind == "page_head":
-        idx = base[:, None] + scale_offset(desc, h) + np.arange(4)[None, :]
+        idx = base[:, None] + scale_rel(desc, h) + np.arange(4)[None, :]
         return pool[idx].copy().view(np.float32).astype(np.float64)[:, :, None]        # [n,1,1]
     if desc.scale_kind == "token_head":
-        offs = np.array([scale_offset(desc, h, t) for t in range(P)])
+        offs = np.array([scale_rel(desc, h, t) for t in range(P)])
         idx = base[:, None, None] + offs[None, :, None] + np.arange(4)[None, None, :]
         return pool[idx].copy().view(np.float32)[..., 0].astype(np.float64)[:, :, None]  # [n,P,1]
-    offs = np.array([[scale_offset(desc, h, t, g) for g in range(D // 32)] for t in range(P)])
+    offs = np.array([[scale_rel(desc, h, t, g) for g in range(D // 32)] for t in range(P)])
     u = pool[base[:, None, None] + offs[None]]                                         # [n,P,D/32]
     return np.repeat(fp8.E8M0_TABLE[u], 32, axis=-1)                                   # [n,P,D]
 
@@ -157,7 +200,7 @@ def _write_codes(pool, desc, row, h, t0, codes):
     n, D = codes.shape
     t = (t0 + np.arange(n))[:, None]
     d = np.arange(D)[None, :]
-    pool[row * desc.row_bytes + code_offset(desc, h, t, d)] = codes
+    pool[row_code_base(desc, row) + code_offset(desc, h, t, d)] = codes
 
 
 def _write_f32(pool, at, value):
@@ -206,15 +249,15 @@ def append_ref(pool, desc: PoolDesc, block_table, positions, x_new, counts=None)
                     for i in range(n):
                         c, s = fp8.quantize_fp32_block(x[i])
                         _write_codes(pool, desc, row, h, slot0 + i, c[None])
-                        _write_f32(pool, row * desc.row_bytes + scale_offset(desc, h, slot0 + i), s)
+                        _write_f32(pool, row_scale_base(desc, row) + scale_rel(desc, h, slot0 + i), s)
                 elif desc.scale_kind == "e8m0_32":
                     c, u = fp8.quantize_e8m0_g32(x)
                     _write_codes(pool, desc, row, h, slot0, c)
                     for i in range(n):
                         for g in range(D // 32):
-                            pool[row * desc.row_bytes + scale_offset(desc, h, slot0 + i, g)] = u[i, g]
+                            pool[row_scale_base(desc, row) + scale_rel(desc, h, slot0 + i, g)] = u[i, g]
                 else:
-                    at = row * desc.row_bytes + scale_offset(desc, h)
+                    at = int(row_scale_base(desc, row)) + scale_rel(desc, h)
                     s_old = 0.0 if slot0 == 0 else _read_f32(pool, at)
                     amax = float(np.abs(x).max()) if x.size else 0.0
                     cand = float(fp8.to_fp32(amax / fp8.E4M3_MAX)) if amax > 0 else 0.0
@@ -224,7 +267,7 @@ def append_ref(pool, desc: PoolDesc, block_table, positions, x_new, counts=None)
                     if slot0 > 0 and s_old > 0.0 and s_new > s_old:
                         tt = np.arange(slot0)[:, None]
                         dd = np.arange(D)[None, :]
-                        idx = row * desc.row_bytes + code_offset(desc, h, tt, dd)
+                        idx = row_code_base(desc, row) + code_offset(desc, h, tt, dd)
                         old = fp8.dequant_fp32(pool[idx], s_old)
                         pool[idx] = fp8.encode_e4m3(fp8.to_fp32(old / s_new))
                     _write_codes(pool, desc, row, h, slot0, fp8.encode_e4m3(fp8.to_fp32(x / s_new)))
@@ -262,20 +305,20 @@ def pack_sequences(pool, desc: PoolDesc, block_table, xs, heads=None):
             if desc.scale_kind == "page_head":
                 s = fp8.fp32_scale_from_amax(np.abs(xp).max(axis=(1, 2)))             # [n]
                 codes = fp8.encode_e4m3(fp8.to_fp32(xp / s[:, None, None]))
-                at = rows * desc.row_bytes + scale_offset(desc, h)
+                at = row_scale_base(desc, rows) + scale_rel(desc, h)
                 pool[at[:, None] + np.arange(4)[None, :]] = s.astype(np.float32).view(np.uint8).reshape(-1, 4)
             elif desc.scale_kind == "token_head":
                 s = fp8.fp32_scale_from_amax(np.abs(xp).max(axis=2))                  # [n, P]
                 codes = fp8.encode_e4m3(fp8.to_fp32(xp / s[..., None]))
-                offs = np.array([scale_offset(desc, h, t) for t in range(P)])
-                idx = rows[:, None, None] * desc.row_bytes + offs[None, :, None] + np.arange(4)[None, None, :]
+                offs = np.array([scale_rel(desc, h, t) for t in range(P)])
+                idx = row_scale_base(desc, rows)[:, None, None] + offs[None, :, None] + np.arange(4)[None, None, :]
                 vals = s.astype(np.float32).view(np.uint8).reshape(n_pages, P, 4)
                 pool[idx[valid]] = vals[valid]
             else:
                 codes, u = fp8.quantize_e8m0_g32(xp)                                  # u [n, P, D/32]
-                offs = np.array([[scale_offset(desc, h, t, g) for g in range(D // 32)] for t in range(P)])
-                idx = rows[:, None, None] * desc.row_bytes + offs[None]
+                offs = np.array([[scale_rel(desc, h, t, g) for g in range(D // 32)] for t in range(P)])
+                idx = row_scale_base(desc, rows)[:, None, None] + offs[None]
                 pool[idx[valid]] = u[valid]
-            idx = rows[:, None, None] * desc.row_bytes + code_offset(desc, h, tt, dd)[None]   # [n, P, D]
+            idx = row_code_base(desc, rows)[:, None, None] + code_offset(desc, h, tt, dd)[None]   # [n, P, D]
             pool[idx[valid]] = codes[valid]
     return pool

@@ -199,3 +199,55 @@ def test_row_layout_matches_reshape_views(layout, kind, P, D):
         got = opool.read_tokens(p.k_pool, d, p.table[0], np.arange(P), h)
         assert np.array_equal(got, want[h])
     assert np.array_equal(np.sort(r[:d.payload_bytes]), np.sort(codes.ravel()))
+
+
+@pytest.mark.parametrize("layout,H,P,D,kind,rb", [
+    ("heads_d64", 8, 16, 128, "page_head", 16384 + 32),      # rows 32 bytes past a 64-byte multiple
+    ("heads_dmajor", 8, 16, 64, "page_head", 8192 + 32),
+    ("heads_dmajor", 2, 32, 512, "page_head", 65536 + 32),   # scales (8 B) fit in a 32-byte gap
+    ("heads", 2, 16, 64, "token_head", 2048 + 128 + 48),      # shifts 0, 16, 32, 48
+    ("tokens", 2, 16, 64, "e8m0_32", 2048 + 64 + 48),
+])
+def test_align64_rows(layout, H, P, D, kind, rb):
+    """Aligned rows: every payload starts on a 64-byte boundary of the pool,
+    payload and scales stay inside their row without overlapping, and the
+    pool decodes to exactly what the unaligned placement of the same data
+    decodes to."""
+    rows = 9
+    plain = opool.PoolDesc(H, D, P, layout, kind, rb, rows)
+    al = replace(plain, align64=True)
+    plain.check()
+    al.check()
+    r = np.arange(rows)
+    cb = opool.row_code_base(al, r)
+    sb = opool.row_scale_base(al, r)
+    assert np.all(cb % 64 == 0)
+    assert np.all(cb >= r * rb) and np.all(cb + al.payload_bytes <= (r + 1) * rb)
+    assert np.all(sb >= r * rb) and np.all(sb + al.scale_bytes <= (r + 1) * rb)
+    assert np.all((sb + al.scale_bytes <= cb) | (sb >= cb + al.payload_bytes))
+    rng = np.random.default_rng(5)
+    L = rows * P - 3
+    table = [rng.permutation(rows)]
+    x = rng.standard_normal((L, H, D))
+    pp = opool.pack_sequences(np.zeros(rows * rb, np.uint8), plain, table, [x])
+    pa = opool.pack_sequences(np.zeros(rows * rb, np.uint8), al, table, [x])
+    pos = np.arange(L)
+    for h in range(H):
+        np.testing.assert_array_equal(opool.read_tokens(pa, al, table[0], pos, h),
+                                      opool.read_tokens(pp, plain, table[0], pos, h))
+    # the same holds for the token-by-token append (page scales that grow)
+    pos0 = np.zeros(1, np.int64)
+    xa = rng.standard_normal((1, 2 * P + 1, H, D))
+    qa = opool.append_ref(np.zeros(rows * rb, np.uint8), al, table, pos0, xa)
+    qp = opool.append_ref(np.zeros(rows * rb, np.uint8), plain, table, pos0, xa)
+    for h in range(H):
+        np.testing.assert_array_equal(opool.read_tokens(qa, al, table[0], np.arange(2 * P + 1), h),
+                                      opool.read_tokens(qp, plain, table[0], np.arange(2 * P + 1), h))
+
+
+def test_align64_needs_room():
+    """A row too narrow for some payload shift is refused."""
+    d = opool.PoolDesc(2, 64, 16, "heads", "token_head", 2048 + 128 + 48, 4, align64=True)
+    d.check()
+    with pytest.raises(AssertionError):
+        replace(d, row_bytes=2048 + 128 + 48 - 64).check()
