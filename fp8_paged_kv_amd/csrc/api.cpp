@@ -62,7 +62,7 @@ int64_t footer_offset(const fp8pa_pool_desc& d) {
 // Checks one pool descriptor; returns 0 or an error code (message set).
 int check_desc(const fp8pa_pool_desc* d, const char* name) {
   if (!d) return fail(FP8PA_EINVAL, "%s: descriptor is NULL", name);
-  if (d->reserved != 0) return fail(FP8PA_EINVAL, "%s: reserved field must be 0", name);
+  if (d->flags != 0 && d->flags != FP8PA_POOL_ALIGN64) return fail(FP8PA_EINVAL, "%s: unknown flags %d", name, d->flags);
   if (d->num_kv_heads < 1) return fail(FP8PA_EINVAL, "%s: num_kv_heads must be >= 1", name);
   if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256 && d->head_dim != 512)
     return fail(FP8PA_EUNSUPPORTED, "%s: head_dim %d not in {64,128,256,512}", name, d->head_dim);
@@ -82,6 +82,17 @@ int check_desc(const fp8pa_pool_desc* d, const char* name) {
   if (foot + scale_bytes(*d) > d->row_bytes)
     return fail(FP8PA_EINVAL, "%s: payload + scales (%lld) exceed row_bytes %lld", name,
                 (long long)(foot + scale_bytes(*d)), (long long)d->row_bytes);
+  if (d->flags & FP8PA_POOL_ALIGN64) {
+    if (d->scale_offset >= 0) return fail(FP8PA_EINVAL, "%s: aligned rows need the default scale_offset", name);
+    // Every payload shift the rows take must leave room for payload and scales.
+    for (int64_t r = 0; r < 64; ++r) {
+      const int64_t sh = (-(r * d->row_bytes)) & 63;
+      const int64_t end = sh >= scale_bytes(*d) ? sh + payload : sh + payload + scale_bytes(*d);
+      if (end > d->row_bytes)
+        return fail(FP8PA_EINVAL, "%s: row_bytes %lld leave no room for a payload shifted by %lld bytes", name,
+                    (long long)d->row_bytes, (long long)sh);
+    }
+  }
   if (d->num_rows < 0) return fail(FP8PA_EINVAL, "%s: num_rows must be >= 0", name);
   if (d->row_bytes > INT64_MAX / (d->num_rows > 0 ? d->num_rows : 1))
     return fail(FP8PA_EINVAL, "%s: pool size overflows", name);
@@ -94,6 +105,9 @@ fp8pa::PoolGeom geometry(const fp8pa_pool_desc& d) {
   const int H = d.num_kv_heads, P = d.page_size, D = d.head_dim;
   g.row_bytes = d.row_bytes;
   g.sc_off = (int32_t)footer_offset(d);
+  g.align64 = (d.flags & FP8PA_POOL_ALIGN64) ? 1 : 0;
+  g.payload_bytes = P * H * D;
+  g.scale_bytes = (int32_t)scale_bytes(d);
   const bool tok = d.layout == FP8PA_LAYOUT_TOKENS;
   g.tblk = P;
   g.tblk_stride = 0;
@@ -254,6 +268,8 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
     return fail(FP8PA_EINVAL, "a required device pointer is NULL");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(FP8PA_EINVAL, "q and out must be 16-byte aligned");
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return fail(FP8PA_EINVAL, "pools must be 16-byte aligned");
+  if (((kd->flags & FP8PA_POOL_ALIGN64) && !aligned(k_pool, 64)) || ((vd->flags & FP8PA_POOL_ALIGN64) && !aligned(v_pool, 64)))
+    return fail(FP8PA_EINVAL, "pools with aligned rows must be 64-byte aligned");
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4)) return fail(FP8PA_EINVAL, "block_table/seq_lens misaligned");
   if (sinks && !aligned(sinks, 4)) return fail(FP8PA_EINVAL, "sinks misaligned");
   if (bt_stride < 1) return fail(FP8PA_EINVAL, "bt_stride must be >= 1");
@@ -359,6 +375,8 @@ int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, ui
   if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(block_table, 4) || !aligned(positions, 4) || (counts && !aligned(counts, 4)))
     return fail(FP8PA_EINVAL, "misaligned pointer");
+  if (((kd->flags & FP8PA_POOL_ALIGN64) && !aligned(k_pool, 64)) || ((vd->flags & FP8PA_POOL_ALIGN64) && !aligned(v_pool, 64)))
+    return fail(FP8PA_EINVAL, "pools with aligned rows must be 64-byte aligned");
   if (bt_stride < 1) return fail(FP8PA_EINVAL, "bt_stride must be >= 1");
   fp8pa::AppendArgs a{};
   a.k_new = static_cast<const uint16_t*>(k_new);

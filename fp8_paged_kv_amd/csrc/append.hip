@@ -66,8 +66,9 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   const int lo = max(pos0, page * P), hi = min(pos0 + nb, (page + 1) * P);
   const int slot0 = lo - page * P, nn = hi - lo;
   const int32_t row = a.bt[(int64_t)b * a.bt_stride + page];
-  uint8_t* rowp = pool + (int64_t)row * gm.row_bytes + (int64_t)h * gm.head_stride;
-  uint8_t* foot = pool + (int64_t)row * gm.row_bytes + gm.sc_off + (int64_t)h * gm.sc_head_stride;
+  const RowBases rbase = row_bases(gm, row);
+  uint8_t* rowp = pool + rbase.code + (int64_t)h * gm.head_stride;
+  uint8_t* foot = pool + rbase.scale + (int64_t)h * gm.sc_head_stride;
   const uint16_t* x = xin + (((size_t)b * a.T + (lo - pos0)) * H + h) * D;   // token i at x + i*H*D
   const int64_t xtok = (int64_t)H * D;
 

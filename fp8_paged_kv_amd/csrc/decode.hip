@@ -295,8 +295,9 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     const int32_t row_k = row_of(tk >> log2P);
     const int32_t row_q = row_of(tq >> log2P);
     const int tpq = tq & (P - 1);
-    const uint8_t* ksc = a.kp + (int64_t)row_q * a.kg.row_bytes + a.kg.sc_off + g * a.kg.sc_head_stride;
-    const uint8_t* vsc = a.vp + (int64_t)row_q * a.vg.row_bytes + a.vg.sc_off + g * a.vg.sc_head_stride;
+    const RowBases rk = row_bases(a.kg, row_k), rqk = row_bases(a.kg, row_q), rqv = row_bases(a.vg, row_q);
+    const uint8_t* ksc = a.kp + rqk.scale + g * a.kg.sc_head_stride;
+    const uint8_t* vsc = a.vp + rqv.scale + g * a.vg.sc_head_stride;
     if constexpr (SK == 0) {
       t.ks = ld_global<float>(ksc);
       t.vs = ld_global<float>(vsc);
@@ -321,12 +322,12 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa) {
           const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
-          const uint8_t* kf = a.kp + (int64_t)row_k * a.kg.row_bytes + a.kg.sc_off + g * a.kg.sc_head_stride +
+          const uint8_t* kf = a.kp + rk.scale + g * a.kg.sc_head_stride +
                               tp * a.kg.sc_tok_stride;
           t.ke8[s][aa] = load_e8_row<NG>(kf);
         }
     }
-    const uint8_t* krow = kpool + (int64_t)row_k * a.kg.row_bytes + 16 * quad;
+    const uint8_t* krow = kpool + rk.code + 16 * quad;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
         }
       }
     // The lane's GT positions lie in one token block of the d-major V layout.
-    const uint8_t* vrow = vpool + (int64_t)row_q * a.vg.row_bytes + (int64_t)(tpq / a.vg.tblk) * a.vg.tblk_stride +
+    const uint8_t* vrow = vpool + rqv.code + (int64_t)(tpq / a.vg.tblk) * a.vg.tblk_stride +
                           (tpq % a.vg.tblk);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {

@@ -22,7 +22,21 @@ struct PoolGeom {
   int32_t sc_off;          // scale footer offset in the row
   int32_t sc_head_stride;  // footer bytes between heads
   int32_t sc_tok_stride;   // footer bytes between tokens (0 for per-page scales)
+  int32_t align64;         // rows placed by FP8PA_POOL_ALIGN64
+  int32_t payload_bytes;   // P * Hkv * D
+  int32_t scale_bytes;     // bytes of a row's scale block
 };
+
+// Byte offsets, from the pool base, of row r's payload and scale block.
+struct RowBases {
+  int64_t code, scale;
+};
+__host__ __device__ inline RowBases row_bases(const PoolGeom& g, int64_t r) {
+  const int64_t base = r * g.row_bytes;
+  if (!g.align64) return {base, base + g.sc_off};
+  const int64_t sh = (-base) & 63;
+  return {base + sh, sh >= g.scale_bytes ? base : base + sh + g.payload_bytes};
+}
 
 struct DecodeArgs {
   const uint16_t* q;       // bf16 [B, Hq, D]

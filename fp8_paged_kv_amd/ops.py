@@ -24,7 +24,7 @@ class Fp8paError(RuntimeError):
 
 class PoolDesc(ctypes.Structure):
     _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("layout", ctypes.c_int32), ("scale_kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("scale_kind", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("row_bytes", ctypes.c_int64), ("scale_offset", ctypes.c_int64), ("num_rows", ctypes.c_int64)]
 
 
@@ -82,9 +82,14 @@ def _check(rc):
         raise Fp8paError(rc, last_error())
 
 
-def pool_desc(num_kv_heads, head_dim, page_size, layout, scale_kind, row_bytes, num_rows, scale_offset=-1):
+POOL_ALIGN64 = 1
+
+
+def pool_desc(num_kv_heads, head_dim, page_size, layout, scale_kind, row_bytes, num_rows, scale_offset=-1,
+              align64=False):
     return PoolDesc(num_kv_heads, head_dim, page_size, LAYOUTS.get(layout, layout),
-                    SCALE_KINDS.get(scale_kind, scale_kind), 0, row_bytes, scale_offset, num_rows)
+                    SCALE_KINDS.get(scale_kind, scale_kind), POOL_ALIGN64 if align64 else 0, row_bytes,
+                    scale_offset, num_rows)
 
 
 def _ptr(t):

@@ -56,6 +56,21 @@ def raw_kv(seed, wl, layer_index, b, tensor, n_pos, Hkv, D):
     return inputs.normal_bf16(seed, wl.index, tensor, layer_index * 4096 + b, (n_pos, Hkv, D))
 
 
+def scale_block_bytes(scale_kind, Hkv, P, D):
+    return {"page_head": 4 * Hkv, "token_head": 4 * Hkv * P, "e8m0_32": Hkv * P * D // 32}[scale_kind]
+
+
+def rows_can_align(row_bytes, payload, scales):
+    """Whether every payload shift rows of this width take (to the 64-byte
+    grid) leaves room for the payload and the scale block."""
+    for r in range(64):
+        sh = (-r * row_bytes) % 64
+        end = sh + payload if sh >= scales else sh + payload + scales
+        if end > row_bytes:
+            return False
+    return True
+
+
 def first_attended_page(L, window, P):
     start = max(0, L - window) if window > 0 else 0
     return start // P
@@ -93,8 +108,12 @@ def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", lay
         lay = wl.layers[li]
         table, pool_rows = tables[li]
         rb = lay.row_bytes
-        kd = ops.pool_desc(lay.Hkv, lay.D, P, "heads_d64", wl.scale_kind, rb, pool_rows)
-        vd = ops.pool_desc(lay.Hkv, lay.D, P, "heads_dmajor", wl.scale_kind, rb, pool_rows)
+        # Rows are placed with their payloads on the 64-byte grid when the row
+        # width leaves room for it (the row widths carry a 32-byte scale
+        # footer, so half the rows would start 32 bytes off the grid).
+        al = rows_can_align(rb, P * lay.Hkv * lay.D, scale_block_bytes(wl.scale_kind, lay.Hkv, P, lay.D))
+        kd = ops.pool_desc(lay.Hkv, lay.D, P, "heads_d64", wl.scale_kind, rb, pool_rows, align64=al)
+        vd = ops.pool_desc(lay.Hkv, lay.D, P, "heads_dmajor", wl.scale_kind, rb, pool_rows, align64=al)
         if wl.shared_pool and "k" in shared:
             k_pool, v_pool = shared["k"], shared["v"]
         else:

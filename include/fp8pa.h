@@ -83,6 +83,17 @@ enum {
   FP8PA_VARIANT_MFMA_BF16 = 1   /* E4M3 -> bf16 exactly, bf16 MFMA, fp32 accumulate */
 };
 
+/* ---- row placement flags (fp8pa_pool_desc.flags).
+ *   FP8PA_POOL_ALIGN64  the payload of row r starts at the row's first 64-byte
+ *       boundary, r*row_bytes + ((-r*row_bytes) mod 64) bytes from the pool
+ *       base (which must then be 64-byte aligned), and the scale block sits
+ *       in the gap before the payload when it fits there, else right after
+ *       the payload.  For rows whose width is not a multiple of 64 bytes
+ *       (a 32-byte scale footer, say), this keeps every 64-byte memory unit
+ *       of the payload inside one wave-wide load.  Needs the default
+ *       scale_offset and a row wide enough for every shift its rows take. */
+enum { FP8PA_POOL_ALIGN64 = 1 };
+
 /* One pool (K or V) of one layer.  K and V pools may differ in layout and
  * stride; several layers may share a pool through row_bytes. */
 typedef struct fp8pa_pool_desc {
@@ -91,7 +102,7 @@ typedef struct fp8pa_pool_desc {
   int32_t page_size;     /* P tokens per row: a power of two in [16, 1024] */
   int32_t layout;        /* FP8PA_LAYOUT_* */
   int32_t scale_kind;    /* FP8PA_SCALE_* */
-  int32_t reserved;      /* must be 0 */
+  int32_t flags;         /* 0 or FP8PA_POOL_ALIGN64 */
   int64_t row_bytes;     /* stride between rows; multiple of 16, >= natural row */
   int64_t scale_offset;  /* footer offset in the row; multiple of 16, >= P*Hkv*D;
                             -1 selects the default P*Hkv*D */

@@ -22,7 +22,7 @@ def say(*a):
 def desc_of(d):
     """ops.PoolDesc from an oracle PoolDesc."""
     return ops.pool_desc(d.num_kv_heads, d.head_dim, d.page_size, d.layout, d.scale_kind, d.row_bytes, d.num_rows,
-                         -1 if d.scale_offset is None else d.scale_offset)
+                         -1 if d.scale_offset is None else d.scale_offset, align64=d.align64)
 
 
 def device_problem(p):

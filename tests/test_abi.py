@@ -106,10 +106,24 @@ def test_decode_refuses_before_launch(case, code):
     assert c["errors"] == 1
 
 
-def test_reserved_field_must_be_zero():
+def test_unknown_flags_are_refused():
     k = kd()
-    k.reserved = 1
+    k.flags = 2
     assert call_decode(k=k) == ops.EINVAL
+
+
+@pytest.mark.parametrize("case", [
+    dict(k=kd(align64=True, scale_offset=16384)),               # aligned rows need the default footer
+    dict(k=kd(head_dim=64, num_kv_heads=2, row_bytes=2048 + 128 + 48 - 64, scale_kind="token_head",
+              align64=True),
+         v=vd(head_dim=64, num_kv_heads=2, row_bytes=2048 + 128 + 48 - 64, scale_kind="token_head"),
+         Hq=8, bt_stride=600),                                    # no room for a 48-byte shift
+    dict(k=kd(align64=True), k_pool=F + 16),                     # aligned rows need a 64-byte aligned pool
+])
+def test_aligned_rows_are_checked(case):
+    ops.reset_counters()
+    assert call_decode(**case) == ops.EINVAL, ops.last_error()
+    assert ops.counters()["decode_calls"] == 0
 
 
 def test_empty_batch_is_a_no_op():

@@ -13,11 +13,17 @@ from tests.problems import round16
 pytestmark = pytest.mark.gpu
 
 
-def make(kind, layout, H=2, D=64, P=16, lens=(40, 17), seed=3):
+def make(kind, layout, H=2, D=64, P=16, lens=(40, 17), seed=3, align64=False):
     table, rows = inputs.block_table(seed, 5, lens, P)
     d = opool.natural_desc(H, D, P, layout, kind, rows)
     from dataclasses import replace
     d = replace(d, row_bytes=round16(d.row_bytes))
+    if align64:
+        # a row width off the 64-byte grid, with room for every payload shift
+        rb = d.row_bytes + 48
+        rb += (32 - rb % 64) % 64 if rb % 64 != 32 else 0
+        d = replace(d, row_bytes=rb, align64=True)
+        d.check()
     return table, d
 
 
@@ -126,3 +132,34 @@ def test_bulk_append_large_pages_bit_exact(kind, P):
     gk, gv = run_gpu(empty_k, empty_v, kd, vd, table, [0, 0], xk, xv, counts=lens)
     assert np.array_equal(gk, opool.append_ref(empty_k, kd, table, [0, 0], xk, counts=lens))
     assert np.array_equal(gv, opool.append_ref(empty_v, vd, table, [0, 0], xv, counts=lens))
+
+
+@pytest.mark.parametrize("kind", opool.SCALE_KINDS)
+@pytest.mark.parametrize("klayout,vlayout", [("heads_d64", "heads_dmajor"), ("tokens", "heads_dmajor")])
+def test_append_aligned_rows_bit_exact(kind, klayout, vlayout):
+    """Rows 32 bytes off the 64-byte grid, payloads placed on it: bulk writes,
+    then T=1 appends with growing page scales, byte-for-byte as the oracle."""
+    say("aligned append", kind, klayout, vlayout)
+    lens = [70, 33]
+    table, kd = make(kind, klayout, D=128, lens=lens, align64=True)
+    _, vd = make(kind, vlayout, D=128, lens=lens, align64=True)
+    from dataclasses import replace
+    vd = replace(vd, num_rows=kd.num_rows)
+    T = max(lens)
+    xk = np.stack([inputs.normal_bf16(2, 0, "k", b, (T, 2, 128)) for b in range(2)])
+    xv = np.stack([inputs.normal_bf16(2, 0, "v", b, (T, 2, 128)) for b in range(2)])
+    k0 = np.full(kd.num_rows * kd.row_bytes, 0xFF, np.uint8)
+    v0 = np.full(vd.num_rows * vd.row_bytes, 0xFF, np.uint8)
+    gk, gv = run_gpu(k0, v0, kd, vd, table, [0, 0], xk, xv, counts=[40, 20])
+    wk = opool.append_ref(k0, kd, table, [0, 0], xk, counts=[40, 20])
+    wv = opool.append_ref(v0, vd, table, [0, 0], xv, counts=[40, 20])
+    assert np.array_equal(gk, wk) and np.array_equal(gv, wv)
+    for step in range(3):
+        pos = [40 + step, 20 + step]
+        x1k = xk[:, 40 + step:41 + step] * np.float32(1.5 ** step)
+        x1v = xv[:, 40 + step:41 + step] * np.float32(1.5 ** step)
+        x1k, x1v = inputs.round_to_bf16(x1k), inputs.round_to_bf16(x1v)
+        gk, gv = run_gpu(gk, gv, kd, vd, table, pos, x1k, x1v)
+        wk = opool.append_ref(wk, kd, table, pos, x1k)
+        wv = opool.append_ref(wv, vd, table, pos, x1v)
+        assert np.array_equal(gk, wk) and np.array_equal(gv, wv), f"step {step}"

@@ -28,6 +28,12 @@ CASES = [
     ("d128-g4", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[513, 64, 1])),
     ("d128-g8-sinks", dict(B=2, Hq=16, Hkv=2, D=128, P=16, lens=[400, 77], sinks=True)),
     ("d64-g8-window", dict(B=3, Hq=16, Hkv=2, D=64, P=16, lens=[500, 100, 20], window=128, sinks=True)),
+    # rows 32 bytes off the 64-byte grid, payloads placed on it
+    ("d128-aligned-rows", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[700, 65, 300], row_pad=32, align64=True)),
+    ("d64-aligned-rows-window", dict(B=2, Hq=16, Hkv=2, D=64, P=16, lens=[900, 130], row_pad=80, align64=True,
+                                     window=200, sinks=True)),
+    ("d512-aligned-rows", dict(B=2, Hq=16, Hkv=2, D=512, P=32, lens=[300, 97], row_pad=16, align64=True,
+                               sm_scale=1.0)),
     ("d256-g2-window-scale1", dict(B=2, Hq=4, Hkv=2, D=256, P=32, lens=[700, 33], window=100, sm_scale=1.0)),
     ("d512-g8-scale1", dict(B=2, Hq=8, Hkv=1, D=512, P=32, lens=[333, 64], sm_scale=1.0)),
     ("d128-e8m0-p128", dict(B=2, Hq=16, Hkv=2, D=128, P=128, lens=[1000, 130], scale_kind="e8m0_32")),

@@ -17,9 +17,11 @@ pytestmark = pytest.mark.gpu
 
 def oracle_panel(wl, layer, b, g, seed=configs.SEED):
     """Host pools holding sequence b, KV head g of the layer, quantized by the oracle."""
-    kd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads_d64", layer.scale_kind, layer.row_bytes, layer.pool_rows)
+    al = bool(layer.kd.flags & 1)
+    kd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads_d64", layer.scale_kind, layer.row_bytes, layer.pool_rows,
+                        align64=al)
     vd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads_dmajor", layer.scale_kind, layer.row_bytes,
-                        layer.pool_rows)
+                        layer.pool_rows, align64=al)
     L, first = int(layer.lens[b]), int(layer.first_pos[b])
     n = L - first
     xk = workloads.raw_kv(seed, wl, layer.layer_index, b, "k", n, layer.Hkv, layer.D)
@@ -44,13 +46,15 @@ def panel_byte_index(desc, rows, g):
     d = np.arange(D)[None, :]
     code = opool.code_offset(desc, g, t, d).ravel()
     if desc.scale_kind == "page_head":
-        sc = opool.scale_offset(desc, g) + np.arange(4)
+        sc = opool.scale_rel(desc, g) + np.arange(4)
     elif desc.scale_kind == "token_head":
-        sc = np.array([opool.scale_offset(desc, g, tt) + i for tt in range(P) for i in range(4)])
+        sc = np.array([opool.scale_rel(desc, g, tt) + i for tt in range(P) for i in range(4)])
     else:
-        sc = np.array([opool.scale_offset(desc, g, tt, gg) for tt in range(P) for gg in range(D // 32)])
-    offs = np.concatenate([code, sc])
-    return (np.asarray(rows, np.int64)[:, None] * desc.row_bytes + offs[None, :]).ravel()
+        sc = np.array([opool.scale_rel(desc, g, tt, gg) for tt in range(P) for gg in range(D // 32)])
+    rows = np.asarray(rows, np.int64)
+    cb = opool.row_code_base(desc, rows)[:, None] + code[None, :]
+    sb = opool.row_scale_base(desc, rows)[:, None] + sc[None, :]
+    return np.concatenate([cb, sb], axis=1).ravel()
 
 
 def check_panel(wl, layer, out_np, b, g):
