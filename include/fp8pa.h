@@ -154,7 +154,11 @@ int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
  *   sm_scale    finite score scale (D ** -0.5 is the usual value).
  *   max_seq_len, workgroups, variant: as for fp8pa_decode_plan.
  *   workspace   device buffer of >= plan.workspace_bytes (256-byte aligned),
- *               or NULL when that is 0.  Its contents need no initialisation.
+ *               or NULL when that is 0.  Its contents need no initialisation
+ *               (split partials are published with flags tagged by a per-call
+ *               epoch, and cleared once merged, so a replayed graph starts
+ *               clean).  Calls that share a workspace must not overlap: issue
+ *               them on one stream.
  * Output rows are bf16 (round to nearest even) of the fp32 result.
  */
 int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t* v_pool,
