@@ -90,13 +90,22 @@ __device__ __forceinline__ u32x4 load_e8_row(const uint8_t* p) {
   else return ld_global<u32x4>(p);
 }
 
-// floor(a / b) for 0 <= a < 2^53, 0 < b: a double-precision quotient
-// corrected by one step either way (much shorter than 64-bit integer division).
+// floor(a / b) for 0 <= a < 2^53, 0 < b: 32-bit division when both fit,
+// else a double-precision quotient corrected by one step either way (much
+// shorter than 64-bit integer division).
 __device__ __forceinline__ int64_t floordiv(int64_t a, int64_t b) {
+  if ((((uint64_t)a | (uint64_t)b) >> 32) == 0) return (int64_t)((uint32_t)a / (uint32_t)b);
   int64_t q = (int64_t)((double)a / (double)b);
   if (q * b > a) --q;
   else if ((q + 1) * b <= a) ++q;
   return q;
+}
+
+// A 64-bit value of lane l (l uniform).
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t byte_of(const u32x4& v, int i) { return (v[i >> 2] >> (8 * (i & 3))) & 0xffu; }
@@ -123,16 +132,16 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   constexpr int NQ = D / 32;    // QK MFMAs per 16 positions
   constexpr int NC = D / 16;    // PV MFMAs per subtile (16 dims each)
   constexpr int NG = D / 32;    // E8M0 groups along D
-  constexpr int CH = kMaxSplitTokens / TT;   // tiles whose page rows are staged at once
   typedef Tile<D, NS, SK> TileT;
 
-  extern __shared__ int s_dyn[];   // [B + 1] tile prefix, then the page-row stage / wave-combine buffer
+  extern __shared__ int s_dyn[];   // tile prefix, non-empty prefix, lengths, then the page-row stage / wave-combine buffer
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_M[16], s_den[16], s_sc[16];
   __shared__ int s_wsum[kWaves], s_wsum_ne[kWaves];
   __shared__ int s_timeout;
   __shared__ int64_t s_bnd[2];
+  __shared__ int s_first[3];   // capped W and the first segment's (b, g), from wave 0
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -151,15 +160,140 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   };
   int* s_pre = s_dyn;                       // [B + 1] tiles before sequence b
   int* s_nep = s_dyn + ((B + 4) & ~3);      // [B + 1] non-empty sequences before b
-  int* s_work_i = s_nep + ((B + 4) & ~3);
+  int* s_len = s_nep + ((B + 4) & ~3);      // [B] seq_lens, read from global memory once
+  int* s_work_i = s_len + ((B + 4) & ~3);
   float* s_work = reinterpret_cast<float*>(s_work_i);
-  {
+  // Shares are balanced in cost: a tile costs TC = 4 and every (non-empty)
+  // unit a fixed SC more (its setup, wave combine and partial), laid out
+  // before its tiles.  Workgroup w takes the tiles whose cost start lies in
+  // [floor(w*Ct/W), floor((w+1)*Ct/W)).  Any cost window of SC + TC holds a
+  // tile start, so capping W at Ct / (SC + TC*min_tiles) keeps every share
+  // non-empty (at least min_tiles tiles' worth).  When units average at most
+  // one tile per wave, a split would only add merges: tiles then cost 0 and a
+  // unit 1, so shares are whole units (unit-aligned mode).
+  int64_t T = 0, U = 0, TC = 0, SC = 0, Ct = 0;
+  auto set_costs = [&](int tiles, int nonempty) {
+    T = (int64_t)tiles * Hkv;
+    U = (int64_t)nonempty * Hkv;
+    const bool unit_mode = T <= (int64_t)kWaves * U;
+    TC = unit_mode ? 0 : 4;
+    SC = unit_mode ? 1 : a.seg_cost;
+    Ct = SC * U + TC * T;
+  };
+  auto cap_W = [&]() {
+    int64_t want = floordiv(Ct, SC + TC * a.min_tiles);
+    if (want < 1) want = 1;
+    if (T == 0) want = 0;
+    if (want < W) W = (int)want;
+  };
+  // A share bound as a global tile index: the first tile whose cost start is
+  // >= c, for c inside the cost range of sequence bb (which starts at lo,
+  // after pre tiles, and has nbb tiles per unit); past a unit's last tile
+  // that is the next unit's first.
+  auto bound_in = [&](int64_t c, int64_t lo, int pre, int nbb) -> int64_t {
+    const int64_t span = SC + TC * nbb;
+    int64_t gg = floordiv(c - lo, span);
+    const int64_t r = c - lo - gg * span;
+    int64_t t = r <= SC ? 0 : (TC > 0 ? (r - SC + 3) >> 2 : nbb);
+    if (t >= nbb) {
+      t = 0;
+      ++gg;
+    }
+    return (int64_t)Hkv * pre + gg * nbb + t;
+  };
+  // Page rows of the chunk [ca, cb) of the current segment's tiles.
+  int b = 0, g = 0, L = 0, start = 0, tbeg = 0, p_first = 0, nstaged = 1;
+  auto chunk_rows = [&](int ca, int cb) {
+    const int pos0 = tbeg + ca * TT > start ? tbeg + ca * TT : start;
+    const int pos1 = tbeg + cb * TT < L ? tbeg + cb * TT : L;
+    p_first = pos0 >> log2P;
+    nstaged = ((pos1 - 1) >> log2P) - p_first + 1;
+  };
+  constexpr int CH = kMaxSplitTokens / TT;   // tiles whose page rows are staged at once
+  int* s_tab = s_work_i;
+
+  // Up to 64 sequences, wave 0 alone computes the prefix sums, the share
+  // bounds and the first segment's unit in registers, and stages that
+  // segment's first page rows, so the workgroup passes a single barrier
+  // before its first tile loads.  Larger batches use all four waves.
+  const bool fast = B <= 64;
+  if (fast) {
+    if (wave == 0) {
+      const int len = lane < B ? a.seq_lens[lane] : 0;
+      const int nt = tiles_of(len), ne = nt > 0 ? 1 : 0;
+      int incl = nt, incl_ne = ne;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off), v2 = __shfl_up(incl_ne, off);
+        if (lane >= off) {
+          incl += v;
+          incl_ne += v2;
+        }
+      }
+      const int pre = incl - nt, nep = incl_ne - ne;
+      if (lane < B) {
+        s_len[lane] = len;
+        s_pre[lane] = pre;
+        s_nep[lane] = nep;
+      }
+      const int tot = __shfl(incl, 63), tot_ne = __shfl(incl_ne, 63);
+      if (lane == 0) {
+        s_pre[B] = tot;
+        s_nep[B] = tot_ne;
+      }
+      set_costs(tot, tot_ne);
+      cap_W();
+      if (w < W) {
+        const int64_t lo = SC * Hkv * nep + TC * (int64_t)Hkv * pre;
+        const int64_t hiw = lo + (int64_t)Hkv * (SC * ne + TC * nt);
+        int64_t bnd[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int64_t c = floordiv((int64_t)(w + e) * Ct, W);
+          const bool hit = lane < B && c >= lo && c < hiw;
+          const int64_t v = hit ? bound_in(c, lo, pre, nt) : 0;
+          const uint64_t mask = __ballot(hit);
+          bnd[e] = mask ? readlane64(v, (int)__builtin_ctzll(mask)) : T;
+        }
+        if (bnd[0] < bnd[1]) {
+          // The first segment's unit: b is the last sequence whose tiles start
+          // at or before bnd[0] (a non-empty one, as bnd[0] < T).
+          const int bl = 63 - (int)__builtin_clzll(__ballot(lane < B && (int64_t)Hkv * pre <= bnd[0]));
+          b = bl;
+          const int nb = __builtin_amdgcn_readlane(nt, bl);
+          const int64_t ubase = (int64_t)Hkv * __builtin_amdgcn_readlane(pre, bl);
+          g = (int)floordiv(bnd[0] - ubase, nb);
+          const int64_t ustart = ubase + (int64_t)g * nb;
+          const int ta = (int)(bnd[0] - ustart);
+          const int tc = (int)((bnd[1] < ustart + nb ? bnd[1] : ustart + nb) - ustart);
+          L = __builtin_amdgcn_readlane(len, bl);
+          start = (a.window > 0 && L > a.window) ? L - a.window : 0;
+          tbeg = start & ~(TT - 1);
+          chunk_rows(ta, tc < ta + CH ? tc : ta + CH);
+          const int32_t* btr0 = a.bt + (int64_t)b * a.bt_stride;
+          for (int i = lane; i < nstaged; i += 64) s_tab[i] = btr0[p_first + i];
+        }
+        if (lane == 0) {
+          s_bnd[0] = bnd[0];
+          s_bnd[1] = bnd[1];
+          s_first[1] = b;
+          s_first[2] = g;
+        }
+      }
+      if (lane == 0) s_first[0] = W;
+    }
+    __syncthreads();
+    W = s_first[0];
+    set_costs(s_pre[B], s_nep[B]);
+  } else {
     const int per = (B + 255) / 256;
     const int bb0 = threadIdx.x * per;
     int local = 0, lne = 0;
     for (int i = 0; i < per; ++i)
       if (bb0 + i < B) {
-        const int nt = tiles_of(a.seq_lens[bb0 + i]);
+        const int len = a.seq_lens[bb0 + i];
+        s_len[bb0 + i] = len;
+        const int nt = tiles_of(len);
         local += nt;
         lne += nt > 0;
       }
@@ -184,7 +318,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     }
     for (int i = 0; i < per; ++i)
       if (bb0 + i < B) {
-        const int nt = tiles_of(a.seq_lens[bb0 + i]);
+        const int nt = tiles_of(s_len[bb0 + i]);
         s_pre[bb0 + i] = excl;
         s_nep[bb0 + i] = excl_ne;
         excl += nt;
@@ -195,34 +329,15 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
       s_nep[B] = s_wsum_ne[0] + s_wsum_ne[1] + s_wsum_ne[2] + s_wsum_ne[3];
     }
     __syncthreads();
+    set_costs(s_pre[B], s_nep[B]);
+    cap_W();
   }
-  const int64_t T = (int64_t)s_pre[B] * Hkv;
 
   // Sequences with nothing to attend get a zero output.
   for (int bb = w; bb < B; bb += (int)gridDim.x) {
     if (s_pre[bb + 1] != s_pre[bb]) continue;
     uint16_t* o = a.out + (size_t)bb * a.Hq * D;
     for (int i = threadIdx.x; i < a.Hq * D; i += 256) o[i] = 0;
-  }
-
-  // Shares are balanced in cost: a tile costs TC = 4 and every (non-empty)
-  // unit a fixed SC more (its setup, wave combine and partial), laid out
-  // before its tiles.  Workgroup w takes the tiles whose cost start lies in
-  // [floor(w*Ct/W), floor((w+1)*Ct/W)).  Any cost window of SC + TC holds a
-  // tile start, so capping W at Ct / (SC + TC*min_tiles) keeps every share
-  // non-empty (at least min_tiles tiles' worth).  When units average at most
-  // one tile per wave, a split would only add merges: tiles then cost 0 and a
-  // unit 1, so shares are whole units (unit-aligned mode).
-  const int64_t U = (int64_t)Hkv * s_nep[B];
-  const bool unit_mode = T <= (int64_t)kWaves * U;
-  const int64_t TC = unit_mode ? 0 : 4;
-  const int64_t SC = unit_mode ? 1 : a.seg_cost;
-  const int64_t Ct = SC * U + TC * T;
-  {
-    int64_t want = Ct / (SC + TC * a.min_tiles);
-    if (want < 1) want = 1;
-    if (T == 0) want = 0;
-    if (want < W) W = (int)want;
   }
   if (w >= W) return;
   auto cpre = [&](int bb) -> int64_t { return SC * Hkv * s_nep[bb] + TC * (int64_t)Hkv * s_pre[bb]; };
@@ -233,10 +348,10 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   };
   // Workgroup holding a tile of cost start c: the largest w with floor(w*Ct/W) <= c.
   auto wg_of_cost = [&](int64_t c) -> int { return (int)(floordiv((c + 1) * W + Ct - 1, Ct) - 1); };
-  // The share's first and end tiles: the first tile whose cost start is >=
-  // floor(w*Ct/W), resp. floor((w+1)*Ct/W), found by the thread whose
-  // sequence's cost range holds that point (T past the end).
-  {
+  if (!fast) {
+    // The share's first and end tiles: the first tile whose cost start is >=
+    // floor(w*Ct/W), resp. floor((w+1)*Ct/W), found by the thread whose
+    // sequence's cost range holds that point (T past the end).
     const int64_t cb[2] = {floordiv((int64_t)w * Ct, W), floordiv((int64_t)(w + 1) * Ct, W)};
     if (threadIdx.x < 2) s_bnd[threadIdx.x] = T;
     __syncthreads();
@@ -248,29 +363,16 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int64_t c = cb[e];
-        if (c >= lo && c < hiw) {
-          const int nbb = s_pre[bb + 1] - s_pre[bb];
-          const int64_t span = SC + TC * nbb;
-          int64_t gg = floordiv(c - lo, span);
-          const int64_t r = c - lo - gg * span;
-          int64_t t = r <= SC ? 0 : (TC > 0 ? (r - SC + 3) >> 2 : nbb);
-          if (t >= nbb) {
-            t = 0;
-            ++gg;
-          }
-          s_bnd[e] = (int64_t)Hkv * s_pre[bb] + gg * nbb + t;
-        }
+        if (c >= lo && c < hiw) s_bnd[e] = bound_in(c, lo, s_pre[bb], s_pre[bb + 1] - s_pre[bb]);
       }
     }
     __syncthreads();
   }
 
   // Per-segment state (captured by the tile helpers below).
-  int b = 0, g = 0, L = 0, start = 0, tbeg = 0, p_first = 0, nstaged = 1;
   const int32_t* btr = a.bt;
   const uint8_t* kpool = a.kp;
   const uint8_t* vpool = a.vp;
-  int* s_tab = s_work_i;
   const int kgrp = n >> 2;      // group of this lane's K row
   const int kslot = n & 3;
   bf16x8 qop[NQ];
@@ -483,9 +585,14 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   int slot = 0;
   // Unit to merge at the end of the share (uniform across the workgroup).
   int pend = 0, pend_b = 0, pend_g = 0, pend_wa = 0, pend_first_slot_a = 0;
+  // Wave 0 located the first segment and staged its first page rows.
+  bool staged = fast;
   while (cur < hi) {
     // ---- the segment: unit (b, g), tiles [ta, tc) of the unit.
-    {
+    if (staged) {
+      b = s_first[1];
+      g = s_first[2];
+    } else {
       int lo_b = 0, hi_b = B - 1;   // largest b with s_pre[b] * Hkv <= cur (a non-empty sequence)
       while (lo_b < hi_b) {
         const int mid = (lo_b + hi_b + 1) >> 1;
@@ -493,15 +600,15 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
         else hi_b = mid - 1;
       }
       b = lo_b;
+      g = (int)floordiv(cur - (int64_t)s_pre[b] * Hkv, s_pre[b + 1] - s_pre[b]);
     }
     const int nb = s_pre[b + 1] - s_pre[b];
     const int64_t ubase = (int64_t)s_pre[b] * Hkv;
-    g = (int)floordiv(cur - ubase, nb);
     const int64_t ustart = ubase + (int64_t)g * nb;
     const int64_t uend = ustart + nb;
     const int64_t send = hi < uend ? hi : uend;
     const int ta = (int)(cur - ustart), tc = (int)(send - ustart);
-    L = a.seq_lens[b];
+    L = s_len[b];
     start = (a.window > 0 && L > a.window) ? L - a.window : 0;
     tbeg = start & ~(TT - 1);
     btr = a.bt + (int64_t)b * a.bt_stride;
@@ -525,13 +632,13 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
 
     for (int ca = ta; ca < tc; ca += CH) {
       const int cb = tc < ca + CH ? tc : ca + CH;
-      const int pos0 = tbeg + ca * TT > start ? tbeg + ca * TT : start;
-      const int pos1 = tbeg + cb * TT < L ? tbeg + cb * TT : L;
-      p_first = pos0 >> log2P;
-      nstaged = ((pos1 - 1) >> log2P) - p_first + 1;
-      __syncthreads();   // earlier readers of the stage are done
-      for (int i = threadIdx.x; i < nstaged; i += 256) s_tab[i] = btr[p_first + i];
-      __syncthreads();
+      chunk_rows(ca, cb);
+      if (!staged) {
+        __syncthreads();   // earlier readers of the stage are done
+        for (int i = threadIdx.x; i < nstaged; i += 256) s_tab[i] = btr[p_first + i];
+        __syncthreads();
+      }
+      staged = false;
       // ---- tile loop: wave w takes tiles ca + w, ca + w + 4, ...
       const int nmine = cb - ca > wave ? (cb - ca - wave + kWaves - 1) / kWaves : 0;
       auto tile_pos = [&](int k) { return tbeg + (ca + wave + kWaves * k) * TT; };
@@ -841,7 +948,7 @@ auto by_shape(int D, int v, F&& f) {
 
 size_t decode_lds_bytes(int D, int tile_variant, int B, int G, int P) {
   const int TT = decode_tile_tokens(D, tile_variant);
-  const size_t pre = (size_t)2 * ((B + 4) & ~3) * 4;
+  const size_t pre = (size_t)3 * ((B + 4) & ~3) * 4;
   const size_t stage = (size_t)(kMaxSplitTokens / TT * TT / P + 2) * 4;
   const size_t combine = (size_t)2 * G * (D + 4) * 4;
   return pre + (stage > combine ? stage : combine);
