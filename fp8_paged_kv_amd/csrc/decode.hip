@@ -809,91 +809,145 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     constexpr int KB = 8;     // partials whose loads are in flight together
     const int ngrp = G * D / 4;
     float* s_wt = s_work;     // [G][CHS]
-    for (int pass0 = 0; pass0 < ngrp; pass0 += 256 * NJ) {
-      f32x4 num[NJ];
+    constexpr int KF = NJ == 1 ? 16 : 4;   // partials merged in registers
+    if (NJ <= 2 && nseg <= KF && ngrp <= 256 * NJ) {
+      // Few partials, one pass, head dim <= 256: every thread issues the lse
+      // values and the float4 groups of its heads together (one round trip)
+      // and merges them in registers, in the same order and arithmetic as the
+      // chunked path.  (At head dim 512 the chunked path measured faster.)
+      constexpr uint32_t kNone = 0xFFFFFFF0u;   // past the buffer: reads zero
+      int hhj[NJ];
+      bool okj[NJ];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) num[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (threadIdx.x < G) {
-        const float sk = a.sinks ? a.sinks[gq * G + threadIdx.x] : kNegInf;
-        s_M[threadIdx.x] = sk;
-        s_den[threadIdx.x] = (sk != kNegInf) ? 1.0f : 0.0f;
+      for (int j = 0; j < NJ; ++j) {
+        const int gi = threadIdx.x + 256 * j;
+        okj[j] = gi < ngrp;
+        hhj[j] = okj[j] ? (4 * gi) / D : 0;
       }
-      for (int c0 = 0; c0 < nseg; c0 += CHS) {
-        const int nc = nseg - c0 < CHS ? nseg - c0 : CHS;
-        for (int i = threadIdx.x; i < G * CHS; i += 256) {
-          const int hh = i / CHS, k = i - hh * CHS;
-          s_wt[i] = k < nc ? __hip_atomic_load(a.part_lse + part_row(w_a + c0 + k) + hh, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT)
-                           : kNegInf;
+      f32x4 ov[NJ][KF];
+      float lv[NJ][KF];
+#pragma unroll
+      for (int k = 0; k < KF; ++k) {
+        const bool ok = k < nseg;
+        const uint32_t row = ok ? part_row(w_a + k) : 0u;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const uint32_t gi = threadIdx.x + 256u * j;
+          ov[j][k] = ld_coherent4(prs, (ok && okj[j]) ? row * (uint32_t)D * 4u + 16u * gi : kNone);
+          lv[j][k] = ok ? __hip_atomic_load(a.part_lse + row + hhj[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : kNegInf;
         }
-        __syncthreads();
-        if (threadIdx.x < G) {
-          const int hh = threadIdx.x;
-          const float Mo = s_M[hh];
-          float Mn = Mo;
-          for (int k = 0; k < nc; ++k) Mn = fmaxf(Mn, s_wt[hh * CHS + k]);
-          const float sc = (Mo == kNegInf) ? 0.0f : __builtin_expf(Mo - Mn);
-          float den = s_den[hh] * sc;
-          for (int k = 0; k < nc; ++k) {
-            const float l = s_wt[hh * CHS + k];
-            const float wv = (l == kNegInf) ? 0.0f : __builtin_expf(l - Mn);
-            s_wt[hh * CHS + k] = wv;
-            den += wv;
-          }
-          s_M[hh] = Mn;
-          s_den[hh] = den;
-          s_sc[hh] = sc;
-        }
-        __syncthreads();
-        {
-          // Loads of KB partials x NJ groups are issued together; absent
-          // ones use an offset past the buffer's range, which reads zero.
-          constexpr uint32_t kNone = 0xFFFFFFF0u;
-          int hhj[NJ];
-          uint32_t offj[NJ];
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const int gi = pass0 + threadIdx.x + 256 * j;
-            hhj[j] = gi < ngrp ? (4 * gi) / D : 0;
-            offj[j] = gi < ngrp ? (uint32_t)(16 * gi) : kNone;
-            num[j] *= s_sc[hhj[j]];
-          }
-          for (int k0 = 0; k0 < nc; k0 += KB) {
-            f32x4 ov[NJ][KB];
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk) {
-              const bool ok = k0 + kk < nc;
-              const uint32_t rb = ok ? part_row(w_a + c0 + k0 + kk) * (uint32_t)D * 4u : 0u;
-#pragma unroll
-              for (int j = 0; j < NJ; ++j) ov[j][kk] = ld_coherent4(prs, (ok && offj[j] != kNone) ? rb + offj[j] : kNone);
-            }
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk) {
-              const int kx = k0 + kk < CHS ? k0 + kk : CHS - 1;
-#pragma unroll
-              for (int j = 0; j < NJ; ++j) {
-                const float wv = (k0 + kk < nc) ? s_wt[hhj[j] * CHS + kx] : 0.0f;
-                num[j] += (wv > 0.0f) ? ov[j][kk] * wv : f32x4{0.f, 0.f, 0.f, 0.f};
-              }
-            }
-          }
-        }
-        __syncthreads();   // s_wt, s_M, s_den are rewritten next
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int gi = pass0 + threadIdx.x + 256 * j;
-        if (gi < ngrp) {
-          const int hh = (4 * gi) / D, d = 4 * gi - hh * D;
-          const float den = s_den[hh];
-          const float inv = (s_M[hh] == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
-          const f32x4 o = num[j] * inv;
-          u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-          if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
-          *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
+        if (!okj[j]) continue;
+        const int gi = threadIdx.x + 256 * j;
+        const int hh = hhj[j], d = 4 * gi - hh * D;
+        const float sk = a.sinks ? a.sinks[gq * G + hh] : kNegInf;
+        float M = sk;
+#pragma unroll
+        for (int k = 0; k < KF; ++k) M = fmaxf(M, lv[j][k]);
+        float den = (sk != kNegInf) ? __builtin_expf(sk - M) : 0.0f;
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KF; ++k) {
+          const float wv = (lv[j][k] == kNegInf) ? 0.0f : __builtin_expf(lv[j][k] - M);
+          den += wv;
+          num += (wv > 0.0f) ? ov[j][k] * wv : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
+        const f32x4 o = num * inv;
+        u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+        *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
       }
-      __syncthreads();   // every thread has read s_M / s_den before the next pass resets them
+    } else {
+      for (int pass0 = 0; pass0 < ngrp; pass0 += 256 * NJ) {
+        f32x4 num[NJ];
+  #pragma unroll
+        for (int j = 0; j < NJ; ++j) num[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (threadIdx.x < G) {
+          const float sk = a.sinks ? a.sinks[gq * G + threadIdx.x] : kNegInf;
+          s_M[threadIdx.x] = sk;
+          s_den[threadIdx.x] = (sk != kNegInf) ? 1.0f : 0.0f;
+        }
+        for (int c0 = 0; c0 < nseg; c0 += CHS) {
+          const int nc = nseg - c0 < CHS ? nseg - c0 : CHS;
+          for (int i = threadIdx.x; i < G * CHS; i += 256) {
+            const int hh = i / CHS, k = i - hh * CHS;
+            s_wt[i] = k < nc ? __hip_atomic_load(a.part_lse + part_row(w_a + c0 + k) + hh, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : kNegInf;
+          }
+          __syncthreads();
+          if (threadIdx.x < G) {
+            const int hh = threadIdx.x;
+            const float Mo = s_M[hh];
+            float Mn = Mo;
+            for (int k = 0; k < nc; ++k) Mn = fmaxf(Mn, s_wt[hh * CHS + k]);
+            const float sc = (Mo == kNegInf) ? 0.0f : __builtin_expf(Mo - Mn);
+            float den = s_den[hh] * sc;
+            for (int k = 0; k < nc; ++k) {
+              const float l = s_wt[hh * CHS + k];
+              const float wv = (l == kNegInf) ? 0.0f : __builtin_expf(l - Mn);
+              s_wt[hh * CHS + k] = wv;
+              den += wv;
+            }
+            s_M[hh] = Mn;
+            s_den[hh] = den;
+            s_sc[hh] = sc;
+          }
+          __syncthreads();
+          {
+            // Loads of KB partials x NJ groups are issued together; absent
+            // ones use an offset past the buffer's range, which reads zero.
+            constexpr uint32_t kNone = 0xFFFFFFF0u;
+            int hhj[NJ];
+            uint32_t offj[NJ];
+  #pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const int gi = pass0 + threadIdx.x + 256 * j;
+              hhj[j] = gi < ngrp ? (4 * gi) / D : 0;
+              offj[j] = gi < ngrp ? (uint32_t)(16 * gi) : kNone;
+              num[j] *= s_sc[hhj[j]];
+            }
+            for (int k0 = 0; k0 < nc; k0 += KB) {
+              f32x4 ov[NJ][KB];
+  #pragma unroll
+              for (int kk = 0; kk < KB; ++kk) {
+                const bool ok = k0 + kk < nc;
+                const uint32_t rb = ok ? part_row(w_a + c0 + k0 + kk) * (uint32_t)D * 4u : 0u;
+  #pragma unroll
+                for (int j = 0; j < NJ; ++j) ov[j][kk] = ld_coherent4(prs, (ok && offj[j] != kNone) ? rb + offj[j] : kNone);
+              }
+  #pragma unroll
+              for (int kk = 0; kk < KB; ++kk) {
+                const int kx = k0 + kk < CHS ? k0 + kk : CHS - 1;
+  #pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                  const float wv = (k0 + kk < nc) ? s_wt[hhj[j] * CHS + kx] : 0.0f;
+                  num[j] += (wv > 0.0f) ? ov[j][kk] * wv : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+              }
+            }
+          }
+          __syncthreads();   // s_wt, s_M, s_den are rewritten next
+        }
+  #pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int gi = pass0 + threadIdx.x + 256 * j;
+          if (gi < ngrp) {
+            const int hh = (4 * gi) / D, d = 4 * gi - hh * D;
+            const float den = s_den[hh];
+            const float inv = (s_M[hh] == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
+            const f32x4 o = num[j] * inv;
+            u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+            *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
+          }
+        }
+        __syncthreads();   // every thread has read s_M / s_den before the next pass resets them
+      }
     }
     // Clear the consumed flags (a replayed graph reuses the epoch).
     for (int i = threadIdx.x; i < nseg - 1; i += 256)

@@ -132,7 +132,9 @@ const char* fp8pa_last_error(void);
 /* Plan a decode call.  B sequences, Hq query heads, K pool `kd`; every
  * seq_lens[b] must be <= max_seq_len; window <= 0 means none; workgroups 0
  * lets the library choose, else it is used as given (>= 1).  Refuses
- * (FP8PA_EUNSUPPORTED) shapes whose LDS needs exceed 64 KiB (B above ~7500). */
+ * (FP8PA_EUNSUPPORTED) shapes whose LDS needs exceed 64 KiB: 12 bytes per
+ * sequence plus the larger of the page-row stage and the wave combine, i.e.
+ * B above about 5000 (head dim 128) or 2700 (head dim 512 with G = 8). */
 int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
                       int window, int workgroups, int variant, fp8pa_plan* out);
 
