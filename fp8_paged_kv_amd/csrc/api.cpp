@@ -151,28 +151,28 @@ int tile_variant() {
   return cached;
 }
 
-// Fewest tiles a workgroup takes: one per wave, so short calls use fewer,
-// fuller workgroups (tunable through FP8PA_MIN_TILES).
-int min_tiles() {
+// Fewest tiles a workgroup takes: by default one per wave, so short calls use
+// fewer, fuller workgroups (tunable through FP8PA_MIN_TILES; 0 = default).
+int min_tiles(int waves) {
   static int cached = -1;
   if (cached < 0) {
     const char* e = getenv("FP8PA_MIN_TILES");
-    cached = e ? atoi(e) : 4;
-    if (cached < 1) cached = 1;
+    cached = e ? atoi(e) : 0;
+    if (cached < 0) cached = 0;
   }
-  return cached;
+  return cached > 0 ? cached : waves;
 }
 
 // Fixed cost of a unit (setup, combine, partial) in the share balance, in
-// quarter tiles (tunable through FP8PA_SEG_COST).
-int seg_cost() {
-  static int cached = -1;
-  if (cached < 0) {
+// quarter tiles: the kernel shape's default, or FP8PA_SEG_COST (tuning).
+int seg_cost(int shape_default) {
+  static int cached = -2;
+  if (cached == -2) {
     const char* e = getenv("FP8PA_SEG_COST");
-    cached = e ? atoi(e) : 24;
-    if (cached < 0) cached = 0;
+    cached = e ? atoi(e) : -1;
+    if (e && cached < 0) cached = 0;
   }
-  return cached;
+  return cached >= 0 ? cached : shape_default;
 }
 
 // Compute units of the current device (0 when no device can be queried).
@@ -305,8 +305,8 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   a.window = window > 0 ? window : 0;
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
   a.tile_variant = tile_variant();
-  a.min_tiles = min_tiles();
-  a.seg_cost = seg_cost();
+  a.min_tiles = min_tiles(fp8pa::decode_waves(D, a.tile_variant));
+  a.seg_cost = seg_cost(fp8pa::decode_seg_cost(D, a.tile_variant));
   a.epoch = g_epoch.fetch_add(1) + 1;
   if (W > 1) {
     const int64_t po = (int64_t)W * 2 * G * D * 4;

@@ -18,9 +18,12 @@
 // non-empty.
 // Every workgroup builds the list itself from seq_lens (a prefix sum in LDS),
 // so the grid depends on host values only.  A workgroup's share cuts units
-// into segments; a workgroup is four wave64s, each wave walks every fourth
-// tile of a segment with its own online softmax, and the four states are
-// combined in LDS.  The block-table rows of a segment are staged in LDS.
+// into segments; a workgroup is NW wave64s (four by default), each wave walks
+// every NW-th tile of a segment with its own online softmax, and the states
+// are combined in LDS.  The block-table rows of a segment are staged in LDS.
+// How many workgroups a CU runs is part of the kernel shape: at head dim 128
+// one four-wave workgroup per CU streams as fast as two and halves the
+// number of cut units.
 //
 // Merging.  A segment that covers a whole unit writes the output.  Otherwise
 // it writes a normalised partial and its log-sum-exp (only a workgroup's first
@@ -70,7 +73,6 @@
 namespace fp8pa {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr float kNegInf = -__builtin_inff();
 
 template <int NS>
@@ -124,8 +126,9 @@ struct Tile {
   u32x4 ve8[NS][NE];    // E8M0 bytes of the lane's 8 score positions, all groups
 };
 
-template <int D, int NS, int SK, bool PF, int OCC, bool KNT>
-__global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
+template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW>
+__global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a) {
+  constexpr int NT = 64 * NW;   // threads (NW wave64s)
   constexpr int TT = 32 * NS;   // positions per tile
   constexpr int GT = 8 * NS;    // positions per group
   constexpr int NM = D / 64;    // 16-byte K pieces per position row per lane
@@ -135,10 +138,10 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   typedef Tile<D, NS, SK> TileT;
 
   extern __shared__ int s_dyn[];   // tile prefix, non-empty prefix, lengths, then the page-row stage / wave-combine buffer
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
+  __shared__ float s_m[NW][16];
+  __shared__ float s_l[NW][16];
   __shared__ float s_M[16], s_den[16], s_sc[16];
-  __shared__ int s_wsum[kWaves], s_wsum_ne[kWaves];
+  __shared__ int s_wsum[NW], s_wsum_ne[NW];
   __shared__ int s_timeout;
   __shared__ int64_t s_bnd[2];
   __shared__ int s_first[3];   // capped W and the first segment's (b, g), from wave 0
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   auto set_costs = [&](int tiles, int nonempty) {
     T = (int64_t)tiles * Hkv;
     U = (int64_t)nonempty * Hkv;
-    const bool unit_mode = T <= (int64_t)kWaves * U;
+    const bool unit_mode = T <= (int64_t)NW * U;
     TC = unit_mode ? 0 : 4;
     SC = unit_mode ? 1 : a.seg_cost;
     Ct = SC * U + TC * T;
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     W = s_first[0];
     set_costs(s_pre[B], s_nep[B]);
   } else {
-    const int per = (B + 255) / 256;
+    const int per = (B + NT - 1) / NT;
     const int bb0 = threadIdx.x * per;
     int local = 0, lne = 0;
     for (int i = 0; i < per; ++i)
@@ -325,8 +328,13 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
         excl_ne += nt > 0;
       }
     if (threadIdx.x == 0) {
-      s_pre[B] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-      s_nep[B] = s_wsum_ne[0] + s_wsum_ne[1] + s_wsum_ne[2] + s_wsum_ne[3];
+      int t = 0, tn = 0;
+      for (int i = 0; i < NW; ++i) {
+        t += s_wsum[i];
+        tn += s_wsum_ne[i];
+      }
+      s_pre[B] = t;
+      s_nep[B] = tn;
     }
     __syncthreads();
     set_costs(s_pre[B], s_nep[B]);
@@ -337,7 +345,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
   for (int bb = w; bb < B; bb += (int)gridDim.x) {
     if (s_pre[bb + 1] != s_pre[bb]) continue;
     uint16_t* o = a.out + (size_t)bb * a.Hq * D;
-    for (int i = threadIdx.x; i < a.Hq * D; i += 256) o[i] = 0;
+    for (int i = threadIdx.x; i < a.Hq * D; i += NT) o[i] = 0;
   }
   if (w >= W) return;
   auto cpre = [&](int bb) -> int64_t { return SC * Hkv * s_nep[bb] + TC * (int64_t)Hkv * s_pre[bb]; };
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     const int64_t cb[2] = {floordiv((int64_t)w * Ct, W), floordiv((int64_t)(w + 1) * Ct, W)};
     if (threadIdx.x < 2) s_bnd[threadIdx.x] = T;
     __syncthreads();
-    const int per = (B + 255) / 256;
+    const int per = (B + NT - 1) / NT;
     for (int i = 0; i < per; ++i) {
       const int bb = threadIdx.x * per + i;
       if (bb >= B) break;
@@ -635,13 +643,13 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
       chunk_rows(ca, cb);
       if (!staged) {
         __syncthreads();   // earlier readers of the stage are done
-        for (int i = threadIdx.x; i < nstaged; i += 256) s_tab[i] = btr[p_first + i];
+        for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = btr[p_first + i];
         __syncthreads();
       }
       staged = false;
       // ---- tile loop: wave w takes tiles ca + w, ca + w + 4, ...
-      const int nmine = cb - ca > wave ? (cb - ca - wave + kWaves - 1) / kWaves : 0;
-      auto tile_pos = [&](int k) { return tbeg + (ca + wave + kWaves * k) * TT; };
+      const int nmine = cb - ca > wave ? (cb - ca - wave + NW - 1) / NW : 0;
+      auto tile_pos = [&](int k) { return tbeg + (ca + wave + NW * k) * TT; };
       if constexpr (PF) {
         // Loads run one tile ahead, ping-ponging two register buffers.  The
         // trip count is fixed and loads are unconditional (a prefetch past
@@ -666,11 +674,11 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
       }
     }
 
-    // ---- combine the four waves' states in LDS.
+    // ---- combine the waves' states in LDS.
     float lsum = l_run;
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
-    float* s_o = s_work;   // [2][G][D + 4]
+    float* s_o = s_work;   // [NW / 2][G][D + 4]
     constexpr int OS = D + 4;
     if (quad == 0) {
       s_m[wave][n] = m_run;
@@ -679,38 +687,32 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     __syncthreads();   // also: every wave is past its last read of the page-row stage
     float M = kNegInf;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i][n]);
+    for (int i = 0; i < NW; ++i) M = fmaxf(M, s_m[i][n]);
     const float M_ref = (M == kNegInf) ? 0.0f : M;
     float Ltot = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) Ltot += s_l[i][n] * __builtin_amdgcn_exp2f(s_m[i][n] - M_ref);
+    for (int i = 0; i < NW; ++i) Ltot += s_l[i][n] * __builtin_amdgcn_exp2f(s_m[i][n] - M_ref);
     {
       const float f = __builtin_amdgcn_exp2f(m_run - M_ref);
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[c] *= f;
     }
-    if (wave >= 2 && col) {
-      float* dst = s_o + ((wave - 2) * G + n) * OS + 4 * quad;
+    // Pairwise tree: at each level the upper half of the remaining waves
+    // hands its accumulators to the lower half through LDS.
 #pragma unroll
-      for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
-    }
-    __syncthreads();
-    if (wave < 2 && col) {
-      const float* src = s_o + (wave * G + n) * OS + 4 * quad;
+    for (int half = NW / 2; half >= 1; half >>= 1) {
+      if (wave >= half && wave < 2 * half && col) {
+        float* dst = s_o + ((wave - half) * G + n) * OS + 4 * quad;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
-    }
-    __syncthreads();
-    if (wave == 1 && col) {
-      float* dst = s_o + n * OS + 4 * quad;
+        for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
+      }
+      __syncthreads();
+      if (wave < half && col) {
+        const float* src = s_o + (wave * G + n) * OS + 4 * quad;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
-    }
-    __syncthreads();
-    if (wave == 0 && col) {
-      const float* src = s_o + n * OS + 4 * quad;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
+        for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
+      }
+      if (half > 1) __syncthreads();
     }
 
     const int h = g * G + n;
@@ -786,7 +788,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     // Wait for the other holders' flags.  They have lower indices, so they
     // were dispatched first and never wait on this workgroup; the wait is
     // bounded all the same (a timeout yields NaN outputs).
-    for (int i = threadIdx.x; i < nseg - 1; i += 256) {
+    for (int i = threadIdx.x; i < nseg - 1; i += NT) {
       const uint32_t* f = a.flags + 2 * (w_a + i) + slot_of(w_a + i);
       int spins = 0;
       while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
@@ -810,7 +812,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
     const int ngrp = G * D / 4;
     float* s_wt = s_work;     // [G][CHS]
     constexpr int KF = NJ == 1 ? 16 : 4;   // partials merged in registers
-    if (NJ <= 2 && nseg <= KF && ngrp <= 256 * NJ) {
+    if (NJ <= 2 && nseg <= KF && ngrp <= NT * NJ) {
       // Few partials, one pass, head dim <= 256: every thread issues the lse
       // values and the float4 groups of its heads together (one round trip)
       // and merges them in registers, in the same order and arithmetic as the
@@ -820,7 +822,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
       bool okj[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int gi = threadIdx.x + 256 * j;
+        const int gi = threadIdx.x + NT * j;
         okj[j] = gi < ngrp;
         hhj[j] = okj[j] ? (4 * gi) / D : 0;
       }
@@ -832,7 +834,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
         const uint32_t row = ok ? part_row(w_a + k) : 0u;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const uint32_t gi = threadIdx.x + 256u * j;
+          const uint32_t gi = threadIdx.x + (uint32_t)NT * j;
           ov[j][k] = ld_coherent4(prs, (ok && okj[j]) ? row * (uint32_t)D * 4u + 16u * gi : kNone);
           lv[j][k] = ok ? __hip_atomic_load(a.part_lse + row + hhj[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                         : kNegInf;
@@ -841,7 +843,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         if (!okj[j]) continue;
-        const int gi = threadIdx.x + 256 * j;
+        const int gi = threadIdx.x + NT * j;
         const int hh = hhj[j], d = 4 * gi - hh * D;
         const float sk = a.sinks ? a.sinks[gq * G + hh] : kNegInf;
         float M = sk;
@@ -862,7 +864,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
         *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
       }
     } else {
-      for (int pass0 = 0; pass0 < ngrp; pass0 += 256 * NJ) {
+      for (int pass0 = 0; pass0 < ngrp; pass0 += NT * NJ) {
         f32x4 num[NJ];
   #pragma unroll
         for (int j = 0; j < NJ; ++j) num[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -873,7 +875,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
         }
         for (int c0 = 0; c0 < nseg; c0 += CHS) {
           const int nc = nseg - c0 < CHS ? nseg - c0 : CHS;
-          for (int i = threadIdx.x; i < G * CHS; i += 256) {
+          for (int i = threadIdx.x; i < G * CHS; i += NT) {
             const int hh = i / CHS, k = i - hh * CHS;
             s_wt[i] = k < nc ? __hip_atomic_load(a.part_lse + part_row(w_a + c0 + k) + hh, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT)
@@ -906,7 +908,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
             uint32_t offj[NJ];
   #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-              const int gi = pass0 + threadIdx.x + 256 * j;
+              const int gi = pass0 + threadIdx.x + NT * j;
               hhj[j] = gi < ngrp ? (4 * gi) / D : 0;
               offj[j] = gi < ngrp ? (uint32_t)(16 * gi) : kNone;
               num[j] *= s_sc[hhj[j]];
@@ -935,7 +937,7 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
         }
   #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int gi = pass0 + threadIdx.x + 256 * j;
+          const int gi = pass0 + threadIdx.x + NT * j;
           if (gi < ngrp) {
             const int hh = (4 * gi) / D, d = 4 * gi - hh * D;
             const float den = s_den[hh];
@@ -950,73 +952,104 @@ __global__ __launch_bounds__(256, OCC) void decode_kernel(const DecodeArgs a) {
       }
     }
     // Clear the consumed flags (a replayed graph reuses the epoch).
-    for (int i = threadIdx.x; i < nseg - 1; i += 256)
+    for (int i = threadIdx.x; i < nseg - 1; i += NT)
       __hip_atomic_store(a.flags + 2 * (w_a + i) + slot_of(w_a + i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-template <int D, int NS, bool PF, int OCC, bool KNT>
+template <int D, int NS, bool PF, int OCC, bool KNT, int NW>
 hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  dim3 grid(W), block(256);
+  dim3 grid(W), block(64 * NW);
   switch (sk) {
-    case 0: hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT>), grid, block, lds, st, e0, e1, 0, a); break;
-    case 1: hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT>), grid, block, lds, st, e0, e1, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT>), grid, block, lds, st, e0, e1, 0, a); break;
+    case 0: hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW>), grid, block, lds, st, e0, e1, 0, a); break;
+    case 1: hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW>), grid, block, lds, st, e0, e1, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW>), grid, block, lds, st, e0, e1, 0, a); break;
   }
   return hipGetLastError();
 }
 
-template <int D, int NS, bool PF, int OCC, bool KNT>
+template <int D, int NS, bool PF, int OCC, bool KNT, int NW>
 int occupancy_d(int sk, size_t lds) {
   int nb = 0;
   hipError_t e;
   switch (sk) {
-    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 0, PF, OCC, KNT>, 256, lds); break;
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 1, PF, OCC, KNT>, 256, lds); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 2, PF, OCC, KNT>, 256, lds); break;
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 0, PF, OCC, KNT, NW>, 64 * NW, lds); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 1, PF, OCC, KNT, NW>, 64 * NW, lds); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 2, PF, OCC, KNT, NW>, 64 * NW, lds); break;
   }
   return e == hipSuccess ? nb : -1;
 }
 
-// Dispatch on head dim and kernel shape.  tile_variant (tuning): 0 default,
-// 1 prefetch at one wave per SIMD, 2 prefetch with 32-position tiles
-// (D = 128), 3 no prefetch, 4 prefetch.
+// Dispatch on head dim and kernel shape.  A shape is <head dim, NS (tile =
+// 32*NS positions), prefetch one tile ahead, register occupancy the kernel is
+// compiled for, whole-line K loads, waves per workgroup, workgroups launched
+// per CU, default unit cost in the share balance (quarter tiles)>.
+// tile_variant (tuning; 0 = default):
+//   head dim 64:  4 prefetch; 7 eight waves, one workgroup per CU; 8 as 7 with prefetch
+//   head dim 128: 1 prefetch at one wave per SIMD; 2 prefetch with 32-position
+//                 tiles; 4 prefetch, two workgroups per CU; 7 eight waves;
+//                 9 two workgroups per CU; 10 compiled for one workgroup per CU
+//   head dim 256: 4 prefetch
 template <bool KNT, typename F>
 auto by_shape(int D, int v, F&& f) {
   switch (D) {
-    case 64: return v == 4 ? f.template operator()<64, 2, true, 2, KNT>() : f.template operator()<64, 2, false, 2, KNT>();
+    case 64:
+      switch (v) {
+        case 4: return f.template operator()<64, 2, true, 2, KNT, 4, 2, 24>();
+        case 7: return f.template operator()<64, 2, false, 1, KNT, 8, 1, 24>();
+        case 8: return f.template operator()<64, 2, true, 1, KNT, 8, 1, 24>();
+        default: return f.template operator()<64, 2, false, 2, KNT, 4, 2, 24>();
+      }
     case 128:
       switch (v) {
-        case 1: return f.template operator()<128, 2, true, 1, KNT>();
-        case 2: return f.template operator()<128, 1, true, 2, KNT>();
-        case 4: return f.template operator()<128, 2, true, 2, KNT>();
-        default: return f.template operator()<128, 2, false, 2, KNT>();
+        case 1: return f.template operator()<128, 2, true, 1, KNT, 4, 1, 36>();
+        case 2: return f.template operator()<128, 1, true, 2, KNT, 4, 2, 24>();
+        case 4: return f.template operator()<128, 2, true, 2, KNT, 4, 2, 24>();
+        case 7: return f.template operator()<128, 2, false, 1, KNT, 8, 1, 24>();
+        case 9: return f.template operator()<128, 2, false, 2, KNT, 4, 2, 24>();
+        case 10: return f.template operator()<128, 2, false, 1, KNT, 4, 1, 36>();
+        default: return f.template operator()<128, 2, false, 2, KNT, 4, 1, 36>();
       }
     case 256:
-      return v == 4 ? f.template operator()<256, 1, true, 1, KNT>() : f.template operator()<256, 1, false, 1, KNT>();
-    default: return f.template operator()<512, 1, false, 1, KNT>();
+      return v == 4 ? f.template operator()<256, 1, true, 1, KNT, 4, 1, 24>()
+                    : f.template operator()<256, 1, false, 1, KNT, 4, 1, 24>();
+    default: return f.template operator()<512, 1, false, 1, KNT, 4, 1, 24>();
   }
 }
 
 }  // namespace
 
+int decode_waves(int D, int tile_variant) {
+  auto q = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() { return NW; };
+  return by_shape<true>(D, tile_variant, q);
+}
+
+int decode_seg_cost(int D, int tile_variant) {
+  auto q = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() { return SCD; };
+  return by_shape<true>(D, tile_variant, q);
+}
+
 size_t decode_lds_bytes(int D, int tile_variant, int B, int G, int P) {
   const int TT = decode_tile_tokens(D, tile_variant);
   const size_t pre = (size_t)3 * ((B + 4) & ~3) * 4;
   const size_t stage = (size_t)(kMaxSplitTokens / TT * TT / P + 2) * 4;
-  const size_t combine = (size_t)2 * G * (D + 4) * 4;
+  const size_t combine = (size_t)(decode_waves(D, tile_variant) / 2) * G * (D + 4) * 4;
   return pre + (stage > combine ? stage : combine);
 }
 
 int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, int tile_variant, size_t lds) {
-  auto q = [&]<int DD, int NS, bool PF, int OCC, bool KNT>() { return occupancy_d<DD, NS, PF, OCC, KNT>(scale_kind, lds); };
+  // Workgroups launched per CU: the shape's count, if that many fit.
+  auto q = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() {
+    const int nb = occupancy_d<DD, NS, PF, OCC, KNT, NW>(scale_kind, lds);
+    return nb < WPC ? nb : WPC;
+  };
   return k_whole_lines ? by_shape<true>(D, tile_variant, q) : by_shape<false>(D, tile_variant, q);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                          hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  auto l = [&]<int DD, int NS, bool PF, int OCC, bool KNT>() {
-    return launch_d<DD, NS, PF, OCC, KNT>(a, scale_kind, W, lds, st, e0, e1);
+  auto l = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() {
+    return launch_d<DD, NS, PF, OCC, KNT, NW>(a, scale_kind, W, lds, st, e0, e1);
   };
   return k_whole_lines ? by_shape<true>(D, a.tile_variant, l) : by_shape<false>(D, a.tile_variant, l);
 }

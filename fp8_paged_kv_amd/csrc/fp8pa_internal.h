@@ -94,6 +94,8 @@ constexpr int kMaxSplitTokens = 16384;
 // itself (start/stop: optional events that time the decode kernel alone;
 // k_whole_lines: the K layout lets every 16-byte K load of a wave cover whole
 // 128-byte lines, so non-temporal loads are used).
+int decode_waves(int D, int tile_variant);   // wave64s per decode workgroup
+int decode_seg_cost(int D, int tile_variant);   // default unit cost in the share balance
 size_t decode_lds_bytes(int D, int tile_variant, int B, int G, int P);
 int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, int tile_variant, size_t lds);
 hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
