@@ -26,9 +26,9 @@
 // number of cut units.
 //
 // Merging.  A segment that covers a whole unit writes the output.  Otherwise
-// it writes a normalised partial and its log-sum-exp (only a workgroup's first
-// and last segments can be partial: two slots per workgroup) and then a flag
-// holding the call's epoch.  The workgroup holding a unit's last piece (its
+// it writes a normalised partial and its base-2 log-sum-exp (only a
+// workgroup's first and last segments can be partial: two slots per
+// workgroup) and then a flag holding the call's epoch.  The workgroup holding a unit's last piece (its
 // first segment) merges the unit's partials at the end of its own share, when
 // the other holders, all of lower index, are finishing too: it waits for
 // their flags, combines (the standard log-sum-exp combination; the sink
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       if (wave == 0 && col) {
         float den = Ltot;
         if (a.sinks) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - M_ref);
-        const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
+        const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
         uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * D + 4 * quad;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -739,13 +739,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
       if (wave == 0 && col) {
         // Lane (head n, quad) holds dims 16c + 4quad .. +3: one 16-byte store per c.
-        const float inv = (Ltot > 0.0f) ? 1.0f / Ltot : 0.0f;
+        const float inv = (Ltot > 0.0f) ? __builtin_amdgcn_rcpf(Ltot) : 0.0f;
         const uint32_t row = (uint32_t)((pbase + n) * D * 4) + 16 * quad;
 #pragma unroll
         for (int c = 0; c < NC; ++c) st_coherent4(prs, row + 64 * c, acc[c] * inv);
         if (quad == 0)
           __hip_atomic_store(a.part_lse + pbase + n,
-                             (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : (M + __builtin_amdgcn_logf(Ltot)) * kLn2,
+                             (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : M + __builtin_amdgcn_logf(Ltot),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       const int w_a = wg_of_cost(tile_cost(b, g, 0)), w_b = wg_of_cost(tile_cost(b, g, nb - 1));
@@ -845,19 +845,19 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
         if (!okj[j]) continue;
         const int gi = threadIdx.x + NT * j;
         const int hh = hhj[j], d = 4 * gi - hh * D;
-        const float sk = a.sinks ? a.sinks[gq * G + hh] : kNegInf;
+        const float sk = a.sinks ? a.sinks[gq * G + hh] * kLog2e : kNegInf;
         float M = sk;
 #pragma unroll
         for (int k = 0; k < KF; ++k) M = fmaxf(M, lv[j][k]);
-        float den = (sk != kNegInf) ? __builtin_expf(sk - M) : 0.0f;
+        float den = (sk != kNegInf) ? __builtin_amdgcn_exp2f(sk - M) : 0.0f;
         f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KF; ++k) {
-          const float wv = (lv[j][k] == kNegInf) ? 0.0f : __builtin_expf(lv[j][k] - M);
+          const float wv = (lv[j][k] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(lv[j][k] - M);
           den += wv;
-          num += (wv > 0.0f) ? ov[j][k] * wv : f32x4{0.f, 0.f, 0.f, 0.f};
+          num += ov[j][k] * wv;
         }
-        const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
+        const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
         const f32x4 o = num * inv;
         u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
@@ -869,7 +869,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   #pragma unroll
         for (int j = 0; j < NJ; ++j) num[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (threadIdx.x < G) {
-          const float sk = a.sinks ? a.sinks[gq * G + threadIdx.x] : kNegInf;
+          const float sk = a.sinks ? a.sinks[gq * G + threadIdx.x] * kLog2e : kNegInf;
           s_M[threadIdx.x] = sk;
           s_den[threadIdx.x] = (sk != kNegInf) ? 1.0f : 0.0f;
         }
@@ -887,11 +887,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
             const float Mo = s_M[hh];
             float Mn = Mo;
             for (int k = 0; k < nc; ++k) Mn = fmaxf(Mn, s_wt[hh * CHS + k]);
-            const float sc = (Mo == kNegInf) ? 0.0f : __builtin_expf(Mo - Mn);
+            const float sc = (Mo == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(Mo - Mn);
             float den = s_den[hh] * sc;
             for (int k = 0; k < nc; ++k) {
               const float l = s_wt[hh * CHS + k];
-              const float wv = (l == kNegInf) ? 0.0f : __builtin_expf(l - Mn);
+              const float wv = (l == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(l - Mn);
               s_wt[hh * CHS + k] = wv;
               den += wv;
             }
@@ -928,7 +928,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                   const float wv = (k0 + kk < nc) ? s_wt[hhj[j] * CHS + kx] : 0.0f;
-                  num[j] += (wv > 0.0f) ? ov[j][kk] * wv : f32x4{0.f, 0.f, 0.f, 0.f};
+                  num[j] += ov[j][kk] * wv;
                 }
               }
             }
@@ -941,7 +941,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
           if (gi < ngrp) {
             const int hh = (4 * gi) / D, d = 4 * gi - hh * D;
             const float den = s_den[hh];
-            const float inv = (s_M[hh] == kNegInf || !(den > 0.0f)) ? 0.0f : 1.0f / den;
+            const float inv = (s_M[hh] == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
             const f32x4 o = num[j] * inv;
             u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
             if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};

@@ -15,7 +15,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 // Two E4M3 codes (bytes 0-1 of w, or bytes 2-3 when HI) to two packed bf16,
 // each exactly code value x 2**(exponent of `scale`) (the gfx950 scaled

@@ -48,7 +48,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const float* sinks;      // [Hq] or null
   float* part_o;           // [W][2][G][D] partial outputs (first / last segment of a workgroup)
-  float* part_lse;         // [W][2][G]
+  float* part_lse;         // [W][2][G] base-2 log-sum-exp of each partial
   uint32_t* flags;         // [W][2] a slot's flag holds the call's epoch once its partial is complete
   uint32_t epoch;          // distinct per call
   int32_t tile_variant;    // kernel shape (tuning; 0 = default)
