@@ -96,7 +96,7 @@ int check_desc(const fp8pa_pool_desc* d, const char* name) {
   if (d->num_rows < 0) return fail(FP8PA_EINVAL, "%s: num_rows must be >= 0", name);
   if (d->row_bytes > INT64_MAX / (d->num_rows > 0 ? d->num_rows : 1))
     return fail(FP8PA_EINVAL, "%s: pool size overflows", name);
-  if (foot + scale_bytes(*d) > INT32_MAX) return fail(FP8PA_EUNSUPPORTED, "%s: row too large", name);
+  if (d->row_bytes > INT32_MAX) return fail(FP8PA_EUNSUPPORTED, "%s: row_bytes %lld >= 2^31", name, (long long)d->row_bytes);
   return 0;
 }
 

@@ -527,8 +527,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
         p[s][i] = e;
       }
     l_run = l_run * alpha + psum;
+    // Once the running maxima settle, alpha is 1 in every lane: skip the
+    // rescale then (multiplying by 1 changes nothing).
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+      for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+    }
     if (!interior) {
       const int base = T0 + GT * quad;
       const int lo = start - base, hi = L - base;   // keep bytes in [lo, hi)
@@ -571,10 +575,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
         float pv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float vsc = 1.0f;
-          if constexpr (SK == 0) vsc = t.vs;
-          if constexpr (SK == 1) vsc = t.vst[s][i];
-          pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * vsc;
+          // A page scale belongs to an attended page (groups outside [start,
+          // L) read a clamped attended one), so p * scale is 0 where p is;
+          // a token scale of a masked position may be anything.
+          if constexpr (SK == 0) pv[i] = p[s][i] * t.vs;
+          if constexpr (SK == 1) pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * t.vst[s][i];
         }
         u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
                     pack_bf16x2(pv[6], pv[7])};

@@ -27,12 +27,13 @@ struct PoolGeom {
   int32_t scale_bytes;     // bytes of a row's scale block
 };
 
-// Byte offsets, from the pool base, of row r's payload and scale block.
+// Byte offsets, from the pool base, of row r's payload and scale block
+// (0 <= r < 2^31 and row_bytes < 2^31: one 32 x 32 -> 64-bit multiply).
 struct RowBases {
   int64_t code, scale;
 };
 __host__ __device__ inline RowBases row_bases(const PoolGeom& g, int64_t r) {
-  const int64_t base = r * g.row_bytes;
+  const int64_t base = (int64_t)((uint64_t)(uint32_t)r * (uint64_t)(uint32_t)g.row_bytes);
   if (!g.align64) return {base, base + g.sc_off};
   const int64_t sh = (-base) & 63;
   return {base + sh, sh >= g.scale_bytes ? base : base + sh + g.payload_bytes};

@@ -103,7 +103,7 @@ typedef struct fp8pa_pool_desc {
   int32_t layout;        /* FP8PA_LAYOUT_* */
   int32_t scale_kind;    /* FP8PA_SCALE_* */
   int32_t flags;         /* 0 or FP8PA_POOL_ALIGN64 */
-  int64_t row_bytes;     /* stride between rows; multiple of 16, >= natural row */
+  int64_t row_bytes;     /* stride between rows; multiple of 16, >= natural row, < 2^31 */
   int64_t scale_offset;  /* footer offset in the row; multiple of 16, >= P*Hkv*D;
                             -1 selects the default P*Hkv*D */
   int64_t num_rows;      /* rows in the pool (host-side sanity only) */

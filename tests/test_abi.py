@@ -72,6 +72,7 @@ def call_decode(k=None, v=None, **kw):
     (dict(k=kd(row_bytes=16400)), ops.EINVAL),                  # payload + scales do not fit
     (dict(k=kd(row_bytes=16424)), ops.EINVAL),                  # not a multiple of 16
     (dict(k=kd(scale_offset=16392)), ops.EINVAL),               # footer not 16-aligned
+    (dict(k=kd(row_bytes=1 << 31)), ops.EUNSUPPORTED),          # rows of 2 GiB or more
     (dict(k=kd(scale_offset=16000)), ops.EINVAL),               # footer inside the payload
     (dict(k=kd(layout="heads_dmajor")), ops.EUNSUPPORTED),      # K must be token-major
     (dict(v=vd(layout="heads")), ops.EUNSUPPORTED),             # V must be d-major
