@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 METRIC = "KV-read HBM GB/s (% of MI355X peak) + µs per decode call, batch×context sweep"
 PEAK_GBPS = 8000.0
 PROFILE_PMC = os.path.join(ROOT, "profiles", "decode_llama3-8b-decode_pmc.json")
-KERNEL_SOURCES = ["fp8_paged_kv_amd/csrc/decode.hip", "fp8_paged_kv_amd/csrc/device_common.h",
+KERNEL_SOURCES = ["fp8_paged_kv_amd/csrc/decode.hip", "fp8_paged_kv_amd/csrc/decode_kernel.h",
+                  "fp8_paged_kv_amd/csrc/append_common.h", "fp8_paged_kv_amd/csrc/device_common.h",
                   "fp8_paged_kv_amd/csrc/fp8pa_internal.h"]
 
 
@@ -158,6 +159,49 @@ def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgr
         kern_ms.append(hip.elapsed_ms(ev[0], ev[1]) / steps)
         hip.destroy(ev)
     return wall, step_ms, kern_ms, outs
+
+
+def time_fused(copies, j, steps, hip, ops, workloads, torch):
+    """One decode step of layer j with its KV append: fp8pa_append_quant of
+    each sequence's new token (position seq_lens - 1) then fp8pa_decode, against
+    fp8pa_append_decode (one launch).  Batch events around `steps` steps each,
+    pool copies rotated.  The appends rewrite each sequence's last token."""
+    R = len(copies)
+    l0 = copies[0][j]
+    B, Hkv, D = len(l0.lens), l0.Hkv, l0.D
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(20261203)
+    k_new = torch.randn((B, Hkv, D), generator=g, device="cuda:0").to(torch.bfloat16)
+    v_new = torch.randn((B, Hkv, D), generator=g, device="cuda:0").to(torch.bfloat16)
+    pos = (l0.seq_lens - 1).clamp(min=0).to(torch.int32)
+    counts = (l0.seq_lens > 0).to(torch.int32)
+    out = torch.empty_like(l0.q)
+    p = ops.decode_plan(B, l0.Hq, l0.kd, l0.max_seq_len, l0.window)
+    ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def two(l):
+        ops.append_quant(k_new[:, None], v_new[:, None], l.k_pool, l.v_pool, l.kd, l.vd, l.block_table, pos, counts)
+        workloads.decode_layer(l, out=out, workspace=ws)
+
+    def one(l):
+        ops.append_decode(l.q, k_new, v_new, l.k_pool, l.v_pool, l.kd, l.vd, l.block_table, l.seq_lens,
+                          l.max_seq_len, window=l.window, sinks=l.sinks, sm_scale=l.sm_scale, out=out, workspace=ws)
+
+    res = {}
+    for name, fn in (("append_then_decode", two), ("fused", one)):
+        for k in range(5):
+            fn(copies[k % R][j])
+        ev = hip.events(2)
+        torch.cuda.synchronize()
+        hip.record(ev[0], stream)
+        for k in range(steps):
+            fn(copies[k % R][j])
+        hip.record(ev[1], stream)
+        torch.cuda.synchronize()
+        res[name] = hip.elapsed_ms(ev[0], ev[1]) / steps * 1e3
+        hip.destroy(ev)
+    return res
 
 
 def clone_layer(l, torch):
@@ -385,6 +429,12 @@ def main():
     rec["roofline"]["frac_of_measured_read"] = round(achieved / rec["read_probe"]["gbps"], 4)
     del x
     rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, layers, args.cpu_budget)
+    # Last, as it rewrites each sequence's last token in the pools.
+    fu = time_fused(copies, dom, args.steps, hip, ops, workloads, torch)
+    rec["fused_append_decode"] = {
+        "layer": layers[dom].name, "us_append_then_decode": round(fu["append_then_decode"], 2),
+        "us_fused": round(fu["fused"], 2),
+        "timing": f"hipEvents around {args.steps} steps (new token per sequence appended, then decoded); mean per step"}
     print(json.dumps(rec), flush=True)
 
 

@@ -21,7 +21,7 @@ thread_local char g_err[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 struct Counters {
-  std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0},
+  std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0}, fused_append{0},
       errors{0};
 };
 Counters g_cnt;
@@ -243,11 +243,16 @@ int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
   return FP8PA_OK;
 }
 
-int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t* v_pool,
-                 const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, const int32_t* block_table,
-                 int64_t bt_stride, const int32_t* seq_lens, int B, int Hq, int window, const float* sinks,
-                 float sm_scale, int max_seq_len, int workgroups, int variant, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+namespace {
+
+// fp8pa_decode, and the fused fp8pa_append_decode when k_new / v_new are
+// given.  dry_run: validate everything, launch nothing.
+int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, const uint8_t* k_pool,
+                const uint8_t* v_pool, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
+                const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int B, int Hq, int window,
+                const float* sinks, float sm_scale, int max_seq_len, int workgroups, int variant, void* workspace,
+                size_t workspace_bytes, void* stream, bool dry_run = false) {
+  const bool fused = k_new != nullptr || v_new != nullptr;
   fp8pa_plan plan;
   size_t lds = 0;
   if (int rc = make_plan(B, Hq, kd, max_seq_len, window, workgroups, variant, &plan, &lds)) return rc;
@@ -260,13 +265,16 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
       vd->scale_kind != kd->scale_kind)
     return fail(FP8PA_EUNSUPPORTED, "K and V pools must share num_kv_heads, head_dim, page_size and scale_kind");
   if (B == 0) {
-    ok();
-    g_cnt.decode_calls.fetch_add(1);
+    if (!dry_run) {
+      ok();
+      g_cnt.decode_calls.fetch_add(1);
+    }
     return FP8PA_OK;
   }
-  if (!q || !out || !k_pool || !v_pool || !block_table || !seq_lens)
+  if (!q || !out || !k_pool || !v_pool || !block_table || !seq_lens || (fused && (!k_new || !v_new)))
     return fail(FP8PA_EINVAL, "a required device pointer is NULL");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(FP8PA_EINVAL, "q and out must be 16-byte aligned");
+  if (fused && (!aligned(k_new, 2) || !aligned(v_new, 2))) return fail(FP8PA_EINVAL, "k_new/v_new misaligned");
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return fail(FP8PA_EINVAL, "pools must be 16-byte aligned");
   if (((kd->flags & FP8PA_POOL_ALIGN64) && !aligned(k_pool, 64)) || ((vd->flags & FP8PA_POOL_ALIGN64) && !aligned(v_pool, 64)))
     return fail(FP8PA_EINVAL, "pools with aligned rows must be 64-byte aligned");
@@ -282,6 +290,7 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 256)) return fail(FP8PA_EINVAL, "workspace must be 256-byte aligned");
   }
+  if (dry_run) return FP8PA_OK;
   const int D = kd->head_dim;
   const int G = Hq / kd->num_kv_heads;
   const int W = plan.workgroups;
@@ -294,6 +303,12 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   a.bt_stride = bt_stride;
   a.seq_lens = seq_lens;
   a.sinks = sinks;
+  if (fused) {
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.kw = const_cast<uint8_t*>(k_pool);
+    a.vw = const_cast<uint8_t*>(v_pool);
+  }
   a.kg = geometry(*kd);
   a.vg = geometry(*vd);
   a.P = kd->page_size;
@@ -304,7 +319,7 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   a.G = G;
   a.window = window > 0 ? window : 0;
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
-  a.tile_variant = tile_variant();
+  a.tile_variant = fused ? 0 : tile_variant();   // the fused kernels exist in the default shapes
   a.min_tiles = min_tiles(fp8pa::decode_waves(D, a.tile_variant));
   a.seg_cost = seg_cost(fp8pa::decode_seg_cost(D, a.tile_variant));
   a.epoch = g_epoch.fetch_add(1) + 1;
@@ -320,13 +335,75 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
   // A wave's 16-byte K loads cover 64 bytes of each of 16 tokens: whole lines
   // when the 64-byte pieces of consecutive tokens are adjacent.
   const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
-  hipError_t e = fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop);
+  hipError_t e = fused ? fp8pa::launch_decode_fused(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                       : fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
   g_cnt.decode_mfma.fetch_add(1);
   if (W > 1) g_cnt.decode_split.fetch_add(1);
+  if (fused) g_cnt.fused_append.fetch_add(1);
   g_cnt.decode_calls.fetch_add(1);
   ok();
   return FP8PA_OK;
+}
+
+}  // namespace
+
+int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t* v_pool,
+                 const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, const int32_t* block_table,
+                 int64_t bt_stride, const int32_t* seq_lens, int B, int Hq, int window, const float* sinks,
+                 float sm_scale, int max_seq_len, int workgroups, int variant, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return decode_impl(nullptr, nullptr, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
+                     window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes, stream);
+}
+
+// Longest attended span (max_seq_len, or the window) for which
+// fp8pa_append_decode appends inside the decode kernel.
+constexpr int kFusedMaxSpan = 2048;
+
+int fp8pa_append_decode(const void* k_new, const void* v_new, const void* q, void* out, uint8_t* k_pool,
+                        uint8_t* v_pool, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
+                        const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int B, int Hq,
+                        int window, const float* sinks, float sm_scale, int max_seq_len, int workgroups, int variant,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return fail(FP8PA_EINVAL, "k_new and v_new are required");
+  // In-kernel appends sit on the critical path of the workgroup that reads
+  // each new token.  Short attended spans are launch-bound, and there the one
+  // launch wins (about 24 -> 13.5 us on the tiny and window-128 calls);
+  // longer ones run the append kernel and then the plain decode.
+  const int span = (window > 0 && window < max_seq_len) ? window : max_seq_len;
+  if (span <= kFusedMaxSpan)
+    return decode_impl(k_new, v_new, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
+                       window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes, stream);
+  // Every check of the call runs before the append launches.
+  if (int rc = decode_impl(k_new, v_new, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
+                           window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes,
+                           stream, true))
+    return rc;
+  if (B == 0) return decode_impl(nullptr, nullptr, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens,
+                                 B, Hq, window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace,
+                                 workspace_bytes, stream);
+  fp8pa::AppendArgs ap{};
+  ap.k_new = static_cast<const uint16_t*>(k_new);
+  ap.v_new = static_cast<const uint16_t*>(v_new);
+  ap.kp = k_pool;
+  ap.vp = v_pool;
+  ap.kg = geometry(*kd);
+  ap.vg = geometry(*vd);
+  ap.k_kind = kd->scale_kind;
+  ap.v_kind = vd->scale_kind;
+  ap.bt = block_table;
+  ap.bt_stride = bt_stride;
+  ap.seq_lens = seq_lens;
+  ap.T = 1;
+  ap.P = kd->page_size;
+  ap.Hkv = kd->num_kv_heads;
+  ap.D = kd->head_dim;
+  hipError_t e = fp8pa::launch_append(ap, B, 1, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP8PA_EHIP, "append launch: %s", hipGetErrorString(e));
+  g_cnt.append.fetch_add(1);
+  return decode_impl(nullptr, nullptr, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
+                     window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes, stream);
 }
 
 int fp8pa_merge_splits(const float* part_o, const float* part_lse, const float* sinks, void* out, int B, int Hq,
@@ -444,6 +521,7 @@ int fp8pa_get_counters(fp8pa_counters* c) {
   c->append_launches = g_cnt.append.load();
   c->debug_launches = g_cnt.debug.load();
   c->errors = g_cnt.errors.load();
+  c->fused_appends = g_cnt.fused_append.load();
   return FP8PA_OK;
 }
 
@@ -463,6 +541,7 @@ int fp8pa_reset_counters(void) {
   g_cnt.append = 0;
   g_cnt.debug = 0;
   g_cnt.errors = 0;
+  g_cnt.fused_append = 0;
   return FP8PA_OK;
 }
 

@@ -1,1028 +1,8 @@
-// Paged flash-decode over an E4M3 KV cache for gfx950.
-//
-// Operation (page "fp8 paged attention for MoE serving", "Smallest correct
-// example" and "Expected result"): for sequence b, KV head g and the G query
-// heads that share it, attend over the positions [start, L) of the sequence
-// through its block table, with E4M3 K/V dequantized as code x scale, a custom
-// sm_scale, and an optional per-head sink logit in the denominator.
-//
-// Work decomposition.  A unit is one (sequence, KV head): the G query heads
-// of the unit share every K/V read (page section "Why it happens": the grid
-// runs over sequence, KV head and split).  A unit's attended positions form a
-// run of tiles; the tiles of all units, sequence by sequence, make one global
-// list, and workgroup w of W takes the w-th equal share of it, so every
-// workgroup streams the same number of bytes however uneven the sequence
-// lengths are, and W is chosen so that all workgroups are resident at once.
-// A call with few tiles uses only the first ceil(T / min_tiles) workgroups
-// (at least one tile per wave), so every active workgroup's share is
-// non-empty.
-// Every workgroup builds the list itself from seq_lens (a prefix sum in LDS),
-// so the grid depends on host values only.  A workgroup's share cuts units
-// into segments; a workgroup is NW wave64s (four by default), each wave walks
-// every NW-th tile of a segment with its own online softmax, and the states
-// are combined in LDS.  The block-table rows of a segment are staged in LDS.
-// How many workgroups a CU runs is part of the kernel shape: at head dim 128
-// one four-wave workgroup per CU streams as fast as two and halves the
-// number of cut units.
-//
-// Merging.  A segment that covers a whole unit writes the output.  Otherwise
-// it writes a normalised partial and its base-2 log-sum-exp (only a
-// workgroup's first and last segments can be partial: two slots per
-// workgroup) and then a flag holding the call's epoch.  The workgroup holding a unit's last piece (its
-// first segment) merges the unit's partials at the end of its own share, when
-// the other holders, all of lower index, are finishing too: it waits for
-// their flags, combines (the standard log-sum-exp combination; the sink
-// enters once) and clears the flags, so a replayed graph (same epoch) starts
-// clean.  Flags need no initialisation: stale ones hold another call's
-// epoch.  No read-modify-write atomics are involved.
-//
-// Tile = 32*NS positions = four groups of 8*NS consecutive positions; a group
-// never crosses a page (P >= 16 and tiles are aligned to their size).
-//
-// QK^T on MFMA 16x16x32 bf16: A = 16 K rows (positions), B = Q^T (the G query
-// heads in columns, zero-padded to 16), K-dim = head dims.  Lane l of the A
-// operand holds position row l%16 and eight dims; the dims a lane holds are
-// chosen so that it reads 16 contiguous bytes of its position's row per 64
-// dims (the dot product does not care which dims share an MFMA as long as Q
-// uses the same assignment).  The rows are assigned to positions so that the
-// C layout (lane holds rows 4*(l/16)..+3 of column l%16) leaves each lane with
-// exactly the probabilities it must supply to the PV MFMA.
-//
-// PV on MFMA 16x16x32 bf16: O^T = V^T P^T with A = V^T (16 head dims x 32
-// positions) and B = P^T.  V is stored d-major per (page, head), so lane
-// (dim l%16, quad l/16) loads the 8*NS positions it needs as one 16-byte (or
-// 8-byte) load straight from HBM; no LDS transpose is needed.
-//
-// Scales.  fp32 per (page, head) or per (token, head): the K scale multiplies
-// the score after the dot product and the V scale multiplies the probability
-// before the PV product (both are exact reassociations of code x scale).
-// E8M0 per 32 dims: the K scale is applied inside the E4M3 -> bf16 conversion
-// (a power of two, exact); the V scale varies along the dims, so the PV B
-// operand is built once per 32-dim group with p x 2**(e - 127).
-//
-// Masked positions (outside [start, L): the tail of the last page, positions
-// before the window) get a score of -inf by selection and their V bytes are
-// zeroed, so NaN codes or scales there never reach the output.  Pages with no
-// attended position are never looked up in the block table.
-#include <hip/hip_ext.h>
-
-#include "device_common.h"
-#include "fp8pa_internal.h"
-#include "merge_common.h"
+// Host side of the paged decode: shape policy, LDS sizing, occupancy and the
+// launch of the plain (no append) kernels.  The kernel is in decode_kernel.h.
+#include "decode_kernel.h"
 
 namespace fp8pa {
-namespace {
-
-constexpr float kNegInf = -__builtin_inff();
-
-template <int NS>
-struct VRaw;
-template <>
-struct VRaw<1> { typedef u32x2 type; };
-template <>
-struct VRaw<2> { typedef u32x4 type; };
-
-// The D/32 E8M0 bytes of one position (one 32-dim group each), zero-extended
-// into a u32x4.
-template <int NG>
-__device__ __forceinline__ u32x4 load_e8_row(const uint8_t* p) {
-  if constexpr (NG == 2) return u32x4{(uint32_t)ld_global<uint16_t>(p), 0, 0, 0};
-  else if constexpr (NG == 4) return u32x4{ld_global<uint32_t>(p), 0, 0, 0};
-  else if constexpr (NG == 8) { const u32x2 v = ld_global<u32x2>(p); return u32x4{v[0], v[1], 0, 0}; }
-  else return ld_global<u32x4>(p);
-}
-
-// floor(a / b) for 0 <= a < 2^53, 0 < b: 32-bit division when both fit,
-// else a double-precision quotient corrected by one step either way (much
-// shorter than 64-bit integer division).
-__device__ __forceinline__ int64_t floordiv(int64_t a, int64_t b) {
-  if ((((uint64_t)a | (uint64_t)b) >> 32) == 0) return (int64_t)((uint32_t)a / (uint32_t)b);
-  int64_t q = (int64_t)((double)a / (double)b);
-  if (q * b > a) --q;
-  else if ((q + 1) * b <= a) ++q;
-  return q;
-}
-
-// A 64-bit value of lane l (l uniform).
-__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ uint32_t byte_of(const u32x4& v, int i) { return (v[i >> 2] >> (8 * (i & 3))) & 0xffu; }
-
-// Registers of one tile for one lane.
-template <int D, int NS, int SK>
-struct Tile {
-  static constexpr int NM = D / 64, NC = D / 16, NG = D / 32, NE = (8 * NG) / 16;
-  typedef typename VRaw<NS>::type vraw_t;
-  u32x4 k[NS][2][NM];   // K codes of the lane's position rows
-  vraw_t v[NC];         // V codes of the lane's dims, GT positions each
-  float ks, vs;         // per-(page, head) scales of the lane's score group
-  float kst[NS][8];     // per-(token, head) scales of the lane's score positions
-  float vst[NS][8];
-  u32x4 ke8[NS][2];     // E8M0 bytes of the lane's K rows
-  u32x4 ve8[NS][NE];    // E8M0 bytes of the lane's 8 score positions, all groups
-};
-
-template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW>
-__global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a) {
-  constexpr int NT = 64 * NW;   // threads (NW wave64s)
-  constexpr int TT = 32 * NS;   // positions per tile
-  constexpr int GT = 8 * NS;    // positions per group
-  constexpr int NM = D / 64;    // 16-byte K pieces per position row per lane
-  constexpr int NQ = D / 32;    // QK MFMAs per 16 positions
-  constexpr int NC = D / 16;    // PV MFMAs per subtile (16 dims each)
-  constexpr int NG = D / 32;    // E8M0 groups along D
-  typedef Tile<D, NS, SK> TileT;
-
-  extern __shared__ int s_dyn[];   // tile prefix, non-empty prefix, lengths, then the page-row stage / wave-combine buffer
-  __shared__ float s_m[NW][16];
-  __shared__ float s_l[NW][16];
-  __shared__ float s_M[16], s_den[16], s_sc[16];
-  __shared__ int s_wsum[NW], s_wsum_ne[NW];
-  __shared__ int s_timeout;
-  __shared__ int64_t s_bnd[2];
-  __shared__ int s_first[3];   // capped W and the first segment's (b, g), from wave 0
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int n = lane & 15;      // MFMA column: query head of the group
-  const int quad = lane >> 4;   // MFMA k/row quad
-  const int G = a.G, P = a.P, log2P = a.log2P, B = a.B, Hkv = a.Hkv;
-  int W = gridDim.x;
-  const int w = blockIdx.x;
-  const bool col = n < G;
-
-  // ---- tiles per sequence and their prefix sums.
-  auto tiles_of = [&](int L) {
-    const int st = (a.window > 0 && L > a.window) ? L - a.window : 0;
-    const int tb = st & ~(TT - 1);
-    return L > st ? (L - tb + TT - 1) / TT : 0;
-  };
-  int* s_pre = s_dyn;                       // [B + 1] tiles before sequence b
-  int* s_nep = s_dyn + ((B + 4) & ~3);      // [B + 1] non-empty sequences before b
-  int* s_len = s_nep + ((B + 4) & ~3);      // [B] seq_lens, read from global memory once
-  int* s_work_i = s_len + ((B + 4) & ~3);
-  float* s_work = reinterpret_cast<float*>(s_work_i);
-  // Shares are balanced in cost: a tile costs TC = 4 and every (non-empty)
-  // unit a fixed SC more (its setup, wave combine and partial), laid out
-  // before its tiles.  Workgroup w takes the tiles whose cost start lies in
-  // [floor(w*Ct/W), floor((w+1)*Ct/W)).  Any cost window of SC + TC holds a
-  // tile start, so capping W at Ct / (SC + TC*min_tiles) keeps every share
-  // non-empty (at least min_tiles tiles' worth).  When units average at most
-  // one tile per wave, a split would only add merges: tiles then cost 0 and a
-  // unit 1, so shares are whole units (unit-aligned mode).
-  int64_t T = 0, U = 0, TC = 0, SC = 0, Ct = 0;
-  auto set_costs = [&](int tiles, int nonempty) {
-    T = (int64_t)tiles * Hkv;
-    U = (int64_t)nonempty * Hkv;
-    const bool unit_mode = T <= (int64_t)NW * U;
-    TC = unit_mode ? 0 : 4;
-    SC = unit_mode ? 1 : a.seg_cost;
-    Ct = SC * U + TC * T;
-  };
-  auto cap_W = [&]() {
-    int64_t want = floordiv(Ct, SC + TC * a.min_tiles);
-    if (want < 1) want = 1;
-    if (T == 0) want = 0;
-    if (want < W) W = (int)want;
-  };
-  // A share bound as a global tile index: the first tile whose cost start is
-  // >= c, for c inside the cost range of sequence bb (which starts at lo,
-  // after pre tiles, and has nbb tiles per unit); past a unit's last tile
-  // that is the next unit's first.
-  auto bound_in = [&](int64_t c, int64_t lo, int pre, int nbb) -> int64_t {
-    const int64_t span = SC + TC * nbb;
-    int64_t gg = floordiv(c - lo, span);
-    const int64_t r = c - lo - gg * span;
-    int64_t t = r <= SC ? 0 : (TC > 0 ? (r - SC + 3) >> 2 : nbb);
-    if (t >= nbb) {
-      t = 0;
-      ++gg;
-    }
-    return (int64_t)Hkv * pre + gg * nbb + t;
-  };
-  // Page rows of the chunk [ca, cb) of the current segment's tiles.
-  int b = 0, g = 0, L = 0, start = 0, tbeg = 0, p_first = 0, nstaged = 1;
-  auto chunk_rows = [&](int ca, int cb) {
-    const int pos0 = tbeg + ca * TT > start ? tbeg + ca * TT : start;
-    const int pos1 = tbeg + cb * TT < L ? tbeg + cb * TT : L;
-    p_first = pos0 >> log2P;
-    nstaged = ((pos1 - 1) >> log2P) - p_first + 1;
-  };
-  constexpr int CH = kMaxSplitTokens / TT;   // tiles whose page rows are staged at once
-  int* s_tab = s_work_i;
-
-  // Up to 64 sequences, wave 0 alone computes the prefix sums, the share
-  // bounds and the first segment's unit in registers, and stages that
-  // segment's first page rows, so the workgroup passes a single barrier
-  // before its first tile loads.  Larger batches use all four waves.
-  const bool fast = B <= 64;
-  if (fast) {
-    if (wave == 0) {
-      const int len = lane < B ? a.seq_lens[lane] : 0;
-      const int nt = tiles_of(len), ne = nt > 0 ? 1 : 0;
-      int incl = nt, incl_ne = ne;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off), v2 = __shfl_up(incl_ne, off);
-        if (lane >= off) {
-          incl += v;
-          incl_ne += v2;
-        }
-      }
-      const int pre = incl - nt, nep = incl_ne - ne;
-      if (lane < B) {
-        s_len[lane] = len;
-        s_pre[lane] = pre;
-        s_nep[lane] = nep;
-      }
-      const int tot = __shfl(incl, 63), tot_ne = __shfl(incl_ne, 63);
-      if (lane == 0) {
-        s_pre[B] = tot;
-        s_nep[B] = tot_ne;
-      }
-      set_costs(tot, tot_ne);
-      cap_W();
-      if (w < W) {
-        const int64_t lo = SC * Hkv * nep + TC * (int64_t)Hkv * pre;
-        const int64_t hiw = lo + (int64_t)Hkv * (SC * ne + TC * nt);
-        int64_t bnd[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int64_t c = floordiv((int64_t)(w + e) * Ct, W);
-          const bool hit = lane < B && c >= lo && c < hiw;
-          const int64_t v = hit ? bound_in(c, lo, pre, nt) : 0;
-          const uint64_t mask = __ballot(hit);
-          bnd[e] = mask ? readlane64(v, (int)__builtin_ctzll(mask)) : T;
-        }
-        if (bnd[0] < bnd[1]) {
-          // The first segment's unit: b is the last sequence whose tiles start
-          // at or before bnd[0] (a non-empty one, as bnd[0] < T).
-          const int bl = 63 - (int)__builtin_clzll(__ballot(lane < B && (int64_t)Hkv * pre <= bnd[0]));
-          b = bl;
-          const int nb = __builtin_amdgcn_readlane(nt, bl);
-          const int64_t ubase = (int64_t)Hkv * __builtin_amdgcn_readlane(pre, bl);
-          g = (int)floordiv(bnd[0] - ubase, nb);
-          const int64_t ustart = ubase + (int64_t)g * nb;
-          const int ta = (int)(bnd[0] - ustart);
-          const int tc = (int)((bnd[1] < ustart + nb ? bnd[1] : ustart + nb) - ustart);
-          L = __builtin_amdgcn_readlane(len, bl);
-          start = (a.window > 0 && L > a.window) ? L - a.window : 0;
-          tbeg = start & ~(TT - 1);
-          chunk_rows(ta, tc < ta + CH ? tc : ta + CH);
-          const int32_t* btr0 = a.bt + (int64_t)b * a.bt_stride;
-          for (int i = lane; i < nstaged; i += 64) s_tab[i] = btr0[p_first + i];
-        }
-        if (lane == 0) {
-          s_bnd[0] = bnd[0];
-          s_bnd[1] = bnd[1];
-          s_first[1] = b;
-          s_first[2] = g;
-        }
-      }
-      if (lane == 0) s_first[0] = W;
-    }
-    __syncthreads();
-    W = s_first[0];
-    set_costs(s_pre[B], s_nep[B]);
-  } else {
-    const int per = (B + NT - 1) / NT;
-    const int bb0 = threadIdx.x * per;
-    int local = 0, lne = 0;
-    for (int i = 0; i < per; ++i)
-      if (bb0 + i < B) {
-        const int len = a.seq_lens[bb0 + i];
-        s_len[bb0 + i] = len;
-        const int nt = tiles_of(len);
-        local += nt;
-        lne += nt > 0;
-      }
-    int incl = local, incl_ne = lne;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off), v2 = __shfl_up(incl_ne, off);
-      if (lane >= off) {
-        incl += v;
-        incl_ne += v2;
-      }
-    }
-    if (lane == 63) {
-      s_wsum[wave] = incl;
-      s_wsum_ne[wave] = incl_ne;
-    }
-    __syncthreads();
-    int excl = incl - local, excl_ne = incl_ne - lne;
-    for (int i = 0; i < wave; ++i) {
-      excl += s_wsum[i];
-      excl_ne += s_wsum_ne[i];
-    }
-    for (int i = 0; i < per; ++i)
-      if (bb0 + i < B) {
-        const int nt = tiles_of(s_len[bb0 + i]);
-        s_pre[bb0 + i] = excl;
-        s_nep[bb0 + i] = excl_ne;
-        excl += nt;
-        excl_ne += nt > 0;
-      }
-    if (threadIdx.x == 0) {
-      int t = 0, tn = 0;
-      for (int i = 0; i < NW; ++i) {
-        t += s_wsum[i];
-        tn += s_wsum_ne[i];
-      }
-      s_pre[B] = t;
-      s_nep[B] = tn;
-    }
-    __syncthreads();
-    set_costs(s_pre[B], s_nep[B]);
-    cap_W();
-  }
-
-  // Sequences with nothing to attend get a zero output.
-  for (int bb = w; bb < B; bb += (int)gridDim.x) {
-    if (s_pre[bb + 1] != s_pre[bb]) continue;
-    uint16_t* o = a.out + (size_t)bb * a.Hq * D;
-    for (int i = threadIdx.x; i < a.Hq * D; i += NT) o[i] = 0;
-  }
-  if (w >= W) return;
-  auto cpre = [&](int bb) -> int64_t { return SC * Hkv * s_nep[bb] + TC * (int64_t)Hkv * s_pre[bb]; };
-  // Cost start of tile i of unit (bb, gg).
-  auto tile_cost = [&](int bb, int gg, int i) -> int64_t {
-    const int nbb = s_pre[bb + 1] - s_pre[bb];
-    return cpre(bb) + (int64_t)gg * (SC + TC * nbb) + SC + TC * i;
-  };
-  // Workgroup holding a tile of cost start c: the largest w with floor(w*Ct/W) <= c.
-  auto wg_of_cost = [&](int64_t c) -> int { return (int)(floordiv((c + 1) * W + Ct - 1, Ct) - 1); };
-  if (!fast) {
-    // The share's first and end tiles: the first tile whose cost start is >=
-    // floor(w*Ct/W), resp. floor((w+1)*Ct/W), found by the thread whose
-    // sequence's cost range holds that point (T past the end).
-    const int64_t cb[2] = {floordiv((int64_t)w * Ct, W), floordiv((int64_t)(w + 1) * Ct, W)};
-    if (threadIdx.x < 2) s_bnd[threadIdx.x] = T;
-    __syncthreads();
-    const int per = (B + NT - 1) / NT;
-    for (int i = 0; i < per; ++i) {
-      const int bb = threadIdx.x * per + i;
-      if (bb >= B) break;
-      const int64_t lo = cpre(bb), hiw = cpre(bb + 1);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t c = cb[e];
-        if (c >= lo && c < hiw) s_bnd[e] = bound_in(c, lo, s_pre[bb], s_pre[bb + 1] - s_pre[bb]);
-      }
-    }
-    __syncthreads();
-  }
-
-  // Per-segment state (captured by the tile helpers below).
-  const int32_t* btr = a.bt;
-  const uint8_t* kpool = a.kp;
-  const uint8_t* vpool = a.vp;
-  const int kgrp = n >> 2;      // group of this lane's K row
-  const int kslot = n & 3;
-  bf16x8 qop[NQ];
-
-  // Row of a page of the current chunk.  A group with no attended position
-  // reads a clamped (attended) page instead: its scores are masked to -inf and
-  // its V bytes zeroed, so every lane issues the same loads and the compiler
-  // can count outstanding loads exactly across the prefetch.
-  auto row_of = [&](int page) -> int32_t {
-    int i = page - p_first;
-    i = i < 0 ? 0 : (i >= nstaged ? nstaged - 1 : i);
-    return s_tab[i];
-  };
-
-  // ---- issue the loads of one tile: scales first, then the K and V codes, so
-  // that the large code loads are the most recent ones in flight (a later
-  // wait for a scale, or for the reuse of a scale's register, then leaves
-  // them outstanding).
-  auto load_tile = [&](TileT& t, int T0) {
-    const int tk = T0 + GT * kgrp;   // first position of the lane's K group
-    const int tq = T0 + GT * quad;   // first position of the lane's score/V group
-    const int32_t row_k = row_of(tk >> log2P);
-    const int32_t row_q = row_of(tq >> log2P);
-    const int tpq = tq & (P - 1);
-    const RowBases rk = row_bases(a.kg, row_k), rqk = row_bases(a.kg, row_q), rqv = row_bases(a.vg, row_q);
-    const uint8_t* ksc = a.kp + rqk.scale + g * a.kg.sc_head_stride;
-    const uint8_t* vsc = a.vp + rqv.scale + g * a.vg.sc_head_stride;
-    if constexpr (SK == 0) {
-      t.ks = ld_global<float>(ksc);
-      t.vs = ld_global<float>(vsc);
-    } else if constexpr (SK == 1) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tt = tpq + 8 * s + i;
-          t.kst[s][i] = ld_global<float>(ksc + tt * a.kg.sc_tok_stride);
-          t.vst[s][i] = ld_global<float>(vsc + tt * a.vg.sc_tok_stride);
-        }
-    } else {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const uint8_t* src = vsc + (tpq + 8 * s) * a.vg.sc_tok_stride;
-#pragma unroll
-        for (int k = 0; k < TileT::NE; ++k) t.ve8[s][k] = ld_global<u32x4>(src + 16 * k);
-      }
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int aa = 0; aa < 2; ++aa) {
-          const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
-          const uint8_t* kf = a.kp + rk.scale + g * a.kg.sc_head_stride +
-                              tp * a.kg.sc_tok_stride;
-          t.ke8[s][aa] = load_e8_row<NG>(kf);
-        }
-    }
-    const uint8_t* krow = kpool + rk.code + 16 * quad;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int aa = 0; aa < 2; ++aa) {
-        const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const uint8_t* src = krow + tp * a.kg.tok_stride + m * a.kg.dchunk_stride;
-          t.k[s][aa][m] = KNT ? ld_stream<u32x4>(src) : ld_global<u32x4>(src);
-        }
-      }
-    // The lane's GT positions lie in one token block of the d-major V layout.
-    const uint8_t* vrow = vpool + rqv.code + (int64_t)(tpq / a.vg.tblk) * a.vg.tblk_stride +
-                          (tpq % a.vg.tblk);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int d = 16 * c + n;
-      t.v[c] = ld_stream<typename TileT::vraw_t>(vrow + (int64_t)(d >> 6) * a.vg.dchunk_stride +
-                                                 (int64_t)(d & 63) * a.vg.d_stride);
-    }
-  };
-
-  float m_run = kNegInf;        // running max (log2 units) of this lane's head column
-  float l_run = 0.0f;           // this lane's share of the running sum
-  f32x4 acc[NC];
-
-  // ---- online-softmax update with one tile.
-  auto compute_tile = [&](TileT& t, int T0) {
-    const bool interior = (T0 >= start) && (T0 + TT <= L);
-    float sc[NS][2][4];
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int aa = 0; aa < 2; ++aa) {
-        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          float cvt = 1.0f;
-          if constexpr (SK == 2) {
-            const uint32_t e = byte_of(t.ke8[s][aa], 2 * m + (quad >> 1));
-            cvt = e8m0_as_scale_operand(e);
-          }
-          const u32x4 w = t.k[s][aa][m];
-          s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[0], w[1], cvt), qop[2 * m], s4);
-          s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[2], w[3], cvt), qop[2 * m + 1], s4);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float f = a.qk_scale;
-          if constexpr (SK == 0) f *= t.ks;
-          if constexpr (SK == 1) f *= t.kst[s][4 * aa + j];
-          sc[s][aa][j] = s4[j] * f;
-        }
-      }
-    if (!interior) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int aa = 0; aa < 2; ++aa)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int pos = T0 + GT * quad + 8 * s + 4 * aa + j;
-            if (pos < start || pos >= L) sc[s][aa][j] = kNegInf;
-          }
-    }
-    float tmax = kNegInf;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int aa = 0; aa < 2; ++aa)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sc[s][aa][j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_ref = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    m_run = m_new;
-    float psum = 0.0f;
-    float p[NS][8];
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e = __builtin_amdgcn_exp2f(sc[s][i >> 2][i & 3] - m_ref);
-        psum += e;
-        p[s][i] = e;
-      }
-    l_run = l_run * alpha + psum;
-    // Once the running maxima settle, alpha is 1 in every lane: skip the
-    // rescale then (multiplying by 1 changes nothing).
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] *= alpha;
-    }
-    if (!interior) {
-      const int base = T0 + GT * quad;
-      const int lo = start - base, hi = L - base;   // keep bytes in [lo, hi)
-#pragma unroll
-      for (int k = 0; k < GT / 4; ++k) {
-        uint32_t mk = 0;
-#pragma unroll
-        for (int byte = 0; byte < 4; ++byte) {
-          const int bi = 4 * k + byte;
-          if (bi >= lo && bi < hi) mk |= 0xffu << (8 * byte);
-        }
-#pragma unroll
-        for (int c = 0; c < NC; ++c) t.v[c][k] &= mk;
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if constexpr (SK == 2) {
-        bf16x8 pop[NG];
-#pragma unroll
-        for (int gq = 0; gq < NG; ++gq) {
-          float pv[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int bi = i * NG + gq;
-            const int ex = (int)byte_of(t.ve8[s][bi >> 4], bi & 15) - 127;
-            const float x = __builtin_amdgcn_ldexpf(p[s][i], ex);
-            pv[i] = (p[s][i] == 0.0f) ? 0.0f : x;
-          }
-          u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                      pack_bf16x2(pv[6], pv[7])};
-          pop[gq] = __builtin_bit_cast(bf16x8, pk);
-        }
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const bf16x8 vop = e4m3x8_to_bf16x8(t.v[c][2 * s], t.v[c][2 * s + 1], 1.0f);
-          acc[c] = mfma_16x16x32_bf16(vop, pop[c >> 1], acc[c]);
-        }
-      } else {
-        float pv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          // A page scale belongs to an attended page (groups outside [start,
-          // L) read a clamped attended one), so p * scale is 0 where p is;
-          // a token scale of a masked position may be anything.
-          if constexpr (SK == 0) pv[i] = p[s][i] * t.vs;
-          if constexpr (SK == 1) pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * t.vst[s][i];
-        }
-        u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                    pack_bf16x2(pv[6], pv[7])};
-        const bf16x8 pop = __builtin_bit_cast(bf16x8, pk);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const bf16x8 vop = e4m3x8_to_bf16x8(t.v[c][2 * s], t.v[c][2 * s + 1], 1.0f);
-          acc[c] = mfma_16x16x32_bf16(vop, pop, acc[c]);
-        }
-      }
-    }
-  };
-
-  int64_t cur = s_bnd[0];
-  const int64_t hi = s_bnd[1];
-  int slot = 0;
-  // Unit to merge at the end of the share (uniform across the workgroup).
-  int pend = 0, pend_b = 0, pend_g = 0, pend_wa = 0, pend_first_slot_a = 0;
-  // Wave 0 located the first segment and staged its first page rows.
-  bool staged = fast;
-  while (cur < hi) {
-    // ---- the segment: unit (b, g), tiles [ta, tc) of the unit.
-    if (staged) {
-      b = s_first[1];
-      g = s_first[2];
-    } else {
-      int lo_b = 0, hi_b = B - 1;   // largest b with s_pre[b] * Hkv <= cur (a non-empty sequence)
-      while (lo_b < hi_b) {
-        const int mid = (lo_b + hi_b + 1) >> 1;
-        if ((int64_t)s_pre[mid] * Hkv <= cur) lo_b = mid;
-        else hi_b = mid - 1;
-      }
-      b = lo_b;
-      g = (int)floordiv(cur - (int64_t)s_pre[b] * Hkv, s_pre[b + 1] - s_pre[b]);
-    }
-    const int nb = s_pre[b + 1] - s_pre[b];
-    const int64_t ubase = (int64_t)s_pre[b] * Hkv;
-    const int64_t ustart = ubase + (int64_t)g * nb;
-    const int64_t uend = ustart + nb;
-    const int64_t send = hi < uend ? hi : uend;
-    const int ta = (int)(cur - ustart), tc = (int)(send - ustart);
-    L = s_len[b];
-    start = (a.window > 0 && L > a.window) ? L - a.window : 0;
-    tbeg = start & ~(TT - 1);
-    btr = a.bt + (int64_t)b * a.bt_stride;
-    kpool = a.kp + (int64_t)g * a.kg.head_stride;
-    vpool = a.vp + (int64_t)g * a.vg.head_stride;
-    {
-      // Q operand (B of QK): lane (head n, quad) holds dims 64m + 16quad + 8h2 + i.
-      const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)g * G + (col ? n : 0)) * D;
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          u32x4 v = col ? ld_global<u32x4>(qrow + 64 * m + 16 * quad + 8 * h2) : u32x4{0, 0, 0, 0};
-          qop[2 * m + h2] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-    m_run = kNegInf;
-    l_run = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int ca = ta; ca < tc; ca += CH) {
-      const int cb = tc < ca + CH ? tc : ca + CH;
-      chunk_rows(ca, cb);
-      if (!staged) {
-        __syncthreads();   // earlier readers of the stage are done
-        for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = btr[p_first + i];
-        __syncthreads();
-      }
-      staged = false;
-      // ---- tile loop: wave w takes tiles ca + w, ca + w + 4, ...
-      const int nmine = cb - ca > wave ? (cb - ca - wave + NW - 1) / NW : 0;
-      auto tile_pos = [&](int k) { return tbeg + (ca + wave + NW * k) * TT; };
-      if constexpr (PF) {
-        // Loads run one tile ahead, ping-ponging two register buffers.  The
-        // trip count is fixed and loads are unconditional (a prefetch past
-        // the last tile re-reads a cache-hot tile), so the waits before each
-        // compute cover only that tile's loads.
-        TileT A, Bt;
-        if (nmine > 0) load_tile(A, tile_pos(0));
-        const int npairs = nmine / 2;
-        for (int k = 0; k < npairs; ++k) {
-          load_tile(Bt, tile_pos(2 * k + 1));
-          compute_tile(A, tile_pos(2 * k));
-          load_tile(A, tile_pos(2 * k + 2 < nmine ? 2 * k + 2 : 2 * k + 1));
-          compute_tile(Bt, tile_pos(2 * k + 1));
-        }
-        if (nmine & 1) compute_tile(A, tile_pos(nmine - 1));
-      } else {
-        TileT A;
-        for (int k = 0; k < nmine; ++k) {
-          load_tile(A, tile_pos(k));
-          compute_tile(A, tile_pos(k));
-        }
-      }
-    }
-
-    // ---- combine the waves' states in LDS.
-    float lsum = l_run;
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    float* s_o = s_work;   // [NW / 2][G][D + 4]
-    constexpr int OS = D + 4;
-    if (quad == 0) {
-      s_m[wave][n] = m_run;
-      s_l[wave][n] = lsum;
-    }
-    __syncthreads();   // also: every wave is past its last read of the page-row stage
-    float M = kNegInf;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) M = fmaxf(M, s_m[i][n]);
-    const float M_ref = (M == kNegInf) ? 0.0f : M;
-    float Ltot = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) Ltot += s_l[i][n] * __builtin_amdgcn_exp2f(s_m[i][n] - M_ref);
-    {
-      const float f = __builtin_amdgcn_exp2f(m_run - M_ref);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] *= f;
-    }
-    // Pairwise tree: at each level the upper half of the remaining waves
-    // hands its accumulators to the lower half through LDS.
-#pragma unroll
-    for (int half = NW / 2; half >= 1; half >>= 1) {
-      if (wave >= half && wave < 2 * half && col) {
-        float* dst = s_o + ((wave - half) * G + n) * OS + 4 * quad;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
-      }
-      __syncthreads();
-      if (wave < half && col) {
-        const float* src = s_o + (wave * G + n) * OS + 4 * quad;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
-      }
-      if (half > 1) __syncthreads();
-    }
-
-    const int h = g * G + n;
-    if (ta == 0 && tc == nb) {
-      // The segment is the whole unit: o = acc / (sum + e^(sink - max)).
-      if (wave == 0 && col) {
-        float den = Ltot;
-        if (a.sinks) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - M_ref);
-        const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
-        uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * D + 4 * quad;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          u32x2 pk = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv), pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + 16 * c) = pk;
-        }
-      }
-    } else {
-      // ---- partial of this segment, then its flag (or, for the unit's last
-      // piece, a merge at the end of the share).  Partials are written and
-      // read with sc1 (agent-coherent) accesses, which on this multi-XCD part
-      // are coherent across the per-XCD L2 caches without a cache write-back
-      // or invalidate.
-      const size_t pbase = ((size_t)w * 2 + slot) * G;
-      const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
-      if (wave == 0 && col) {
-        // Lane (head n, quad) holds dims 16c + 4quad .. +3: one 16-byte store per c.
-        const float inv = (Ltot > 0.0f) ? __builtin_amdgcn_rcpf(Ltot) : 0.0f;
-        const uint32_t row = (uint32_t)((pbase + n) * D * 4) + 16 * quad;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) st_coherent4(prs, row + 64 * c, acc[c] * inv);
-        if (quad == 0)
-          __hip_atomic_store(a.part_lse + pbase + n,
-                             (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : M + __builtin_amdgcn_logf(Ltot),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      const int w_a = wg_of_cost(tile_cost(b, g, 0)), w_b = wg_of_cost(tile_cost(b, g, nb - 1));
-      if (w == w_b) {
-        // This is the unit's last piece: merge the unit at the end of the share.
-        pend = 1;
-        pend_b = b;
-        pend_g = g;
-        // w_a's share holds an earlier segment (so this unit sits in its
-        // last slot) iff it starts at or before the previous unit's last
-        // tile, whose cost start is 4 below this unit's.
-        pend_first_slot_a = floordiv((int64_t)w_a * Ct, W) <= tile_cost(b, g, 0) - SC - TC ? 1 : 0;
-        pend_wa = w_a;
-      } else if (threadIdx.x == 0) {
-        // Wave 0 wrote the partial; once its stores have completed at the
-        // coherence point, publish the slot.
-        __builtin_amdgcn_s_waitcnt(0);
-        __hip_atomic_store(a.flags + 2 * w + slot, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();   // LDS is reused by the next segment
-    cur = send;
-    slot = 1;
-  }
-
-  if (pend) {
-    // ---- merge the unit whose last piece was this share's first segment.
-    // Its pieces are held by workgroups w_a..w; w_a holds it in its last
-    // slot when its share began before the unit, every other one in its
-    // first slot.
-    const int w_a = pend_wa;
-    const int nseg = w - w_a + 1;
-    const int first_slot_a = pend_first_slot_a;
-    auto slot_of = [&](int wi) -> int { return wi == w_a ? first_slot_a : 0; };
-    auto part_row = [&](int wi) -> uint32_t { return (uint32_t)(((size_t)wi * 2 + slot_of(wi)) * G); };
-    if (threadIdx.x == 0) {
-      __builtin_amdgcn_s_waitcnt(0);   // this workgroup's own partial (wave 0) is complete
-      s_timeout = 0;
-    }
-    // Wait for the other holders' flags.  They have lower indices, so they
-    // were dispatched first and never wait on this workgroup; the wait is
-    // bounded all the same (a timeout yields NaN outputs).
-    for (int i = threadIdx.x; i < nseg - 1; i += NT) {
-      const uint32_t* f = a.flags + 2 * (w_a + i) + slot_of(w_a + i);
-      int spins = 0;
-      while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
-        if (++spins > (1 << 22)) {
-          s_timeout = 1;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    __syncthreads();
-    const int bq = pend_b, gq = pend_g;
-    const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
-    // Merged 64 partials at a time with a running maximum per head (the sink
-    // is the initial maximum, with weight 1): per chunk the weights go to LDS
-    // and every thread accumulates float4 groups of the G x D outputs in
-    // registers.
-    constexpr int CHS = 64;   // partials per chunk
-    constexpr int NJ = D >= 512 ? 4 : (D >= 256 ? 2 : 1);   // float4 groups per thread per pass
-    constexpr int KB = 8;     // partials whose loads are in flight together
-    const int ngrp = G * D / 4;
-    float* s_wt = s_work;     // [G][CHS]
-    constexpr int KF = NJ == 1 ? 16 : 4;   // partials merged in registers
-    if (NJ <= 2 && nseg <= KF && ngrp <= NT * NJ) {
-      // Few partials, one pass, head dim <= 256: every thread issues the lse
-      // values and the float4 groups of its heads together (one round trip)
-      // and merges them in registers, in the same order and arithmetic as the
-      // chunked path.  (At head dim 512 the chunked path measured faster.)
-      constexpr uint32_t kNone = 0xFFFFFFF0u;   // past the buffer: reads zero
-      int hhj[NJ];
-      bool okj[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int gi = threadIdx.x + NT * j;
-        okj[j] = gi < ngrp;
-        hhj[j] = okj[j] ? (4 * gi) / D : 0;
-      }
-      f32x4 ov[NJ][KF];
-      float lv[NJ][KF];
-#pragma unroll
-      for (int k = 0; k < KF; ++k) {
-        const bool ok = k < nseg;
-        const uint32_t row = ok ? part_row(w_a + k) : 0u;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const uint32_t gi = threadIdx.x + (uint32_t)NT * j;
-          ov[j][k] = ld_coherent4(prs, (ok && okj[j]) ? row * (uint32_t)D * 4u + 16u * gi : kNone);
-          lv[j][k] = ok ? __hip_atomic_load(a.part_lse + row + hhj[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                        : kNegInf;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (!okj[j]) continue;
-        const int gi = threadIdx.x + NT * j;
-        const int hh = hhj[j], d = 4 * gi - hh * D;
-        const float sk = a.sinks ? a.sinks[gq * G + hh] * kLog2e : kNegInf;
-        float M = sk;
-#pragma unroll
-        for (int k = 0; k < KF; ++k) M = fmaxf(M, lv[j][k]);
-        float den = (sk != kNegInf) ? __builtin_amdgcn_exp2f(sk - M) : 0.0f;
-        f32x4 num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < KF; ++k) {
-          const float wv = (lv[j][k] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(lv[j][k] - M);
-          den += wv;
-          num += ov[j][k] * wv;
-        }
-        const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
-        const f32x4 o = num * inv;
-        u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
-        *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
-      }
-    } else {
-      for (int pass0 = 0; pass0 < ngrp; pass0 += NT * NJ) {
-        f32x4 num[NJ];
-  #pragma unroll
-        for (int j = 0; j < NJ; ++j) num[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (threadIdx.x < G) {
-          const float sk = a.sinks ? a.sinks[gq * G + threadIdx.x] * kLog2e : kNegInf;
-          s_M[threadIdx.x] = sk;
-          s_den[threadIdx.x] = (sk != kNegInf) ? 1.0f : 0.0f;
-        }
-        for (int c0 = 0; c0 < nseg; c0 += CHS) {
-          const int nc = nseg - c0 < CHS ? nseg - c0 : CHS;
-          for (int i = threadIdx.x; i < G * CHS; i += NT) {
-            const int hh = i / CHS, k = i - hh * CHS;
-            s_wt[i] = k < nc ? __hip_atomic_load(a.part_lse + part_row(w_a + c0 + k) + hh, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)
-                             : kNegInf;
-          }
-          __syncthreads();
-          if (threadIdx.x < G) {
-            const int hh = threadIdx.x;
-            const float Mo = s_M[hh];
-            float Mn = Mo;
-            for (int k = 0; k < nc; ++k) Mn = fmaxf(Mn, s_wt[hh * CHS + k]);
-            const float sc = (Mo == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(Mo - Mn);
-            float den = s_den[hh] * sc;
-            for (int k = 0; k < nc; ++k) {
-              const float l = s_wt[hh * CHS + k];
-              const float wv = (l == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(l - Mn);
-              s_wt[hh * CHS + k] = wv;
-              den += wv;
-            }
-            s_M[hh] = Mn;
-            s_den[hh] = den;
-            s_sc[hh] = sc;
-          }
-          __syncthreads();
-          {
-            // Loads of KB partials x NJ groups are issued together; absent
-            // ones use an offset past the buffer's range, which reads zero.
-            constexpr uint32_t kNone = 0xFFFFFFF0u;
-            int hhj[NJ];
-            uint32_t offj[NJ];
-  #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-              const int gi = pass0 + threadIdx.x + NT * j;
-              hhj[j] = gi < ngrp ? (4 * gi) / D : 0;
-              offj[j] = gi < ngrp ? (uint32_t)(16 * gi) : kNone;
-              num[j] *= s_sc[hhj[j]];
-            }
-            for (int k0 = 0; k0 < nc; k0 += KB) {
-              f32x4 ov[NJ][KB];
-  #pragma unroll
-              for (int kk = 0; kk < KB; ++kk) {
-                const bool ok = k0 + kk < nc;
-                const uint32_t rb = ok ? part_row(w_a + c0 + k0 + kk) * (uint32_t)D * 4u : 0u;
-  #pragma unroll
-                for (int j = 0; j < NJ; ++j) ov[j][kk] = ld_coherent4(prs, (ok && offj[j] != kNone) ? rb + offj[j] : kNone);
-              }
-  #pragma unroll
-              for (int kk = 0; kk < KB; ++kk) {
-                const int kx = k0 + kk < CHS ? k0 + kk : CHS - 1;
-  #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                  const float wv = (k0 + kk < nc) ? s_wt[hhj[j] * CHS + kx] : 0.0f;
-                  num[j] += ov[j][kk] * wv;
-                }
-              }
-            }
-          }
-          __syncthreads();   // s_wt, s_M, s_den are rewritten next
-        }
-  #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int gi = pass0 + threadIdx.x + NT * j;
-          if (gi < ngrp) {
-            const int hh = (4 * gi) / D, d = 4 * gi - hh * D;
-            const float den = s_den[hh];
-            const float inv = (s_M[hh] == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
-            const f32x4 o = num[j] * inv;
-            u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-            if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
-            *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
-          }
-        }
-        __syncthreads();   // every thread has read s_M / s_den before the next pass resets them
-      }
-    }
-    // Clear the consumed flags (a replayed graph reuses the epoch).
-    for (int i = threadIdx.x; i < nseg - 1; i += NT)
-      __hip_atomic_store(a.flags + 2 * (w_a + i) + slot_of(w_a + i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-template <int D, int NS, bool PF, int OCC, bool KNT, int NW>
-hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  dim3 grid(W), block(64 * NW);
-  switch (sk) {
-    case 0: hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW>), grid, block, lds, st, e0, e1, 0, a); break;
-    case 1: hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW>), grid, block, lds, st, e0, e1, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW>), grid, block, lds, st, e0, e1, 0, a); break;
-  }
-  return hipGetLastError();
-}
-
-template <int D, int NS, bool PF, int OCC, bool KNT, int NW>
-int occupancy_d(int sk, size_t lds) {
-  int nb = 0;
-  hipError_t e;
-  switch (sk) {
-    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 0, PF, OCC, KNT, NW>, 64 * NW, lds); break;
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 1, PF, OCC, KNT, NW>, 64 * NW, lds); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 2, PF, OCC, KNT, NW>, 64 * NW, lds); break;
-  }
-  return e == hipSuccess ? nb : -1;
-}
-
-// Dispatch on head dim and kernel shape.  A shape is <head dim, NS (tile =
-// 32*NS positions), prefetch one tile ahead, register occupancy the kernel is
-// compiled for, whole-line K loads, waves per workgroup, workgroups launched
-// per CU, default unit cost in the share balance (quarter tiles)>.
-// tile_variant (tuning; 0 = default):
-//   head dim 64:  4 prefetch; 7 eight waves, one workgroup per CU; 8 as 7 with prefetch
-//   head dim 128: 1 prefetch at one wave per SIMD; 2 prefetch with 32-position
-//                 tiles; 4 prefetch, two workgroups per CU; 7 eight waves;
-//                 9 two workgroups per CU; 10 compiled for one workgroup per CU
-//   head dim 256: 4 prefetch
-template <bool KNT, typename F>
-auto by_shape(int D, int v, F&& f) {
-  switch (D) {
-    case 64:
-      switch (v) {
-        case 4: return f.template operator()<64, 2, true, 2, KNT, 4, 2, 24>();
-        case 7: return f.template operator()<64, 2, false, 1, KNT, 8, 1, 24>();
-        case 8: return f.template operator()<64, 2, true, 1, KNT, 8, 1, 24>();
-        default: return f.template operator()<64, 2, false, 2, KNT, 4, 2, 24>();
-      }
-    case 128:
-      switch (v) {
-        case 1: return f.template operator()<128, 2, true, 1, KNT, 4, 1, 36>();
-        case 2: return f.template operator()<128, 1, true, 2, KNT, 4, 2, 24>();
-        case 4: return f.template operator()<128, 2, true, 2, KNT, 4, 2, 24>();
-        case 7: return f.template operator()<128, 2, false, 1, KNT, 8, 1, 24>();
-        case 9: return f.template operator()<128, 2, false, 2, KNT, 4, 2, 24>();
-        case 10: return f.template operator()<128, 2, false, 1, KNT, 4, 1, 36>();
-        default: return f.template operator()<128, 2, false, 2, KNT, 4, 1, 36>();
-      }
-    case 256:
-      return v == 4 ? f.template operator()<256, 1, true, 1, KNT, 4, 1, 24>()
-                    : f.template operator()<256, 1, false, 1, KNT, 4, 1, 24>();
-    default: return f.template operator()<512, 1, false, 1, KNT, 4, 1, 24>();
-  }
-}
-
-}  // namespace
 
 int decode_waves(int D, int tile_variant) {
   auto q = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() { return NW; };
@@ -1054,7 +34,7 @@ int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, int tile_var
 hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                          hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   auto l = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() {
-    return launch_d<DD, NS, PF, OCC, KNT, NW>(a, scale_kind, W, lds, st, e0, e1);
+    return launch_d<DD, NS, PF, OCC, KNT, NW, false>(a, scale_kind, W, lds, st, e0, e1);
   };
   return k_whole_lines ? by_shape<true>(D, a.tile_variant, l) : by_shape<false>(D, a.tile_variant, l);
 }

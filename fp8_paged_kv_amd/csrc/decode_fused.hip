@@ -1,0 +1,17 @@
+// The decode kernels that also append each sequence's new token (page
+// "FlashAttention Course, Lecture 08 - Inference Path KV Cache and Decode",
+// section "In-kernel KV cache update"): the default kernel shape of each head
+// dim, compiled apart from the plain kernels.
+#include "decode_kernel.h"
+
+namespace fp8pa {
+
+hipError_t launch_decode_fused(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                               hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  auto l = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() {
+    return launch_d<DD, NS, PF, OCC, KNT, NW, true>(a, scale_kind, W, lds, st, e0, e1);
+  };
+  return k_whole_lines ? default_shape<true>(D, l) : default_shape<false>(D, l);
+}
+
+}  // namespace fp8pa

@@ -48,6 +48,10 @@ struct DecodeArgs {
   int64_t bt_stride;
   const int32_t* seq_lens;
   const float* sinks;      // [Hq] or null
+  const uint16_t* k_new;   // fused append: bf16 [B, Hkv, D], the token at position seq_lens[b] - 1; or null
+  const uint16_t* v_new;
+  uint8_t* kw;             // the pools, writable (fused append only)
+  uint8_t* vw;
   float* part_o;           // [W][2][G][D] partial outputs (first / last segment of a workgroup)
   float* part_lse;         // [W][2][G] base-2 log-sum-exp of each partial
   uint32_t* flags;         // [W][2] a slot's flag holds the call's epoch once its partial is complete
@@ -78,8 +82,9 @@ struct AppendArgs {
   int32_t k_kind, v_kind;  // FP8PA_SCALE_*
   const int32_t* bt;
   int64_t bt_stride;
-  const int32_t* positions;
+  const int32_t* positions; // or null: one token per sequence, at seq_lens[b] - 1
   const int32_t* counts;   // or null
+  const int32_t* seq_lens; // with positions null
   int32_t T, P, Hkv, D;
 };
 
@@ -101,6 +106,10 @@ size_t decode_lds_bytes(int D, int tile_variant, int B, int G, int P);
 int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, int tile_variant, size_t lds);
 hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                          hipStream_t st, hipEvent_t start, hipEvent_t stop);
+// The same with the new tokens appended in-kernel (a.k_new, a.v_new), default
+// kernel shape only (tile_variant 0).
+hipError_t launch_decode_fused(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                               hipStream_t st, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int B, int max_pages, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);

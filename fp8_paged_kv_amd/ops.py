@@ -35,7 +35,7 @@ class Plan(ctypes.Structure):
 
 class Counters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("decode_calls", "decode_mfma_bf16", "decode_split", "merge_launches",
-                                              "append_launches", "debug_launches", "errors")]
+                                              "append_launches", "debug_launches", "errors", "fused_appends")]
 
 
 _lib = None
@@ -47,6 +47,8 @@ SIGNATURES = {
     "fp8pa_decode_plan": ([_I, _I, ctypes.POINTER(PoolDesc), _I, _I, _I, _I, ctypes.POINTER(Plan)], _I),
     "fp8pa_decode": ([_P, _P, _P, _P, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _P, _I64, _P, _I, _I, _I,
                       _P, _F, _I, _I, _I, _P, _SZ, _P], _I),
+    "fp8pa_append_decode": ([_P, _P, _P, _P, _P, _P, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _P, _I64,
+                             _P, _I, _I, _I, _P, _F, _I, _I, _I, _P, _SZ, _P], _I),
     "fp8pa_merge_splits": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "fp8pa_append_quant": ([_P, _P, _P, _P, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _P, _I64, _P, _P,
                             _I, _I, _P], _I),
@@ -142,6 +144,37 @@ def decode(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window
                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, Hq, window, _ptr(sinks),
                               scale, max_seq_len, workgroups, VARIANTS.get(variant, variant), _ptr(workspace),
                               ws_bytes, _stream(stream)))
+    return out
+
+
+def append_decode(q, k_new, v_new, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window=0, sinks=None,
+                  sm_scale=None, workgroups=0, variant="auto", out=None, workspace=None, stream=None):
+    """Append each sequence's new token (bf16 [B, Hkv, D] k_new / v_new, at
+    position seq_lens[b] - 1) into the pools and decode, in one launch."""
+    _need(q, "q", torch.bfloat16)
+    _need(k_new, "k_new", torch.bfloat16)
+    _need(v_new, "v_new", torch.bfloat16)
+    _need(k_pool, "k_pool", torch.uint8)
+    _need(v_pool, "v_pool", torch.uint8)
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32)
+    B, Hq, D = q.shape
+    if tuple(k_new.shape) != (B, kd.num_kv_heads, D) or tuple(v_new.shape) != (B, kd.num_kv_heads, D):
+        raise ValueError("k_new / v_new must be [B, Hkv, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16)
+    scale = D ** -0.5 if sm_scale is None else float(sm_scale)
+    plan = decode_plan(B, Hq, kd, max_seq_len, window, workgroups, variant)
+    if plan.workspace_bytes > 0 and workspace is None:
+        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8pa_append_decode(_ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), _ptr(k_pool), _ptr(v_pool),
+                                     ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table), block_table.shape[1],
+                                     _ptr(seq_lens), B, Hq, window, _ptr(sinks), scale, max_seq_len, workgroups,
+                                     VARIANTS.get(variant, variant), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

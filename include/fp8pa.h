@@ -171,6 +171,35 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Append + decode (page "FlashAttention Course, Lecture 08 - Inference Path
+ * KV Cache and Decode", section "In-kernel KV cache update": the attention
+ * kernel itself writes the new token's K and V, saving the separate append
+ * launch).  When the attended span (window if set and smaller, else
+ * max_seq_len) is at most 2048 positions, which makes the call launch-bound,
+ * the decode kernel performs the appends (one launch); otherwise the append
+ * kernel runs first and then the decode (two launches on `stream`), since an
+ * in-kernel append delays the workgroups that read the new tokens by more
+ * than a launch costs.  Same contract as fp8pa_decode, plus:
+ *   k_new, v_new  device bf16 [B, Hkv, D], 2-byte aligned: sequence b's new
+ *               token, written at position seq_lens[b] - 1 (seq_lens counts it)
+ *               and attended in the same call.  Sequences with seq_lens[b] = 0
+ *               get no append.
+ *   k_pool, v_pool  are written: exactly as fp8pa_append_quant(k_new, v_new,
+ *               ..., positions = seq_lens - 1, counts = NULL, T = 1) would, and
+ *               the output equals that append followed by fp8pa_decode.
+ * In the one-launch form, the workgroup holding a unit's last tile performs
+ * the unit's append before it reads that tile; no other workgroup reads the
+ * new token's page.  Every check runs before anything is launched.
+ */
+int fp8pa_append_decode(const void* k_new, const void* v_new, const void* q, void* out,
+                        uint8_t* k_pool, uint8_t* v_pool,
+                        const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
+                        const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                        int B, int Hq, int window, const float* sinks, float sm_scale,
+                        int max_seq_len, int workgroups, int variant,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Log-sum-exp merge of split partials (page section "Why it happens": the
  * grid splits each sequence; the partial results are combined afterwards).
  *   part_o    device fp32 [B, Hq, S, D]: each split's normalised output.
@@ -230,6 +259,7 @@ typedef struct fp8pa_counters {
   int64_t append_launches;
   int64_t debug_launches;
   int64_t errors;           /* calls refused or failed */
+  int64_t fused_appends;    /* decode launches that also appended (fp8pa_append_decode) */
 } fp8pa_counters;
 
 int fp8pa_get_counters(fp8pa_counters* out);

@@ -33,7 +33,7 @@ def test_version_and_struct_sizes():
     assert b"gfx950" in ops.lib().fp8pa_version()
     assert ctypes.sizeof(ops.PoolDesc) == 48
     assert ctypes.sizeof(ops.Plan) == 24
-    assert ctypes.sizeof(ops.Counters) == 56
+    assert ctypes.sizeof(ops.Counters) == 64
 
 
 def kd(**kw):
@@ -125,6 +125,33 @@ def test_aligned_rows_are_checked(case):
     ops.reset_counters()
     assert call_decode(**case) == ops.EINVAL, ops.last_error()
     assert ops.counters()["decode_calls"] == 0
+
+
+def call_append_decode(k_new=F, v_new=F, **kw):
+    a = dict(q=F, out=F, k_pool=F, v_pool=F, bt=F, bt_stride=512, seq_lens=F, B=2, Hq=32, window=0, sinks=None,
+             sm_scale=0.1, max_seq_len=8192, workgroups=1, variant=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return ops.lib().fp8pa_append_decode(P(k_new) if k_new else None, P(v_new) if v_new else None, P(a["q"]),
+                                         P(a["out"]), P(a["k_pool"]), P(a["v_pool"]), ctypes.byref(kd()),
+                                         ctypes.byref(vd()), P(a["bt"]), a["bt_stride"], P(a["seq_lens"]), a["B"],
+                                         a["Hq"], a["window"], None, a["sm_scale"], a["max_seq_len"],
+                                         a["workgroups"], a["variant"], None, 0, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(k_new=0), ops.EINVAL),
+    (dict(v_new=0), ops.EINVAL),
+    (dict(k_new=F + 1), ops.EINVAL),          # bf16 tokens must be 2-byte aligned
+    (dict(k_new=F + 1, max_seq_len=1024), ops.EINVAL),   # the same on the one-launch path
+    (dict(v_new=0, max_seq_len=1024), ops.EINVAL),
+    (dict(Hq=30), ops.EINVAL),                # every decode check applies
+])
+def test_append_decode_refuses_before_launch(case, code):
+    ops.reset_counters()
+    assert call_append_decode(**case) == code, ops.last_error()
+    c = ops.counters()
+    assert c["decode_calls"] == 0 and c["fused_appends"] == 0 and c["errors"] == 1
 
 
 def test_empty_batch_is_a_no_op():
