@@ -431,9 +431,12 @@ def main():
     rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, layers, args.cpu_budget)
     # Last, as it rewrites each sequence's last token in the pools.
     fu = time_fused(copies, dom, args.steps, hip, ops, workloads, torch)
+    ld = layers[dom]
+    span = min(ld.window, ld.max_seq_len) if ld.window > 0 else ld.max_seq_len
     rec["fused_append_decode"] = {
-        "layer": layers[dom].name, "us_append_then_decode": round(fu["append_then_decode"], 2),
-        "us_fused": round(fu["fused"], 2),
+        "layer": ld.name, "us_append_quant_then_decode": round(fu["append_then_decode"], 2),
+        "us_append_decode": round(fu["fused"], 2),
+        "append_decode_path": "one launch" if span <= 2048 else "append kernel, then decode",
         "timing": f"hipEvents around {args.steps} steps (new token per sequence appended, then decoded); mean per step"}
     print(json.dumps(rec), flush=True)
 

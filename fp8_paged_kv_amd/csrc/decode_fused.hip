@@ -1,7 +1,7 @@
 // The decode kernels that also append each sequence's new token (page
-// "FlashAttention Course, Lecture 08 - Inference Path KV Cache and Decode",
-// section "In-kernel KV cache update"): the default kernel shape of each head
-// dim, compiled apart from the plain kernels.
+// "Lecture 8 — Inference Path: KV Cache, Decode, RoPE, GQA, Paged KV" of the
+// FlashAttention course, section "In-kernel KV cache update"): the default
+// kernel shape of each head dim, compiled apart from the plain kernels.
 #include "decode_kernel.h"
 
 namespace fp8pa {

@@ -171,10 +171,10 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Append + decode (page "FlashAttention Course, Lecture 08 - Inference Path
- * KV Cache and Decode", section "In-kernel KV cache update": the attention
- * kernel itself writes the new token's K and V, saving the separate append
- * launch).  When the attended span (window if set and smaller, else
+ * Append + decode (page "Lecture 8 — Inference Path: KV Cache, Decode, RoPE,
+ * GQA, Paged KV" of the FlashAttention course, section "In-kernel KV cache
+ * update": the attention kernel itself writes the new token's K and V,
+ * saving the separate append launch).  When the attended span (window if set and smaller, else
  * max_seq_len) is at most 2048 positions, which makes the call launch-bound,
  * the decode kernel performs the appends (one launch); otherwise the append
  * kernel runs first and then the decode (two launches on `stream`), since an
