@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB copy (PMC scale reference)")
+    ap.add_argument("--formats", action="store_true",
+                    help="time the workload's decode in each pool format (K layout x scale kind; JSON per format)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time one step of all layers as eager launches and as a replayed HIP graph")
     return ap.parse_args()
 
 
@@ -306,6 +310,120 @@ def run_sweep(args, torch, ops, workloads, hip):
             torch.cuda.empty_cache()
 
 
+FORMATS = (("heads_d64", "heads_dmajor", None), ("heads", "heads_dmajor", None), ("tokens", "heads_dmajor", None),
+           ("heads_d64", "heads_dmajor", "token_head"), ("heads", "heads_dmajor", "token_head"),
+           ("tokens", "heads_dmajor", "token_head"))
+
+
+def copies_of(layers, wl, R, torch):
+    copies = [layers]
+    for _ in range(R - 1):
+        if wl.shared_pool:
+            import dataclasses
+            k2, v2 = layers[0].k_pool.clone(), layers[0].v_pool.clone()
+            copies.append([dataclasses.replace(l, k_pool=k2, v_pool=v2) for l in layers])
+        else:
+            copies.append([clone_layer(l, torch) for l in layers])
+    torch.cuda.synchronize()
+    return copies
+
+
+def rotation(layers, wl, np):
+    per_copy = sum(2 * l.k_pool.numel() for l in layers) if not wl.shared_pool else 2 * layers[0].k_pool.numel()
+    return max(2, min(16, int(np.ceil(2 * 2 ** 30 / per_copy))))
+
+
+def run_formats(args, wl, torch, np, ops, workloads, hip):
+    """The workload in each pool format: same seeded values, written by the
+    library's append in that format.  Formats that share a scale kind hold the
+    same codes and scales, so their outputs must agree bit for bit."""
+    first = {}
+    for kl, vl, sk in FORMATS:
+        sk = wl.scale_kind if sk is None else sk
+        layers = workloads.build_workload(wl, k_layout=kl, v_layout=vl, scale_kind=sk)
+        R = args.copies or rotation(layers, wl, np)
+        copies = copies_of(layers, wl, R, torch)
+        outs = [workloads.decode_layer(l).clone() for l in layers]
+        if sk in first:
+            for j, o in enumerate(outs):
+                assert torch.equal(o.view(torch.int16), first[sk][j].view(torch.int16)), \
+                    f"{kl}/{sk}: output differs from {sk} in another layout"
+        else:
+            first[sk] = outs
+        _, step_ms, kern_ms, _ = time_layers(copies, args.steps, args.warmup, hip, ops, workloads, torch,
+                                             args.workgroups)
+        rows = []
+        for l, km in zip(layers, kern_ms):
+            b = workloads.kv_bytes(l)
+            rows.append({"name": l.name, "kernel_us_mean": round(km * 1e3, 2), "kv_bytes": b,
+                         "kernel_gbps": round(b / (km * 1e-3) / 1e9, 1),
+                         "pct_peak": round(100 * b / (km * 1e-3) / 1e9 / PEAK_GBPS, 1)})
+        print(json.dumps({"format": {"k_layout": kl, "v_layout": vl, "scale_kind": sk,
+                                     "row_bytes": layers[0].row_bytes}, "workload": wl.name, "layers": rows,
+                          "timing": f"hipEvents around {args.steps} back-to-back launches per layer, "
+                                    f"{R} pool copies rotated"}), flush=True)
+        del copies, layers
+        torch.cuda.empty_cache()
+
+
+def run_graph(args, wl, torch, np, ops, workloads, hip):
+    """One decode step over all layers of the workload: eager launches against
+    a replayed HIP graph (one graph per pool copy, grids fixed at capture)."""
+    layers = workloads.build_workload(wl)
+    R = args.copies or rotation(layers, wl, np)
+    copies = copies_of(layers, wl, R, torch)
+    outs = [torch.empty_like(l.q) for l in layers]
+    ws = []
+    for l in layers:
+        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window)
+        ws.append(torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0"))
+
+    def step(c):
+        for j, l in enumerate(c):
+            workloads.decode_layer(l, out=outs[j], workspace=ws[j])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(copies[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    graphs = []
+    for c in copies:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(c)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for o in outs:
+        o.zero_()
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    for o, e in zip(outs, eager):
+        assert torch.equal(o.view(torch.int16), e.view(torch.int16)), "graph replay differs from eager"
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for name, fn in (("eager", lambda k: step(copies[k % R])), ("graph", lambda k: graphs[k % R].replay())):
+        for k in range(args.warmup):
+            fn(k)
+        ev = hip.events(2)
+        torch.cuda.synchronize()
+        hip.record(ev[0], stream)
+        for k in range(args.steps):
+            fn(k)
+        hip.record(ev[1], stream)
+        torch.cuda.synchronize()
+        res[name] = hip.elapsed_ms(ev[0], ev[1]) / args.steps * 1e3
+        hip.destroy(ev)
+    print(json.dumps({"graph_step": {"workload": wl.name, "layers": [l.name for l in layers],
+                                     "us_per_step_eager": round(res["eager"], 2),
+                                     "us_per_step_graph": round(res["graph"], 2),
+                                     "timing": f"hipEvents around {args.steps} steps, {R} pool copies rotated"}}),
+          flush=True)
+    del graphs
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -324,20 +442,17 @@ def main():
         run_sweep(args, torch, ops, workloads, hip)
         return
     wl = {w.name: w for w in configs.ALL}[args.workload]
+    if args.formats:
+        run_formats(args, wl, torch, np, ops, workloads, hip)
+        return
+    if args.graph:
+        run_graph(args, wl, torch, np, ops, workloads, hip)
+        return
     t_build = time.perf_counter()
     layers = workloads.build_workload(wl)
     build_s = time.perf_counter() - t_build
-    per_copy = sum(2 * l.k_pool.numel() for l in layers) if not wl.shared_pool else 2 * layers[0].k_pool.numel()
-    R = args.copies or max(2, min(16, int(np.ceil(2 * 2 ** 30 / per_copy))))
-    copies = [layers]
-    for _ in range(R - 1):
-        if wl.shared_pool:
-            import dataclasses
-            k2, v2 = layers[0].k_pool.clone(), layers[0].v_pool.clone()
-            copies.append([dataclasses.replace(l, k_pool=k2, v_pool=v2) for l in layers])
-        else:
-            copies.append([clone_layer(l, torch) for l in layers])
-    torch.cuda.synchronize()
+    R = args.copies or rotation(layers, wl, np)
+    copies = copies_of(layers, wl, R, torch)
     # Copies hold identical bytes: every copy must give the same output bit for bit.
     ref = [workloads.decode_layer(l).clone() for l in copies[0]]
     for c in copies[1:]:

@@ -1,8 +1,8 @@
 """Device-resident synthetic decode workloads (the shapes in ``configs``),
 built with the library's own append kernel from seeded bf16 inputs.
 
-Per layer: K pool in the "heads_d64" layout, V pool in "heads_dmajor", both with
-the workload's scale kind and row stride; pages that hold no attended position
+Per layer: by default K pool in the "heads_d64" layout, V pool in "heads_dmajor",
+both with the workload's scale kind and row stride; pages that hold no attended position
 (before a window) get no row (their table entries are -1); unused slots and
 spare rows hold 0xFF (NaN codes and scales).  Raw K/V of sequence b in layer l
 are N(0,1) bf16 drawn for positions [first attended page * P, L) only, with
@@ -76,10 +76,15 @@ def first_attended_page(L, window, P):
     return start // P
 
 
-def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", layers=None, verbose=False):
+def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", layers=None, verbose=False,
+                   k_layout="heads_d64", v_layout="heads_dmajor", scale_kind=None):
     """Build the device pools of the workload's layers (all, or the indices in
     ``layers``).  Layers of a shared-pool workload index disjoint rows of one
-    K pool and one V pool."""
+    K pool and one V pool.  ``k_layout``, ``v_layout`` and ``scale_kind``
+    replace the defaults (the workload's own scale kind); a scale block that
+    does not fit the layer's row width widens the rows to the natural row,
+    rounded up to 16 bytes."""
+    scale_kind = wl.scale_kind if scale_kind is None else scale_kind
     lens = inputs.seq_lens(seed, wl.index, wl.B, wl.L_lo, wl.L_hi)
     P = wl.P
     idx = list(range(len(wl.layers))) if layers is None else list(layers)
@@ -101,19 +106,25 @@ def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", lay
         for li in range(len(wl.layers)):
             t, _, pool_rows = inputs.block_table_ranges(seed, wl.index, ranges[li], P, tag=li, width=width)
             tables[li] = (t, pool_rows)
+    row_width = {}
+    for li, lay in enumerate(wl.layers):
+        natural = P * lay.Hkv * lay.D + scale_block_bytes(scale_kind, lay.Hkv, P, lay.D)
+        row_width[li] = max(lay.row_bytes, -(-natural // 16) * 16)
+    if wl.shared_pool:   # one row width for the layers of a shared pool
+        row_width = {li: max(row_width.values()) for li in row_width}
     sinks_np = inputs.sinks(seed, wl.index, wl.layers[0].Hq) if wl.sinks else None
     shared = {}
     out = []
     for li in idx:
         lay = wl.layers[li]
         table, pool_rows = tables[li]
-        rb = lay.row_bytes
+        rb = row_width[li]
         # Rows are placed with their payloads on the 64-byte grid when the row
         # width leaves room for it (the row widths carry a 32-byte scale
         # footer, so half the rows would start 32 bytes off the grid).
-        al = rows_can_align(rb, P * lay.Hkv * lay.D, scale_block_bytes(wl.scale_kind, lay.Hkv, P, lay.D))
-        kd = ops.pool_desc(lay.Hkv, lay.D, P, "heads_d64", wl.scale_kind, rb, pool_rows, align64=al)
-        vd = ops.pool_desc(lay.Hkv, lay.D, P, "heads_dmajor", wl.scale_kind, rb, pool_rows, align64=al)
+        al = rows_can_align(rb, P * lay.Hkv * lay.D, scale_block_bytes(scale_kind, lay.Hkv, P, lay.D))
+        kd = ops.pool_desc(lay.Hkv, lay.D, P, k_layout, scale_kind, rb, pool_rows, align64=al)
+        vd = ops.pool_desc(lay.Hkv, lay.D, P, v_layout, scale_kind, rb, pool_rows, align64=al)
         if wl.shared_pool and "k" in shared:
             k_pool, v_pool = shared["k"], shared["v"]
         else:
@@ -137,7 +148,7 @@ def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", lay
             torch.bfloat16).to(device)
         out.append(DeviceLayer(
             name=f"{wl.name}/{lay.name}", Hq=lay.Hq, Hkv=lay.Hkv, D=lay.D, P=P, window=lay.window,
-            sm_scale=lay.D ** -0.5 if lay.sm_scale is None else lay.sm_scale, scale_kind=wl.scale_kind,
+            sm_scale=lay.D ** -0.5 if lay.sm_scale is None else lay.sm_scale, scale_kind=scale_kind,
             row_bytes=rb, pool_rows=pool_rows, kd=kd, vd=vd, k_pool=k_pool, v_pool=v_pool, block_table=bt,
             table_np=table, seq_lens=torch.from_numpy(lens.astype(np.int32)).to(device), lens=lens,
             first_pos=first, q=q, sinks=None if sinks_np is None else torch.from_numpy(sinks_np).to(device),
