@@ -310,9 +310,12 @@ def run_sweep(args, torch, ops, workloads, hip):
             torch.cuda.empty_cache()
 
 
+# (K layout, V layout, scale kind; None: the workload's own).  The last four
+# are the page's own payload orders for both pools.
 FORMATS = (("heads_d64", "heads_dmajor", None), ("heads", "heads_dmajor", None), ("tokens", "heads_dmajor", None),
            ("heads_d64", "heads_dmajor", "token_head"), ("heads", "heads_dmajor", "token_head"),
-           ("tokens", "heads_dmajor", "token_head"))
+           ("tokens", "heads_dmajor", "token_head"), ("heads", "heads", None), ("tokens", "tokens", None),
+           ("heads", "heads", "token_head"), ("tokens", "tokens", "token_head"))
 
 
 def copies_of(layers, wl, R, torch):

@@ -22,7 +22,7 @@ thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 struct Counters {
   std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0}, fused_append{0},
-      errors{0};
+      decode_vtok{0}, errors{0};
 };
 Counters g_cnt;
 std::atomic<uint32_t> g_epoch{0};
@@ -259,8 +259,22 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   if (int rc = check_desc(vd, "vd")) return rc;
   if (kd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
     return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS_D64, HEADS or TOKENS layout");
-  if (vd->layout != FP8PA_LAYOUT_HEADS_DMAJOR)
-    return fail(FP8PA_EUNSUPPORTED, "vd: decode reads V in the HEADS_DMAJOR layout");
+  if (vd->layout == FP8PA_LAYOUT_HEADS_D64)
+    return fail(FP8PA_EUNSUPPORTED, "vd: decode reads V in the HEADS_DMAJOR, HEADS or TOKENS layout");
+  // V in a token-major layout is staged through LDS (default kernel shapes).
+  const bool vt = vd->layout == FP8PA_LAYOUT_HEADS || vd->layout == FP8PA_LAYOUT_TOKENS;
+  if (vt && fused) return fail(FP8PA_EUNSUPPORTED, "the one-launch append reads V in the HEADS_DMAJOR layout");
+  const int tv_launch = (fused || vt) ? 0 : tile_variant();
+  if (tv_launch != tile_variant())
+    lds = fp8pa::decode_lds_bytes(kd->head_dim, tv_launch, B, Hq / kd->num_kv_heads, kd->page_size);
+  size_t vstage_off = 0;
+  if (vt) {
+    vstage_off = (lds + 15) / 16 * 16;
+    lds = vstage_off + fp8pa::decode_vstage_bytes(kd->head_dim);
+    if (lds > 65536)
+      return fail(FP8PA_EUNSUPPORTED, "B=%d, head_dim %d with V staged through LDS need %zu bytes of LDS (> 64 KiB)",
+                  B, kd->head_dim, lds);
+  }
   if (vd->num_kv_heads != kd->num_kv_heads || vd->head_dim != kd->head_dim || vd->page_size != kd->page_size ||
       vd->scale_kind != kd->scale_kind)
     return fail(FP8PA_EUNSUPPORTED, "K and V pools must share num_kv_heads, head_dim, page_size and scale_kind");
@@ -319,7 +333,8 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   a.G = G;
   a.window = window > 0 ? window : 0;
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
-  a.tile_variant = fused ? 0 : tile_variant();   // the fused kernels exist in the default shapes
+  a.tile_variant = tv_launch;   // the fused and V-token-major kernels exist in the default shapes
+  a.vstage_off = (int32_t)vstage_off;
   a.min_tiles = min_tiles(fp8pa::decode_waves(D, a.tile_variant));
   a.seg_cost = seg_cost(fp8pa::decode_seg_cost(D, a.tile_variant));
   a.epoch = g_epoch.fetch_add(1) + 1;
@@ -336,11 +351,13 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   // when the 64-byte pieces of consecutive tokens are adjacent.
   const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
   hipError_t e = fused ? fp8pa::launch_decode_fused(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                 : vt  ? fp8pa::launch_decode_vtok(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
                        : fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
   g_cnt.decode_mfma.fetch_add(1);
   if (W > 1) g_cnt.decode_split.fetch_add(1);
   if (fused) g_cnt.fused_append.fetch_add(1);
+  if (vt) g_cnt.decode_vtok.fetch_add(1);
   g_cnt.decode_calls.fetch_add(1);
   ok();
   return FP8PA_OK;
@@ -367,17 +384,19 @@ int fp8pa_append_decode(const void* k_new, const void* v_new, const void* q, voi
                         int window, const float* sinks, float sm_scale, int max_seq_len, int workgroups, int variant,
                         void* workspace, size_t workspace_bytes, void* stream) {
   if (B > 0 && (!k_new || !v_new)) return fail(FP8PA_EINVAL, "k_new and v_new are required");
+  if (B > 0 && (!aligned(k_new, 2) || !aligned(v_new, 2))) return fail(FP8PA_EINVAL, "k_new/v_new misaligned");
   // In-kernel appends sit on the critical path of the workgroup that reads
   // each new token.  Short attended spans are launch-bound, and there the one
   // launch wins (about 24 -> 13.5 us on the tiny and window-128 calls);
   // longer ones run the append kernel and then the plain decode.
+  // V in a token-major layout takes the two launches as well.
   const int span = (window > 0 && window < max_seq_len) ? window : max_seq_len;
-  if (span <= kFusedMaxSpan)
+  if (span <= kFusedMaxSpan && vd && vd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
     return decode_impl(k_new, v_new, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
                        window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes, stream);
   // Every check of the call runs before the append launches.
-  if (int rc = decode_impl(k_new, v_new, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
-                           window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes,
+  if (int rc = decode_impl(nullptr, nullptr, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B,
+                           Hq, window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes,
                            stream, true))
     return rc;
   if (B == 0) return decode_impl(nullptr, nullptr, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens,
@@ -522,6 +541,7 @@ int fp8pa_get_counters(fp8pa_counters* c) {
   c->debug_launches = g_cnt.debug.load();
   c->errors = g_cnt.errors.load();
   c->fused_appends = g_cnt.fused_append.load();
+  c->decode_v_token_major = g_cnt.decode_vtok.load();
   return FP8PA_OK;
 }
 
@@ -542,6 +562,7 @@ int fp8pa_reset_counters(void) {
   g_cnt.debug = 0;
   g_cnt.errors = 0;
   g_cnt.fused_append = 0;
+  g_cnt.decode_vtok = 0;
   return FP8PA_OK;
 }
 

@@ -54,9 +54,12 @@
 // exactly the probabilities it must supply to the PV MFMA.
 //
 // PV on MFMA 16x16x32 bf16: O^T = V^T P^T with A = V^T (16 head dims x 32
-// positions) and B = P^T.  V is stored d-major per (page, head), so lane
-// (dim l%16, quad l/16) loads the 8*NS positions it needs as one 16-byte (or
-// 8-byte) load straight from HBM; no LDS transpose is needed.
+// positions) and B = P^T.  V stored d-major per (page, head) lets lane
+// (dim l%16, quad l/16) load the 8*NS positions it needs as one 16-byte (or
+// 8-byte) load straight from HBM.  V stored token-major (the page's "heads"
+// and "tokens" orders, VT) is loaded as whole 16-byte pieces of position rows,
+// written to a per-wave LDS stage and read back with gfx950's 8-bit transpose
+// read (ds_read_b64_tr_b8), which hands each lane 8 positions of one dim.
 //
 // Scales.  fp32 per (page, head) or per (token, head): the K scale multiplies
 // the score after the dot product and the V scale multiplies the probability
@@ -118,13 +121,26 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
 
 __device__ __forceinline__ uint32_t byte_of(const u32x4& v, int i) { return (v[i >> 2] >> (8 * (i & 3))) & 0xffu; }
 
+// V token-major (VT): a lane loads NIV = NS*D/32 16-byte pieces, dims
+// 16*(l % (D/16)).. +15 of NIV consecutive positions (one page).  The stage of
+// a wave holds the tile's positions as rows of VH dims (VH + 16 bytes apart,
+// which spreads the 8 rows of a transpose read over distinct banks); D > VH
+// takes D/VH passes.
+template <int D>
+struct VStage {
+  static constexpr int VH = D < 128 ? D : 128;   // dims per pass
+  static constexpr int RS = VH + 16;             // stage row stride, bytes
+};
+
 // Registers of one tile for one lane.
-template <int D, int NS, int SK>
+template <int D, int NS, int SK, bool VT>
 struct Tile {
   static constexpr int NM = D / 64, NC = D / 16, NG = D / 32, NE = (8 * NG) / 16;
+  static constexpr int NIV = NS * D / 32;
   typedef typename VRaw<NS>::type vraw_t;
   u32x4 k[NS][2][NM];   // K codes of the lane's position rows
   vraw_t v[NC];         // V codes of the lane's dims, GT positions each
+  u32x4 vt[VT ? NIV : 1];   // VT: the lane's pieces of V position rows, as loaded
   float ks, vs;         // per-(page, head) scales of the lane's score group
   float kst[NS][8];     // per-(token, head) scales of the lane's score positions
   float vst[NS][8];
@@ -134,7 +150,8 @@ struct Tile {
 
 // FUSED: also append each sequence's new token (DecodeArgs::k_new / v_new)
 // before reading it.
-template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW, bool FUSED>
+// VT: V in a token-major layout (HEADS or TOKENS), staged through LDS.
+template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT>
 __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a) {
   static_assert(!(FUSED && PF), "the fused append waits inside the non-prefetching tile loop");
   constexpr int NT = 64 * NW;   // threads (NW wave64s)
@@ -144,7 +161,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   constexpr int NQ = D / 32;    // QK MFMAs per 16 positions
   constexpr int NC = D / 16;    // PV MFMAs per subtile (16 dims each)
   constexpr int NG = D / 32;    // E8M0 groups along D
-  typedef Tile<D, NS, SK> TileT;
+  typedef Tile<D, NS, SK, VT> TileT;
 
   extern __shared__ int s_dyn[];   // tile prefix, non-empty prefix, lengths, then the page-row stage / wave-combine buffer
   __shared__ float s_m[NW][16];
@@ -432,11 +449,35 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
           t.vst[s][i] = ld_global<float>(vsc + tt * a.vg.sc_tok_stride);
         }
     } else {
+      if constexpr (VT) {
+        // One position's NG bytes at a time: in the TOKENS layout consecutive
+        // positions' scale bytes are Hkv*NG apart.
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const uint8_t* src = vsc + (tpq + 8 * s) * a.vg.sc_tok_stride;
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int k = 0; k < TileT::NE; ++k) t.ve8[s][k] = ld_global<u32x4>(src + 16 * k);
+          for (int i = 0; i < 8; ++i) {
+            const uint8_t* src = vsc + (tpq + 8 * s + i) * a.vg.sc_tok_stride;
+            if constexpr (NG == 16) {
+              t.ve8[s][i] = ld_global<u32x4>(src);
+            } else if constexpr (NG == 8) {
+              const u32x2 v2 = ld_global<u32x2>(src);
+              t.ve8[s][i >> 1][2 * (i & 1)] = v2[0];
+              t.ve8[s][i >> 1][2 * (i & 1) + 1] = v2[1];
+            } else if constexpr (NG == 4) {
+              t.ve8[s][i >> 2][i & 3] = ld_global<uint32_t>(src);
+            } else {
+              const uint32_t h16 = ld_global<uint16_t>(src);
+              if (i & 1) t.ve8[s][0][i >> 1] |= h16 << 16;
+              else t.ve8[s][0][i >> 1] = h16;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const uint8_t* src = vsc + (tpq + 8 * s) * a.vg.sc_tok_stride;
+#pragma unroll
+          for (int k = 0; k < TileT::NE; ++k) t.ve8[s][k] = ld_global<u32x4>(src + 16 * k);
+        }
       }
 #pragma unroll
       for (int s = 0; s < NS; ++s)
@@ -460,14 +501,62 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
           t.k[s][aa][m] = KNT ? ld_stream<u32x4>(src) : ld_global<u32x4>(src);
         }
       }
-    // The lane's GT positions lie in one token block of the d-major V layout.
-    const uint8_t* vrow = vpool + rqv.code + (int64_t)(tpq / a.vg.tblk) * a.vg.tblk_stride +
-                          (tpq % a.vg.tblk);
+    if constexpr (VT) {
+      // Whole 16-byte pieces of NIV consecutive position rows (NIV <= 16
+      // divides P, so they share a page).
+      constexpr int LPP = D / 16, NIV = TileT::NIV;
+      const int tv0 = T0 + (lane / LPP) * NIV;
+      const RowBases rv = row_bases(a.vg, row_of(tv0 >> log2P));
+      const uint8_t* src = vpool + rv.code + (int64_t)(tv0 & (P - 1)) * a.vg.tok_stride + 16 * (lane % LPP);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int d = 16 * c + n;
-      t.v[c] = ld_stream<typename TileT::vraw_t>(vrow + (int64_t)(d >> 6) * a.vg.dchunk_stride +
-                                                 (int64_t)(d & 63) * a.vg.d_stride);
+      for (int j = 0; j < NIV; ++j) t.vt[j] = ld_stream<u32x4>(src + (int64_t)j * a.vg.tok_stride);
+    } else {
+      // The lane's GT positions lie in one token block of the d-major V layout.
+      const uint8_t* vrow = vpool + rqv.code + (int64_t)(tpq / a.vg.tblk) * a.vg.tblk_stride +
+                            (tpq % a.vg.tblk);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int d = 16 * c + n;
+        t.v[c] = ld_stream<typename TileT::vraw_t>(vrow + (int64_t)(d >> 6) * a.vg.dchunk_stride +
+                                                   (int64_t)(d & 63) * a.vg.d_stride);
+      }
+    }
+  };
+
+  // VT: turn the loaded position-row pieces into the PV operand layout (lane
+  // (dim n, quad) gets the GT positions of its group for every 16-dim chunk).
+  // A transpose read takes, in each 16-lane group, eight 8-byte row pieces
+  // (lane i reads half i&1 of the 16 dims of row i>>1) and gives lane m the
+  // byte m&7 of the pieces of lanes m>>3, 2+(m>>3), ..., 14+(m>>3): dim m of
+  // the eight rows.  The stage is private to the wave, whose LDS operations
+  // complete in order.
+  // (vstage_off leaves 16 bytes of slack to round the stage up to 16 bytes.)
+  uint8_t* const vstage = reinterpret_cast<uint8_t*>(s_dyn) + a.vstage_off +
+                          ((0u - (uint32_t)reinterpret_cast<uintptr_t>(s_dyn)) & 15u) + wave * (TT * VStage<D>::RS);
+  auto stage_v = [&](TileT& t) {
+    constexpr int VH = VStage<D>::VH, RS = VStage<D>::RS, NIV = TileT::NIV, LPP = D / 16, CPP = VH / 16;
+    const int prow = (lane / LPP) * NIV, pc = lane % LPP;
+#pragma unroll
+    for (int h = 0; h < D / VH; ++h) {
+      if (pc / CPP == h) {
+#pragma unroll
+        for (int j = 0; j < NIV; ++j)
+          *reinterpret_cast<u32x4*>(vstage + (prow + j) * RS + 16 * (pc % CPP)) = t.vt[j];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int cc = 0; cc < CPP; ++cc)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const uint8_t* src = vstage + (GT * quad + 8 * s + (n >> 1)) * RS + 16 * cc + 8 * (n & 1);
+          const v2i32 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) v2i32*)(src));
+          t.v[h * CPP + cc][2 * s] = (uint32_t)r[0];
+          t.v[h * CPP + cc][2 * s + 1] = (uint32_t)r[1];
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   };
 
@@ -544,6 +633,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[c] *= alpha;
     }
+    if constexpr (VT) stage_v(t);
     if (!interior) {
       const int base = T0 + GT * quad;
       const int lo = start - base, hi = L - base;   // keep bytes in [lo, hi)
@@ -996,18 +1086,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   }
 }
 
-template <int D, int NS, bool PF, int OCC, bool KNT, int NW, bool FUSED>
+template <int D, int NS, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT = false>
 hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(W), block(64 * NW);
   switch (sk) {
     case 0:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW, FUSED>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW, FUSED, VT>), grid, block, lds, st, e0, e1, 0, a);
       break;
     case 1:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED, VT>), grid, block, lds, st, e0, e1, 0, a);
       break;
     default:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED, VT>), grid, block, lds, st, e0, e1, 0, a);
       break;
   }
   return hipGetLastError();
@@ -1018,9 +1108,9 @@ int occupancy_d(int sk, size_t lds) {
   int nb = 0;
   hipError_t e;
   switch (sk) {
-    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 0, PF, OCC, KNT, NW, false>, 64 * NW, lds); break;
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 1, PF, OCC, KNT, NW, false>, 64 * NW, lds); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 2, PF, OCC, KNT, NW, false>, 64 * NW, lds); break;
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 0, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 1, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 2, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
   }
   return e == hipSuccess ? nb : -1;
 }

@@ -62,6 +62,7 @@ struct DecodeArgs {
   PoolGeom kg, vg;
   int32_t P, log2P, B, Hq, Hkv, G, window;
   float qk_scale;          // sm_scale * log2(e)
+  int32_t vstage_off;      // V token-major: byte offset of the per-wave V stages in dynamic LDS
 };
 
 struct MergeArgs {
@@ -110,6 +111,11 @@ hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whol
 // kernel shape only (tile_variant 0).
 hipError_t launch_decode_fused(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                                hipStream_t st, hipEvent_t start, hipEvent_t stop);
+// V in a token-major layout (HEADS or TOKENS), staged through LDS: the
+// decode with default kernel shapes, and the dynamic LDS its V stages add.
+hipError_t launch_decode_vtok(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                              hipStream_t st, hipEvent_t start, hipEvent_t stop);
+size_t decode_vstage_bytes(int D);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int B, int max_pages, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);

@@ -35,7 +35,8 @@ class Plan(ctypes.Structure):
 
 class Counters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("decode_calls", "decode_mfma_bf16", "decode_split", "merge_launches",
-                                              "append_launches", "debug_launches", "errors", "fused_appends")]
+                                              "append_launches", "debug_launches", "errors", "fused_appends",
+                                              "decode_v_token_major")]
 
 
 _lib = None

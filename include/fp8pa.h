@@ -51,7 +51,8 @@ enum {
  * 64-byte pieces of consecutive tokens side by side), HEADS_DMAJOR for values
  * (token-contiguous per dim, which the value operand of the MFMA that
  * contracts over tokens needs).  The decode kernel reads K in HEADS, TOKENS or
- * HEADS_D64 (fastest) and V in HEADS_DMAJOR. */
+ * HEADS_D64 (fastest) and V in HEADS_DMAJOR (fastest), HEADS or TOKENS (the
+ * last two through a transposing stage in LDS). */
 enum {
   FP8PA_LAYOUT_HEADS = 0,         /* [Hkv][P][D]: (h*P + t)*D + d */
   FP8PA_LAYOUT_TOKENS = 1,        /* [P][Hkv][D]: (t*Hkv + h)*D + d */
@@ -145,7 +146,10 @@ int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
  *   k_pool,
  *   v_pool      device uint8 pools, 16-byte aligned, described by kd / vd.
  *               kd: layout HEADS_D64, HEADS or TOKENS; vd: layout
- *               HEADS_DMAJOR.  Both: same Hkv, D, P and scale kind.
+ *               HEADS_DMAJOR, HEADS or TOKENS.  Both: same Hkv, D, P and
+ *               scale kind.  With V in HEADS or TOKENS the launch needs
+ *               more LDS (B up to about 2000 at D = 128; FP8PA_EUNSUPPORTED
+ *               beyond).
  *   block_table device int32 [B, bt_stride]: logical page -> row.
  *   seq_lens    device int32 [B]: valid positions of each sequence, the token
  *               being decoded included (append first, then decode); each
@@ -179,7 +183,8 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
  * the decode kernel performs the appends (one launch); otherwise the append
  * kernel runs first and then the decode (two launches on `stream`), since an
  * in-kernel append delays the workgroups that read the new tokens by more
- * than a launch costs.  Same contract as fp8pa_decode, plus:
+ * than a launch costs.  V pools in the HEADS or TOKENS layout always take the
+ * two launches.  Same contract as fp8pa_decode, plus:
  *   k_new, v_new  device bf16 [B, Hkv, D], 2-byte aligned: sequence b's new
  *               token, written at position seq_lens[b] - 1 (seq_lens counts it)
  *               and attended in the same call.  Sequences with seq_lens[b] = 0
@@ -260,6 +265,7 @@ typedef struct fp8pa_counters {
   int64_t debug_launches;
   int64_t errors;           /* calls refused or failed */
   int64_t fused_appends;    /* decode launches that also appended (fp8pa_append_decode) */
+  int64_t decode_v_token_major; /* decode launches reading V in the HEADS or TOKENS layout */
 } fp8pa_counters;
 
 int fp8pa_get_counters(fp8pa_counters* out);

@@ -33,7 +33,7 @@ def test_version_and_struct_sizes():
     assert b"gfx950" in ops.lib().fp8pa_version()
     assert ctypes.sizeof(ops.PoolDesc) == 48
     assert ctypes.sizeof(ops.Plan) == 24
-    assert ctypes.sizeof(ops.Counters) == 64
+    assert ctypes.sizeof(ops.Counters) == 72
 
 
 def kd(**kw):
@@ -75,7 +75,8 @@ def call_decode(k=None, v=None, **kw):
     (dict(k=kd(row_bytes=1 << 31)), ops.EUNSUPPORTED),          # rows of 2 GiB or more
     (dict(k=kd(scale_offset=16000)), ops.EINVAL),               # footer inside the payload
     (dict(k=kd(layout="heads_dmajor")), ops.EUNSUPPORTED),      # K must be token-major
-    (dict(v=vd(layout="heads")), ops.EUNSUPPORTED),             # V must be d-major
+    (dict(v=vd(layout="heads_d64")), ops.EUNSUPPORTED),         # V in HEADS_D64 is not read
+    (dict(v=vd(layout="tokens"), B=2100), ops.EUNSUPPORTED),    # tile prefix + V stage exceed 64 KiB of LDS
     (dict(v=vd(num_kv_heads=4, row_bytes=8208)), ops.EUNSUPPORTED),
     (dict(v=vd(scale_kind="token_head", row_bytes=16384 + 512)), ops.EUNSUPPORTED),
     (dict(Hq=30), ops.EINVAL),
