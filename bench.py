@@ -50,6 +50,8 @@ def parse():
                     help="time the workload's decode in each pool format (K layout x scale kind; JSON per format)")
     ap.add_argument("--graph", action="store_true",
                     help="time one step of all layers as eager launches and as a replayed HIP graph")
+    ap.add_argument("--graph-depth", type=int, default=1,
+                    help="--graph: decodes of the layer list per step (a model's depth), pool copies in turn")
     return ap.parse_args()
 
 
@@ -370,33 +372,37 @@ def run_formats(args, wl, torch, np, ops, workloads, hip):
 
 
 def run_graph(args, wl, torch, np, ops, workloads, hip):
-    """One decode step over all layers of the workload: eager launches against
-    a replayed HIP graph (one graph per pool copy, grids fixed at capture)."""
+    """One decode step, `--graph-depth` passes over all layers of the workload
+    (pass r reads pool copy r mod R, so a deep step still streams from HBM):
+    eager launches against a replayed HIP graph (one graph per starting copy,
+    grids fixed at capture)."""
     layers = workloads.build_workload(wl)
     R = args.copies or rotation(layers, wl, np)
     copies = copies_of(layers, wl, R, torch)
+    depth = max(1, args.graph_depth)
     outs = [torch.empty_like(l.q) for l in layers]
     ws = []
     for l in layers:
         p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window)
         ws.append(torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0"))
 
-    def step(c):
-        for j, l in enumerate(c):
-            workloads.decode_layer(l, out=outs[j], workspace=ws[j])
+    def step(c0):
+        for r in range(depth):
+            for j, l in enumerate(copies[(c0 + r) % R]):
+                workloads.decode_layer(l, out=outs[j], workspace=ws[j])
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        step(copies[0])
+        step(0)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     eager = [o.clone() for o in outs]
     graphs = []
-    for c in copies:
+    for c0 in range(R):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(c)
+            step(c0)
         graphs.append(g)
     torch.cuda.synchronize()
     for o in outs:
@@ -407,7 +413,7 @@ def run_graph(args, wl, torch, np, ops, workloads, hip):
         assert torch.equal(o.view(torch.int16), e.view(torch.int16)), "graph replay differs from eager"
     stream = torch.cuda.current_stream().cuda_stream
     res = {}
-    for name, fn in (("eager", lambda k: step(copies[k % R])), ("graph", lambda k: graphs[k % R].replay())):
+    for name, fn in (("eager", lambda k: step(k % R)), ("graph", lambda k: graphs[k % R].replay())):
         for k in range(args.warmup):
             fn(k)
         ev = hip.events(2)
@@ -419,7 +425,7 @@ def run_graph(args, wl, torch, np, ops, workloads, hip):
         torch.cuda.synchronize()
         res[name] = hip.elapsed_ms(ev[0], ev[1]) / args.steps * 1e3
         hip.destroy(ev)
-    print(json.dumps({"graph_step": {"workload": wl.name, "layers": [l.name for l in layers],
+    print(json.dumps({"graph_step": {"workload": wl.name, "layers": [l.name for l in layers], "depth": depth,
                                      "us_per_step_eager": round(res["eager"], 2),
                                      "us_per_step_graph": round(res["graph"], 2),
                                      "timing": f"hipEvents around {args.steps} steps, {R} pool copies rotated"}}),
