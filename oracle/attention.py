@@ -28,6 +28,7 @@ import math
 
 import numpy as np
 
+from . import fp8 as fp8mod
 from . import pool as poolmod
 
 
@@ -47,6 +48,23 @@ def _softmax_out(s, v, sigma):
     e = np.exp(s - m[:, None])
     z = e.sum(axis=1) + np.exp(sigma - m)
     return (e @ v) / z[:, None]
+
+
+def fp8_query(q):
+    """The query of the fp8 compute mode, as exact float64 values.
+
+    The fp8 path of page "fp8 paged attention for MoE serving" (section "Two
+    compute paths") adds one E4M3 rounding of q.  Reading: each (sequence,
+    query head) row of q is quantized like a KV block, with one fp32 scale
+    fp32(amax / 448) (1 for an all-zero row) and codes e4m3(fp32(q / scale)),
+    and the mode attends with code x scale.  The fp8-mode output is then
+    ``decode_ref(fp8_query(q), ...)``."""
+    q = np.asarray(q, dtype=np.float64)
+    out = np.empty_like(q)
+    for idx in np.ndindex(q.shape[:-1]):
+        codes, scale = fp8mod.quantize_fp32_block(q[idx])
+        out[idx] = fp8mod.dequant(codes, scale)
+    return out
 
 
 def decode_ref(q, k_pool, v_pool, kdesc, vdesc, block_table, seq_lens,

@@ -228,3 +228,30 @@ def test_page_example_structure(golden_dir):
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
     # and the dequantized K is the quantised input to within E4M3 precision
     np.testing.assert_allclose(kd, kt[:T].transpose(1, 0, 2), rtol=2 ** -4, atol=2e-3)
+
+
+def test_fp8_query_pins():
+    """The fp8-mode query: a row that already is E4M3 values times a power of
+    two whose largest magnitude is 448 x that power is returned unchanged; an
+    all-zero row stays zero; the rounding is per row (a row 2**-20 times
+    smaller than its neighbour keeps E4M3 relative precision); every element
+    is within E4M3's half-step of q (2**-4 relative in the normal range,
+    2**-10 x scale below it); and the map commutes with sign and with powers of
+    two."""
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 0x7F, size=(3, 5, 64)).astype(np.uint8)
+    codes[..., 7] = 0x7E                                               # 448 in every row
+    exact = fp8.E4M3_TABLE[codes] * np.where(rng.random((3, 5, 64)) < 0.5, -1.0, 1.0)
+    for k in (-9, 0, 5):
+        q = exact * 2.0 ** k
+        np.testing.assert_array_equal(oatt.fp8_query(q), q)
+    assert np.all(oatt.fp8_query(np.zeros((2, 3, 64))) == 0.0)
+    q = rng.standard_normal((4, 6, 128))
+    q[:, 1] *= 2.0 ** -20
+    got = oatt.fp8_query(q)
+    scale = fp8.to_fp32(np.abs(q).max(-1, keepdims=True) / 448.0)
+    bound = np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10 * scale) * (1 + 2 ** -20)
+    assert np.all(np.abs(got - q) <= bound)
+    assert np.max(np.abs(got - q) / np.abs(q)) > 2 ** -6                # it does round
+    np.testing.assert_array_equal(oatt.fp8_query(-q), -got)
+    np.testing.assert_array_equal(oatt.fp8_query(q * 2.0 ** 7), got * 2.0 ** 7)
