@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough for 2 GiB)")
     ap.add_argument("--sweep", action="store_true", help="batch x context sweep (CSV on stderr, JSON per point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", default="auto", choices=["auto", "mfma_bf16", "mfma_fp8"],
+                    help="decode variant (mfma_fp8: the fp8 compute mode, q rounded to E4M3)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB copy (PMC scale reference)")
     ap.add_argument("--formats", action="store_true",
@@ -114,7 +116,7 @@ def stored_traffic(workload):
     return rec.get("traffic_bytes_per_launch")
 
 
-def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgroups):
+def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgroups, variant="auto"):
     """Runs `steps` timed steps; a step decodes every layer once (copy k % R).
     Returns wall seconds, per-step GPU ms, and per-layer mean decode ms."""
     R = len(layers_copies)
@@ -128,7 +130,7 @@ def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgr
 
     def step(k):
         for j, l in enumerate(layers_copies[k % R]):
-            workloads.decode_layer(l, out=outs[j], workspace=ws[j], workgroups=workgroups)
+            workloads.decode_layer(l, out=outs[j], workspace=ws[j], workgroups=workgroups, variant=variant)
 
     for k in range(warmup):
         step(k)
@@ -159,7 +161,7 @@ def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgr
         hip.record(ev[0], stream)
         for k in range(steps):
             l = layers_copies[k % R][j]
-            workloads.decode_layer(l, out=outs[j], workspace=ws[j], workgroups=workgroups)
+            workloads.decode_layer(l, out=outs[j], workspace=ws[j], workgroups=workgroups, variant=variant)
         hip.record(ev[1], stream)
         torch.cuda.synchronize()
         kern_ms.append(hip.elapsed_ms(ev[0], ev[1]) / steps)
@@ -463,14 +465,14 @@ def main():
     R = args.copies or rotation(layers, wl, np)
     copies = copies_of(layers, wl, R, torch)
     # Copies hold identical bytes: every copy must give the same output bit for bit.
-    ref = [workloads.decode_layer(l).clone() for l in copies[0]]
+    ref = [workloads.decode_layer(l, variant=args.variant).clone() for l in copies[0]]
     for c in copies[1:]:
         for j, l in enumerate(c):
-            assert torch.equal(workloads.decode_layer(l), ref[j]), "pool copies disagree"
+            assert torch.equal(workloads.decode_layer(l, variant=args.variant), ref[j]), "pool copies disagree"
     torch.cuda.synchronize()
 
     wall, step_ms, kern_ms, _ = time_layers(copies, args.steps, args.warmup, hip, ops, workloads, torch,
-                                            args.workgroups)
+                                            args.workgroups, args.variant)
     layer_bytes = [workloads.kv_bytes(l) for l in layers]
     total_bytes = sum(layer_bytes)
     ms_per_step = wall * 1e3 / args.steps
@@ -493,7 +495,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.variant != "mfma_fp8" else "fp8 QK (q rounded to e4m3), bf16 PV",
         "data": "synthetic",
         "config": {
             "workload": wl.name, "B": wl.B, "page": wl.P, "seq_lens": f"U[{wl.L_lo},{wl.L_hi}]",

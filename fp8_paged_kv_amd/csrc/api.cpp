@@ -22,7 +22,7 @@ thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 struct Counters {
   std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0}, fused_append{0},
-      decode_vtok{0}, errors{0};
+      decode_vtok{0}, decode_fp8{0}, errors{0};
 };
 Counters g_cnt;
 std::atomic<uint32_t> g_epoch{0};
@@ -193,7 +193,7 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   if (G > 16) return fail(FP8PA_EUNSUPPORTED, "query heads per KV head G=%d > 16", G);
   if (max_seq_len < 0) return fail(FP8PA_EINVAL, "max_seq_len must be >= 0");
   if (workgroups < 0) return fail(FP8PA_EINVAL, "workgroups must be >= 0");
-  if (variant != FP8PA_VARIANT_AUTO && variant != FP8PA_VARIANT_MFMA_BF16)
+  if (variant != FP8PA_VARIANT_AUTO && variant != FP8PA_VARIANT_MFMA_BF16 && variant != FP8PA_VARIANT_MFMA_FP8)
     return fail(FP8PA_EUNSUPPORTED, "variant %d is not available", variant);
   const int D = kd->head_dim;
   const int tv = tile_variant();
@@ -211,7 +211,7 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   }
   out->workgroups = W;
   out->tile_tokens = fp8pa::decode_tile_tokens(D, tv);
-  out->variant = FP8PA_VARIANT_MFMA_BF16;
+  out->variant = variant == FP8PA_VARIANT_MFMA_FP8 ? FP8PA_VARIANT_MFMA_FP8 : FP8PA_VARIANT_MFMA_BF16;
   out->reserved = 0;
   if (W > 1) {
     const int64_t po = (int64_t)W * 2 * G * D * 4;
@@ -264,7 +264,10 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   // V in a token-major layout is staged through LDS (default kernel shapes).
   const bool vt = vd->layout == FP8PA_LAYOUT_HEADS || vd->layout == FP8PA_LAYOUT_TOKENS;
   if (vt && fused) return fail(FP8PA_EUNSUPPORTED, "the one-launch append reads V in the HEADS_DMAJOR layout");
-  const int tv_launch = (fused || vt) ? 0 : tile_variant();
+  const bool f8 = variant == FP8PA_VARIANT_MFMA_FP8;
+  if (f8 && (kd->scale_kind == FP8PA_SCALE_E8M0_G32 || vt || fused))
+    return fail(FP8PA_EUNSUPPORTED, "the fp8 compute mode takes fp32 scales, V in HEADS_DMAJOR and no fused append");
+  const int tv_launch = (fused || vt || f8) ? 0 : tile_variant();
   if (tv_launch != tile_variant())
     lds = fp8pa::decode_lds_bytes(kd->head_dim, tv_launch, B, Hq / kd->num_kv_heads, kd->page_size);
   size_t vstage_off = 0;
@@ -333,7 +336,7 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   a.G = G;
   a.window = window > 0 ? window : 0;
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
-  a.tile_variant = tv_launch;   // the fused and V-token-major kernels exist in the default shapes
+  a.tile_variant = tv_launch;   // the fused, V-token-major and fp8 kernels exist in the default shapes
   a.vstage_off = (int32_t)vstage_off;
   a.min_tiles = min_tiles(fp8pa::decode_waves(D, a.tile_variant));
   a.seg_cost = seg_cost(fp8pa::decode_seg_cost(D, a.tile_variant));
@@ -352,9 +355,11 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
   hipError_t e = fused ? fp8pa::launch_decode_fused(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
                  : vt  ? fp8pa::launch_decode_vtok(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                 : f8  ? fp8pa::launch_decode_fp8q(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
                        : fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
-  g_cnt.decode_mfma.fetch_add(1);
+  if (f8) g_cnt.decode_fp8.fetch_add(1);
+  else g_cnt.decode_mfma.fetch_add(1);
   if (W > 1) g_cnt.decode_split.fetch_add(1);
   if (fused) g_cnt.fused_append.fetch_add(1);
   if (vt) g_cnt.decode_vtok.fetch_add(1);
@@ -389,9 +394,10 @@ int fp8pa_append_decode(const void* k_new, const void* v_new, const void* q, voi
   // each new token.  Short attended spans are launch-bound, and there the one
   // launch wins (about 24 -> 13.5 us on the tiny and window-128 calls);
   // longer ones run the append kernel and then the plain decode.
-  // V in a token-major layout takes the two launches as well.
+  // V in a token-major layout and the fp8 compute mode take the two launches
+  // as well.
   const int span = (window > 0 && window < max_seq_len) ? window : max_seq_len;
-  if (span <= kFusedMaxSpan && vd && vd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
+  if (span <= kFusedMaxSpan && vd && vd->layout == FP8PA_LAYOUT_HEADS_DMAJOR && variant != FP8PA_VARIANT_MFMA_FP8)
     return decode_impl(k_new, v_new, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
                        window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes, stream);
   // Every check of the call runs before the append launches.
@@ -542,6 +548,7 @@ int fp8pa_get_counters(fp8pa_counters* c) {
   c->errors = g_cnt.errors.load();
   c->fused_appends = g_cnt.fused_append.load();
   c->decode_v_token_major = g_cnt.decode_vtok.load();
+  c->decode_mfma_fp8 = g_cnt.decode_fp8.load();
   return FP8PA_OK;
 }
 
@@ -563,6 +570,7 @@ int fp8pa_reset_counters(void) {
   g_cnt.errors = 0;
   g_cnt.fused_append = 0;
   g_cnt.decode_vtok = 0;
+  g_cnt.decode_fp8 = 0;
   return FP8PA_OK;
 }
 

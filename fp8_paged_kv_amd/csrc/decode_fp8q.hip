@@ -1,0 +1,19 @@
+// The decode kernels of the fp8 compute mode (page "fp8 paged attention for
+// MoE serving", section "Two compute paths": an fp8 tensor-core dot that
+// rounds q to E4M3): QK^T on the gfx950 fp8 MFMA with the K codes as they are
+// stored, PV in bf16 as in the default mode.  Default kernel shapes, per-page
+// and per-token fp32 scales.
+#include "decode_kernel.h"
+
+namespace fp8pa {
+
+hipError_t launch_decode_fp8q(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                              hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  if (scale_kind == 2) return hipErrorNotSupported;
+  auto l = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() {
+    return launch_d<DD, NS, PF, OCC, KNT, NW, false, false, true>(a, scale_kind, W, lds, st, e0, e1);
+  };
+  return k_whole_lines ? default_shape<true>(D, l) : default_shape<false>(D, l);
+}
+
+}  // namespace fp8pa

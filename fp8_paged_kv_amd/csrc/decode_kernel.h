@@ -151,8 +151,12 @@ struct Tile {
 // FUSED: also append each sequence's new token (DecodeArgs::k_new / v_new)
 // before reading it.
 // VT: V in a token-major layout (HEADS or TOKENS), staged through LDS.
-template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT>
+// F8: fp8 compute mode for QK^T: each query row is rounded to E4M3 with one
+// fp32 scale (amax / 448), and the K codes enter an fp8 MFMA unconverted; the
+// PV product stays bf16.
+template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT, bool F8 = false>
 __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a) {
+  static_assert(!(F8 && SK == 2), "E8M0 K scales vary inside one fp8 MFMA");
   static_assert(!(FUSED && PF), "the fused append waits inside the non-prefetching tile loop");
   constexpr int NT = 64 * NW;   // threads (NW wave64s)
   constexpr int TT = 32 * NS;   // positions per tile
@@ -412,6 +416,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   const int kgrp = n >> 2;      // group of this lane's K row
   const int kslot = n & 3;
   bf16x8 qop[NQ];
+  uint64_t qop8[NQ];   // F8: E4M3 codes of the same dims
+  float qsc = 1.0f;    // F8: scale of the lane's query row
 
   // Row of a page of the current chunk.  A group with no attended position
   // reads a clamped (attended) page instead: its scores are masked to -inf and
@@ -606,12 +612,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
             cvt = e8m0_as_scale_operand(e);
           }
           const u32x4 w = t.k[s][aa][m];
-          s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[0], w[1], cvt), qop[2 * m], s4);
-          s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[2], w[3], cvt), qop[2 * m + 1], s4);
+          if constexpr (F8) {
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)(((uint64_t)w[1] << 32) | w[0]), (long)qop8[2 * m],
+                                                            s4, 0, 0, 0);
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)(((uint64_t)w[3] << 32) | w[2]),
+                                                            (long)qop8[2 * m + 1], s4, 0, 0, 0);
+          } else {
+            s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[0], w[1], cvt), qop[2 * m], s4);
+            s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[2], w[3], cvt), qop[2 * m + 1], s4);
+          }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float f = a.qk_scale;
+          if constexpr (F8) f *= qsc;
           if constexpr (SK == 0) f *= t.ks;
           if constexpr (SK == 1) f *= t.kst[s][4 * aa + j];
           sc[s][aa][j] = s4[j] * f;
@@ -765,6 +779,33 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
           u32x4 v = col ? ld_global<u32x4>(qrow + 64 * m + 16 * quad + 8 * h2) : u32x4{0, 0, 0, 0};
           qop[2 * m + h2] = __builtin_bit_cast(bf16x8, v);
         }
+      if constexpr (F8) {
+        // The row's amax (the four quads of a head column hold its dims),
+        // its scale fp32(amax / 448) (1 for a zero row), and the codes
+        // e4m3(q / scale), byte i of a dword pair = dim i of the operand.
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          const u32x4 v = __builtin_bit_cast(u32x4, qop[i]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            am = fmaxf(am, fmaxf(fabsf(bf16_to_f32((uint16_t)v[j])), fabsf(bf16_to_f32((uint16_t)(v[j] >> 16)))));
+        }
+        am = fmaxf(am, __shfl_xor(am, 16));
+        am = fmaxf(am, __shfl_xor(am, 32));
+        qsc = am > 0.0f ? am / 448.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          const u32x4 v = __builtin_bit_cast(u32x4, qop[i]);
+          uint64_t c = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)v[j]) / qsc) << (16 * j);
+            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)(v[j] >> 16)) / qsc) << (16 * j + 8);
+          }
+          qop8[i] = c;
+        }
+      }
     }
     m_run = kNegInf;
     l_run = 0.0f;
@@ -1111,18 +1152,19 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   }
 }
 
-template <int D, int NS, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT = false>
+template <int D, int NS, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT = false, bool F8 = false>
 hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(W), block(64 * NW);
   switch (sk) {
     case 0:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW, FUSED, VT>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW, FUSED, VT, F8>), grid, block, lds, st, e0, e1, 0, a);
       break;
     case 1:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED, VT>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED, VT, F8>), grid, block, lds, st, e0, e1, 0, a);
       break;
     default:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED, VT>), grid, block, lds, st, e0, e1, 0, a);
+      if constexpr (F8) return hipErrorNotSupported;
+      else hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED, VT, F8>), grid, block, lds, st, e0, e1, 0, a);
       break;
   }
   return hipGetLastError();

@@ -157,10 +157,10 @@ def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", lay
     return out
 
 
-def decode_layer(layer: DeviceLayer, out=None, workspace=None, workgroups=0, stream=None):
+def decode_layer(layer: DeviceLayer, out=None, workspace=None, workgroups=0, stream=None, variant="auto"):
     return ops.decode(layer.q, layer.k_pool, layer.v_pool, layer.kd, layer.vd, layer.block_table, layer.seq_lens,
                       layer.max_seq_len, window=layer.window, sinks=layer.sinks, sm_scale=layer.sm_scale,
-                      workgroups=workgroups, out=out, workspace=workspace, stream=stream)
+                      workgroups=workgroups, variant=variant, out=out, workspace=workspace, stream=stream)
 
 
 def kv_bytes(layer: DeviceLayer):

@@ -81,7 +81,17 @@ enum {
  *      FP8PA_EUNSUPPORTED, never replaced by another variant. */
 enum {
   FP8PA_VARIANT_AUTO = 0,
-  FP8PA_VARIANT_MFMA_BF16 = 1   /* E4M3 -> bf16 exactly, bf16 MFMA, fp32 accumulate */
+  FP8PA_VARIANT_MFMA_BF16 = 1,  /* E4M3 -> bf16 exactly, bf16 MFMA, fp32 accumulate */
+  FP8PA_VARIANT_MFMA_FP8 = 2    /* fp8 compute mode (page "fp8 paged attention for MoE
+                                   serving", "Two compute paths": the fp8 dot rounds q to
+                                   E4M3): each query row (sequence, query head) is
+                                   quantized with one fp32 scale fp32(amax/448) (1 for a
+                                   zero row) and codes e4m3(fp32(q/scale)); QK^T takes the
+                                   K codes unconverted on the fp8 MFMA; PV and the softmax
+                                   as in MFMA_BF16.  Only on explicit request; pools with
+                                   fp32 scales and V in HEADS_DMAJOR, not with the fused
+                                   append (else FP8PA_EUNSUPPORTED); fp8pa_append_decode
+                                   runs it after the append kernel. */
 };
 
 /* ---- row placement flags (fp8pa_pool_desc.flags).
@@ -183,8 +193,8 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
  * the decode kernel performs the appends (one launch); otherwise the append
  * kernel runs first and then the decode (two launches on `stream`), since an
  * in-kernel append delays the workgroups that read the new tokens by more
- * than a launch costs.  V pools in the HEADS or TOKENS layout always take the
- * two launches.  Same contract as fp8pa_decode, plus:
+ * than a launch costs.  V pools in the HEADS or TOKENS layout and the fp8
+ * compute mode always take the two launches.  Same contract as fp8pa_decode, plus:
  *   k_new, v_new  device bf16 [B, Hkv, D], 2-byte aligned: sequence b's new
  *               token, written at position seq_lens[b] - 1 (seq_lens counts it)
  *               and attended in the same call.  Sequences with seq_lens[b] = 0
@@ -266,6 +276,7 @@ typedef struct fp8pa_counters {
   int64_t errors;           /* calls refused or failed */
   int64_t fused_appends;    /* decode launches that also appended (fp8pa_append_decode) */
   int64_t decode_v_token_major; /* decode launches reading V in the HEADS or TOKENS layout */
+  int64_t decode_mfma_fp8;  /* decode kernels launched, fp8 compute mode */
 } fp8pa_counters;
 
 int fp8pa_get_counters(fp8pa_counters* out);

@@ -33,7 +33,7 @@ def test_version_and_struct_sizes():
     assert b"gfx950" in ops.lib().fp8pa_version()
     assert ctypes.sizeof(ops.PoolDesc) == 48
     assert ctypes.sizeof(ops.Plan) == 24
-    assert ctypes.sizeof(ops.Counters) == 72
+    assert ctypes.sizeof(ops.Counters) == 80
 
 
 def kd(**kw):
@@ -90,6 +90,9 @@ def call_decode(k=None, v=None, **kw):
     (dict(sm_scale=float("nan")), ops.EINVAL),
     (dict(sm_scale=float("inf")), ops.EINVAL),
     (dict(variant=7), ops.EUNSUPPORTED),
+    (dict(variant=2, k=kd(scale_kind="e8m0_32", row_bytes=16384 + 4096),
+          v=vd(scale_kind="e8m0_32", row_bytes=16384 + 4096)), ops.EUNSUPPORTED),   # fp8 mode: fp32 scales only
+    (dict(variant=2, v=vd(layout="tokens")), ops.EUNSUPPORTED),                    # fp8 mode: V d-major only
     (dict(max_seq_len=-1), ops.EINVAL),
     (dict(workgroups=-2), ops.EINVAL),
     (dict(workgroups=4), ops.EWORKSPACE),                       # cut units need a workspace
