@@ -86,3 +86,30 @@ def test_fp8_mode_refusals():
         gpu_decode(p, variant="mfma_fp8")
     c = ops.counters()
     assert c["decode_calls"] == 0 and c["decode_mfma_fp8"] == 0 and c["errors"] == 2
+
+
+def test_fp8_mode_append_decode_takes_two_launches():
+    """fp8pa_append_decode in the fp8 mode: the append kernel, then the fp8
+    decode; the same pools and output as fp8pa_append_quant then the decode."""
+    from tests.gpu_util import DEV, desc_of
+    p = make_problem(404, B=3, Hq=16, Hkv=4, D=128, P=16, lens=[300, 33, 16])
+    kd, vd = desc_of(p.kdesc), desc_of(p.vdesc)
+    table = torch.from_numpy(np.ascontiguousarray(p.table)).to(DEV)
+    sl = torch.from_numpy(p.seq_lens.astype(np.int32)).to(DEV)
+    q = torch.from_numpy(np.ascontiguousarray(p.q)).to(torch.bfloat16).to(DEV)
+    g = torch.Generator().manual_seed(5)
+    kn = torch.randn((3, 4, 128), generator=g).to(torch.bfloat16).to(DEV)
+    vn = torch.randn((3, 4, 128), generator=g).to(torch.bfloat16).to(DEV)
+    ka, va = torch.from_numpy(p.k_pool).to(DEV), torch.from_numpy(p.v_pool).to(DEV)
+    kb, vb = ka.clone(), va.clone()
+    pos = (sl - 1).to(torch.int32)
+    ops.append_quant(kn[:, None], vn[:, None], ka, va, kd, vd, table, pos)
+    want = ops.decode(q, ka, va, kd, vd, table, sl, int(p.seq_lens.max()), sm_scale=p.sm_scale, variant="mfma_fp8")
+    ops.reset_counters()
+    got = ops.append_decode(q, kn, vn, kb, vb, kd, vd, table, sl, int(p.seq_lens.max()), sm_scale=p.sm_scale,
+                            variant="mfma_fp8")
+    torch.cuda.synchronize()
+    c = ops.counters()
+    assert c["append_launches"] == 1 and c["fused_appends"] == 0 and c["decode_mfma_fp8"] == 1
+    assert torch.equal(kb, ka) and torch.equal(vb, va)
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
