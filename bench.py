@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough for 2 GiB)")
     ap.add_argument("--sweep", action="store_true", help="batch x context sweep (CSV on stderr, JSON per point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", default="auto", choices=["auto", "mfma_bf16", "mfma_fp8"],
-                    help="decode variant (mfma_fp8: the fp8 compute mode, q rounded to E4M3)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "mfma_bf16", "mfma_fp8", "packed_heads"],
+                    help="decode variant (mfma_fp8: the fp8 compute mode, q rounded to E4M3; packed_heads: one "
+                         "workgroup per sequence and group of KV heads, no split)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB copy (PMC scale reference)")
     ap.add_argument("--formats", action="store_true",
@@ -346,11 +347,13 @@ def run_formats(args, wl, torch, np, ops, workloads, hip):
     same codes and scales, so their outputs must agree bit for bit."""
     first = {}
     for kl, vl, sk in FORMATS:
+        if args.variant in ("mfma_fp8", "packed_heads") and vl != "heads_dmajor":
+            continue   # these variants read V d-major only
         sk = wl.scale_kind if sk is None else sk
         layers = workloads.build_workload(wl, k_layout=kl, v_layout=vl, scale_kind=sk)
         R = args.copies or rotation(layers, wl, np)
         copies = copies_of(layers, wl, R, torch)
-        outs = [workloads.decode_layer(l).clone() for l in layers]
+        outs = [workloads.decode_layer(l, variant=args.variant).clone() for l in layers]
         if sk in first:
             for j, o in enumerate(outs):
                 assert torch.equal(o.view(torch.int16), first[sk][j].view(torch.int16)), \
@@ -358,7 +361,7 @@ def run_formats(args, wl, torch, np, ops, workloads, hip):
         else:
             first[sk] = outs
         _, step_ms, kern_ms, _ = time_layers(copies, args.steps, args.warmup, hip, ops, workloads, torch,
-                                             args.workgroups)
+                                             args.workgroups, args.variant)
         rows = []
         for l, km in zip(layers, kern_ms):
             b = workloads.kv_bytes(l)
@@ -366,7 +369,8 @@ def run_formats(args, wl, torch, np, ops, workloads, hip):
                          "kernel_gbps": round(b / (km * 1e-3) / 1e9, 1),
                          "pct_peak": round(100 * b / (km * 1e-3) / 1e9 / PEAK_GBPS, 1)})
         print(json.dumps({"format": {"k_layout": kl, "v_layout": vl, "scale_kind": sk,
-                                     "row_bytes": layers[0].row_bytes}, "workload": wl.name, "layers": rows,
+                                     "row_bytes": layers[0].row_bytes}, "variant": args.variant,
+                          "workload": wl.name, "layers": rows,
                           "timing": f"hipEvents around {args.steps} back-to-back launches per layer, "
                                     f"{R} pool copies rotated"}), flush=True)
         del copies, layers

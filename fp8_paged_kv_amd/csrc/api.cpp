@@ -22,7 +22,7 @@ thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 struct Counters {
   std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0}, fused_append{0},
-      decode_vtok{0}, decode_fp8{0}, errors{0};
+      decode_vtok{0}, decode_fp8{0}, decode_packed{0}, errors{0};
 };
 Counters g_cnt;
 std::atomic<uint32_t> g_epoch{0};
@@ -193,15 +193,22 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   if (G > 16) return fail(FP8PA_EUNSUPPORTED, "query heads per KV head G=%d > 16", G);
   if (max_seq_len < 0) return fail(FP8PA_EINVAL, "max_seq_len must be >= 0");
   if (workgroups < 0) return fail(FP8PA_EINVAL, "workgroups must be >= 0");
-  if (variant != FP8PA_VARIANT_AUTO && variant != FP8PA_VARIANT_MFMA_BF16 && variant != FP8PA_VARIANT_MFMA_FP8)
+  if (variant != FP8PA_VARIANT_AUTO && variant != FP8PA_VARIANT_MFMA_BF16 && variant != FP8PA_VARIANT_MFMA_FP8 &&
+      variant != FP8PA_VARIANT_PACKED_HEADS)
     return fail(FP8PA_EUNSUPPORTED, "variant %d is not available", variant);
+  const bool packed = variant == FP8PA_VARIANT_PACKED_HEADS;
+  if (packed && workgroups != 0) return fail(FP8PA_EUNSUPPORTED, "packed heads fix the grid: workgroups must be 0");
   const int D = kd->head_dim;
   const int tv = tile_variant();
   const size_t lds = fp8pa::decode_lds_bytes(D, tv, B, G, kd->page_size);
   if (lds > 65536)
     return fail(FP8PA_EUNSUPPORTED, "B=%d, G=%d, head_dim %d need %zu bytes of LDS (> 64 KiB)", B, G, D, lds);
   int W = workgroups;
-  if (W == 0) {
+  if (packed) {
+    const int nw = fp8pa::decode_waves(D, 0);
+    W = B * ((kd->num_kv_heads + nw - 1) / nw);
+    if (W < 1) W = 1;
+  } else if (W == 0) {
     // One resident generation: every workgroup gets an equal share of the
     // tiles and all of them run at once.
     const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
@@ -211,9 +218,9 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   }
   out->workgroups = W;
   out->tile_tokens = fp8pa::decode_tile_tokens(D, tv);
-  out->variant = variant == FP8PA_VARIANT_MFMA_FP8 ? FP8PA_VARIANT_MFMA_FP8 : FP8PA_VARIANT_MFMA_BF16;
+  out->variant = (variant == FP8PA_VARIANT_MFMA_FP8 || packed) ? variant : FP8PA_VARIANT_MFMA_BF16;
   out->reserved = 0;
-  if (W > 1) {
+  if (W > 1 && !packed) {
     const int64_t po = (int64_t)W * 2 * G * D * 4;
     const int64_t pl = (int64_t)W * 2 * G * 4;
     const int64_t pc = (int64_t)W * 2 * 4;
@@ -267,7 +274,10 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   const bool f8 = variant == FP8PA_VARIANT_MFMA_FP8;
   if (f8 && (kd->scale_kind == FP8PA_SCALE_E8M0_G32 || vt || fused))
     return fail(FP8PA_EUNSUPPORTED, "the fp8 compute mode takes fp32 scales, V in HEADS_DMAJOR and no fused append");
-  const int tv_launch = (fused || vt || f8) ? 0 : tile_variant();
+  const bool packed = variant == FP8PA_VARIANT_PACKED_HEADS;
+  if (packed && (vt || fused))
+    return fail(FP8PA_EUNSUPPORTED, "packed heads take V in HEADS_DMAJOR and no fused append");
+  const int tv_launch = (fused || vt || f8 || packed) ? 0 : tile_variant();
   if (tv_launch != tile_variant())
     lds = fp8pa::decode_lds_bytes(kd->head_dim, tv_launch, B, Hq / kd->num_kv_heads, kd->page_size);
   size_t vstage_off = 0;
@@ -356,11 +366,14 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   hipError_t e = fused ? fp8pa::launch_decode_fused(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
                  : vt  ? fp8pa::launch_decode_vtok(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
                  : f8  ? fp8pa::launch_decode_fp8q(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                 : packed ? fp8pa::launch_decode_packed(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start,
+                                                        g_ev_stop)
                        : fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
   if (f8) g_cnt.decode_fp8.fetch_add(1);
   else g_cnt.decode_mfma.fetch_add(1);
-  if (W > 1) g_cnt.decode_split.fetch_add(1);
+  if (W > 1 && !packed) g_cnt.decode_split.fetch_add(1);
+  if (packed) g_cnt.decode_packed.fetch_add(1);
   if (fused) g_cnt.fused_append.fetch_add(1);
   if (vt) g_cnt.decode_vtok.fetch_add(1);
   g_cnt.decode_calls.fetch_add(1);
@@ -397,7 +410,8 @@ int fp8pa_append_decode(const void* k_new, const void* v_new, const void* q, voi
   // V in a token-major layout and the fp8 compute mode take the two launches
   // as well.
   const int span = (window > 0 && window < max_seq_len) ? window : max_seq_len;
-  if (span <= kFusedMaxSpan && vd && vd->layout == FP8PA_LAYOUT_HEADS_DMAJOR && variant != FP8PA_VARIANT_MFMA_FP8)
+  if (span <= kFusedMaxSpan && vd && vd->layout == FP8PA_LAYOUT_HEADS_DMAJOR && variant != FP8PA_VARIANT_MFMA_FP8 &&
+      variant != FP8PA_VARIANT_PACKED_HEADS)
     return decode_impl(k_new, v_new, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
                        window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes, stream);
   // Every check of the call runs before the append launches.
@@ -549,6 +563,7 @@ int fp8pa_get_counters(fp8pa_counters* c) {
   c->fused_appends = g_cnt.fused_append.load();
   c->decode_v_token_major = g_cnt.decode_vtok.load();
   c->decode_mfma_fp8 = g_cnt.decode_fp8.load();
+  c->decode_packed_heads = g_cnt.decode_packed.load();
   return FP8PA_OK;
 }
 
@@ -571,6 +586,7 @@ int fp8pa_reset_counters(void) {
   g_cnt.fused_append = 0;
   g_cnt.decode_vtok = 0;
   g_cnt.decode_fp8 = 0;
+  g_cnt.decode_packed = 0;
   return FP8PA_OK;
 }
 

@@ -154,9 +154,15 @@ struct Tile {
 // F8: fp8 compute mode for QK^T: each query row is rounded to E4M3 with one
 // fp32 scale (amax / 448), and the K codes enter an fp8 MFMA unconverted; the
 // PV product stays bf16.
-template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT, bool F8 = false>
+// PK: packed heads (low latency, no splits): workgroup w holds sequence
+// w / ceil(Hkv/NW) and NW consecutive KV heads, one per wave, each wave
+// streaming every tile of its head; the waves read the same page rows
+// together and nothing is merged.
+template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT, bool F8 = false,
+          bool PK = false>
 __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a) {
   static_assert(!(F8 && SK == 2), "E8M0 K scales vary inside one fp8 MFMA");
+  static_assert(!(PK && (FUSED || F8 || PF)), "packed heads: plain bf16 kernels without prefetch");
   static_assert(!(FUSED && PF), "the fused append waits inside the non-prefetching tile loop");
   constexpr int NT = 64 * NW;   // threads (NW wave64s)
   constexpr int TT = 32 * NS;   // positions per tile
@@ -251,8 +257,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   // bounds and the first segment's unit in registers, and stages that
   // segment's first page rows, so the workgroup passes a single barrier
   // before its first tile loads.  Larger batches use all four waves.
-  const bool fast = B <= 64;
-  if (fast) {
+  const bool fast = !PK && B <= 64;
+  if constexpr (PK) {
+  } else if (fast) {
     if (wave == 0) {
       const int len = lane < B ? a.seq_lens[lane] : 0;
       const int nt = tiles_of(len), ne = nt > 0 ? 1 : 0;
@@ -373,13 +380,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
     cap_W();
   }
 
-  // Sequences with nothing to attend get a zero output.
-  for (int bb = w; bb < B; bb += (int)gridDim.x) {
-    if (s_pre[bb + 1] != s_pre[bb]) continue;
-    uint16_t* o = a.out + (size_t)bb * a.Hq * D;
-    for (int i = threadIdx.x; i < a.Hq * D; i += NT) o[i] = 0;
+  // Sequences with nothing to attend get a zero output (packed heads: each
+  // wave writes its own head's, and the tile prefix is not built).
+  if constexpr (!PK) {
+    for (int bb = w; bb < B; bb += (int)gridDim.x) {
+      if (s_pre[bb + 1] != s_pre[bb]) continue;
+      uint16_t* o = a.out + (size_t)bb * a.Hq * D;
+      for (int i = threadIdx.x; i < a.Hq * D; i += NT) o[i] = 0;
+    }
+    if (w >= W) return;
   }
-  if (w >= W) return;
   auto cpre = [&](int bb) -> int64_t { return SC * Hkv * s_nep[bb] + TC * (int64_t)Hkv * s_pre[bb]; };
   // Cost start of tile i of unit (bb, gg).
   auto tile_cost = [&](int bb, int gg, int i) -> int64_t {
@@ -732,6 +742,65 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       }
     }
   };
+
+  if constexpr (PK) {
+    const int hpg = (Hkv + NW - 1) / NW;
+    b = w / hpg;
+    g = (w - b * hpg) * NW + wave;
+    const bool active = g < Hkv;
+    if (!active) g = Hkv - 1;   // an idle wave: in-range pointers, no tiles, no output
+    L = a.seq_lens[b];
+    start = (a.window > 0 && L > a.window) ? L - a.window : 0;
+    tbeg = start & ~(TT - 1);
+    btr = a.bt + (int64_t)b * a.bt_stride;
+    kpool = a.kp + (int64_t)g * a.kg.head_stride;
+    vpool = a.vp + (int64_t)g * a.vg.head_stride;
+    {
+      const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)g * G + (col ? n : 0)) * D;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          u32x4 v = col ? ld_global<u32x4>(qrow + 64 * m + 16 * quad + 8 * h2) : u32x4{0, 0, 0, 0};
+          qop[2 * m + h2] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nb = tiles_of(L);
+    for (int ca = 0; ca < nb; ca += CH) {
+      const int cb = nb < ca + CH ? nb : ca + CH;
+      chunk_rows(ca, cb);
+      __syncthreads();   // earlier readers of the stage are done
+      for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = btr[p_first + i];
+      __syncthreads();
+      if (active) {
+        TileT A;
+        for (int k = ca; k < cb; ++k) {
+          load_tile(A, tbeg + k * TT);
+          compute_tile(A, tbeg + k * TT);
+        }
+      }
+    }
+    // The wave's head is complete: o = acc / (sum + e^(sink - max)).
+    float lsum = l_run;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (active && col) {
+      const int h = g * G + n;
+      const float m_ref = (m_run == kNegInf) ? 0.0f : m_run;
+      float den = lsum;
+      if (a.sinks) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - m_ref);
+      const float inv = (m_run == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
+      uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * D + 4 * quad;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x2 pk = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv), pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + 16 * c) = pk;
+      }
+    }
+    return;
+  }
 
   int64_t cur = s_bnd[0];
   const int64_t hi = s_bnd[1];
@@ -1152,19 +1221,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   }
 }
 
-template <int D, int NS, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT = false, bool F8 = false>
+template <int D, int NS, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT = false, bool F8 = false,
+          bool PK = false>
 hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(W), block(64 * NW);
   switch (sk) {
     case 0:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW, FUSED, VT, F8>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW, FUSED, VT, F8, PK>), grid, block, lds, st, e0, e1, 0, a);
       break;
     case 1:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED, VT, F8>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED, VT, F8, PK>), grid, block, lds, st, e0, e1, 0, a);
       break;
     default:
       if constexpr (F8) return hipErrorNotSupported;
-      else hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED, VT, F8>), grid, block, lds, st, e0, e1, 0, a);
+      else hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED, VT, F8, PK>), grid, block, lds, st, e0, e1, 0, a);
       break;
   }
   return hipGetLastError();

@@ -120,6 +120,10 @@ size_t decode_vstage_bytes(int D);
 // kernel shapes, fp32 scales only.
 hipError_t launch_decode_fp8q(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                               hipStream_t st, hipEvent_t start, hipEvent_t stop);
+// Packed heads: grid B * ceil(Hkv / decode_waves(D, 0)), no splits, default
+// kernel shapes.
+hipError_t launch_decode_packed(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                                hipStream_t st, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int B, int max_pages, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);

@@ -82,7 +82,7 @@ enum {
 enum {
   FP8PA_VARIANT_AUTO = 0,
   FP8PA_VARIANT_MFMA_BF16 = 1,  /* E4M3 -> bf16 exactly, bf16 MFMA, fp32 accumulate */
-  FP8PA_VARIANT_MFMA_FP8 = 2    /* fp8 compute mode (page "fp8 paged attention for MoE
+  FP8PA_VARIANT_MFMA_FP8 = 2,   /* fp8 compute mode (page "fp8 paged attention for MoE
                                    serving", "Two compute paths": the fp8 dot rounds q to
                                    E4M3): each query row (sequence, query head) is
                                    quantized with one fp32 scale fp32(amax/448) (1 for a
@@ -92,6 +92,15 @@ enum {
                                    fp32 scales and V in HEADS_DMAJOR, not with the fused
                                    append (else FP8PA_EUNSUPPORTED); fp8pa_append_decode
                                    runs it after the append kernel. */
+  FP8PA_VARIANT_PACKED_HEADS = 3  /* packed heads (page "fp8 paged attention for MoE
+                                   serving", pack_heads): one workgroup per (sequence,
+                                   group of KV heads), one KV head per wave, no split and
+                                   no merge; arithmetic as MFMA_BF16.  For short or
+                                   windowed calls.  The grid is fixed (workgroups must be
+                                   0; the plan reports B * ceil(Hkv / 4), no workspace);
+                                   V in HEADS_DMAJOR, no fused append (else
+                                   FP8PA_EUNSUPPORTED); fp8pa_append_decode runs it
+                                   after the append kernel. */
 };
 
 /* ---- row placement flags (fp8pa_pool_desc.flags).
@@ -277,6 +286,7 @@ typedef struct fp8pa_counters {
   int64_t fused_appends;    /* decode launches that also appended (fp8pa_append_decode) */
   int64_t decode_v_token_major; /* decode launches reading V in the HEADS or TOKENS layout */
   int64_t decode_mfma_fp8;  /* decode kernels launched, fp8 compute mode */
+  int64_t decode_packed_heads; /* decode kernels launched, packed heads */
 } fp8pa_counters;
 
 int fp8pa_get_counters(fp8pa_counters* out);

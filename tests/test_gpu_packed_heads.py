@@ -1,0 +1,100 @@
+"""Packed heads (FP8PA_VARIANT_PACKED_HEADS) on the GPU: one workgroup per
+(sequence, group of KV heads), one head per wave, no split.  Parity against
+the float64 oracle over head dims 64-512, every scale kind, windows, sinks,
+aligned rows, KV-head counts that do not fill a workgroup, empty and short
+sequences; the plan's fixed grid; the counter; refusals; the append + decode
+call; and poison outside the attended positions."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_paged_kv_amd import ops
+from oracle import attention as oatt
+from tests.gpu_util import DEV, assert_parity, desc_of, gpu_decode, say, to_np
+from tests.problems import make_problem
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle(p):
+    return oatt.decode_ref(p.q, p.k_pool, p.v_pool, p.kdesc, p.vdesc, p.table, p.seq_lens, window=p.window,
+                           sinks=p.sinks, sm_scale=p.sm_scale)
+
+
+CASES = [
+    ("tiny-hkv2", dict(B=1, Hq=8, Hkv=2, D=64, P=16, lens=[256])),
+    ("d64-g8-window-sinks", dict(B=3, Hq=64, Hkv=8, D=64, P=16, lens=[500, 100, 20], window=128, sinks=True)),
+    ("d128-g4", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[513, 64, 1])),
+    ("d128-hkv8-ktokens", dict(B=2, Hq=32, Hkv=8, D=128, P=16, lens=[260, 5], k_layout="tokens")),
+    ("d128-hkv6-kheads", dict(B=2, Hq=24, Hkv=6, D=128, P=32, lens=[260, 77], k_layout="heads")),
+    ("d128-token-scales", dict(B=2, Hq=16, Hkv=4, D=128, P=16, lens=[700, 65], scale_kind="token_head")),
+    ("d128-aligned-rows", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[700, 65, 300], row_pad=32, align64=True)),
+    ("d128-e8m0-p128", dict(B=2, Hq=16, Hkv=2, D=128, P=128, lens=[1000, 130], scale_kind="e8m0_32")),
+    ("d256-hkv8-window", dict(B=2, Hq=16, Hkv=8, D=256, P=32, lens=[1500, 33], window=1024, sm_scale=1.0)),
+    ("d512-g8", dict(B=2, Hq=16, Hkv=2, D=512, P=32, lens=[333, 64], sm_scale=1.0)),
+    ("g16-hkv1", dict(B=1, Hq=16, Hkv=1, D=64, P=64, lens=[450])),
+    ("empty-and-short", dict(B=4, Hq=8, Hkv=2, D=64, P=16, lens=[0, 1, 15, 65], sinks=True)),
+    ("long-20k", dict(B=1, Hq=8, Hkv=2, D=64, P=16, lens=[20000])),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_packed_heads_parity(name, kw):
+    say("packed heads parity", name)
+    p = make_problem(501, **kw)
+    plan = ops.decode_plan(p.B, p.Hq, desc_of(p.kdesc), int(p.seq_lens.max()), p.window, variant="packed_heads")
+    assert plan.workgroups == p.B * -(-p.Hkv // 4) and plan.workspace_bytes == 0
+    ops.reset_counters()
+    got = to_np(gpu_decode(p, variant="packed_heads"))
+    c = ops.counters()
+    assert c["decode_packed_heads"] == 1 and c["decode_split"] == 0 and c["decode_mfma_bf16"] == 1
+    assert_parity(got, oracle(p), name)
+
+
+def test_packed_heads_poison_never_leaks():
+    p = make_problem(502, B=3, Hq=8, Hkv=2, D=64, P=16, lens=[37, 16, 250], window=50, sinks=True)
+    t = p.table.copy()
+    for b in range(3):
+        used = -(-int(p.seq_lens[b]) // 16)
+        t[b, used:] = -1
+    t[2, : (250 - 50) // 16] = -7
+    got = to_np(gpu_decode(replace(p, table=t), variant="packed_heads"))
+    assert np.all(np.isfinite(got))
+    assert_parity(got, oracle(p), "poison")
+
+
+def test_packed_heads_refusals():
+    p = make_problem(503, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[100, 30], v_layout="tokens")
+    with pytest.raises(RuntimeError):
+        gpu_decode(p, variant="packed_heads")
+    p = make_problem(503, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[100, 30])
+    with pytest.raises(RuntimeError):
+        gpu_decode(p, variant="packed_heads", workgroups=3)
+
+
+def test_packed_heads_append_decode():
+    """fp8pa_append_decode with packed heads: the append kernel, then the
+    packed decode; the same pools and output as the two calls."""
+    p = make_problem(504, B=3, Hq=32, Hkv=8, D=64, P=16, lens=[200, 33, 16], window=128)
+    kd, vd = desc_of(p.kdesc), desc_of(p.vdesc)
+    table = torch.from_numpy(np.ascontiguousarray(p.table)).to(DEV)
+    sl = torch.from_numpy(p.seq_lens.astype(np.int32)).to(DEV)
+    q = torch.from_numpy(np.ascontiguousarray(p.q)).to(torch.bfloat16).to(DEV)
+    g = torch.Generator().manual_seed(6)
+    kn = torch.randn((3, 8, 64), generator=g).to(torch.bfloat16).to(DEV)
+    vn = torch.randn((3, 8, 64), generator=g).to(torch.bfloat16).to(DEV)
+    ka, va = torch.from_numpy(p.k_pool).to(DEV), torch.from_numpy(p.v_pool).to(DEV)
+    kb, vb = ka.clone(), va.clone()
+    msl = int(p.seq_lens.max())
+    ops.append_quant(kn[:, None], vn[:, None], ka, va, kd, vd, table, (sl - 1).to(torch.int32))
+    want = ops.decode(q, ka, va, kd, vd, table, sl, msl, window=128, sm_scale=p.sm_scale, variant="packed_heads")
+    ops.reset_counters()
+    got = ops.append_decode(q, kn, vn, kb, vb, kd, vd, table, sl, msl, window=128, sm_scale=p.sm_scale,
+                            variant="packed_heads")
+    torch.cuda.synchronize()
+    c = ops.counters()
+    assert c["append_launches"] == 1 and c["fused_appends"] == 0 and c["decode_packed_heads"] == 1
+    assert torch.equal(kb, ka) and torch.equal(vb, va)
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
