@@ -125,7 +125,12 @@ def decode_plan(B, Hq, kd, max_seq_len, window=0, workgroups=0, variant="auto"):
 
 def decode(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window=0, sinks=None, sm_scale=None,
            workgroups=0, variant="auto", out=None, workspace=None, stream=None):
-    """Decode attention.  q bf16 [B, Hq, D]; returns bf16 [B, Hq, D]."""
+    """Decode attention.  q bf16 [B, Hq, D]; returns bf16 [B, Hq, D].
+
+    variant: "auto" or "mfma_bf16" (the default bf16 MFMA path), "mfma_fp8"
+    (the fp8 compute mode: query rows rounded to E4M3) or "packed_heads" (one
+    workgroup per sequence and group of KV heads, no split; workgroups must be
+    0).  A variant the call cannot run raises; none is replaced by another."""
     _need(q, "q", torch.bfloat16)
     _need(k_pool, "k_pool", torch.uint8)
     _need(v_pool, "v_pool", torch.uint8)
@@ -152,7 +157,9 @@ def decode(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window
 def append_decode(q, k_new, v_new, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window=0, sinks=None,
                   sm_scale=None, workgroups=0, variant="auto", out=None, workspace=None, stream=None):
     """Append each sequence's new token (bf16 [B, Hkv, D] k_new / v_new, at
-    position seq_lens[b] - 1) into the pools and decode, in one launch."""
+    position seq_lens[b] - 1) into the pools and decode: in one launch for
+    attended spans up to 2048 positions with V in "heads_dmajor" and the
+    default variant, else the append kernel and then the decode."""
     _need(q, "q", torch.bfloat16)
     _need(k_new, "k_new", torch.bfloat16)
     _need(v_new, "v_new", torch.bfloat16)
