@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough for 2 GiB)")
     ap.add_argument("--sweep", action="store_true", help="batch x context sweep (CSV on stderr, JSON per point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", default="auto", choices=["auto", "mfma_bf16", "mfma_fp8", "packed_heads"],
+    ap.add_argument("--variant", default="auto", choices=["auto", "mfma_bf16", "mfma_fp8", "packed_heads", "packed_split"],
                     help="decode variant (mfma_fp8: the fp8 compute mode, q rounded to E4M3; packed_heads: one "
                          "workgroup per sequence and group of KV heads, no split)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
@@ -125,7 +125,7 @@ def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgr
     outs = [torch.empty_like(l.q) for l in layers_copies[0]]
     ws = []
     for l in layers_copies[0]:
-        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, workgroups)
+        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, workgroups, variant)
         ws.append(torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0"))
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -347,7 +347,7 @@ def run_formats(args, wl, torch, np, ops, workloads, hip):
     same codes and scales, so their outputs must agree bit for bit."""
     first = {}
     for kl, vl, sk in FORMATS:
-        if args.variant in ("mfma_fp8", "packed_heads") and vl != "heads_dmajor":
+        if args.variant in ("mfma_fp8", "packed_heads", "packed_split") and vl != "heads_dmajor":
             continue   # these variants read V d-major only
         sk = wl.scale_kind if sk is None else sk
         layers = workloads.build_workload(wl, k_layout=kl, v_layout=vl, scale_kind=sk)
@@ -487,7 +487,8 @@ def main():
     traffic = stored_traffic(wl.name)
     us = sorted(x * 1e3 for x in step_ms)
     pct = lambda p: us[min(len(us) - 1, int(p * len(us)))]
-    plans = [ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, args.workgroups) for l in layers]
+    plans = [ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, args.workgroups, args.variant)
+             for l in layers]
     rec = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -16,7 +16,7 @@ OUT = os.path.join(PKG, "libfp8pa.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["decode.hip", "decode_fused.hip", "decode_vtok.hip", "decode_fp8q.hip", "decode_packed.hip", "merge.hip", "append.hip", "probe.hip", "api.cpp"]
+SOURCES = ["decode.hip", "decode_fused.hip", "decode_vtok.hip", "decode_fp8q.hip", "decode_packed.hip", "decode_pksplit.hip", "merge.hip", "append.hip", "probe.hip", "api.cpp"]
 # Packed fp32 VALU instructions are kept out of generated code (the device
 # pass honours the feature flag; the host pass warns that it does not know it).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

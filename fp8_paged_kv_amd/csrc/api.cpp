@@ -22,7 +22,7 @@ thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 struct Counters {
   std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0}, fused_append{0},
-      decode_vtok{0}, decode_fp8{0}, decode_packed{0}, errors{0};
+      decode_vtok{0}, decode_fp8{0}, decode_packed{0}, decode_psplit{0}, errors{0};
 };
 Counters g_cnt;
 std::atomic<uint32_t> g_epoch{0};
@@ -184,6 +184,28 @@ int device_cus() {
 }
 
 // Host-only decode plan.  Returns 0 or an error code.
+// Whether an automatic plan takes packed heads: when the (sequence, group of
+// four KV heads) units alone fill every resident workgroup slot, reading all
+// heads of the page rows together streams faster than cutting units into
+// balanced shares (measured at D = 128: B 256 x L 1024 4.8 -> 6.1 TB/s,
+// B 1024 x L 256 2.9 -> 5.4 TB/s; below one unit per slot it is slower).
+// No side effects; false for any invalid argument.
+bool auto_packs(int B, int Hq, const fp8pa_pool_desc* kd, int workgroups, int variant) {
+  if (variant != FP8PA_VARIANT_AUTO || workgroups != 0 || !kd || B <= 0 || kd->num_kv_heads < 1 ||
+      Hq < 1 || Hq % kd->num_kv_heads || Hq / kd->num_kv_heads > 16 || kd->page_size < 1)
+    return false;
+  const int D = kd->head_dim;
+  if (D != 64 && D != 128) return false;   // the head dims where the gain was measured
+  const int cus = device_cus();
+  if (cus <= 0) return false;
+  const int tv = tile_variant();
+  const size_t lds = fp8pa::decode_lds_bytes(D, tv, B, Hq / kd->num_kv_heads, kd->page_size);
+  const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
+  const int per_cu = fp8pa::decode_blocks_per_cu(D, kd->scale_kind, k_whole, tv, lds);
+  const int nw = fp8pa::decode_waves(D, 0);
+  return per_cu > 0 && (int64_t)B * ((kd->num_kv_heads + nw - 1) / nw) >= (int64_t)cus * per_cu;
+}
+
 int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int window, int workgroups, int variant,
               fp8pa_plan* out, size_t* lds_out) {
   if (int rc = check_desc(kd, "kd")) return rc;
@@ -194,13 +216,20 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   if (max_seq_len < 0) return fail(FP8PA_EINVAL, "max_seq_len must be >= 0");
   if (workgroups < 0) return fail(FP8PA_EINVAL, "workgroups must be >= 0");
   if (variant != FP8PA_VARIANT_AUTO && variant != FP8PA_VARIANT_MFMA_BF16 && variant != FP8PA_VARIANT_MFMA_FP8 &&
-      variant != FP8PA_VARIANT_PACKED_HEADS)
+      variant != FP8PA_VARIANT_PACKED_HEADS && variant != FP8PA_VARIANT_PACKED_SPLIT)
     return fail(FP8PA_EUNSUPPORTED, "variant %d is not available", variant);
+  if (variant == FP8PA_VARIANT_PACKED_HEADS && workgroups != 0)
+    return fail(FP8PA_EUNSUPPORTED, "packed heads fix the grid: workgroups must be 0");
   const bool packed = variant == FP8PA_VARIANT_PACKED_HEADS;
-  if (packed && workgroups != 0) return fail(FP8PA_EUNSUPPORTED, "packed heads fix the grid: workgroups must be 0");
   const int D = kd->head_dim;
-  const int tv = tile_variant();
-  const size_t lds = fp8pa::decode_lds_bytes(D, tv, B, G, kd->page_size);
+  // Packed splits: units of nw KV heads, nw * G query heads merged together.
+  const bool psplit = variant == FP8PA_VARIANT_PACKED_SPLIT;
+  const int nw0 = fp8pa::decode_waves(D, 0);
+  if (psplit && (kd->num_kv_heads % nw0 || G * nw0 > 16))
+    return fail(FP8PA_EUNSUPPORTED, "packed splits need Hkv %% %d == 0 and G <= %d", nw0, 16 / nw0);
+  const int Gu = psplit ? G * nw0 : G;   // query heads per unit
+  const int tv = psplit ? 0 : tile_variant();
+  const size_t lds = fp8pa::decode_lds_bytes(D, tv, B, Gu, kd->page_size);
   if (lds > 65536)
     return fail(FP8PA_EUNSUPPORTED, "B=%d, G=%d, head_dim %d need %zu bytes of LDS (> 64 KiB)", B, G, D, lds);
   int W = workgroups;
@@ -218,11 +247,11 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   }
   out->workgroups = W;
   out->tile_tokens = fp8pa::decode_tile_tokens(D, tv);
-  out->variant = (variant == FP8PA_VARIANT_MFMA_FP8 || packed) ? variant : FP8PA_VARIANT_MFMA_BF16;
+  out->variant = (variant == FP8PA_VARIANT_MFMA_FP8 || packed || psplit) ? variant : FP8PA_VARIANT_MFMA_BF16;
   out->reserved = 0;
   if (W > 1 && !packed) {
-    const int64_t po = (int64_t)W * 2 * G * D * 4;
-    const int64_t pl = (int64_t)W * 2 * G * 4;
+    const int64_t po = (int64_t)W * 2 * Gu * D * 4;
+    const int64_t pl = (int64_t)W * 2 * Gu * 4;
     const int64_t pc = (int64_t)W * 2 * 4;
     out->workspace_bytes = (po + 255) / 256 * 256 + (pl + 255) / 256 * 256 + (pc + 255) / 256 * 256;
   } else {
@@ -260,7 +289,7 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
                 const float* sinks, float sm_scale, int max_seq_len, int workgroups, int variant, void* workspace,
                 size_t workspace_bytes, void* stream, bool dry_run = false) {
   const bool fused = k_new != nullptr || v_new != nullptr;
-  fp8pa_plan plan;
+  fp8pa_plan plan{};
   size_t lds = 0;
   if (int rc = make_plan(B, Hq, kd, max_seq_len, window, workgroups, variant, &plan, &lds)) return rc;
   if (int rc = check_desc(vd, "vd")) return rc;
@@ -274,11 +303,16 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   const bool f8 = variant == FP8PA_VARIANT_MFMA_FP8;
   if (f8 && (kd->scale_kind == FP8PA_SCALE_E8M0_G32 || vt || fused))
     return fail(FP8PA_EUNSUPPORTED, "the fp8 compute mode takes fp32 scales, V in HEADS_DMAJOR and no fused append");
-  const bool packed = variant == FP8PA_VARIANT_PACKED_HEADS;
-  if (packed && (vt || fused))
-    return fail(FP8PA_EUNSUPPORTED, "packed heads take V in HEADS_DMAJOR and no fused append");
-  const int tv_launch = (fused || vt || f8 || packed) ? 0 : tile_variant();
-  if (tv_launch != tile_variant())
+  // Packed heads: requested, or taken automatically when the units fill the
+  // device (V d-major, no fused append; the plan's workspace then goes
+  // unused).
+  const bool psplit = variant == FP8PA_VARIANT_PACKED_SPLIT;
+  const bool packed_req = variant == FP8PA_VARIANT_PACKED_HEADS;
+  if ((packed_req || psplit) && (vt || fused))
+    return fail(FP8PA_EUNSUPPORTED, "packed heads read V in HEADS_DMAJOR and take no fused append");
+  const bool packed = packed_req || (!vt && !fused && auto_packs(B, Hq, kd, workgroups, variant));
+  const int tv_launch = (fused || vt || f8 || packed || psplit) ? 0 : tile_variant();
+  if (tv_launch != tile_variant() && !psplit)
     lds = fp8pa::decode_lds_bytes(kd->head_dim, tv_launch, B, Hq / kd->num_kv_heads, kd->page_size);
   size_t vstage_off = 0;
   if (vt) {
@@ -320,7 +354,8 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   if (dry_run) return FP8PA_OK;
   const int D = kd->head_dim;
   const int G = Hq / kd->num_kv_heads;
-  const int W = plan.workgroups;
+  const int nw_pk = fp8pa::decode_waves(D, 0);
+  const int W = (packed && !packed_req) ? B * ((kd->num_kv_heads + nw_pk - 1) / nw_pk) : plan.workgroups;
   fp8pa::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.out = static_cast<uint16_t*>(out);
@@ -348,12 +383,18 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
   a.tile_variant = tv_launch;   // the fused, V-token-major and fp8 kernels exist in the default shapes
   a.vstage_off = (int32_t)vstage_off;
-  a.min_tiles = min_tiles(fp8pa::decode_waves(D, a.tile_variant));
-  a.seg_cost = seg_cost(fp8pa::decode_seg_cost(D, a.tile_variant));
+  // Packed splits: every wave reads every tile of a segment, so one tile per
+  // share suffices, and a tile carries NW heads, so a unit's fixed cost is
+  // NW times smaller in tiles.
+  const int nw = fp8pa::decode_waves(D, a.tile_variant);
+  a.min_tiles = min_tiles(psplit ? 1 : nw);
+  a.seg_cost = seg_cost(psplit ? fp8pa::decode_seg_cost(D, a.tile_variant) / nw
+                               : fp8pa::decode_seg_cost(D, a.tile_variant));
   a.epoch = g_epoch.fetch_add(1) + 1;
-  if (W > 1) {
-    const int64_t po = (int64_t)W * 2 * G * D * 4;
-    const int64_t pl = (int64_t)W * 2 * G * 4;
+  if (W > 1 && !packed) {
+    const int Gu = psplit ? G * nw : G;   // query heads per unit (as in the plan)
+    const int64_t po = (int64_t)W * 2 * Gu * D * 4;
+    const int64_t pl = (int64_t)W * 2 * Gu * 4;
     char* ws = static_cast<char*>(workspace);
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_lse = reinterpret_cast<float*>(ws + (po + 255) / 256 * 256);
@@ -368,12 +409,15 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
                  : f8  ? fp8pa::launch_decode_fp8q(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
                  : packed ? fp8pa::launch_decode_packed(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start,
                                                         g_ev_stop)
+                 : psplit ? fp8pa::launch_decode_pksplit(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start,
+                                                         g_ev_stop)
                        : fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
   if (f8) g_cnt.decode_fp8.fetch_add(1);
   else g_cnt.decode_mfma.fetch_add(1);
   if (W > 1 && !packed) g_cnt.decode_split.fetch_add(1);
   if (packed) g_cnt.decode_packed.fetch_add(1);
+  if (psplit) g_cnt.decode_psplit.fetch_add(1);
   if (fused) g_cnt.fused_append.fetch_add(1);
   if (vt) g_cnt.decode_vtok.fetch_add(1);
   g_cnt.decode_calls.fetch_add(1);
@@ -410,8 +454,11 @@ int fp8pa_append_decode(const void* k_new, const void* v_new, const void* q, voi
   // V in a token-major layout and the fp8 compute mode take the two launches
   // as well.
   const int span = (window > 0 && window < max_seq_len) ? window : max_seq_len;
+  // So do calls whose automatic plan takes packed heads (then the output
+  // equals the append followed by the same decode).
   if (span <= kFusedMaxSpan && vd && vd->layout == FP8PA_LAYOUT_HEADS_DMAJOR && variant != FP8PA_VARIANT_MFMA_FP8 &&
-      variant != FP8PA_VARIANT_PACKED_HEADS)
+      variant != FP8PA_VARIANT_PACKED_HEADS && variant != FP8PA_VARIANT_PACKED_SPLIT &&
+      !auto_packs(B, Hq, kd, workgroups, variant))
     return decode_impl(k_new, v_new, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
                        window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes, stream);
   // Every check of the call runs before the append launches.
@@ -564,6 +611,7 @@ int fp8pa_get_counters(fp8pa_counters* c) {
   c->decode_v_token_major = g_cnt.decode_vtok.load();
   c->decode_mfma_fp8 = g_cnt.decode_fp8.load();
   c->decode_packed_heads = g_cnt.decode_packed.load();
+  c->decode_packed_split = g_cnt.decode_psplit.load();
   return FP8PA_OK;
 }
 
@@ -587,6 +635,7 @@ int fp8pa_reset_counters(void) {
   g_cnt.decode_vtok = 0;
   g_cnt.decode_fp8 = 0;
   g_cnt.decode_packed = 0;
+  g_cnt.decode_psplit = 0;
   return FP8PA_OK;
 }
 

@@ -91,6 +91,22 @@ struct VRaw<1> { typedef u32x2 type; };
 template <>
 struct VRaw<2> { typedef u32x4 type; };
 
+// The probabilities of a PV operand as two bf16 octets, hi = bf16(v) and
+// lo = bf16(v - hi), so that the product carries v to about 16 significant
+// bits: a single bf16 rounding of p (relative error up to 2^-8) can move an
+// output whose terms cancel by more than 4e-3.
+__device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+    const float h0 = __builtin_bit_cast(float, h[j] << 16), h1 = __builtin_bit_cast(float, h[j] & 0xffff0000u);
+    l[j] = pack_bf16x2(v[2 * j] - h0, v[2 * j + 1] - h1);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // The D/32 E8M0 bytes of one position (one 32-dim group each), zero-extended
 // into a u32x4.
 template <int NG>
@@ -158,9 +174,15 @@ struct Tile {
 // w / ceil(Hkv/NW) and NW consecutive KV heads, one per wave, each wave
 // streaming every tile of its head; the waves read the same page rows
 // together and nothing is merged.
+// PS: packed heads with splits: a unit is (sequence, NW consecutive KV heads),
+// its NW*G query heads merged as one; wave v of a workgroup streams every
+// tile of its segment for KV head NW*g + v (the NW waves read the same page
+// rows together), so no wave combine is needed; shares, partials and merges
+// are those of the split kernel over these wider units.
 template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT, bool F8 = false,
-          bool PK = false>
+          bool PK = false, bool PS = false>
 __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a) {
+  static_assert(!(PS && (FUSED || PK || PF)), "packed splits: plain kernels without prefetch");
   static_assert(!(F8 && SK == 2), "E8M0 K scales vary inside one fp8 MFMA");
   static_assert(!(PK && (FUSED || F8 || PF)), "packed heads: plain bf16 kernels without prefetch");
   static_assert(!(FUSED && PF), "the fused append waits inside the non-prefetching tile loop");
@@ -188,10 +210,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   if (FUSED && threadIdx.x == 0) s_app = 0;   // ordered by the set-up barriers below
   const int n = lane & 15;      // MFMA column: query head of the group
   const int quad = lane >> 4;   // MFMA k/row quad
-  const int G = a.G, P = a.P, log2P = a.log2P, B = a.B, Hkv = a.Hkv;
+  // PS: G and Hkv count the query heads and units of a packed unit.
+  const int G = PS ? a.G * NW : a.G, P = a.P, log2P = a.log2P, B = a.B, Hkv = PS ? a.Hkv / NW : a.Hkv;
   int W = gridDim.x;
   const int w = blockIdx.x;
-  const bool col = n < G;
+  const bool col = n < (PS ? a.G : G);
 
   // ---- tiles per sequence and their prefix sums.
   auto tiles_of = [&](int L) {
@@ -216,7 +239,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   auto set_costs = [&](int tiles, int nonempty) {
     T = (int64_t)tiles * Hkv;
     U = (int64_t)nonempty * Hkv;
-    const bool unit_mode = T <= (int64_t)NW * U;
+    const bool unit_mode = T <= (int64_t)(PS ? 1 : NW) * U;
     TC = unit_mode ? 0 : 4;
     SC = unit_mode ? 1 : a.seg_cost;
     Ct = SC * U + TC * T;
@@ -450,8 +473,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
     const int32_t row_q = row_of(tq >> log2P);
     const int tpq = tq & (P - 1);
     const RowBases rk = row_bases(a.kg, row_k), rqk = row_bases(a.kg, row_q), rqv = row_bases(a.vg, row_q);
-    const uint8_t* ksc = a.kp + rqk.scale + g * a.kg.sc_head_stride;
-    const uint8_t* vsc = a.vp + rqv.scale + g * a.vg.sc_head_stride;
+    const int kvh = PS ? g * NW + wave : g;   // the lane's KV head
+    const uint8_t* ksc = a.kp + rqk.scale + kvh * a.kg.sc_head_stride;
+    const uint8_t* vsc = a.vp + rqv.scale + kvh * a.vg.sc_head_stride;
     if constexpr (SK == 0) {
       t.ks = ld_global<float>(ksc);
       t.vs = ld_global<float>(vsc);
@@ -525,7 +549,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa) {
           const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
-          const uint8_t* kf = a.kp + rk.scale + g * a.kg.sc_head_stride +
+          const uint8_t* kf = a.kp + rk.scale + kvh * a.kg.sc_head_stride +
                               tp * a.kg.sc_tok_stride;
           t.ke8[s][aa] = load_e8_row<NG>(kf);
         }
@@ -701,7 +725,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if constexpr (SK == 2) {
-        bf16x8 pop[NG];
+        bf16x8 pop[NG], pol[NG];
 #pragma unroll
         for (int gq = 0; gq < NG; ++gq) {
           float pv[8];
@@ -712,14 +736,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
             const float x = __builtin_amdgcn_ldexpf(p[s][i], ex);
             pv[i] = (p[s][i] == 0.0f) ? 0.0f : x;
           }
-          u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                      pack_bf16x2(pv[6], pv[7])};
-          pop[gq] = __builtin_bit_cast(bf16x8, pk);
+          split_bf16x8(pv, pop[gq], pol[gq]);
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const bf16x8 vop = e4m3x8_to_bf16x8(t.v[c][2 * s], t.v[c][2 * s + 1], 1.0f);
           acc[c] = mfma_16x16x32_bf16(vop, pop[c >> 1], acc[c]);
+          acc[c] = mfma_16x16x32_bf16(vop, pol[c >> 1], acc[c]);
         }
       } else {
         float pv[8];
@@ -731,13 +754,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
           if constexpr (SK == 0) pv[i] = p[s][i] * t.vs;
           if constexpr (SK == 1) pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * t.vst[s][i];
         }
-        u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                    pack_bf16x2(pv[6], pv[7])};
-        const bf16x8 pop = __builtin_bit_cast(bf16x8, pk);
+        bf16x8 pop, pol;
+        split_bf16x8(pv, pop, pol);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const bf16x8 vop = e4m3x8_to_bf16x8(t.v[c][2 * s], t.v[c][2 * s + 1], 1.0f);
           acc[c] = mfma_16x16x32_bf16(vop, pop, acc[c]);
+          acc[c] = mfma_16x16x32_bf16(vop, pol, acc[c]);
         }
       }
     }
@@ -836,11 +859,12 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
     start = (a.window > 0 && L > a.window) ? L - a.window : 0;
     tbeg = start & ~(TT - 1);
     btr = a.bt + (int64_t)b * a.bt_stride;
-    kpool = a.kp + (int64_t)g * a.kg.head_stride;
-    vpool = a.vp + (int64_t)g * a.vg.head_stride;
+    const int kvh = PS ? g * NW + wave : g;   // this wave's KV head
+    kpool = a.kp + (int64_t)kvh * a.kg.head_stride;
+    vpool = a.vp + (int64_t)kvh * a.vg.head_stride;
     {
       // Q operand (B of QK): lane (head n, quad) holds dims 64m + 16quad + 8h2 + i.
-      const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)g * G + (col ? n : 0)) * D;
+      const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G + (col ? n : 0)) * D;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -891,8 +915,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       }
       staged = false;
       // ---- tile loop: wave w takes tiles ca + w, ca + w + 4, ...
-      const int nmine = cb - ca > wave ? (cb - ca - wave + NW - 1) / NW : 0;
-      auto tile_pos = [&](int k) { return tbeg + (ca + wave + NW * k) * TT; };
+      // (PS: every wave takes every tile, for its own KV head.)
+      const int nmine = PS ? cb - ca : (cb - ca > wave ? (cb - ca - wave + NW - 1) / NW : 0);
+      auto tile_pos = [&](int k) { return PS ? tbeg + (ca + k) * TT : tbeg + (ca + wave + NW * k) * TT; };
       // Fused append: a segment that holds its unit's last tile holds the
       // only tile that reads the new token's page (position L - 1; groups
       // past L read a clamped page of that tile).  The last wave, which has
@@ -949,40 +974,50 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       s_l[wave][n] = lsum;
     }
     __syncthreads();   // also: every wave is past its last read of the page-row stage
+    // (PS: each wave's state is already its KV head's whole segment.)
     float M = kNegInf;
+    if constexpr (PS) {
+      M = m_run;
+    } else {
 #pragma unroll
-    for (int i = 0; i < NW; ++i) M = fmaxf(M, s_m[i][n]);
+      for (int i = 0; i < NW; ++i) M = fmaxf(M, s_m[i][n]);
+    }
     const float M_ref = (M == kNegInf) ? 0.0f : M;
     float Ltot = 0.0f;
+    if constexpr (PS) {
+      Ltot = lsum;
+    } else {
 #pragma unroll
-    for (int i = 0; i < NW; ++i) Ltot += s_l[i][n] * __builtin_amdgcn_exp2f(s_m[i][n] - M_ref);
-    {
-      const float f = __builtin_amdgcn_exp2f(m_run - M_ref);
+      for (int i = 0; i < NW; ++i) Ltot += s_l[i][n] * __builtin_amdgcn_exp2f(s_m[i][n] - M_ref);
+      {
+        const float f = __builtin_amdgcn_exp2f(m_run - M_ref);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] *= f;
-    }
-    // Pairwise tree: at each level the upper half of the remaining waves
-    // hands its accumulators to the lower half through LDS.
-#pragma unroll
-    for (int half = NW / 2; half >= 1; half >>= 1) {
-      if (wave >= half && wave < 2 * half && col) {
-        float* dst = s_o + ((wave - half) * G + n) * OS + 4 * quad;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
+        for (int c = 0; c < NC; ++c) acc[c] *= f;
       }
-      __syncthreads();
-      if (wave < half && col) {
-        const float* src = s_o + (wave * G + n) * OS + 4 * quad;
+      // Pairwise tree: at each level the upper half of the remaining waves
+      // hands its accumulators to the lower half through LDS.
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
+      for (int half = NW / 2; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half && col) {
+          float* dst = s_o + ((wave - half) * G + n) * OS + 4 * quad;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
+        }
+        __syncthreads();
+        if (wave < half && col) {
+          const float* src = s_o + (wave * G + n) * OS + 4 * quad;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
+        }
+        if (half > 1) __syncthreads();
       }
-      if (half > 1) __syncthreads();
     }
 
-    const int h = g * G + n;
+    const int h = PS ? kvh * a.G + n : g * G + n;   // the lane's query head
+    const int prow = PS ? wave * a.G + n : n;         // its row among the unit's G
     if (ta == 0 && tc == nb) {
       // The segment is the whole unit: o = acc / (sum + e^(sink - max)).
-      if (wave == 0 && col) {
+      if ((PS || wave == 0) && col) {
         float den = Ltot;
         if (a.sinks) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - M_ref);
         const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
@@ -1001,16 +1036,22 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       // or invalidate.
       const size_t pbase = ((size_t)w * 2 + slot) * G;
       const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
-      if (wave == 0 && col) {
+      if ((PS || wave == 0) && col) {
         // Lane (head n, quad) holds dims 16c + 4quad .. +3: one 16-byte store per c.
         const float inv = (Ltot > 0.0f) ? __builtin_amdgcn_rcpf(Ltot) : 0.0f;
-        const uint32_t row = (uint32_t)((pbase + n) * D * 4) + 16 * quad;
+        const uint32_t row = (uint32_t)((pbase + prow) * D * 4) + 16 * quad;
 #pragma unroll
         for (int c = 0; c < NC; ++c) st_coherent4(prs, row + 64 * c, acc[c] * inv);
         if (quad == 0)
-          __hip_atomic_store(a.part_lse + pbase + n,
+          __hip_atomic_store(a.part_lse + pbase + prow,
                              (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : M + __builtin_amdgcn_logf(Ltot),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if constexpr (PS) {
+        // Every wave wrote its rows: all stores complete before the slot is
+        // published (or merged by this workgroup).
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
       }
       const int w_a = wg_of_cost(tile_cost(b, g, 0)), w_b = wg_of_cost(tile_cost(b, g, nb - 1));
       if (w == w_b) {
@@ -1222,19 +1263,19 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
 }
 
 template <int D, int NS, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT = false, bool F8 = false,
-          bool PK = false>
+          bool PK = false, bool PS = false>
 hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(W), block(64 * NW);
   switch (sk) {
     case 0:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW, FUSED, VT, F8, PK>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
     case 1:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED, VT, F8, PK>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
     default:
       if constexpr (F8) return hipErrorNotSupported;
-      else hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED, VT, F8, PK>), grid, block, lds, st, e0, e1, 0, a);
+      else hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
   }
   return hipGetLastError();

@@ -1,0 +1,18 @@
+// The packed-heads decode kernels with splits: a unit is (sequence, group of
+// KV heads read by one workgroup together, one head per wave), and long spans
+// are cut into balanced shares and merged like the split kernel's units
+// (page "fp8 paged attention for MoE serving", pack_heads; the split grid of
+// section "Why it happens").  Default kernel shapes.
+#include "decode_kernel.h"
+
+namespace fp8pa {
+
+hipError_t launch_decode_pksplit(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                                 hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  auto l = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() {
+    return launch_d<DD, NS, PF, OCC, KNT, NW, false, false, false, false, true>(a, scale_kind, W, lds, st, e0, e1);
+  };
+  return k_whole_lines ? default_shape<true>(D, l) : default_shape<false>(D, l);
+}
+
+}  // namespace fp8pa

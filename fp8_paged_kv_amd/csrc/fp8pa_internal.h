@@ -124,6 +124,10 @@ hipError_t launch_decode_fp8q(const DecodeArgs& a, int D, int scale_kind, bool k
 // kernel shapes.
 hipError_t launch_decode_packed(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                                 hipStream_t st, hipEvent_t start, hipEvent_t stop);
+// Packed heads with splits: units of decode_waves(D, 0) KV heads (a.G and
+// a.Hkv are the per-KV-head values), default kernel shapes.
+hipError_t launch_decode_pksplit(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                                 hipStream_t st, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int B, int max_pages, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);

@@ -11,7 +11,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8pa.s
 
 LAYOUTS = {"heads": 0, "tokens": 1, "heads_dmajor": 2, "heads_d64": 3}
 SCALE_KINDS = {"page_head": 0, "token_head": 1, "e8m0_32": 2}
-VARIANTS = {"auto": 0, "mfma_bf16": 1, "mfma_fp8": 2, "packed_heads": 3}
+VARIANTS = {"auto": 0, "mfma_bf16": 1, "mfma_fp8": 2, "packed_heads": 3, "packed_split": 4}
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 
@@ -37,7 +37,8 @@ class Counters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("decode_calls", "decode_mfma_bf16", "decode_split", "merge_launches",
                                               "append_launches", "debug_launches", "errors", "fused_appends",
                                               "decode_v_token_major", "decode_mfma_fp8",
-                                              "decode_packed_heads")]
+                                              "decode_packed_heads",
+                                              "decode_packed_split")]
 
 
 _lib = None

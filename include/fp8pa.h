@@ -96,9 +96,24 @@ enum {
                                    serving", pack_heads): one workgroup per (sequence,
                                    group of KV heads), one KV head per wave, no split and
                                    no merge; arithmetic as MFMA_BF16.  For short or
-                                   windowed calls.  The grid is fixed (workgroups must be
-                                   0; the plan reports B * ceil(Hkv / 4), no workspace);
-                                   V in HEADS_DMAJOR, no fused append (else
+                                   windowed calls and for large batches.  The grid is fixed
+                                   (workgroups must be 0; the plan reports B * ceil(Hkv / 4),
+                                   no workspace); no fused append (fp8pa_append_decode runs
+                                   it after the append kernel); V in HEADS_DMAJOR (else
+                                   FP8PA_EUNSUPPORTED).  With AUTO and workgroups 0,
+                                   fp8pa_decode runs it instead of the split kernel when V
+                                   is in HEADS_DMAJOR, D <= 128 and the B * ceil(Hkv / 4) units alone
+                                   fill every resident workgroup slot of the device (the
+                                   plan still reports the split kernel's grid and
+                                   workspace, which then go unused; the counters record
+                                   what ran). */,
+  FP8PA_VARIANT_PACKED_SPLIT = 4  /* packed heads with splits: a unit is (sequence, 4
+                                   consecutive KV heads), one KV head per wave, so a
+                                   workgroup reads whole groups of heads of each page row
+                                   together; long spans are split over workgroups and
+                                   merged as in MFMA_BF16 (same arithmetic, another
+                                   summation order).  Needs Hkv % 4 == 0 and G <= 4; V in
+                                   HEADS_DMAJOR; no fused append (else
                                    FP8PA_EUNSUPPORTED); fp8pa_append_decode runs it
                                    after the append kernel. */
 };
@@ -287,6 +302,7 @@ typedef struct fp8pa_counters {
   int64_t decode_v_token_major; /* decode launches reading V in the HEADS or TOKENS layout */
   int64_t decode_mfma_fp8;  /* decode kernels launched, fp8 compute mode */
   int64_t decode_packed_heads; /* decode kernels launched, packed heads */
+  int64_t decode_packed_split;  /* decode kernels launched, packed heads with splits */
 } fp8pa_counters;
 
 int fp8pa_get_counters(fp8pa_counters* out);

@@ -33,7 +33,7 @@ def test_version_and_struct_sizes():
     assert b"gfx950" in ops.lib().fp8pa_version()
     assert ctypes.sizeof(ops.PoolDesc) == 48
     assert ctypes.sizeof(ops.Plan) == 24
-    assert ctypes.sizeof(ops.Counters) == 88
+    assert ctypes.sizeof(ops.Counters) == 96
 
 
 def kd(**kw):
@@ -94,7 +94,8 @@ def call_decode(k=None, v=None, **kw):
           v=vd(scale_kind="e8m0_32", row_bytes=16384 + 4096)), ops.EUNSUPPORTED),   # fp8 mode: fp32 scales only
     (dict(variant=2, v=vd(layout="tokens")), ops.EUNSUPPORTED),                    # fp8 mode: V d-major only
     (dict(variant=3, workgroups=4, ws=F, ws_bytes=1 << 20), ops.EUNSUPPORTED),      # packed heads fix the grid
-    (dict(variant=3, workgroups=0, v=vd(layout="heads")), ops.EUNSUPPORTED),        # packed heads: V d-major only
+    (dict(variant=4, workgroups=0, v=vd(layout="heads")), ops.EUNSUPPORTED),        # packed splits: V d-major only
+    (dict(variant=4, workgroups=0, Hq=64), ops.EUNSUPPORTED),                       # packed splits: G <= 4
     (dict(max_seq_len=-1), ops.EINVAL),
     (dict(workgroups=-2), ops.EINVAL),
     (dict(workgroups=4), ops.EWORKSPACE),                       # cut units need a workspace

@@ -65,6 +65,20 @@ def test_packed_heads_poison_never_leaks():
     assert_parity(got, oracle(p), "poison")
 
 
+@pytest.mark.skip(reason="packed heads with V in a token-major order took a GPU memory fault at head dim 256 "
+                         "(P 16, tokens) whose cause was not found; the combination is refused")
+@pytest.mark.parametrize("v_layout,D", [("tokens", 64), ("heads", 128), ("tokens", 256), ("heads", 512)])
+def test_packed_heads_token_major_v(v_layout, D):
+    say("packed heads V", v_layout, D)
+    p = make_problem(505, B=3, Hq=16, Hkv=4, D=D, P=16, lens=[300, 65, 7], v_layout=v_layout, sinks=True,
+                     sm_scale=1.0 if D >= 256 else None)
+    ops.reset_counters()
+    got = to_np(gpu_decode(p, variant="packed_heads"))
+    c = ops.counters()
+    assert c["decode_packed_heads"] == 1 and c["decode_v_token_major"] == 1
+    assert_parity(got, oracle(p), f"V {v_layout}")
+
+
 def test_packed_heads_refusals():
     p = make_problem(503, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[100, 30], v_layout="tokens")
     with pytest.raises(RuntimeError):
@@ -98,3 +112,48 @@ def test_packed_heads_append_decode():
     assert c["append_launches"] == 1 and c["fused_appends"] == 0 and c["decode_packed_heads"] == 1
     assert torch.equal(kb, ka) and torch.equal(vb, va)
     assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
+def test_auto_takes_packed_heads_when_units_fill_the_device():
+    """A batch whose (sequence, four KV heads) units fill every resident
+    workgroup slot: an automatic call runs packed heads (and the append +
+    decode call runs the append kernel, then that decode); V token-major or a
+    small batch keeps the split kernel."""
+    say("auto packed")
+    p = make_problem(506, B=320, Hq=32, Hkv=8, D=64, P=16, lens=list(range(1, 321)), sinks=True)
+    kd = desc_of(p.kdesc)
+    ops.reset_counters()
+    got = gpu_decode(p)
+    c = ops.counters()
+    assert c["decode_packed_heads"] == 1 and c["decode_split"] == 0
+    assert_parity(to_np(got), oracle(p), "auto packed")
+    # V token-major, or a small batch: the split kernel
+    pv = make_problem(506, B=320, Hq=32, Hkv=8, D=64, P=16, lens=list(range(1, 321)), v_layout="tokens")
+    ops.reset_counters()
+    assert_parity(to_np(gpu_decode(pv)), oracle(pv), "auto V tokens")
+    assert ops.counters()["decode_packed_heads"] == 0
+    ps = make_problem(507, B=3, Hq=32, Hkv=8, D=64, P=16, lens=[100, 30, 5])
+    ops.reset_counters()
+    gpu_decode(ps)
+    assert ops.counters()["decode_packed_heads"] == 0
+    # append + decode: two launches, the same output as append then decode
+    table = torch.from_numpy(np.ascontiguousarray(p.table)).to(DEV)
+    sl = torch.from_numpy(p.seq_lens.astype(np.int32)).to(DEV)
+    q = torch.from_numpy(np.ascontiguousarray(p.q)).to(torch.bfloat16).to(DEV)
+    sinks = torch.from_numpy(p.sinks).to(DEV)
+    g = torch.Generator().manual_seed(7)
+    kn = torch.randn((p.B, 8, 64), generator=g).to(torch.bfloat16).to(DEV)
+    vn = torch.randn((p.B, 8, 64), generator=g).to(torch.bfloat16).to(DEV)
+    ka, va = torch.from_numpy(p.k_pool).to(DEV), torch.from_numpy(p.v_pool).to(DEV)
+    kb, vb = ka.clone(), va.clone()
+    msl = int(p.seq_lens.max())
+    vd = desc_of(p.vdesc)
+    ops.append_quant(kn[:, None], vn[:, None], ka, va, kd, vd, table, (sl - 1).to(torch.int32))
+    want = ops.decode(q, ka, va, kd, vd, table, sl, msl, sinks=sinks, sm_scale=p.sm_scale)
+    ops.reset_counters()
+    out = ops.append_decode(q, kn, vn, kb, vb, kd, vd, table, sl, msl, sinks=sinks, sm_scale=p.sm_scale)
+    torch.cuda.synchronize()
+    c = ops.counters()
+    assert c["append_launches"] == 1 and c["fused_appends"] == 0 and c["decode_packed_heads"] == 1
+    assert torch.equal(kb, ka) and torch.equal(vb, va)
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
