@@ -276,7 +276,9 @@ def run_sweep(args, torch, ops, workloads, hip):
     gen = torch.Generator(device="cuda:0")
     print("B,L,us_per_call_median,kv_gbps,pct_peak", file=sys.stderr)
     for L in (128, 1024, 4096, 16384, 32000, 131072):
-        for B in (1, 8, 32, 128):
+        for B in (1, 8, 32, 128, 256, 1024):
+            if B > 128 and L > 4096:
+                continue
             pages = -(-L // P)
             rows = B * pages
             if rows * rb * 2 > 60e9:
@@ -304,11 +306,13 @@ def run_sweep(args, torch, ops, workloads, hip):
             R = max(1, min(8, int(np.ceil(2 * 2 ** 30 / (2 * rows * rb)))))
             copies = [[layer]] + [[clone_layer(layer, torch)] for _ in range(R - 1)]
             steps = max(20, min(args.steps, 200))
-            wall, step_ms, kern_ms, _ = time_layers(copies, steps, 5, hip, ops, workloads, torch, args.workgroups)
+            wall, step_ms, kern_ms, _ = time_layers(copies, steps, 5, hip, ops, workloads, torch, args.workgroups,
+                                                    args.variant)
             med = statistics.median(step_ms) * 1e3
             gbps = nbytes / (kern_ms[0] * 1e-3) / 1e9
             print(f"{B},{L},{med:.2f},{gbps:.1f},{100 * gbps / PEAK_GBPS:.1f}", file=sys.stderr, flush=True)
-            print(json.dumps({"sweep_point": {"B": B, "L": L, "us_per_call_median": round(med, 2),
+            print(json.dumps({"sweep_point": {"B": B, "L": L, "variant": args.variant,
+                                              "us_per_call_median": round(med, 2),
                                               "kernel_gbps": round(gbps, 1),
                                               "pct_peak": round(100 * gbps / PEAK_GBPS, 1)}}), flush=True)
             del copies, layer, k_pool, v_pool
