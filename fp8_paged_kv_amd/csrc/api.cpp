@@ -175,11 +175,16 @@ int seg_cost(int shape_default) {
   return cached >= 0 ? cached : shape_default;
 }
 
-// Compute units of the current device (0 when no device can be queried).
+// Compute units of the current device (0 when no device can be queried),
+// remembered per thread for the last device asked about.
 int device_cus() {
+  thread_local int last_dev = -1, last_n = 0;
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev == last_dev) return last_n;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  last_dev = dev;
+  last_n = n;
   return n;
 }
 

@@ -144,9 +144,10 @@ def decode(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window
         out = torch.empty_like(q)
     _need(out, "out", torch.bfloat16)
     scale = D ** -0.5 if sm_scale is None else float(sm_scale)
-    plan = decode_plan(B, Hq, kd, max_seq_len, window, workgroups, variant)
-    if plan.workspace_bytes > 0 and workspace is None:
-        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is None:   # (a given workspace is checked by the library)
+        plan = decode_plan(B, Hq, kd, max_seq_len, window, workgroups, variant)
+        if plan.workspace_bytes > 0:
+            workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8pa_decode(_ptr(q), _ptr(out), _ptr(k_pool), _ptr(v_pool), ctypes.byref(kd), ctypes.byref(vd),
                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, Hq, window, _ptr(sinks),
@@ -177,9 +178,10 @@ def append_decode(q, k_new, v_new, k_pool, v_pool, kd, vd, block_table, seq_lens
         out = torch.empty_like(q)
     _need(out, "out", torch.bfloat16)
     scale = D ** -0.5 if sm_scale is None else float(sm_scale)
-    plan = decode_plan(B, Hq, kd, max_seq_len, window, workgroups, variant)
-    if plan.workspace_bytes > 0 and workspace is None:
-        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is None:   # (a given workspace is checked by the library)
+        plan = decode_plan(B, Hq, kd, max_seq_len, window, workgroups, variant)
+        if plan.workspace_bytes > 0:
+            workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8pa_append_decode(_ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), _ptr(k_pool), _ptr(v_pool),
                                      ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table), block_table.shape[1],
