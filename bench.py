@@ -446,7 +446,7 @@ def run_graph(args, wl, torch, np, ops, workloads, hip):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; the decode path shards by sequence or KV head with no "
+        print("bench.py: this library runs on one GPU only; the decode path shards by sequence or KV head with no "
               "exchange, which needs no multi-GPU run to measure (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import numpy as np

@@ -38,7 +38,7 @@ extern "C" {
 enum {
   FP8PA_OK = 0,
   FP8PA_EINVAL = -1,        /* a bad argument (null, misaligned, out of range) */
-  FP8PA_EUNSUPPORTED = -2,  /* valid request this build does not implement     */
+  FP8PA_EUNSUPPORTED = -2,  /* valid request this library does not implement   */
   FP8PA_EWORKSPACE = -3,    /* workspace missing or smaller than required      */
   FP8PA_EHIP = -4           /* a HIP launch reported an error                  */
 };
