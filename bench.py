@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--workgroups", type=int, default=0, help="0: one resident generation (auto)")
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough for 2 GiB)")
     ap.add_argument("--sweep", action="store_true", help="batch x context sweep (CSV on stderr, JSON per point)")
+    ap.add_argument("--sweep-points", default="", help="--sweep: only these BxL points, e.g. 256x1024,1024x256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", default="auto", choices=["auto", "mfma_bf16", "mfma_fp8", "packed_heads", "packed_split"],
                     help="decode variant (mfma_fp8: the fp8 compute mode, q rounded to E4M3; packed_heads: one "
@@ -274,10 +275,13 @@ def run_sweep(args, torch, ops, workloads, hip):
     D, Hq, Hkv, P = 128, 32, 8, 16
     rb = 16416
     gen = torch.Generator(device="cuda:0")
+    only = {tuple(int(x) for x in pt.split("x")) for pt in args.sweep_points.split(",") if pt}
     print("B,L,us_per_call_median,kv_gbps,pct_peak", file=sys.stderr)
     for L in (128, 1024, 4096, 16384, 32000, 131072):
         for B in (1, 8, 32, 128, 256, 1024):
             if B > 128 and L > 4096:
+                continue
+            if only and (B, L) not in only:
                 continue
             pages = -(-L // P)
             rows = B * pages
