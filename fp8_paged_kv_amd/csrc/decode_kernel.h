@@ -54,7 +54,8 @@
 // exactly the probabilities it must supply to the PV MFMA.
 //
 // PV on MFMA 16x16x32 bf16: O^T = V^T P^T with A = V^T (16 head dims x 32
-// positions) and B = P^T.  V stored d-major per (page, head) lets lane
+// positions) and B = P^T, the probabilities as a hi/lo pair of bf16 operands
+// in two MFMAs (split_bf16x8).  V stored d-major per (page, head) lets lane
 // (dim l%16, quad l/16) load the 8*NS positions it needs as one 16-byte (or
 // 8-byte) load straight from HBM.  V stored token-major (the page's "heads"
 // and "tokens" orders, VT) is loaded as whole 16-byte pieces of position rows,
