@@ -220,3 +220,21 @@ def test_merge_and_debug_refuse_before_launch():
     assert ops.lib().fp8pa_debug_dequant(None, P(F), 0, 16, P(F), None) == ops.EINVAL
     c = ops.counters()
     assert c["merge_launches"] == 0 and c["debug_launches"] == 0 and c["errors"] == 5
+
+
+def test_plan_of_the_variants():
+    """Host-only plans: packed heads fix the grid at B * ceil(Hkv / 4) with no
+    workspace; packed splits need partials for 4 * G query heads per unit;
+    the fp8 mode plans like the default; the plan reports the variant."""
+    k = kd()                                   # Hkv 8, D 128
+    pk = ops.decode_plan(5, 32, k, 8192, variant="packed_heads")
+    assert pk.workgroups == 10 and pk.workspace_bytes == 0 and pk.variant == ops.VARIANTS["packed_heads"]
+    k6 = kd(num_kv_heads=6, row_bytes=12320)
+    assert ops.decode_plan(3, 24, k6, 8192, variant="packed_heads").workgroups == 6
+    ps = ops.decode_plan(4, 32, k, 8192, workgroups=7, variant="packed_split")
+    df = ops.decode_plan(4, 32, k, 8192, workgroups=7)
+    assert ps.variant == ops.VARIANTS["packed_split"] and ps.workgroups == 7
+    assert ps.workspace_bytes >= 7 * 2 * 16 * (128 + 1) * 4 > df.workspace_bytes
+    f8 = ops.decode_plan(4, 32, k, 8192, workgroups=7, variant="mfma_fp8")
+    assert f8.variant == ops.VARIANTS["mfma_fp8"] and f8.workspace_bytes == df.workspace_bytes
+    assert df.variant == ops.VARIANTS["mfma_bf16"]
