@@ -98,12 +98,19 @@ def pool_desc(num_kv_heads, head_dim, page_size, layout, scale_kind, row_bytes, 
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # (ctypes turns a Python int into the c_void_p argument itself.)
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:   # the current stream's handle without building a Stream object
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _need(t, name, dtype=None, device=True):
