@@ -113,3 +113,28 @@ def test_workload_full_size(wl):
         for b, g in pairs:
             err, frac = check_panel(wl, layer, out_np, b, g)
             say(f"  {layer.name} b={b} L={int(layer.lens[b])} g={g}: max err {err:.2e} ({frac:.2f} of bound)")
+
+
+@pytest.fixture(scope="module")
+def llama_layer():
+    return workloads.build_workload(configs.LLAMA3_8B)[0]
+
+
+@pytest.mark.parametrize("variant", ["packed_split", "packed_heads"])
+def test_llama_full_size_other_variants(llama_layer, variant):
+    """The Llama-3-8B-shaped call at full size through the packed variants:
+    sampled panels (the longest sequence among them) within the oracle bound,
+    and the same output as the default variant up to summation order."""
+    say("workload variant", variant)
+    layer = llama_layer
+    out = workloads.decode_layer(layer, variant=variant)
+    ref = workloads.decode_layer(layer)
+    torch.cuda.synchronize()
+    out_np = to_np(out)
+    assert np.all(np.isfinite(out_np))
+    rng = np.random.default_rng(17)
+    for b, g in [(int(np.argmax(layer.lens)), int(rng.integers(layer.Hkv))),
+                 (int(rng.integers(len(layer.lens))), int(rng.integers(layer.Hkv)))]:
+        err, frac = check_panel(configs.LLAMA3_8B, layer, out_np, b, g)
+        say(f"  {variant} b={b} g={g}: max err {err:.2e} ({frac:.2f} of bound)")
+    assert float((out.float() - ref.float()).abs().max()) < 2e-2
