@@ -876,7 +876,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       if constexpr (F8) {
         // The row's amax (the four quads of a head column hold its dims),
         // its scale fp32(amax / 448) (1 for a zero row), and the codes
-        // e4m3(q / scale), byte i of a dword pair = dim i of the operand.
+        // e4m3(fp32(q * fp32(1 / scale))), byte i of a dword pair = dim i of
+        // the operand.
         float am = 0.0f;
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
@@ -888,14 +889,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
         am = fmaxf(am, __shfl_xor(am, 16));
         am = fmaxf(am, __shfl_xor(am, 32));
         qsc = am > 0.0f ? am / 448.0f : 1.0f;
+        const float rq = 1.0f / qsc;   // one division; the codes take a product each
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
           const u32x4 v = __builtin_bit_cast(u32x4, qop[i]);
           uint64_t c = 0;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)v[j]) / qsc) << (16 * j);
-            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)(v[j] >> 16)) / qsc) << (16 * j + 8);
+            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)v[j]) * rq) << (16 * j);
+            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)(v[j] >> 16)) * rq) << (16 * j + 8);
           }
           qop8[i] = c;
         }

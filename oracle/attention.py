@@ -55,14 +55,19 @@ def fp8_query(q):
 
     The fp8 path of page "fp8 paged attention for MoE serving" (section "Two
     compute paths") adds one E4M3 rounding of q.  Reading: each (sequence,
-    query head) row of q is quantized like a KV block, with one fp32 scale
-    fp32(amax / 448) (1 for an all-zero row) and codes e4m3(fp32(q / scale)),
-    and the mode attends with code x scale.  The fp8-mode output is then
-    ``decode_ref(fp8_query(q), ...)``."""
+    query head) row of q gets one fp32 scale fp32(amax / 448) (1 for an
+    all-zero row), like a KV block, and codes e4m3(fp32(q * fp32(1 / scale)))
+    (the page does not say how q is scaled; a product by the rounded
+    reciprocal is the plainest per-element step), and the mode attends with
+    code x scale.  The fp8-mode output is then ``decode_ref(fp8_query(q),
+    ...)``."""
     q = np.asarray(q, dtype=np.float64)
     out = np.empty_like(q)
     for idx in np.ndindex(q.shape[:-1]):
-        codes, scale = fp8mod.quantize_fp32_block(q[idx])
+        row = q[idx]
+        scale = float(fp8mod.fp32_scale_from_amax(np.abs(row).max() if row.size else 0.0))
+        inv = float(fp8mod.to_fp32(1.0 / scale))
+        codes = fp8mod.encode_e4m3(fp8mod.to_fp32(row * inv))
         out[idx] = fp8mod.dequant(codes, scale)
     return out
 
