@@ -34,6 +34,9 @@ Scale footer (byte offset from the scale block's start):
   "token_head" fp32 per (token, head): 4*(h*P + t), or 4*(t*H + h) for "tokens"
   "e8m0_32"    one E8M0 byte per (token, head, 32 dims along D):
                (h*P + t)*(D/32) + d//32, or (t*H + h)*(D/32) + d//32 for "tokens"
+  "f32_g<S>"   fp32 per (token, head, S dims along D), S in 32, 64, 128, 256 (the
+               page's sub-row key groups, k_groups = D/S):
+               4*((h*P + t)*(D/S) + d//S), or 4*((t*H + h)*(D/S) + d//S) for "tokens"
 """
 from dataclasses import dataclass, replace
 from typing import Optional
@@ -43,7 +46,8 @@ import numpy as np
 from . import fp8
 
 LAYOUTS = ("heads", "tokens", "heads_d64", "heads_dmajor")
-SCALE_KINDS = ("page_head", "token_head", "e8m0_32")
+GROUP_KINDS = {"f32_g32": 32, "f32_g64": 64, "f32_g128": 128, "f32_g256": 256}
+SCALE_KINDS = ("page_head", "token_head", "e8m0_32") + tuple(GROUP_KINDS)
 
 
 @dataclass(frozen=True)
@@ -65,6 +69,8 @@ class PoolDesc:
     @property
     def scale_bytes(self) -> int:
         H, P, D = self.num_kv_heads, self.page_size, self.head_dim
+        if self.scale_kind in GROUP_KINDS:
+            return 4 * H * P * (D // GROUP_KINDS[self.scale_kind])
         return {"page_head": 4 * H, "token_head": 4 * H * P, "e8m0_32": H * P * D // 32}[self.scale_kind]
 
     @property
@@ -91,6 +97,8 @@ class PoolDesc:
                 assert end <= self.row_bytes
         if self.scale_kind == "e8m0_32":
             assert self.head_dim % 32 == 0
+        if self.scale_kind in GROUP_KINDS:
+            assert self.head_dim % GROUP_KINDS[self.scale_kind] == 0
         if self.layout == "heads_d64":
             assert self.head_dim % 64 == 0
         if self.layout == "heads_dmajor":
@@ -141,6 +149,8 @@ def scale_rel(desc: PoolDesc, h, t=0, g=0):
         return 4 * h
     if desc.scale_kind == "token_head":
         return 4 * slot
+    if desc.scale_kind in GROUP_KINDS:
+        return 4 * (slot * (D // GROUP_KINDS[desc.scale_kind]) + g)
     return slot * (D // 32) + g
 
 
@@ -171,6 +181,12 @@ def _page_scales(pool, desc, rows, h):
         offs = np.array([scale_rel(desc, h, t) for t in range(P)])
         idx = base[:, None, None] + offs[None, :, None] + np.arange(4)[None, None, :]
         return pool[idx].copy().view(np.float32)[..., 0].astype(np.float64)[:, :, None]  # [n,P,1]
+    if desc.scale_kind in GROUP_KINDS:
+        S = GROUP_KINDS[desc.scale_kind]
+        offs = np.array([[scale_rel(desc, h, t, g) for g in range(D // S)] for t in range(P)])
+        idx = base[:, None, None, None] + offs[None, :, :, None] + np.arange(4)[None, None, None, :]
+        s = pool[idx].copy().view(np.float32)[..., 0].astype(np.float64)               # [n,P,D/S]
+        return np.repeat(s, S, axis=-1)                                                # [n,P,D]
     offs = np.array([[scale_rel(desc, h, t, g) for g in range(D // 32)] for t in range(P)])
     u = pool[base[:, None, None] + offs[None]]                                         # [n,P,D/32]
     return np.repeat(fp8.E8M0_TABLE[u], 32, axis=-1)                                   # [n,P,D]
@@ -220,6 +236,8 @@ def append_ref(pool, desc: PoolDesc, block_table, positions, x_new, counts=None)
     sub-row groups, and a one-launch T=1 append ("Supported scope").  Readings:
     * "token_head": stateless, one fp32 scale per (token, head).
     * "e8m0_32": stateless, one E8M0 scale per (token, head, 32 dims).
+    * "f32_g<S>": stateless, one fp32 scale per (token, head, S dims), each
+      group quantized like a "token_head" row of S dims.
     * "page_head": the page's scale only grows.  If this call writes the page's
       first slot, the old scale counts as 0 and there are no old tokens; else the
       old tokens are slots [0, first written slot).  s_new = max(s_old,
@@ -250,6 +268,14 @@ def append_ref(pool, desc: PoolDesc, block_table, positions, x_new, counts=None)
                         c, s = fp8.quantize_fp32_block(x[i])
                         _write_codes(pool, desc, row, h, slot0 + i, c[None])
                         _write_f32(pool, row_scale_base(desc, row) + scale_rel(desc, h, slot0 + i), s)
+                elif desc.scale_kind in GROUP_KINDS:
+                    S = GROUP_KINDS[desc.scale_kind]
+                    for i in range(n):
+                        for g in range(D // S):
+                            c, s = fp8.quantize_fp32_block(x[i, g * S:(g + 1) * S])
+                            tt, dd = np.array([[slot0 + i]]), (g * S + np.arange(S))[None, :]
+                            pool[row_code_base(desc, row) + code_offset(desc, h, tt, dd)] = c[None]
+                            _write_f32(pool, row_scale_base(desc, row) + scale_rel(desc, h, slot0 + i, g), s)
                 elif desc.scale_kind == "e8m0_32":
                     c, u = fp8.quantize_e8m0_g32(x)
                     _write_codes(pool, desc, row, h, slot0, c)
@@ -313,6 +339,16 @@ def pack_sequences(pool, desc: PoolDesc, block_table, xs, heads=None):
                 offs = np.array([scale_rel(desc, h, t) for t in range(P)])
                 idx = row_scale_base(desc, rows)[:, None, None] + offs[None, :, None] + np.arange(4)[None, None, :]
                 vals = s.astype(np.float32).view(np.uint8).reshape(n_pages, P, 4)
+                pool[idx[valid]] = vals[valid]
+            elif desc.scale_kind in GROUP_KINDS:
+                S = GROUP_KINDS[desc.scale_kind]
+                xg = xp.reshape(n_pages, P, D // S, S)
+                s = fp8.fp32_scale_from_amax(np.abs(xg).max(axis=3))                  # [n, P, D/S]
+                codes = fp8.encode_e4m3(fp8.to_fp32(xg / s[..., None])).reshape(n_pages, P, D)
+                offs = np.array([[scale_rel(desc, h, t, g) for g in range(D // S)] for t in range(P)])
+                idx = (row_scale_base(desc, rows)[:, None, None, None] + offs[None, :, :, None] +
+                       np.arange(4)[None, None, None, :])
+                vals = s.astype(np.float32).view(np.uint8).reshape(n_pages, P, D // S, 4)
                 pool[idx[valid]] = vals[valid]
             else:
                 codes, u = fp8.quantize_e8m0_g32(xp)                                  # u [n, P, D/32]

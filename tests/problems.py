@@ -42,12 +42,17 @@ class Problem:
 
 def make_problem(seed, B, Hq, Hkv, D, P, lens, scale_kind="page_head", k_layout="heads_d64",
                  v_layout="heads_dmajor", window=0, sinks=False, sm_scale=None, row_pad=0,
-                 poison=True, cfg=99, spare_frac=0.1, k_gain=1.0, align64=False):
+                 poison=True, cfg=99, spare_frac=0.1, k_gain=1.0, align64=False, v_scale_kind=None):
+    """A seeded decode problem.  V takes the K scale kind, except that sub-row
+    fp32 key groups ("f32_g<S>") pair with per-(token, head) V scales unless
+    ``v_scale_kind`` says otherwise."""
     lens = np.asarray(lens, dtype=np.int32)
     assert len(lens) == B
+    if v_scale_kind is None:
+        v_scale_kind = "token_head" if scale_kind in opool.GROUP_KINDS else scale_kind
     table, rows = inputs.block_table(seed, cfg, lens, P, spare_frac=spare_frac)
     kd = opool.natural_desc(Hkv, D, P, k_layout, scale_kind, rows)
-    vd = opool.natural_desc(Hkv, D, P, v_layout, scale_kind, rows)
+    vd = opool.natural_desc(Hkv, D, P, v_layout, v_scale_kind, rows)
     from dataclasses import replace
     kd = replace(kd, row_bytes=round16(kd.row_bytes) + row_pad, align64=align64)
     vd = replace(vd, row_bytes=round16(vd.row_bytes) + row_pad, align64=align64)
