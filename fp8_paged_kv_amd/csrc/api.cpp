@@ -46,12 +46,17 @@ int ilog2(int64_t v) {
   return r;
 }
 
+// Dims per scale of the fp32 sub-row kinds (FP8PA_SCALE_F32_G32..G256).
+int group_dims(int kind) { return 32 << (kind - FP8PA_SCALE_F32_G32); }
+bool grouped(int kind) { return kind >= FP8PA_SCALE_F32_G32 && kind <= FP8PA_SCALE_F32_G256; }
+
 int64_t scale_bytes(const fp8pa_pool_desc& d) {
   const int64_t H = d.num_kv_heads, P = d.page_size, D = d.head_dim;
   switch (d.scale_kind) {
     case FP8PA_SCALE_F32_PAGE_HEAD: return 4 * H;
     case FP8PA_SCALE_F32_TOKEN_HEAD: return 4 * H * P;
-    default: return H * P * D / 32;
+    case FP8PA_SCALE_E8M0_G32: return H * P * D / 32;
+    default: return 4 * H * P * (D / group_dims(d.scale_kind));
   }
 }
 
@@ -70,8 +75,11 @@ int check_desc(const fp8pa_pool_desc* d, const char* name) {
     return fail(FP8PA_EUNSUPPORTED, "%s: page_size %d is not a power of two in [16,1024]", name, d->page_size);
   if (d->layout < FP8PA_LAYOUT_HEADS || d->layout > FP8PA_LAYOUT_HEADS_D64)
     return fail(FP8PA_EINVAL, "%s: unknown layout %d", name, d->layout);
-  if (d->scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || d->scale_kind > FP8PA_SCALE_E8M0_G32)
+  if (d->scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || d->scale_kind > FP8PA_SCALE_F32_G256)
     return fail(FP8PA_EINVAL, "%s: unknown scale_kind %d", name, d->scale_kind);
+  if (grouped(d->scale_kind) && group_dims(d->scale_kind) > d->head_dim)
+    return fail(FP8PA_EINVAL, "%s: %d dims per scale exceed head_dim %d", name, group_dims(d->scale_kind),
+                d->head_dim);
   const int64_t payload = (int64_t)d->page_size * d->num_kv_heads * d->head_dim;
   const int64_t foot = footer_offset(*d);
   if (d->row_bytes <= 0 || d->row_bytes % 16)
@@ -134,10 +142,17 @@ fp8pa::PoolGeom geometry(const fp8pa_pool_desc& d) {
       g.sc_head_stride = tok ? 4 : 4 * P;
       g.sc_tok_stride = tok ? 4 * H : 4;
       break;
-    default:
+    case FP8PA_SCALE_E8M0_G32:
       g.sc_head_stride = tok ? D / 32 : P * (D / 32);
       g.sc_tok_stride = tok ? H * (D / 32) : D / 32;
       break;
+    default: {
+      const int ng = D / group_dims(d.scale_kind);
+      g.sc_head_stride = tok ? 4 * ng : 4 * P * ng;
+      g.sc_tok_stride = tok ? 4 * H * ng : 4 * ng;
+      g.sc_gshift = ilog2(group_dims(d.scale_kind));
+      break;
+    }
   }
   return g;
 }
@@ -300,14 +315,22 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   if (int rc = check_desc(vd, "vd")) return rc;
   if (kd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
     return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS_D64, HEADS or TOKENS layout");
+  if (grouped(vd->scale_kind))
+    return fail(FP8PA_EUNSUPPORTED, "vd: decode reads fp32 sub-row scales for K only");
   if (vd->layout == FP8PA_LAYOUT_HEADS_D64)
     return fail(FP8PA_EUNSUPPORTED, "vd: decode reads V in the HEADS_DMAJOR, HEADS or TOKENS layout");
   // V in a token-major layout is staged through LDS (default kernel shapes).
   const bool vt = vd->layout == FP8PA_LAYOUT_HEADS || vd->layout == FP8PA_LAYOUT_TOKENS;
   if (vt && fused) return fail(FP8PA_EUNSUPPORTED, "the one-launch append reads V in the HEADS_DMAJOR layout");
   const bool f8 = variant == FP8PA_VARIANT_MFMA_FP8;
-  if (f8 && (kd->scale_kind == FP8PA_SCALE_E8M0_G32 || vt || fused))
-    return fail(FP8PA_EUNSUPPORTED, "the fp8 compute mode takes fp32 scales, V in HEADS_DMAJOR and no fused append");
+  if (f8 && (kd->scale_kind == FP8PA_SCALE_E8M0_G32 || grouped(kd->scale_kind) || vt || fused))
+    return fail(FP8PA_EUNSUPPORTED,
+                "the fp8 compute mode takes fp32 page or token scales, V in HEADS_DMAJOR and no fused append");
+  // fp32 sub-row K scales: K pieces are scaled before the MFMA (plain,
+  // token-major-V and split kernels only).
+  const bool kgroups = grouped(kd->scale_kind);
+  if (kgroups && (fused || variant == FP8PA_VARIANT_PACKED_HEADS || variant == FP8PA_VARIANT_PACKED_SPLIT))
+    return fail(FP8PA_EUNSUPPORTED, "sub-row K scales take the split kernels and no fused append");
   // Packed heads: requested, or taken automatically when the units fill the
   // device (V d-major, no fused append; the plan's workspace then goes
   // unused).
@@ -315,7 +338,7 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   const bool packed_req = variant == FP8PA_VARIANT_PACKED_HEADS;
   if ((packed_req || psplit) && (vt || fused))
     return fail(FP8PA_EUNSUPPORTED, "packed heads read V in HEADS_DMAJOR and take no fused append");
-  const bool packed = packed_req || (!vt && !fused && auto_packs(B, Hq, kd, workgroups, variant));
+  const bool packed = packed_req || (!vt && !fused && !kgroups && auto_packs(B, Hq, kd, workgroups, variant));
   const int tv_launch = (fused || vt || f8 || packed || psplit) ? 0 : tile_variant();
   if (tv_launch != tile_variant() && !psplit)
     lds = fp8pa::decode_lds_bytes(kd->head_dim, tv_launch, B, Hq / kd->num_kv_heads, kd->page_size);
@@ -328,8 +351,10 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
                   B, kd->head_dim, lds);
   }
   if (vd->num_kv_heads != kd->num_kv_heads || vd->head_dim != kd->head_dim || vd->page_size != kd->page_size ||
-      vd->scale_kind != kd->scale_kind)
-    return fail(FP8PA_EUNSUPPORTED, "K and V pools must share num_kv_heads, head_dim, page_size and scale_kind");
+      (vd->scale_kind != kd->scale_kind && !(kgroups && vd->scale_kind == FP8PA_SCALE_F32_TOKEN_HEAD)))
+    return fail(FP8PA_EUNSUPPORTED,
+                "K and V pools must share num_kv_heads, head_dim, page_size and scale_kind (or K in fp32 "
+                "sub-row scales with V in F32_TOKEN_HEAD)");
   if (B == 0) {
     if (!dry_run) {
       ok();
@@ -462,6 +487,7 @@ int fp8pa_append_decode(const void* k_new, const void* v_new, const void* q, voi
   // So do calls whose automatic plan takes packed heads (then the output
   // equals the append followed by the same decode).
   if (span <= kFusedMaxSpan && vd && vd->layout == FP8PA_LAYOUT_HEADS_DMAJOR && variant != FP8PA_VARIANT_MFMA_FP8 &&
+      !(kd && grouped(kd->scale_kind)) &&
       variant != FP8PA_VARIANT_PACKED_HEADS && variant != FP8PA_VARIANT_PACKED_SPLIT &&
       !auto_packs(B, Hq, kd, workgroups, variant))
     return decode_impl(k_new, v_new, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
@@ -574,7 +600,7 @@ int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, ui
 int fp8pa_debug_dequant(const uint8_t* codes, const void* scales, int scale_kind, int n, float* out,
                         void* stream) {
   if (n < 0) return fail(FP8PA_EINVAL, "n must be >= 0");
-  if (scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || scale_kind > FP8PA_SCALE_E8M0_G32)
+  if (scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || scale_kind > FP8PA_SCALE_F32_G256)
     return fail(FP8PA_EINVAL, "unknown scale_kind %d", scale_kind);
   if (n == 0) {
     ok();

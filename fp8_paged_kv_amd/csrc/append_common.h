@@ -9,6 +9,7 @@
 // to +-448, rounded to the nearest E4M3 with ties to even.
 // Scales:
 //  * fp32 per (token, head):  s = fp32(amax / 448), 1 if amax = 0.
+//  * fp32 per (token, head, S dims): each group of S dims as a per-token row.
 //  * E8M0 per 32 dims:        the smallest 2**k with amax <= 448 * 2**k,
 //                             stored as k + 127 clamped to [0, 254].
 //  * fp32 per (page, head):   the page scale only grows.  s_old counts as 0
@@ -87,6 +88,18 @@ __device__ inline void append_token_wave(uint8_t* pool, const PoolGeom& gm, int 
     const float s = am > 0.0f ? am / 448.0f : 1.0f;
     for (int d = lane; d < D; d += 64) rowp[code_at(gm, slot, d)] = (uint8_t)f32_to_e4m3(bf16_to_f32(x[d]) / s);
     if (lane == 0) *reinterpret_cast<float*>(foot + (int64_t)slot * gm.sc_tok_stride) = s;
+  } else if (kind >= 3) {
+    const int S = 1 << gm.sc_gshift;
+    for (int g0 = 0; g0 < D; g0 += S) {
+      float am = 0.0f;
+      for (int d = g0 + lane; d < g0 + S; d += 64) am = fmaxf(am, fabsf(bf16_to_f32(x[d])));
+      am = wave_max(am);
+      const float s = am > 0.0f ? am / 448.0f : 1.0f;
+      for (int d = g0 + lane; d < g0 + S; d += 64)
+        rowp[code_at(gm, slot, d)] = (uint8_t)f32_to_e4m3(bf16_to_f32(x[d]) / s);
+      if (lane == 0)
+        *reinterpret_cast<float*>(foot + (int64_t)slot * gm.sc_tok_stride + 4 * (g0 >> gm.sc_gshift)) = s;
+    }
   } else {
     // lanes 0-31 / 32-63 form the 32-dim groups
     for (int d0 = 0; d0 < D; d0 += 64) {

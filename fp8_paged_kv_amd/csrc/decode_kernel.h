@@ -68,6 +68,10 @@
 // E8M0 per 32 dims: the K scale is applied inside the E4M3 -> bf16 conversion
 // (a power of two, exact); the V scale varies along the dims, so the PV B
 // operand is built once per 32-dim group with p x 2**(e - 127).
+// fp32 per (token, head, S dims) for K (sub-row key scales, SK = 3): each
+// lane's 8-code MFMA piece lies in one position row and one group, so the
+// lane scales its codes in fp32 and feeds the product as a hi/lo pair of bf16
+// operands (two MFMAs); V then takes per-(token, head) scales.
 //
 // Masked positions (outside [start, L): the tail of the last page, positions
 // before the window) get a score of -inf by selection and their V bytes are
@@ -106,6 +110,24 @@ __device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8& hi, bf
   }
   hi = __builtin_bit_cast(bf16x8, h);
   lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// Eight E4M3 codes (element i from byte i of w0:w1) times an fp32 scale, as
+// a hi/lo pair of bf16 operands: x = fp32(code * s), hi = bf16(x), lo =
+// bf16(x - hi).
+__device__ __forceinline__ void scaled_e4m3x8_hilo(uint32_t w0, uint32_t w1, float s, bf16x8& hi, bf16x8& lo) {
+  float v[8];
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  v[0] = a[0] * s;
+  v[1] = a[1] * s;
+  v[2] = b[0] * s;
+  v[3] = b[1] * s;
+  v[4] = c[0] * s;
+  v[5] = c[1] * s;
+  v[6] = d[0] * s;
+  v[7] = d[1] * s;
+  split_bf16x8(v, hi, lo);
 }
 
 // The D/32 E8M0 bytes of one position (one 32-dim group each), zero-extended
@@ -163,6 +185,7 @@ struct Tile {
   float vst[NS][8];
   u32x4 ke8[NS][2];     // E8M0 bytes of the lane's K rows
   u32x4 ve8[NS][NE];    // E8M0 bytes of the lane's 8 score positions, all groups
+  float kgs[NS][2][NM]; // fp32 sub-row scales of the lane's K pieces
 };
 
 // FUSED: also append each sequence's new token (DecodeArgs::k_new / v_new)
@@ -184,7 +207,8 @@ template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW, bool FUSED,
           bool PK = false, bool PS = false>
 __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a) {
   static_assert(!(PS && (FUSED || PK || PF)), "packed splits: plain kernels without prefetch");
-  static_assert(!(F8 && SK == 2), "E8M0 K scales vary inside one fp8 MFMA");
+  static_assert(!(F8 && SK >= 2), "E8M0 and sub-row K scales vary inside one fp8 MFMA");
+  static_assert(!(SK == 3 && (FUSED || PK || PS)), "sub-row K scales: split kernels without the fused append");
   static_assert(!(PK && (FUSED || F8 || PF)), "packed heads: plain bf16 kernels without prefetch");
   static_assert(!(FUSED && PF), "the fused append waits inside the non-prefetching tile loop");
   constexpr int NT = 64 * NW;   // threads (NW wave64s)
@@ -514,6 +538,23 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
         scales8(t.kst[s], ksc, tpq + 8 * s, a.kg.sc_tok_stride);
         scales8(t.vst[s], vsc, tpq + 8 * s, a.vg.sc_tok_stride);
       }
+    } else if constexpr (SK == 3) {
+      // K: the scale of each of the lane's 16-dim pieces (position row tk +
+      // 8s + 4aa + kslot, dims 64m + 16*quad..: one group, as groups span
+      // at least 32 dims).  V: per (token, head), as for SK = 1.
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
+          const uint8_t* kf = a.kp + rk.scale + kvh * a.kg.sc_head_stride + tp * a.kg.sc_tok_stride;
+#pragma unroll
+          for (int m = 0; m < NM; ++m) t.kgs[s][aa][m] = ld_global<float>(kf + 4 * ((64 * m + 16 * quad) >> a.kg.sc_gshift));
+        }
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t.vst[s][i] = ld_global<float>(vsc + (tpq + 8 * s + i) * a.vg.sc_tok_stride);
     } else {
       if constexpr (VT) {
         // One position's NG bytes at a time: in the TOKENS layout consecutive
@@ -652,6 +693,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
                                                             s4, 0, 0, 0);
             s4 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)(((uint64_t)w[3] << 32) | w[2]),
                                                             (long)qop8[2 * m + 1], s4, 0, 0, 0);
+          } else if constexpr (SK == 3) {
+            const float ks = t.kgs[s][aa][m];
+            bf16x8 hi, lo;
+            scaled_e4m3x8_hilo(w[0], w[1], ks, hi, lo);
+            s4 = mfma_16x16x32_bf16(hi, qop[2 * m], s4);
+            s4 = mfma_16x16x32_bf16(lo, qop[2 * m], s4);
+            scaled_e4m3x8_hilo(w[2], w[3], ks, hi, lo);
+            s4 = mfma_16x16x32_bf16(hi, qop[2 * m + 1], s4);
+            s4 = mfma_16x16x32_bf16(lo, qop[2 * m + 1], s4);
           } else {
             s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[0], w[1], cvt), qop[2 * m], s4);
             s4 = mfma_16x16x32_bf16(e4m3x8_to_bf16x8(w[2], w[3], cvt), qop[2 * m + 1], s4);
@@ -753,7 +803,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
           // L) read a clamped attended one), so p * scale is 0 where p is;
           // a token scale of a masked position may be anything.
           if constexpr (SK == 0) pv[i] = p[s][i] * t.vs;
-          if constexpr (SK == 1) pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * t.vst[s][i];
+          if constexpr (SK == 1 || SK == 3) pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * t.vst[s][i];
         }
         bf16x8 pop, pol;
         split_bf16x8(pv, pop, pol);
@@ -1276,9 +1326,13 @@ hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t 
     case 1:
       hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
-    default:
+    case 2:
       if constexpr (F8) return hipErrorNotSupported;
       else hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
+      break;
+    default:   // fp32 sub-row K scales
+      if constexpr (F8 || FUSED || PK || PS) return hipErrorNotSupported;
+      else hipExtLaunchKernelGGL((decode_kernel<D, NS, 3, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
   }
   return hipGetLastError();
@@ -1291,7 +1345,8 @@ int occupancy_d(int sk, size_t lds) {
   switch (sk) {
     case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 0, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
     case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 1, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 2, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 2, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 3, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
   }
   return e == hipSuccess ? nb : -1;
 }

@@ -25,6 +25,7 @@ struct PoolGeom {
   int32_t align64;         // rows placed by FP8PA_POOL_ALIGN64
   int32_t payload_bytes;   // P * Hkv * D
   int32_t scale_bytes;     // bytes of a row's scale block
+  int32_t sc_gshift;       // fp32 sub-row scales: log2 of the dims per scale (else 0)
 };
 
 // Byte offsets, from the pool base, of row r's payload and scale block

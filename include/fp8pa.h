@@ -70,11 +70,21 @@ enum {
  *   F32_TOKEN_HEAD  fp32 per (token, head):         4*slot
  *   E8M0_G32        E8M0 per (token, head, 32 dims along D), the MXFP8 scale
  *                   of page "Attention MXFP8 TKG Kernel API Reference":
- *                   slot*(D/32) + d/32.  Value 2**(u-127).                  */
+ *                   slot*(D/32) + d/32.  Value 2**(u-127).
+ *   F32_G<S>        fp32 per (token, head, S dims along D), S = 32, 64, 128 or
+ *                   256 dividing D: the sub-row key scales of page "fp8 paged
+ *                   attention for MoE serving" ("Supported scope", k_groups =
+ *                   D/S): 4*(slot*(D/S) + d/S).  Written by fp8pa_append_quant
+ *                   for K or V; fp8pa_decode reads them for K, with V in
+ *                   F32_TOKEN_HEAD (else FP8PA_EUNSUPPORTED).              */
 enum {
   FP8PA_SCALE_F32_PAGE_HEAD = 0,
   FP8PA_SCALE_F32_TOKEN_HEAD = 1,
-  FP8PA_SCALE_E8M0_G32 = 2
+  FP8PA_SCALE_E8M0_G32 = 2,
+  FP8PA_SCALE_F32_G32 = 3,
+  FP8PA_SCALE_F32_G64 = 4,
+  FP8PA_SCALE_F32_G128 = 5,
+  FP8PA_SCALE_F32_G256 = 6
 };
 
 /* ---- decode variants.  An explicit request is honoured or refused with
