@@ -323,12 +323,15 @@ def run_sweep(args, torch, ops, workloads, hip):
             torch.cuda.empty_cache()
 
 
-# (K layout, V layout, scale kind; None: the workload's own).  The last four
-# are the page's own payload orders for both pools.
+# (K layout, V layout, scale kind; None: the workload's own).  Rows 7-10 are
+# the page's own payload orders for both pools; the last three take fp32
+# sub-row K scales (V per (token, head)).
 FORMATS = (("heads_d64", "heads_dmajor", None), ("heads", "heads_dmajor", None), ("tokens", "heads_dmajor", None),
            ("heads_d64", "heads_dmajor", "token_head"), ("heads", "heads_dmajor", "token_head"),
            ("tokens", "heads_dmajor", "token_head"), ("heads", "heads", None), ("tokens", "tokens", None),
-           ("heads", "heads", "token_head"), ("tokens", "tokens", "token_head"))
+           ("heads", "heads", "token_head"), ("tokens", "tokens", "token_head"),
+           ("heads_d64", "heads_dmajor", "f32_g32"), ("heads_d64", "heads_dmajor", "f32_g64"),
+           ("tokens", "tokens", "f32_g32"))
 
 
 def copies_of(layers, wl, R, torch):
@@ -355,8 +358,9 @@ def run_formats(args, wl, torch, np, ops, workloads, hip):
     same codes and scales, so their outputs must agree bit for bit."""
     first = {}
     for kl, vl, sk in FORMATS:
-        if args.variant in ("mfma_fp8", "packed_heads", "packed_split") and vl != "heads_dmajor":
-            continue   # these variants read V d-major only
+        if args.variant in ("mfma_fp8", "packed_heads", "packed_split") and (vl != "heads_dmajor" or
+                                                                              (sk or "").startswith("f32_g")):
+            continue   # these variants read V d-major only, and no sub-row K scales
         sk = wl.scale_kind if sk is None else sk
         layers = workloads.build_workload(wl, k_layout=kl, v_layout=vl, scale_kind=sk)
         R = args.copies or rotation(layers, wl, np)

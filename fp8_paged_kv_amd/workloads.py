@@ -56,8 +56,18 @@ def raw_kv(seed, wl, layer_index, b, tensor, n_pos, Hkv, D):
     return inputs.normal_bf16(seed, wl.index, tensor, layer_index * 4096 + b, (n_pos, Hkv, D))
 
 
+GROUP_DIMS = {"f32_g32": 32, "f32_g64": 64, "f32_g128": 128, "f32_g256": 256}
+
+
 def scale_block_bytes(scale_kind, Hkv, P, D):
+    if scale_kind in GROUP_DIMS:
+        return 4 * Hkv * P * (D // GROUP_DIMS[scale_kind])
     return {"page_head": 4 * Hkv, "token_head": 4 * Hkv * P, "e8m0_32": Hkv * P * D // 32}[scale_kind]
+
+
+def v_kind_of(scale_kind):
+    """V scale kind paired with a K kind: per-(token, head) V for sub-row K groups."""
+    return "token_head" if scale_kind in GROUP_DIMS else scale_kind
 
 
 def rows_can_align(row_bytes, payload, scales):
@@ -108,7 +118,8 @@ def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", lay
             tables[li] = (t, pool_rows)
     row_width = {}
     for li, lay in enumerate(wl.layers):
-        natural = P * lay.Hkv * lay.D + scale_block_bytes(scale_kind, lay.Hkv, P, lay.D)
+        natural = P * lay.Hkv * lay.D + max(scale_block_bytes(scale_kind, lay.Hkv, P, lay.D),
+                                            scale_block_bytes(v_kind_of(scale_kind), lay.Hkv, P, lay.D))
         row_width[li] = max(lay.row_bytes, -(-natural // 16) * 16)
     if wl.shared_pool:   # one row width for the layers of a shared pool
         row_width = {li: max(row_width.values()) for li in row_width}
@@ -122,9 +133,10 @@ def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", lay
         # Rows are placed with their payloads on the 64-byte grid when the row
         # width leaves room for it (the row widths carry a 32-byte scale
         # footer, so half the rows would start 32 bytes off the grid).
-        al = rows_can_align(rb, P * lay.Hkv * lay.D, scale_block_bytes(scale_kind, lay.Hkv, P, lay.D))
+        al = all(rows_can_align(rb, P * lay.Hkv * lay.D, scale_block_bytes(k, lay.Hkv, P, lay.D))
+                 for k in (scale_kind, v_kind_of(scale_kind)))
         kd = ops.pool_desc(lay.Hkv, lay.D, P, k_layout, scale_kind, rb, pool_rows, align64=al)
-        vd = ops.pool_desc(lay.Hkv, lay.D, P, v_layout, scale_kind, rb, pool_rows, align64=al)
+        vd = ops.pool_desc(lay.Hkv, lay.D, P, v_layout, v_kind_of(scale_kind), rb, pool_rows, align64=al)
         if wl.shared_pool and "k" in shared:
             k_pool, v_pool = shared["k"], shared["v"]
         else:
@@ -179,6 +191,8 @@ def kv_bytes(layer: DeviceLayer):
             sc = 2 * 4 * pages * layer.Hkv
         elif layer.scale_kind == "token_head":
             sc = 2 * 4 * n * layer.Hkv
+        elif layer.scale_kind in GROUP_DIMS:   # K: one fp32 per group; V: one per (token, head)
+            sc = 4 * n * (layer.D // GROUP_DIMS[layer.scale_kind]) * layer.Hkv + 4 * n * layer.Hkv
         else:
             sc = 2 * n * (layer.D // 32) * layer.Hkv
         total += payload + sc

@@ -20,8 +20,8 @@ def oracle_panel(wl, layer, b, g, seed=configs.SEED):
     al = bool(layer.kd.flags & 1)
     kd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads_d64", layer.scale_kind, layer.row_bytes, layer.pool_rows,
                         align64=al)
-    vd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads_dmajor", layer.scale_kind, layer.row_bytes,
-                        layer.pool_rows, align64=al)
+    vd = opool.PoolDesc(layer.Hkv, layer.D, layer.P, "heads_dmajor", workloads.v_kind_of(layer.scale_kind),
+                        layer.row_bytes, layer.pool_rows, align64=al)
     L, first = int(layer.lens[b]), int(layer.first_pos[b])
     n = L - first
     xk = workloads.raw_kv(seed, wl, layer.layer_index, b, "k", n, layer.Hkv, layer.D)
@@ -49,6 +49,9 @@ def panel_byte_index(desc, rows, g):
         sc = opool.scale_rel(desc, g) + np.arange(4)
     elif desc.scale_kind == "token_head":
         sc = np.array([opool.scale_rel(desc, g, tt) + i for tt in range(P) for i in range(4)])
+    elif desc.scale_kind in opool.GROUP_KINDS:
+        ng = D // opool.GROUP_KINDS[desc.scale_kind]
+        sc = np.array([opool.scale_rel(desc, g, tt, gg) + i for tt in range(P) for gg in range(ng) for i in range(4)])
     else:
         sc = np.array([opool.scale_rel(desc, g, tt, gg) for tt in range(P) for gg in range(D // 32)])
     rows = np.asarray(rows, np.int64)
@@ -138,3 +141,19 @@ def test_llama_full_size_other_variants(llama_layer, variant):
         err, frac = check_panel(configs.LLAMA3_8B, layer, out_np, b, g)
         say(f"  {variant} b={b} g={g}: max err {err:.2e} ({frac:.2f} of bound)")
     assert float((out.float() - ref.float()).abs().max()) < 2e-2
+
+
+def test_llama_full_size_sub_row_key_scales():
+    """The Llama-3-8B-shaped call at full size with fp32 K scales per 32 dims
+    (V per token): sampled panels within the oracle bound."""
+    say("workload k groups")
+    layer = workloads.build_workload(configs.LLAMA3_8B, scale_kind="f32_g32")[0]
+    out = workloads.decode_layer(layer)
+    torch.cuda.synchronize()
+    out_np = to_np(out)
+    assert np.all(np.isfinite(out_np))
+    rng = np.random.default_rng(23)
+    for b, g in [(int(np.argmax(layer.lens)), int(rng.integers(layer.Hkv))),
+                 (int(rng.integers(len(layer.lens))), int(rng.integers(layer.Hkv)))]:
+        err, frac = check_panel(configs.LLAMA3_8B, layer, out_np, b, g)
+        say(f"  f32_g32 b={b} g={g}: max err {err:.2e} ({frac:.2f} of bound)")
