@@ -191,7 +191,10 @@ int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
  *   v_pool      device uint8 pools, 16-byte aligned, described by kd / vd.
  *               kd: layout HEADS_D64, HEADS or TOKENS; vd: layout
  *               HEADS_DMAJOR, HEADS or TOKENS.  Both: same Hkv, D, P and
- *               scale kind.  With V in HEADS or TOKENS the launch needs
+ *               scale kind, except that K in F32_G<S> takes V in
+ *               F32_TOKEN_HEAD (V in F32_G<S> is refused; K in F32_G<S>
+ *               runs the MFMA_BF16 split kernels only, without the fused
+ *               append).  With V in HEADS or TOKENS the launch needs
  *               more LDS (B up to about 2000 at D = 128; FP8PA_EUNSUPPORTED
  *               beyond).
  *   block_table device int32 [B, bt_stride]: logical page -> row.
