@@ -3,6 +3,7 @@
 // anything is enqueued; an invalid call launches nothing (the page's
 // convention: an explicit request is honoured or refused, never silently
 // replaced, and what ran is recorded).
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -19,6 +20,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+thread_local uint32_t* g_dbg = nullptr;   // debug checks: device error words [2], or null
 
 struct Counters {
   std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0}, fused_append{0},
@@ -317,6 +319,8 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
     return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS_D64, HEADS or TOKENS layout");
   if (grouped(vd->scale_kind))
     return fail(FP8PA_EUNSUPPORTED, "vd: decode reads fp32 sub-row scales for K only");
+  if (g_dbg && (kd->num_rows < 1 || vd->num_rows < 1))
+    return fail(FP8PA_EINVAL, "debug checks need num_rows >= 1 in both descriptors");
   if (vd->layout == FP8PA_LAYOUT_HEADS_D64)
     return fail(FP8PA_EUNSUPPORTED, "vd: decode reads V in the HEADS_DMAJOR, HEADS or TOKENS layout");
   // V in a token-major layout is staged through LDS (default kernel shapes).
@@ -413,6 +417,9 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
   a.tile_variant = tv_launch;   // the fused, V-token-major and fp8 kernels exist in the default shapes
   a.vstage_off = (int32_t)vstage_off;
+  a.dbg = g_dbg;
+  a.dbg_rows = (int32_t)std::min<int64_t>(std::min(kd->num_rows, vd->num_rows), INT32_MAX);
+  a.dbg_max_len = max_seq_len;
   // Packed splits: every wave reads every tile of a segment, so one tile per
   // share suffices, and a tile carries NW heads, so a unit's fixed cost is
   // NW times smaller in tiles.
@@ -487,7 +494,7 @@ int fp8pa_append_decode(const void* k_new, const void* v_new, const void* q, voi
   // So do calls whose automatic plan takes packed heads (then the output
   // equals the append followed by the same decode).
   if (span <= kFusedMaxSpan && vd && vd->layout == FP8PA_LAYOUT_HEADS_DMAJOR && variant != FP8PA_VARIANT_MFMA_FP8 &&
-      !(kd && grouped(kd->scale_kind)) &&
+      !(kd && grouped(kd->scale_kind)) && !g_dbg &&
       variant != FP8PA_VARIANT_PACKED_HEADS && variant != FP8PA_VARIANT_PACKED_SPLIT &&
       !auto_packs(B, Hq, kd, workgroups, variant))
     return decode_impl(k_new, v_new, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
@@ -509,6 +516,8 @@ int fp8pa_append_decode(const void* k_new, const void* v_new, const void* q, voi
   ap.vg = geometry(*vd);
   ap.k_kind = kd->scale_kind;
   ap.v_kind = vd->scale_kind;
+  ap.dbg = g_dbg;
+  ap.dbg_rows = (int32_t)std::min<int64_t>(std::min(kd->num_rows, vd->num_rows), INT32_MAX);
   ap.bt = block_table;
   ap.bt_stride = bt_stride;
   ap.seq_lens = seq_lens;
@@ -572,6 +581,8 @@ int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, ui
   if (((kd->flags & FP8PA_POOL_ALIGN64) && !aligned(k_pool, 64)) || ((vd->flags & FP8PA_POOL_ALIGN64) && !aligned(v_pool, 64)))
     return fail(FP8PA_EINVAL, "pools with aligned rows must be 64-byte aligned");
   if (bt_stride < 1) return fail(FP8PA_EINVAL, "bt_stride must be >= 1");
+  if (g_dbg && (kd->num_rows < 1 || vd->num_rows < 1))
+    return fail(FP8PA_EINVAL, "debug checks need num_rows >= 1 in both descriptors");
   fp8pa::AppendArgs a{};
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
@@ -581,6 +592,8 @@ int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, ui
   a.vg = geometry(*vd);
   a.k_kind = kd->scale_kind;
   a.v_kind = vd->scale_kind;
+  a.dbg = g_dbg;
+  a.dbg_rows = (int32_t)std::min<int64_t>(std::min(kd->num_rows, vd->num_rows), INT32_MAX);
   a.bt = block_table;
   a.bt_stride = bt_stride;
   a.positions = positions;
@@ -650,6 +663,13 @@ int fp8pa_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr)) return fail(FP8PA_EINVAL, "set both events or neither");
   g_ev_start = static_cast<hipEvent_t>(start);
   g_ev_stop = static_cast<hipEvent_t>(stop);
+  ok();
+  return FP8PA_OK;
+}
+
+int fp8pa_set_debug_checks(uint32_t* err) {
+  if (err && !aligned(err, 4)) return fail(FP8PA_EINVAL, "err must be 4-byte aligned");
+  g_dbg = err;
   ok();
   return FP8PA_OK;
 }

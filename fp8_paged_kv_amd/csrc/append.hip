@@ -30,10 +30,20 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     pos0 = L - 1;
   }
   if (nb == 0) return;
+  // Debug checks: positions outside the table's pages, or rows outside the
+  // pools, skip the write and set an error word.
+  if (a.dbg && (pos0 < 0 || (int64_t)(pos0 + nb - 1) / P >= a.bt_stride)) {
+    if (threadIdx.x == 0) __hip_atomic_store(a.dbg + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   const int page = pos0 / P + pi;
   if (page > (pos0 + nb - 1) / P) return;
   const int lo = max(pos0, page * P), hi = min(pos0 + nb, (page + 1) * P);
   const int32_t row = a.bt[(int64_t)b * a.bt_stride + page];
+  if (a.dbg && (uint32_t)row >= (uint32_t)a.dbg_rows) {
+    if (threadIdx.x == 0) __hip_atomic_store(a.dbg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   const uint16_t* x = xin + (((size_t)b * a.T + (lo - pos0)) * H + h) * D;   // token i at x + i*H*D
   append_page<4>(pool, gm, kind, row, h, P, D, lo, hi - lo, x, (int64_t)H * D, red);
 }

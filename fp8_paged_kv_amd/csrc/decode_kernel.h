@@ -241,6 +241,24 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   const int w = blockIdx.x;
   const bool col = n < (PS ? a.G : G);
 
+  // Debug checks (a.dbg set): a length outside [0, dbg_max_len] counts as 0
+  // and a table entry outside [0, dbg_rows) as row 0, each setting its error
+  // word, so nothing is read outside the pools.
+  auto chk_len = [&](int len) -> int {
+    if (a.dbg && (len < 0 || len > a.dbg_max_len)) {
+      __hip_atomic_store(a.dbg + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return 0;
+    }
+    return len;
+  };
+  auto chk_row = [&](int32_t r) -> int32_t {
+    if (a.dbg && (uint32_t)r >= (uint32_t)a.dbg_rows) {
+      __hip_atomic_store(a.dbg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return 0;
+    }
+    return r;
+  };
+
   // ---- tiles per sequence and their prefix sums.
   auto tiles_of = [&](int L) {
     const int st = (a.window > 0 && L > a.window) ? L - a.window : 0;
@@ -309,7 +327,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   if constexpr (PK) {
   } else if (fast) {
     if (wave == 0) {
-      const int len = lane < B ? a.seq_lens[lane] : 0;
+      const int len = lane < B ? chk_len(a.seq_lens[lane]) : 0;
       const int nt = tiles_of(len), ne = nt > 0 ? 1 : 0;
       int incl = nt, incl_ne = ne;
 #pragma unroll
@@ -361,7 +379,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
           tbeg = start & ~(TT - 1);
           chunk_rows(ta, tc < ta + CH ? tc : ta + CH);
           const int32_t* btr0 = a.bt + (int64_t)b * a.bt_stride;
-          for (int i = lane; i < nstaged; i += 64) s_tab[i] = btr0[p_first + i];
+          for (int i = lane; i < nstaged; i += 64) s_tab[i] = chk_row(btr0[p_first + i]);
         }
         if (lane == 0) {
           s_bnd[0] = bnd[0];
@@ -381,7 +399,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
     int local = 0, lne = 0;
     for (int i = 0; i < per; ++i)
       if (bb0 + i < B) {
-        const int len = a.seq_lens[bb0 + i];
+        const int len = chk_len(a.seq_lens[bb0 + i]);
         s_len[bb0 + i] = len;
         const int nt = tiles_of(len);
         local += nt;
@@ -823,7 +841,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
     g = (w - b * hpg) * NW + wave;
     const bool active = g < Hkv;
     if (!active) g = Hkv - 1;   // an idle wave: in-range pointers, no tiles, no output
-    L = a.seq_lens[b];
+    L = chk_len(a.seq_lens[b]);
     start = (a.window > 0 && L > a.window) ? L - a.window : 0;
     tbeg = start & ~(TT - 1);
     btr = a.bt + (int64_t)b * a.bt_stride;
@@ -846,7 +864,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       const int cb = nb < ca + CH ? nb : ca + CH;
       chunk_rows(ca, cb);
       __syncthreads();   // earlier readers of the stage are done
-      for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = btr[p_first + i];
+      for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = chk_row(btr[p_first + i]);
       __syncthreads();
       if (active) {
         TileT A;
@@ -963,7 +981,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       chunk_rows(ca, cb);
       if (!staged) {
         __syncthreads();   // earlier readers of the stage are done
-        for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = btr[p_first + i];
+        for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = chk_row(btr[p_first + i]);
         __syncthreads();
       }
       staged = false;

@@ -64,6 +64,9 @@ struct DecodeArgs {
   int32_t P, log2P, B, Hq, Hkv, G, window;
   float qk_scale;          // sm_scale * log2(e)
   int32_t vstage_off;      // V token-major: byte offset of the per-wave V stages in dynamic LDS
+  uint32_t* dbg;           // debug checks: error words [2] (table, lengths), or null (no checks)
+  int32_t dbg_rows;        // rows of the smaller pool (debug checks)
+  int32_t dbg_max_len;     // largest valid seq_lens[b] (debug checks)
 };
 
 struct MergeArgs {
@@ -88,6 +91,8 @@ struct AppendArgs {
   const int32_t* counts;   // or null
   const int32_t* seq_lens; // with positions null
   int32_t T, P, Hkv, D;
+  uint32_t* dbg;           // as in DecodeArgs
+  int32_t dbg_rows;
 };
 
 // Tokens per decode tile (one tile = one MFMA round of one wave).

@@ -58,6 +58,7 @@ SIGNATURES = {
     "fp8pa_debug_dequant": ([_P, _P, _I, _I, _P, _P], _I),
     "fp8pa_get_counters": ([ctypes.POINTER(Counters)], _I),
     "fp8pa_reset_counters": ([], _I),
+    "fp8pa_set_debug_checks": ([_P], _I),
     "fp8pa_set_decode_events": ([_P, _P], _I),
     "fp8pa_stream_read": ([_P, _SZ, _P, _P], _I),
 }
@@ -237,6 +238,17 @@ def counters():
 
 def reset_counters():
     lib().fp8pa_reset_counters()
+
+
+def set_debug_checks(err=None):
+    """Turn the in-kernel checks of block-table entries and sequence lengths
+    on (``err``: a device uint32 tensor of 2 words, zeroed by the caller; word
+    0 flags a table entry outside the pools, word 1 a bad length) or off
+    (None), for later calls on this thread."""
+    if err is not None:
+        assert err.dtype == torch.uint32 or err.dtype == torch.int32, "err: 32-bit words"
+        assert err.numel() >= 2 and err.is_cuda
+    _check(lib().fp8pa_set_debug_checks(None if err is None else _ptr(err)))
 
 
 def stream_read(buf, sink, stream=None):

@@ -319,6 +319,20 @@ typedef struct fp8pa_counters {
 } fp8pa_counters;
 
 int fp8pa_get_counters(fp8pa_counters* out);
+
+/* Debug checks of the device-resident arguments (off by default; the
+ * boundary otherwise trusts them).  With err (device uint32 [2], 4-byte
+ * aligned, cleared by the caller) set, later calls on this thread check in
+ * the kernels every block-table entry they read against [0, num_rows) of the
+ * smaller pool and, in decode, every seq_lens[b] against [0, max_seq_len]
+ * (append: the written pages against bt_stride).  A bad entry reads row 0 (in
+ * append: nothing is written) and sets err[0] = 1; a bad length counts as 0
+ * (that sequence's output is zeros) and sets err[1] = 1.  So a bad value
+ * never leads to an access outside the pools, and the output of a call that
+ * sets an error word is not meaningful.  fp8pa_append_decode runs the append
+ * kernel then the decode while the checks are on.  Both descriptors need
+ * num_rows >= 1 (else FP8PA_EINVAL).  err NULL turns the checks off. */
+int fp8pa_set_debug_checks(uint32_t* err);
 int fp8pa_reset_counters(void);
 
 /* Profiling hook (calling thread only): while set, every fp8pa_decode records

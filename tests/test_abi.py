@@ -251,3 +251,18 @@ def test_plan_of_the_variants():
     f8 = ops.decode_plan(4, 32, k, 8192, workgroups=7, variant="mfma_fp8")
     assert f8.variant == ops.VARIANTS["mfma_fp8"] and f8.workspace_bytes == df.workspace_bytes
     assert df.variant == ops.VARIANTS["mfma_bf16"]
+
+
+def test_debug_checks_setting():
+    """fp8pa_set_debug_checks: a misaligned word is refused; with checks on, a
+    descriptor without a row count is refused before launch; NULL turns them off."""
+    P = ctypes.c_void_p
+    assert ops.lib().fp8pa_set_debug_checks(P(F + 2)) == ops.EINVAL
+    assert ops.lib().fp8pa_set_debug_checks(P(F)) == ops.OK
+    try:
+        ops.reset_counters()
+        assert call_decode(k=kd(num_rows=0)) == ops.EINVAL, ops.last_error()
+        assert ops.counters()["decode_calls"] == 0
+    finally:
+        assert ops.lib().fp8pa_set_debug_checks(None) == ops.OK
+    assert call_decode(k=kd(num_rows=0), workgroups=4) == ops.EWORKSPACE   # checks off: the next check applies
