@@ -242,21 +242,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   const bool col = n < (PS ? a.G : G);
 
   // Debug checks (a.dbg set): a length outside [0, dbg_max_len] counts as 0
-  // and a table entry outside [0, dbg_rows) as row 0, each setting its error
-  // word, so nothing is read outside the pools.
-  auto chk_len = [&](int len) -> int {
-    if (a.dbg && (len < 0 || len > a.dbg_max_len)) {
-      __hip_atomic_store(a.dbg + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return 0;
-    }
-    return len;
+  // and a table entry outside [0, dbg_rows) as row 0, so nothing is read
+  // outside the pools; the caller gathers the verdicts and sets the error word
+  // once after its loads (a store among them would order the loads behind it).
+  auto chk_len = [&](int len, bool& bad) -> int {
+    const bool b = a.dbg && (len < 0 || len > a.dbg_max_len);
+    bad |= b;
+    return b ? 0 : len;
   };
-  auto chk_row = [&](int32_t r) -> int32_t {
-    if (a.dbg && (uint32_t)r >= (uint32_t)a.dbg_rows) {
-      __hip_atomic_store(a.dbg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return 0;
-    }
-    return r;
+  auto chk_row = [&](int32_t r, bool& bad) -> int32_t {
+    const bool b = a.dbg && (uint32_t)r >= (uint32_t)a.dbg_rows;
+    bad |= b;
+    return b ? 0 : r;
+  };
+  auto flag = [&](bool bad, int word) {
+    if (bad) __hip_atomic_store(a.dbg + word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
   // ---- tiles per sequence and their prefix sums.
@@ -327,7 +327,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   if constexpr (PK) {
   } else if (fast) {
     if (wave == 0) {
-      const int len = lane < B ? chk_len(a.seq_lens[lane]) : 0;
+      bool bad_len = false;
+      const int len = lane < B ? chk_len(a.seq_lens[lane], bad_len) : 0;
+      flag(bad_len, 1);
       const int nt = tiles_of(len), ne = nt > 0 ? 1 : 0;
       int incl = nt, incl_ne = ne;
 #pragma unroll
@@ -379,7 +381,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
           tbeg = start & ~(TT - 1);
           chunk_rows(ta, tc < ta + CH ? tc : ta + CH);
           const int32_t* btr0 = a.bt + (int64_t)b * a.bt_stride;
-          for (int i = lane; i < nstaged; i += 64) s_tab[i] = chk_row(btr0[p_first + i]);
+          bool bad = false;
+          for (int i = lane; i < nstaged; i += 64) s_tab[i] = chk_row(btr0[p_first + i], bad);
+          flag(bad, 0);
         }
         if (lane == 0) {
           s_bnd[0] = bnd[0];
@@ -397,14 +401,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
     const int per = (B + NT - 1) / NT;
     const int bb0 = threadIdx.x * per;
     int local = 0, lne = 0;
+    bool bad_len = false;
     for (int i = 0; i < per; ++i)
       if (bb0 + i < B) {
-        const int len = chk_len(a.seq_lens[bb0 + i]);
+        const int len = chk_len(a.seq_lens[bb0 + i], bad_len);
         s_len[bb0 + i] = len;
         const int nt = tiles_of(len);
         local += nt;
         lne += nt > 0;
       }
+    flag(bad_len, 1);
     int incl = local, incl_ne = lne;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -841,7 +847,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
     g = (w - b * hpg) * NW + wave;
     const bool active = g < Hkv;
     if (!active) g = Hkv - 1;   // an idle wave: in-range pointers, no tiles, no output
-    L = chk_len(a.seq_lens[b]);
+    bool bad_len = false;
+    L = chk_len(a.seq_lens[b], bad_len);
+    flag(bad_len, 1);
     start = (a.window > 0 && L > a.window) ? L - a.window : 0;
     tbeg = start & ~(TT - 1);
     btr = a.bt + (int64_t)b * a.bt_stride;
@@ -864,7 +872,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       const int cb = nb < ca + CH ? nb : ca + CH;
       chunk_rows(ca, cb);
       __syncthreads();   // earlier readers of the stage are done
-      for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = chk_row(btr[p_first + i]);
+      bool bad = false;
+      for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = chk_row(btr[p_first + i], bad);
+      flag(bad, 0);
       __syncthreads();
       if (active) {
         TileT A;
@@ -981,7 +991,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       chunk_rows(ca, cb);
       if (!staged) {
         __syncthreads();   // earlier readers of the stage are done
-        for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = chk_row(btr[p_first + i]);
+        bool bad = false;
+        for (int i = threadIdx.x; i < nstaged; i += NT) s_tab[i] = chk_row(btr[p_first + i], bad);
+        flag(bad, 0);
         __syncthreads();
       }
       staged = false;
