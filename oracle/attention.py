@@ -55,19 +55,16 @@ def fp8_query(q):
 
     The fp8 path of page "fp8 paged attention for MoE serving" (section "Two
     compute paths") adds one E4M3 rounding of q.  Reading: each (sequence,
-    query head) row of q gets one fp32 scale fp32(amax / 448) (1 for an
-    all-zero row), like a KV block, and codes e4m3(fp32(q * fp32(1 / scale)))
-    (the page does not say how q is scaled; a product by the rounded
-    reciprocal is the plainest per-element step), and the mode attends with
-    code x scale.  The fp8-mode output is then ``decode_ref(fp8_query(q),
-    ...)``."""
+    query head) row of q is quantized exactly like one KV block of the page's
+    quantizer (section "Supported scope"): one fp32 scale s = fp32(amax / 448)
+    (1 for an all-zero row) and codes e4m3(fp32(q / s)) with the correctly
+    rounded fp32 quotient; the mode then attends with code x s.  The page does
+    not say how q is scaled, and this is the rule it gives for every other
+    E4M3 block.  The fp8-mode output is ``decode_ref(fp8_query(q), ...)``."""
     q = np.asarray(q, dtype=np.float64)
     out = np.empty_like(q)
     for idx in np.ndindex(q.shape[:-1]):
-        row = q[idx]
-        scale = float(fp8mod.fp32_scale_from_amax(np.abs(row).max() if row.size else 0.0))
-        inv = float(fp8mod.to_fp32(1.0 / scale))
-        codes = fp8mod.encode_e4m3(fp8mod.to_fp32(row * inv))
+        codes, scale = fp8mod.quantize_fp32_block(q[idx])
         out[idx] = fp8mod.dequant(codes, scale)
     return out
 

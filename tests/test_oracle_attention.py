@@ -255,3 +255,55 @@ def test_fp8_query_pins():
     assert np.max(np.abs(got - q) / np.abs(q)) > 2 ** -6                # it does round
     np.testing.assert_array_equal(oatt.fp8_query(-q), -got)
     np.testing.assert_array_equal(oatt.fp8_query(q * 2.0 ** 7), got * 2.0 ** 7)
+
+
+def _nearest_e4m3_brute(y):
+    """Nearest finite E4M3 code to each fp32 value by exhaustive search over the
+    254 finite codes (ties to the even code, the sign of zero kept)."""
+    fin = np.array([c for c in range(256) if c not in (0x7F, 0xFF)])
+    vals = np.array([fp8.e4m3_value(int(c)) for c in fin])
+    out = np.empty(len(y), np.uint8)
+    for i, v in enumerate(np.minimum(np.abs(y), 448.0)):
+        pos = fin[(fin < 0x80)]
+        d = np.abs(vals[fin < 0x80] - v)
+        best = pos[d == d.min()]
+        c = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+        out[i] = c | (0x80 if np.signbit(y[i]) else 0)
+    return out
+
+
+def test_fp8_query_divides_by_the_row_scale():
+    """The fp8-mode query codes are e4m3(fp32(q / s)) with s = fp32(amax / 448),
+    the block quantizer's rule, and not e4m3(fp32(q * fp32(1 / s))).  Rows are
+    built from (amax, q) bf16 pairs where the two rules give different codes
+    (found by search here; the pin needs at least one); the expected values
+    come from numpy's IEEE fp32 division and an exhaustive nearest-code
+    search."""
+    amaxs = np.array([(1 + m / 128) for m in range(128)])
+    qs = np.array([(1 + m / 128) * 2.0 ** e for e in range(-12, 1) for m in range(128)])
+    rows = []
+    for a in amaxs:
+        s32 = np.float32(a / 448.0)
+        q32 = qs.astype(np.float32)
+        div = (q32 / s32).astype(np.float64)
+        mul = (q32 * (np.float32(1.0) / s32)).astype(np.float64)
+        sep = (_nearest_e4m3_brute(div) != _nearest_e4m3_brute(mul)) & (qs <= a)
+        if sep.any():
+            sel = qs[sep][:63]
+            row = np.zeros(64)
+            row[0] = a
+            row[1:1 + len(sel)] = sel * np.where(np.arange(len(sel)) % 2, -1.0, 1.0)
+            rows.append(row)
+        if len(rows) == 6:
+            break
+    assert len(rows) >= 1, "no separating row found"
+    q = np.stack(rows)[None]                                           # [1, R, 64]
+    got = oatt.fp8_query(q)[0]
+    for r, row in enumerate(q[0]):
+        s32 = np.float32(np.abs(row).max() / 448.0)
+        y = (row.astype(np.float32) / s32).astype(np.float64)
+        want = np.array([fp8.e4m3_value(int(c)) for c in _nearest_e4m3_brute(y)]) * float(s32)
+        np.testing.assert_array_equal(got[r], want)
+        y_mul = (row.astype(np.float32) * (np.float32(1.0) / s32)).astype(np.float64)
+        alt = np.array([fp8.e4m3_value(int(c)) for c in _nearest_e4m3_brute(y_mul)]) * float(s32)
+        assert not np.array_equal(got[r], alt), "the row does not separate the two rules"
