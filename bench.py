@@ -126,7 +126,7 @@ def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgr
     outs = [torch.empty_like(l.q) for l in layers_copies[0]]
     ws = []
     for l in layers_copies[0]:
-        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, workgroups, variant)
+        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.vd, l.max_seq_len, l.window, workgroups, variant)
         ws.append(torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0"))
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -186,7 +186,7 @@ def time_fused(copies, j, steps, hip, ops, workloads, torch):
     pos = (l0.seq_lens - 1).clamp(min=0).to(torch.int32)
     counts = (l0.seq_lens > 0).to(torch.int32)
     out = torch.empty_like(l0.q)
-    p = ops.decode_plan(B, l0.Hq, l0.kd, l0.max_seq_len, l0.window)
+    p = ops.decode_plan(B, l0.Hq, l0.kd, l0.vd, l0.max_seq_len, l0.window)
     ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -401,7 +401,7 @@ def run_graph(args, wl, torch, np, ops, workloads, hip):
     outs = [torch.empty_like(l.q) for l in layers]
     ws = []
     for l in layers:
-        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window)
+        p = ops.decode_plan(len(l.lens), l.Hq, l.kd, l.vd, l.max_seq_len, l.window)
         ws.append(torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0"))
 
     def step(c0):
@@ -499,7 +499,7 @@ def main():
     traffic = stored_traffic(wl.name)
     us = sorted(x * 1e3 for x in step_ms)
     pct = lambda p: us[min(len(us) - 1, int(p * len(us)))]
-    plans = [ops.decode_plan(len(l.lens), l.Hq, l.kd, l.max_seq_len, l.window, args.workgroups, args.variant)
+    plans = [ops.decode_plan(len(l.lens), l.Hq, l.kd, l.vd, l.max_seq_len, l.window, args.workgroups, args.variant)
              for l in layers]
     rec = {
         "metric": METRIC,

@@ -19,7 +19,9 @@ ARCH = "gfx950"
 SOURCES = ["decode.hip", "decode_fused.hip", "decode_vtok.hip", "decode_fp8q.hip", "decode_packed.hip", "decode_pksplit.hip", "merge.hip", "append.hip", "probe.hip", "api.cpp"]
 # Packed fp32 VALU instructions are kept out of generated code (the device
 # pass honours the feature flag; the host pass warns that it does not know it).
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # fp32 "/" is the IEEE correctly rounded quotient (the quantizers rely on it)
+                "-fhip-fp32-correctly-rounded-divide-sqrt"]
 COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

@@ -21,6 +21,7 @@ namespace {
 thread_local char g_err[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 thread_local uint32_t* g_dbg = nullptr;   // debug checks: device error words [2], or null
+thread_local bool g_force_timeout = false;   // test hook: merges give up waiting
 
 struct Counters {
   std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0}, fused_append{0},
@@ -82,6 +83,8 @@ int check_desc(const fp8pa_pool_desc* d, const char* name) {
   if (grouped(d->scale_kind) && group_dims(d->scale_kind) > d->head_dim)
     return fail(FP8PA_EINVAL, "%s: %d dims per scale exceed head_dim %d", name, group_dims(d->scale_kind),
                 d->head_dim);
+  // (head counts up to 2^31, pages up to 2^10 and head dims up to 2^9 keep
+  // the payload and scale sizes below 2^52.)
   const int64_t payload = (int64_t)d->page_size * d->num_kv_heads * d->head_dim;
   const int64_t foot = footer_offset(*d);
   if (d->row_bytes <= 0 || d->row_bytes % 16)
@@ -89,9 +92,9 @@ int check_desc(const fp8pa_pool_desc* d, const char* name) {
   if (foot < payload || foot % 16)
     return fail(FP8PA_EINVAL, "%s: scale_offset %lld must be a multiple of 16 and >= the payload (%lld)", name,
                 (long long)foot, (long long)payload);
-  if (foot + scale_bytes(*d) > d->row_bytes)
-    return fail(FP8PA_EINVAL, "%s: payload + scales (%lld) exceed row_bytes %lld", name,
-                (long long)(foot + scale_bytes(*d)), (long long)d->row_bytes);
+  if (foot > d->row_bytes || scale_bytes(*d) > d->row_bytes - foot)
+    return fail(FP8PA_EINVAL, "%s: payload + scales exceed row_bytes %lld", name, (long long)d->row_bytes);
+  if (d->row_bytes > INT32_MAX) return fail(FP8PA_EUNSUPPORTED, "%s: row_bytes %lld >= 2^31", name, (long long)d->row_bytes);
   if (d->flags & FP8PA_POOL_ALIGN64) {
     if (d->scale_offset >= 0) return fail(FP8PA_EINVAL, "%s: aligned rows need the default scale_offset", name);
     // Every payload shift the rows take must leave room for payload and scales.
@@ -106,7 +109,6 @@ int check_desc(const fp8pa_pool_desc* d, const char* name) {
   if (d->num_rows < 0) return fail(FP8PA_EINVAL, "%s: num_rows must be >= 0", name);
   if (d->row_bytes > INT64_MAX / (d->num_rows > 0 ? d->num_rows : 1))
     return fail(FP8PA_EINVAL, "%s: pool size overflows", name);
-  if (d->row_bytes > INT32_MAX) return fail(FP8PA_EUNSUPPORTED, "%s: row_bytes %lld >= 2^31", name, (long long)d->row_bytes);
   return 0;
 }
 
@@ -159,39 +161,6 @@ fp8pa::PoolGeom geometry(const fp8pa_pool_desc& d) {
   return g;
 }
 
-int tile_variant() {
-  static int cached = -1;
-  if (cached < 0) {
-    const char* e = getenv("FP8PA_TILE_VARIANT");
-    cached = e ? atoi(e) : 0;
-  }
-  return cached;
-}
-
-// Fewest tiles a workgroup takes: by default one per wave, so short calls use
-// fewer, fuller workgroups (tunable through FP8PA_MIN_TILES; 0 = default).
-int min_tiles(int waves) {
-  static int cached = -1;
-  if (cached < 0) {
-    const char* e = getenv("FP8PA_MIN_TILES");
-    cached = e ? atoi(e) : 0;
-    if (cached < 0) cached = 0;
-  }
-  return cached > 0 ? cached : waves;
-}
-
-// Fixed cost of a unit (setup, combine, partial) in the share balance, in
-// quarter tiles: the kernel shape's default, or FP8PA_SEG_COST (tuning).
-int seg_cost(int shape_default) {
-  static int cached = -2;
-  if (cached == -2) {
-    const char* e = getenv("FP8PA_SEG_COST");
-    cached = e ? atoi(e) : -1;
-    if (e && cached < 0) cached = 0;
-  }
-  return cached >= 0 ? cached : shape_default;
-}
-
 // Compute units of the current device (0 when no device can be queried),
 // remembered per thread for the last device asked about.
 int device_cus() {
@@ -205,8 +174,7 @@ int device_cus() {
   return n;
 }
 
-// Host-only decode plan.  Returns 0 or an error code.
-// Whether an automatic plan takes packed heads: when the (sequence, group of
+// Whether an automatic call takes packed heads: when the (sequence, group of
 // four KV heads) units alone fill every resident workgroup slot, reading all
 // heads of the page rows together streams faster than cutting units into
 // balanced shares (measured at D = 128: B 256 x L 1024 4.8 -> 6.1 TB/s,
@@ -214,22 +182,40 @@ int device_cus() {
 // No side effects; false for any invalid argument.
 bool auto_packs(int B, int Hq, const fp8pa_pool_desc* kd, int workgroups, int variant) {
   if (variant != FP8PA_VARIANT_AUTO || workgroups != 0 || !kd || B <= 0 || kd->num_kv_heads < 1 ||
-      Hq < 1 || Hq % kd->num_kv_heads || Hq / kd->num_kv_heads > 16 || kd->page_size < 1)
+      kd->num_kv_heads > (1 << 24) || Hq < 1 || Hq % kd->num_kv_heads || Hq / kd->num_kv_heads > 16 ||
+      kd->page_size < 1)
     return false;
   const int D = kd->head_dim;
   if (D != 64 && D != 128) return false;   // the head dims where the gain was measured
   const int cus = device_cus();
   if (cus <= 0) return false;
-  const int tv = tile_variant();
-  const size_t lds = fp8pa::decode_lds_bytes(D, tv, B, Hq / kd->num_kv_heads, kd->page_size);
+  const size_t lds = fp8pa::decode_lds_bytes(D, B, Hq / kd->num_kv_heads, kd->page_size);
   const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
-  const int per_cu = fp8pa::decode_blocks_per_cu(D, kd->scale_kind, k_whole, tv, lds);
-  const int nw = fp8pa::decode_waves(D, 0);
+  const int per_cu = fp8pa::decode_blocks_per_cu(D, kd->scale_kind, k_whole, lds);
+  const int nw = fp8pa::decode_waves(D);
   return per_cu > 0 && (int64_t)B * ((kd->num_kv_heads + nw - 1) / nw) >= (int64_t)cus * per_cu;
 }
 
-int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int window, int workgroups, int variant,
-              fp8pa_plan* out, size_t* lds_out) {
+// Everything a decode call launches, decided on the host from host values
+// only (the grid and the workspace never depend on device data, so a call can
+// be captured in a graph).  The plan and the call use the same resolution.
+struct Resolved {
+  int variant;             // FP8PA_VARIANT_* that runs
+  bool vt, f8, packed, psplit, kgroups, k_whole;
+  int W;                   // workgroups launched
+  int Gu;                  // query heads per unit (packed splits: NW * G)
+  size_t lds;              // dynamic LDS bytes
+  size_t vstage_off;       // V token-major: offset of the per-wave V stages
+  int64_t part_o_bytes, part_lse_bytes, flag_bytes;   // workspace pieces, 256-byte aligned
+  int64_t workspace_bytes; // 0 when nothing is split
+};
+
+int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
+
+// Validates a decode request (everything but pointers and scalars of the
+// call) and resolves what it launches.  fused: the one-launch append.
+int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, int max_seq_len, int workgroups,
+            int variant, bool fused, Resolved* r) {
   if (int rc = check_desc(kd, "kd")) return rc;
   if (B < 0) return fail(FP8PA_EINVAL, "B must be >= 0");
   if (Hq < 1 || Hq % kd->num_kv_heads) return fail(FP8PA_EINVAL, "Hq must be a positive multiple of num_kv_heads");
@@ -240,49 +226,102 @@ int make_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int win
   if (variant != FP8PA_VARIANT_AUTO && variant != FP8PA_VARIANT_MFMA_BF16 && variant != FP8PA_VARIANT_MFMA_FP8 &&
       variant != FP8PA_VARIANT_PACKED_HEADS && variant != FP8PA_VARIANT_PACKED_SPLIT)
     return fail(FP8PA_EUNSUPPORTED, "variant %d is not available", variant);
-  if (variant == FP8PA_VARIANT_PACKED_HEADS && workgroups != 0)
+  const bool packed_req = variant == FP8PA_VARIANT_PACKED_HEADS;
+  if (packed_req && workgroups != 0)
     return fail(FP8PA_EUNSUPPORTED, "packed heads fix the grid: workgroups must be 0");
-  const bool packed = variant == FP8PA_VARIANT_PACKED_HEADS;
   const int D = kd->head_dim;
+  const int nw = fp8pa::decode_waves(D);
   // Packed splits: units of nw KV heads, nw * G query heads merged together.
   const bool psplit = variant == FP8PA_VARIANT_PACKED_SPLIT;
-  const int nw0 = fp8pa::decode_waves(D, 0);
-  if (psplit && (kd->num_kv_heads % nw0 || G * nw0 > 16))
-    return fail(FP8PA_EUNSUPPORTED, "packed splits need Hkv %% %d == 0 and G <= %d", nw0, 16 / nw0);
-  const int Gu = psplit ? G * nw0 : G;   // query heads per unit
-  const int tv = psplit ? 0 : tile_variant();
-  const size_t lds = fp8pa::decode_lds_bytes(D, tv, B, Gu, kd->page_size);
+  if (psplit && (kd->num_kv_heads % nw || G * nw > 16))
+    return fail(FP8PA_EUNSUPPORTED, "packed splits need Hkv %% %d == 0 and G <= %d", nw, 16 / nw);
+  const int Gu = psplit ? G * nw : G;
+  size_t lds = fp8pa::decode_lds_bytes(D, B, Gu, kd->page_size);
   if (lds > 65536)
     return fail(FP8PA_EUNSUPPORTED, "B=%d, G=%d, head_dim %d need %zu bytes of LDS (> 64 KiB)", B, G, D, lds);
+  if (int rc = check_desc(vd, "vd")) return rc;
+  if (kd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
+    return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS_D64, HEADS or TOKENS layout");
+  if (grouped(vd->scale_kind))
+    return fail(FP8PA_EUNSUPPORTED, "vd: decode reads fp32 sub-row scales for K only");
+  if (g_dbg && (kd->num_rows < 1 || vd->num_rows < 1))
+    return fail(FP8PA_EINVAL, "debug checks need num_rows >= 1 in both descriptors");
+  if (vd->layout == FP8PA_LAYOUT_HEADS_D64)
+    return fail(FP8PA_EUNSUPPORTED, "vd: decode reads V in the HEADS_DMAJOR, HEADS or TOKENS layout");
+  // V in a token-major layout is staged through LDS.
+  const bool vt = vd->layout == FP8PA_LAYOUT_HEADS || vd->layout == FP8PA_LAYOUT_TOKENS;
+  if (vt && fused) return fail(FP8PA_EUNSUPPORTED, "the one-launch append reads V in the HEADS_DMAJOR layout");
+  const bool f8 = variant == FP8PA_VARIANT_MFMA_FP8;
+  if (f8 && (kd->scale_kind == FP8PA_SCALE_E8M0_G32 || grouped(kd->scale_kind) || vt || fused))
+    return fail(FP8PA_EUNSUPPORTED,
+                "the fp8 compute mode takes fp32 page or token scales, V in HEADS_DMAJOR and no fused append");
+  // fp32 sub-row K scales: K pieces are scaled before the MFMA (plain,
+  // token-major-V and split kernels only).
+  const bool kgroups = grouped(kd->scale_kind);
+  if (kgroups && (fused || packed_req || psplit))
+    return fail(FP8PA_EUNSUPPORTED, "sub-row K scales take the split kernels and no fused append");
+  if ((packed_req || psplit) && (vt || fused))
+    return fail(FP8PA_EUNSUPPORTED, "packed heads read V in HEADS_DMAJOR and take no fused append");
+  size_t vstage_off = 0;
+  if (vt) {
+    vstage_off = (lds + 15) / 16 * 16;
+    lds = vstage_off + fp8pa::decode_vstage_bytes(D);
+    if (lds > 65536)
+      return fail(FP8PA_EUNSUPPORTED, "B=%d, head_dim %d with V staged through LDS need %zu bytes of LDS (> 64 KiB)",
+                  B, D, lds);
+  }
+  if (vd->num_kv_heads != kd->num_kv_heads || vd->head_dim != kd->head_dim || vd->page_size != kd->page_size ||
+      (vd->scale_kind != kd->scale_kind && !(kgroups && vd->scale_kind == FP8PA_SCALE_F32_TOKEN_HEAD)))
+    return fail(FP8PA_EUNSUPPORTED,
+                "K and V pools must share num_kv_heads, head_dim, page_size and scale_kind (or K in fp32 "
+                "sub-row scales with V in F32_TOKEN_HEAD)");
+  // Packed heads: requested, or taken automatically when the units fill the
+  // device (V d-major, no fused append).
+  const bool packed = packed_req || (!vt && !fused && !kgroups && auto_packs(B, Hq, kd, workgroups, variant));
+  const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
   int W = workgroups;
   if (packed) {
-    const int nw = fp8pa::decode_waves(D, 0);
-    W = B * ((kd->num_kv_heads + nw - 1) / nw);
-    if (W < 1) W = 1;
+    const int64_t Wp = (int64_t)B * ((kd->num_kv_heads + nw - 1) / nw);
+    if (Wp > INT32_MAX) return fail(FP8PA_EUNSUPPORTED, "packed heads: %lld workgroups exceed the grid", (long long)Wp);
+    W = Wp < 1 ? 1 : (int)Wp;
   } else if (W == 0) {
     // One resident generation: every workgroup gets an equal share of the
     // tiles and all of them run at once.
-    const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
     const int cus = device_cus();
-    const int per_cu = cus > 0 ? fp8pa::decode_blocks_per_cu(D, kd->scale_kind, k_whole, tv, lds) : 0;
+    const int per_cu = cus > 0 ? fp8pa::decode_blocks_per_cu(D, kd->scale_kind, k_whole, lds) : 0;
     W = (cus > 0 && per_cu > 0) ? cus * per_cu : 1024;
   }
-  out->workgroups = W;
-  out->tile_tokens = fp8pa::decode_tile_tokens(D, tv);
-  out->variant = (variant == FP8PA_VARIANT_MFMA_FP8 || packed || psplit) ? variant : FP8PA_VARIANT_MFMA_BF16;
-  out->reserved = 0;
+  r->variant = f8 ? FP8PA_VARIANT_MFMA_FP8
+               : packed ? FP8PA_VARIANT_PACKED_HEADS
+               : psplit ? FP8PA_VARIANT_PACKED_SPLIT
+                        : FP8PA_VARIANT_MFMA_BF16;
+  r->vt = vt;
+  r->f8 = f8;
+  r->packed = packed;
+  r->psplit = psplit;
+  r->kgroups = kgroups;
+  r->k_whole = k_whole;
+  r->W = W;
+  r->Gu = Gu;
+  r->lds = lds;
+  r->vstage_off = vstage_off;
   if (W > 1 && !packed) {
-    const int64_t po = (int64_t)W * 2 * Gu * D * 4;
-    const int64_t pl = (int64_t)W * 2 * Gu * 4;
-    const int64_t pc = (int64_t)W * 2 * 4;
-    out->workspace_bytes = (po + 255) / 256 * 256 + (pl + 255) / 256 * 256 + (pc + 255) / 256 * 256;
+    r->part_o_bytes = round256((int64_t)W * 2 * Gu * D * 4);
+    r->part_lse_bytes = round256((int64_t)W * 2 * Gu * 4);
+    r->flag_bytes = round256((int64_t)W * 2 * 4);
   } else {
-    out->workspace_bytes = 0;
+    r->part_o_bytes = r->part_lse_bytes = r->flag_bytes = 0;
   }
-  if (lds_out) *lds_out = lds;
-  (void)max_seq_len;
-  (void)window;
+  r->workspace_bytes = r->part_o_bytes + r->part_lse_bytes + r->flag_bytes;
   return 0;
+}
+
+// Epochs tag published split partials; a merger clears consumed flags to 0,
+// so 0 is never handed out (the counter skips it when it wraps).
+uint32_t next_epoch(std::atomic<uint32_t>& counter) {
+  uint32_t e = counter.fetch_add(1) + 1;
+  while (e == 0) e = counter.fetch_add(1) + 1;
+  return e;
 }
 
 }  // namespace
@@ -293,12 +332,26 @@ const char* fp8pa_version(void) { return "fp8pa 0.1.0 gfx950"; }
 
 const char* fp8pa_last_error(void) { return g_err; }
 
-int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len, int window, int workgroups,
-                      int variant, fp8pa_plan* out) {
+int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, int max_seq_len,
+                      int window, int workgroups, int variant, fp8pa_plan* out) {
   if (!out) return fail(FP8PA_EINVAL, "plan output is NULL");
-  if (int rc = make_plan(B, Hq, kd, max_seq_len, window, workgroups, variant, out, nullptr)) return rc;
+  Resolved r{};
+  if (int rc = resolve(B, Hq, kd, vd, max_seq_len, workgroups, variant, false, &r)) return rc;
+  (void)window;   // the grid never depends on the window (nor on the lengths)
+  out->workgroups = r.W;
+  out->tile_tokens = fp8pa::decode_tile_tokens(kd->head_dim);
+  out->variant = r.variant;
+  out->reserved = 0;
+  out->workspace_bytes = r.workspace_bytes;
   ok();
   return FP8PA_OK;
+}
+
+int64_t fp8pa_decode_workspace_bytes(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
+                                     int max_seq_len, int window, int workgroups, int variant) {
+  fp8pa_plan p{};
+  if (int rc = fp8pa_decode_plan(B, Hq, kd, vd, max_seq_len, window, workgroups, variant, &p)) return rc;
+  return p.workspace_bytes;
 }
 
 namespace {
@@ -311,54 +364,16 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
                 const float* sinks, float sm_scale, int max_seq_len, int workgroups, int variant, void* workspace,
                 size_t workspace_bytes, void* stream, bool dry_run = false) {
   const bool fused = k_new != nullptr || v_new != nullptr;
-  fp8pa_plan plan{};
-  size_t lds = 0;
-  if (int rc = make_plan(B, Hq, kd, max_seq_len, window, workgroups, variant, &plan, &lds)) return rc;
-  if (int rc = check_desc(vd, "vd")) return rc;
-  if (kd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
-    return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS_D64, HEADS or TOKENS layout");
-  if (grouped(vd->scale_kind))
-    return fail(FP8PA_EUNSUPPORTED, "vd: decode reads fp32 sub-row scales for K only");
-  if (g_dbg && (kd->num_rows < 1 || vd->num_rows < 1))
-    return fail(FP8PA_EINVAL, "debug checks need num_rows >= 1 in both descriptors");
-  if (vd->layout == FP8PA_LAYOUT_HEADS_D64)
-    return fail(FP8PA_EUNSUPPORTED, "vd: decode reads V in the HEADS_DMAJOR, HEADS or TOKENS layout");
-  // V in a token-major layout is staged through LDS (default kernel shapes).
-  const bool vt = vd->layout == FP8PA_LAYOUT_HEADS || vd->layout == FP8PA_LAYOUT_TOKENS;
-  if (vt && fused) return fail(FP8PA_EUNSUPPORTED, "the one-launch append reads V in the HEADS_DMAJOR layout");
-  const bool f8 = variant == FP8PA_VARIANT_MFMA_FP8;
-  if (f8 && (kd->scale_kind == FP8PA_SCALE_E8M0_G32 || grouped(kd->scale_kind) || vt || fused))
-    return fail(FP8PA_EUNSUPPORTED,
-                "the fp8 compute mode takes fp32 page or token scales, V in HEADS_DMAJOR and no fused append");
-  // fp32 sub-row K scales: K pieces are scaled before the MFMA (plain,
-  // token-major-V and split kernels only).
-  const bool kgroups = grouped(kd->scale_kind);
-  if (kgroups && (fused || variant == FP8PA_VARIANT_PACKED_HEADS || variant == FP8PA_VARIANT_PACKED_SPLIT))
-    return fail(FP8PA_EUNSUPPORTED, "sub-row K scales take the split kernels and no fused append");
-  // Packed heads: requested, or taken automatically when the units fill the
-  // device (V d-major, no fused append; the plan's workspace then goes
-  // unused).
-  const bool psplit = variant == FP8PA_VARIANT_PACKED_SPLIT;
-  const bool packed_req = variant == FP8PA_VARIANT_PACKED_HEADS;
-  if ((packed_req || psplit) && (vt || fused))
-    return fail(FP8PA_EUNSUPPORTED, "packed heads read V in HEADS_DMAJOR and take no fused append");
-  const bool packed = packed_req || (!vt && !fused && !kgroups && auto_packs(B, Hq, kd, workgroups, variant));
-  const int tv_launch = (fused || vt || f8 || packed || psplit) ? 0 : tile_variant();
-  if (tv_launch != tile_variant() && !psplit)
-    lds = fp8pa::decode_lds_bytes(kd->head_dim, tv_launch, B, Hq / kd->num_kv_heads, kd->page_size);
-  size_t vstage_off = 0;
-  if (vt) {
-    vstage_off = (lds + 15) / 16 * 16;
-    lds = vstage_off + fp8pa::decode_vstage_bytes(kd->head_dim);
-    if (lds > 65536)
-      return fail(FP8PA_EUNSUPPORTED, "B=%d, head_dim %d with V staged through LDS need %zu bytes of LDS (> 64 KiB)",
-                  B, kd->head_dim, lds);
-  }
-  if (vd->num_kv_heads != kd->num_kv_heads || vd->head_dim != kd->head_dim || vd->page_size != kd->page_size ||
-      (vd->scale_kind != kd->scale_kind && !(kgroups && vd->scale_kind == FP8PA_SCALE_F32_TOKEN_HEAD)))
-    return fail(FP8PA_EUNSUPPORTED,
-                "K and V pools must share num_kv_heads, head_dim, page_size and scale_kind (or K in fp32 "
-                "sub-row scales with V in F32_TOKEN_HEAD)");
+  Resolved r{};
+  if (int rc = resolve(B, Hq, kd, vd, max_seq_len, workgroups, variant, fused, &r)) return rc;
+  const bool vt = r.vt, f8 = r.f8, packed = r.packed, psplit = r.psplit;
+  // The fp8 mode's E4M3 query moves each logit by up to 2^-4 of sm_scale *
+  // sum |q_d k_d|: within the page's fp8 tolerance class at the default score
+  // scale D^-0.5, not at larger ones (sm_scale = 1 with D = 256 spreads the
+  // logits over tens of units).  Larger scales are refused.
+  if (f8 && std::fabs((double)sm_scale) * std::sqrt((double)kd->head_dim) > 1.0 + 1e-6)
+    return fail(FP8PA_EUNSUPPORTED, "the fp8 compute mode serves |sm_scale| <= head_dim^-0.5 only (got %g at head_dim %d)",
+                (double)sm_scale, kd->head_dim);
   if (B == 0) {
     if (!dry_run) {
       ok();
@@ -379,17 +394,18 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   if (max_seq_len > 0 && bt_stride < (max_seq_len + kd->page_size - 1) / kd->page_size)
     return fail(FP8PA_EINVAL, "bt_stride %lld is smaller than the pages of max_seq_len", (long long)bt_stride);
   if (!std::isfinite(sm_scale)) return fail(FP8PA_EINVAL, "sm_scale must be finite");
-  if (plan.workspace_bytes > 0) {
-    if (!workspace || workspace_bytes < (size_t)plan.workspace_bytes)
-      return fail(FP8PA_EWORKSPACE, "workspace of %lld bytes required (%zu given)", (long long)plan.workspace_bytes,
+  if (r.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < (size_t)r.workspace_bytes)
+      return fail(FP8PA_EWORKSPACE, "workspace of %lld bytes required (%zu given)", (long long)r.workspace_bytes,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 256)) return fail(FP8PA_EINVAL, "workspace must be 256-byte aligned");
   }
   if (dry_run) return FP8PA_OK;
+  uint32_t* status = fp8pa::device_status_words();
+  if (!status) return fail(FP8PA_EHIP, "the device status words cannot be resolved on this device");
   const int D = kd->head_dim;
   const int G = Hq / kd->num_kv_heads;
-  const int nw_pk = fp8pa::decode_waves(D, 0);
-  const int W = (packed && !packed_req) ? B * ((kd->num_kv_heads + nw_pk - 1) / nw_pk) : plan.workgroups;
+  const int W = r.W;
   fp8pa::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.out = static_cast<uint16_t*>(out);
@@ -415,32 +431,32 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   a.G = G;
   a.window = window > 0 ? window : 0;
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
-  a.tile_variant = tv_launch;   // the fused, V-token-major and fp8 kernels exist in the default shapes
-  a.vstage_off = (int32_t)vstage_off;
+  a.vstage_off = (int32_t)r.vstage_off;
   a.dbg = g_dbg;
   a.dbg_rows = (int32_t)std::min<int64_t>(std::min(kd->num_rows, vd->num_rows), INT32_MAX);
   a.dbg_max_len = max_seq_len;
   // Packed splits: every wave reads every tile of a segment, so one tile per
   // share suffices, and a tile carries NW heads, so a unit's fixed cost is
   // NW times smaller in tiles.
-  const int nw = fp8pa::decode_waves(D, a.tile_variant);
-  a.min_tiles = min_tiles(psplit ? 1 : nw);
-  a.seg_cost = seg_cost(psplit ? fp8pa::decode_seg_cost(D, a.tile_variant) / nw
-                               : fp8pa::decode_seg_cost(D, a.tile_variant));
-  a.epoch = g_epoch.fetch_add(1) + 1;
+  const int nw = fp8pa::decode_waves(D);
+  a.min_tiles = psplit ? 1 : nw;
+  a.seg_cost = psplit ? fp8pa::decode_seg_cost(D) / nw : fp8pa::decode_seg_cost(D);
+  a.epoch = next_epoch(g_epoch);
+  // A forced timeout (test hook) waits for a flag value no holder writes.
+  a.wait_epoch = g_force_timeout ? a.epoch ^ 0x80000000u : a.epoch;
+  a.spin_limit = g_force_timeout ? (1 << 10) : (1 << 22);
+  a.status = status;
   if (W > 1 && !packed) {
-    const int Gu = psplit ? G * nw : G;   // query heads per unit (as in the plan)
-    const int64_t po = (int64_t)W * 2 * Gu * D * 4;
-    const int64_t pl = (int64_t)W * 2 * Gu * 4;
     char* ws = static_cast<char*>(workspace);
     a.part_o = reinterpret_cast<float*>(ws);
-    a.part_lse = reinterpret_cast<float*>(ws + (po + 255) / 256 * 256);
-    a.flags = reinterpret_cast<uint32_t*>(ws + (po + 255) / 256 * 256 + (pl + 255) / 256 * 256);
+    a.part_lse = reinterpret_cast<float*>(ws + r.part_o_bytes);
+    a.flags = reinterpret_cast<uint32_t*>(ws + r.part_o_bytes + r.part_lse_bytes);
   }
+  const size_t lds = r.lds;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // A wave's 16-byte K loads cover 64 bytes of each of 16 tokens: whole lines
   // when the 64-byte pieces of consecutive tokens are adjacent.
-  const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
+  const bool k_whole = r.k_whole;
   hipError_t e = fused ? fp8pa::launch_decode_fused(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
                  : vt  ? fp8pa::launch_decode_vtok(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
                  : f8  ? fp8pa::launch_decode_fp8q(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
@@ -536,6 +552,9 @@ int fp8pa_merge_splits(const float* part_o, const float* part_lse, const float* 
                        int S, int D, void* stream) {
   if (B < 0 || Hq < 1 || S < 0) return fail(FP8PA_EINVAL, "bad B/Hq/S");
   if (D != 64 && D != 128 && D != 256 && D != 512) return fail(FP8PA_EUNSUPPORTED, "D %d not in {64,128,256,512}", D);
+  // Grid (Hq, B); the S lse weights of a head are staged in LDS.
+  if (S > 16384 || B > 65535 || Hq > (1 << 24))
+    return fail(FP8PA_EUNSUPPORTED, "merge of B %d, Hq %d, S %d exceeds the grid or LDS", B, Hq, S);
   if (B == 0) {
     ok();
     return FP8PA_OK;
@@ -573,6 +592,10 @@ int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, ui
     ok();
     return FP8PA_OK;
   }
+  // Grid: (pages of the span, KV heads, 2 B) workgroups of 256 threads.
+  const int64_t max_pages = ((int64_t)T + kd->page_size - 1) / kd->page_size + 1;
+  if (B > (1 << 24) || max_pages > (1 << 23) || kd->num_kv_heads > 65535)
+    return fail(FP8PA_EUNSUPPORTED, "append grid too large (B %d, T %d, Hkv %d)", B, T, kd->num_kv_heads);
   if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !positions)
     return fail(FP8PA_EINVAL, "a required device pointer is NULL");
   if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
@@ -602,8 +625,7 @@ int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, ui
   a.P = kd->page_size;
   a.Hkv = kd->num_kv_heads;
   a.D = kd->head_dim;
-  const int max_pages = (T + kd->page_size - 1) / kd->page_size + 1;
-  hipError_t e = fp8pa::launch_append(a, B, max_pages, static_cast<hipStream_t>(stream));
+  hipError_t e = fp8pa::launch_append(a, B, (int)max_pages, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FP8PA_EHIP, "append launch: %s", hipGetErrorString(e));
   g_cnt.append.fetch_add(1);
   ok();
@@ -670,6 +692,30 @@ int fp8pa_set_decode_events(void* start, void* stop) {
 int fp8pa_set_debug_checks(uint32_t* err) {
   if (err && !aligned(err, 4)) return fail(FP8PA_EINVAL, "err must be 4-byte aligned");
   g_dbg = err;
+  ok();
+  return FP8PA_OK;
+}
+
+int fp8pa_get_device_status(fp8pa_device_status* out, int reset) {
+  if (!out) return fail(FP8PA_EINVAL, "status output is NULL");
+  uint32_t* w = fp8pa::device_status_words();
+  if (!w) return fail(FP8PA_EHIP, "the device status words cannot be resolved on this device");
+  hipError_t e = hipDeviceSynchronize();
+  uint32_t words[4] = {0, 0, 0, 0};
+  if (e == hipSuccess) e = hipMemcpy(words, w, sizeof(words), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) {
+    const uint32_t zero[4] = {0, 0, 0, 0};
+    e = hipMemcpy(w, zero, sizeof(zero), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) return fail(FP8PA_EHIP, "device status: %s", hipGetErrorString(e));
+  out->merge_timeouts = words[0];
+  for (int i = 0; i < 3; ++i) out->reserved[i] = 0;
+  ok();
+  return FP8PA_OK;
+}
+
+int fp8pa_debug_force_merge_timeout(int on) {
+  g_force_timeout = on != 0;
   ok();
   return FP8PA_OK;
 }

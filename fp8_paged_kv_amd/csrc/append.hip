@@ -56,6 +56,12 @@ __global__ void debug_dequant_kernel(const uint8_t* codes, const void* scales, i
     // The decode path's K conversion with an E8M0 scale.
     const uint32_t u = reinterpret_cast<const uint8_t*>(scales)[i];
     out[i] = __builtin_bit_cast(float, e4m3x2_to_bf16x2<false>(c, e8m0_as_scale_operand(u)) << 16);
+  } else if (kind >= 3) {
+    // The sub-row key path's conversion: fp32(code x scale), formed before
+    // the hi/lo split into bf16 operands.
+    float v[8];
+    scaled_e4m3x8(c, 0u, reinterpret_cast<const float*>(scales)[i], v);
+    out[i] = v[0];
   } else {
     // The decode path's conversion, then the fp32 scale.
     const float v = __builtin_bit_cast(float, e4m3x2_to_bf16x2<false>(c, 1.0f) << 16);

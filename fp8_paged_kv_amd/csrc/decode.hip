@@ -1,54 +1,55 @@
-// Host side of the paged decode: shape policy, LDS sizing, occupancy and the
-// launch of the plain (no append) kernels.  The kernel is in decode_kernel.h.
+// Host side of the paged decode: LDS sizing, occupancy, the device status
+// words and the launch of the plain (no append) kernels.  The kernel is in
+// decode_kernel.h.
+#include <mutex>
 #include <unordered_map>
 
 #include "decode_kernel.h"
 
 namespace fp8pa {
 
-int decode_waves(int D, int tile_variant) {
-  auto q = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() { return NW; };
-  return by_shape<true>(D, tile_variant, q);
-}
-
-int decode_seg_cost(int D, int tile_variant) {
-  auto q = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() { return SCD; };
-  return by_shape<true>(D, tile_variant, q);
-}
-
-size_t decode_lds_bytes(int D, int tile_variant, int B, int G, int P) {
-  const int TT = decode_tile_tokens(D, tile_variant);
-  const size_t pre = (size_t)3 * ((B + 4) & ~3) * 4;
-  const size_t stage = (size_t)(kMaxSplitTokens / TT * TT / P + 2) * 4;
-  const size_t combine = (size_t)(decode_waves(D, tile_variant) / 2) * G * (D + 4) * 4;
-  return pre + (stage > combine ? stage : combine);
-}
-
-int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, int tile_variant, size_t lds) {
+int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, size_t lds) {
   // Workgroups launched per CU: the shape's count, if that many fit.  The
   // occupancy query is a host call; its answers are remembered per thread
   // (they depend only on the kernel and its LDS, the same on every device
   // of this architecture).
   thread_local std::unordered_map<uint64_t, int> memo;
   const uint64_t key = (uint64_t)D | ((uint64_t)scale_kind << 12) | ((uint64_t)k_whole_lines << 14) |
-                       ((uint64_t)tile_variant << 16) | ((uint64_t)lds << 24);
+                       ((uint64_t)lds << 24);
   const auto it = memo.find(key);
   if (it != memo.end()) return it->second;
-  auto q = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() {
-    const int nb = occupancy_d<DD, NS, PF, OCC, KNT, NW>(scale_kind, lds);
-    return nb < WPC ? nb : WPC;
-  };
-  const int r = k_whole_lines ? by_shape<true>(D, tile_variant, q) : by_shape<false>(D, tile_variant, q);
+  const int r = with_head_dim(D, [&]<int DD>() {
+    const int nb = k_whole_lines ? occupancy_d<DD, true>(scale_kind, lds) : occupancy_d<DD, false>(scale_kind, lds);
+    return nb < Shape<DD>::WPC ? nb : Shape<DD>::WPC;
+  });
   if (r > 0) memo.emplace(key, r);
   return r;
 }
 
+namespace {
+// Status words of each device (DecodeArgs::status): one copy per device,
+// which holds it until the process ends.
+__device__ __align__(16) uint32_t status_words[4];
+}  // namespace
+
+uint32_t* device_status_words() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint32_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(status_words)) != hipSuccess) return nullptr;
+    addr[dev] = static_cast<uint32_t*>(p);
+  }
+  return addr[dev];
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                          hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  auto l = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() {
-    return launch_d<DD, NS, PF, OCC, KNT, NW, false>(a, scale_kind, W, lds, st, e0, e1);
-  };
-  return k_whole_lines ? by_shape<true>(D, a.tile_variant, l) : by_shape<false>(D, a.tile_variant, l);
+  return launch_family<false>(a, D, scale_kind, k_whole_lines, W, lds, st, e0, e1);
 }
 
 }  // namespace fp8pa

@@ -113,20 +113,11 @@ __device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8& hi, bf
 }
 
 // Eight E4M3 codes (element i from byte i of w0:w1) times an fp32 scale, as
-// a hi/lo pair of bf16 operands: x = fp32(code * s), hi = bf16(x), lo =
-// bf16(x - hi).
+// a hi/lo pair of bf16 operands: x = fp32(code * s) (scaled_e4m3x8), hi =
+// bf16(x), lo = bf16(x - hi).
 __device__ __forceinline__ void scaled_e4m3x8_hilo(uint32_t w0, uint32_t w1, float s, bf16x8& hi, bf16x8& lo) {
   float v[8];
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-  v[0] = a[0] * s;
-  v[1] = a[1] * s;
-  v[2] = b[0] * s;
-  v[3] = b[1] * s;
-  v[4] = c[0] * s;
-  v[5] = c[1] * s;
-  v[6] = d[0] * s;
-  v[7] = d[1] * s;
+  scaled_e4m3x8(w0, w1, s, v);
   split_bf16x8(v, hi, lo);
 }
 
@@ -161,15 +152,8 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
 __device__ __forceinline__ uint32_t byte_of(const u32x4& v, int i) { return (v[i >> 2] >> (8 * (i & 3))) & 0xffu; }
 
 // V token-major (VT): a lane loads NIV = NS*D/32 16-byte pieces, dims
-// 16*(l % (D/16)).. +15 of NIV consecutive positions (one page).  The stage of
-// a wave holds the tile's positions as rows of VH dims (VH + 16 bytes apart,
-// which spreads the 8 rows of a transpose read over distinct banks); D > VH
-// takes D/VH passes.
-template <int D>
-struct VStage {
-  static constexpr int VH = D < 128 ? D : 128;   // dims per pass
-  static constexpr int RS = VH + 16;             // stage row stride, bytes
-};
+// 16*(l % (D/16)).. +15 of NIV consecutive positions (one page), staged per
+// wave in LDS (VStage<D>).
 
 // Registers of one tile for one lane.
 template <int D, int NS, int SK, bool VT>
@@ -203,14 +187,14 @@ struct Tile {
 // tile of its segment for KV head NW*g + v (the NW waves read the same page
 // rows together), so no wave combine is needed; shares, partials and merges
 // are those of the split kernel over these wider units.
-template <int D, int NS, int SK, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT, bool F8 = false,
-          bool PK = false, bool PS = false>
-__global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a) {
-  static_assert(!(PS && (FUSED || PK || PF)), "packed splits: plain kernels without prefetch");
+template <int D, int SK, bool KNT, bool FUSED, bool VT, bool F8 = false, bool PK = false, bool PS = false>
+__global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kernel(const DecodeArgs a) {
+  static_assert(!(PS && (FUSED || PK)), "packed splits: plain kernels");
   static_assert(!(F8 && SK >= 2), "E8M0 and sub-row K scales vary inside one fp8 MFMA");
   static_assert(!(SK == 3 && (FUSED || PK || PS)), "sub-row K scales: split kernels without the fused append");
-  static_assert(!(PK && (FUSED || F8 || PF)), "packed heads: plain bf16 kernels without prefetch");
-  static_assert(!(FUSED && PF), "the fused append waits inside the non-prefetching tile loop");
+  static_assert(!(PK && (FUSED || F8)), "packed heads: plain bf16 kernels");
+  constexpr int NS = Shape<D>::NS;
+  constexpr int NW = Shape<D>::NW;
   constexpr int NT = 64 * NW;   // threads (NW wave64s)
   constexpr int TT = 32 * NS;   // positions per tile
   constexpr int GT = 8 * NS;    // positions per group
@@ -954,8 +938,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       if constexpr (F8) {
         // The row's amax (the four quads of a head column hold its dims),
         // its scale fp32(amax / 448) (1 for a zero row), and the codes
-        // e4m3(fp32(q * fp32(1 / scale))), byte i of a dword pair = dim i of
-        // the operand.
+        // e4m3(fp32(q / scale)) with the IEEE-rounded quotient (the rule of
+        // the KV quantizer), byte i of a dword pair = dim i of the operand.
         float am = 0.0f;
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
@@ -967,15 +951,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
         am = fmaxf(am, __shfl_xor(am, 16));
         am = fmaxf(am, __shfl_xor(am, 32));
         qsc = am > 0.0f ? am / 448.0f : 1.0f;
-        const float rq = 1.0f / qsc;   // one division; the codes take a product each
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
           const u32x4 v = __builtin_bit_cast(u32x4, qop[i]);
           uint64_t c = 0;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)v[j]) * rq) << (16 * j);
-            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)(v[j] >> 16)) * rq) << (16 * j + 8);
+            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)v[j]) / qsc) << (16 * j);
+            c |= (uint64_t)f32_to_e4m3(bf16_to_f32((uint16_t)(v[j] >> 16)) / qsc) << (16 * j + 8);
           }
           qop8[i] = c;
         }
@@ -1021,22 +1004,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
           while (__hip_atomic_load(&s_app, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != seg_no)
             __builtin_amdgcn_s_sleep(1);
       };
-      if constexpr (PF) {
-        // Loads run one tile ahead, ping-ponging two register buffers.  The
-        // trip count is fixed and loads are unconditional (a prefetch past
-        // the last tile re-reads a cache-hot tile), so the waits before each
-        // compute cover only that tile's loads.
-        TileT A, Bt;
-        if (nmine > 0) load_tile(A, tile_pos(0));
-        const int npairs = nmine / 2;
-        for (int k = 0; k < npairs; ++k) {
-          load_tile(Bt, tile_pos(2 * k + 1));
-          compute_tile(A, tile_pos(2 * k));
-          load_tile(A, tile_pos(2 * k + 2 < nmine ? 2 * k + 2 : 2 * k + 1));
-          compute_tile(Bt, tile_pos(2 * k + 1));
-        }
-        if (nmine & 1) compute_tile(A, tile_pos(nmine - 1));
-      } else {
+      {
         TileT A;
         for (int k = 0; k < nmine; ++k) {
           if constexpr (FUSED) await_append(k);
@@ -1175,12 +1143,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
     }
     // Wait for the other holders' flags.  They have lower indices, so they
     // were dispatched first and never wait on this workgroup; the wait is
-    // bounded all the same (a timeout yields NaN outputs).
+    // bounded all the same: a merge that gives up writes NaN outputs and
+    // counts itself in the device status word.
     for (int i = threadIdx.x; i < nseg - 1; i += NT) {
       const uint32_t* f = a.flags + 2 * (w_a + i) + slot_of(w_a + i);
       int spins = 0;
-      while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
-        if (++spins > (1 << 22)) {
+      while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.wait_epoch) {
+        if (++spins > a.spin_limit) {
           s_timeout = 1;
           break;
         }
@@ -1188,6 +1157,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
       }
     }
     __syncthreads();
+    if (threadIdx.x == 0 && s_timeout)
+      __hip_atomic_fetch_add(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int bq = pend_b, gq = pend_g;
     const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
     // Merged 64 partials at a time with a running maximum per head (the sink
@@ -1345,91 +1316,51 @@ __global__ __launch_bounds__(64 * NW, OCC) void decode_kernel(const DecodeArgs a
   }
 }
 
-template <int D, int NS, bool PF, int OCC, bool KNT, int NW, bool FUSED, bool VT = false, bool F8 = false,
-          bool PK = false, bool PS = false>
+template <int D, bool KNT, bool FUSED, bool VT = false, bool F8 = false, bool PK = false, bool PS = false>
 hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  dim3 grid(W), block(64 * NW);
+  dim3 grid(W), block(64 * Shape<D>::NW);
   switch (sk) {
     case 0:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 0, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, 0, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
     case 1:
-      hipExtLaunchKernelGGL((decode_kernel<D, NS, 1, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
+      hipExtLaunchKernelGGL((decode_kernel<D, 1, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
     case 2:
       if constexpr (F8) return hipErrorNotSupported;
-      else hipExtLaunchKernelGGL((decode_kernel<D, NS, 2, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
+      else hipExtLaunchKernelGGL((decode_kernel<D, 2, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
     default:   // fp32 sub-row K scales
       if constexpr (F8 || FUSED || PK || PS) return hipErrorNotSupported;
-      else hipExtLaunchKernelGGL((decode_kernel<D, NS, 3, PF, OCC, KNT, NW, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
+      else hipExtLaunchKernelGGL((decode_kernel<D, 3, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
   }
   return hipGetLastError();
 }
 
-template <int D, int NS, bool PF, int OCC, bool KNT, int NW>
+// Launch of one kernel family (FUSED, VT, F8, PK, PS) at the head dim and K
+// line coverage of the call.
+template <bool FUSED, bool VT = false, bool F8 = false, bool PK = false, bool PS = false>
+hipError_t launch_family(const DecodeArgs& a, int D, int sk, bool k_whole_lines, int W, size_t lds, hipStream_t st,
+                         hipEvent_t e0, hipEvent_t e1) {
+  return with_head_dim(D, [&]<int DD>() {
+    return k_whole_lines ? launch_d<DD, true, FUSED, VT, F8, PK, PS>(a, sk, W, lds, st, e0, e1)
+                         : launch_d<DD, false, FUSED, VT, F8, PK, PS>(a, sk, W, lds, st, e0, e1);
+  });
+}
+
+template <int D, bool KNT>
 int occupancy_d(int sk, size_t lds) {
   int nb = 0;
   hipError_t e;
+  constexpr int NT = 64 * Shape<D>::NW;
   switch (sk) {
-    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 0, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 1, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 2, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, NS, 3, PF, OCC, KNT, NW, false, false>, 64 * NW, lds); break;
+    case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 0, KNT, false, false>, NT, lds); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 1, KNT, false, false>, NT, lds); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 2, KNT, false, false>, NT, lds); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 3, KNT, false, false>, NT, lds); break;
   }
   return e == hipSuccess ? nb : -1;
-}
-
-// The default shape of each head dim.
-template <bool KNT, typename F>
-auto default_shape(int D, F&& f) {
-  switch (D) {
-    case 64: return f.template operator()<64, 2, false, 2, KNT, 4, 2, 24>();
-    case 128: return f.template operator()<128, 2, false, 2, KNT, 4, 1, 36>();
-    case 256: return f.template operator()<256, 1, false, 1, KNT, 4, 1, 24>();
-    default: return f.template operator()<512, 1, false, 1, KNT, 4, 1, 24>();
-  }
-}
-
-// Dispatch on head dim and kernel shape.  A shape is <head dim, NS (tile =
-// 32*NS positions), prefetch one tile ahead, register occupancy the kernel is
-// compiled for, whole-line K loads, waves per workgroup, workgroups launched
-// per CU, default unit cost in the share balance (quarter tiles)>.
-// tile_variant (tuning; 0 = default):
-//   head dim 64:  4 prefetch; 7 eight waves, one workgroup per CU; 8 as 7 with prefetch
-//   head dim 128: 1 prefetch at one wave per SIMD; 2 prefetch with 32-position
-//                 tiles; 4 prefetch, two workgroups per CU; 7 eight waves;
-//                 9 two workgroups per CU; 10 compiled for one workgroup per CU
-//   head dim 256: 4 prefetch
-template <bool KNT, typename F>
-auto by_shape(int D, int v, F&& f) {
-  switch (D) {
-    case 64:
-      switch (v) {
-        case 4: return f.template operator()<64, 2, true, 2, KNT, 4, 2, 24>();
-        case 7: return f.template operator()<64, 2, false, 1, KNT, 8, 1, 24>();
-        case 8: return f.template operator()<64, 2, true, 1, KNT, 8, 1, 24>();
-        default: break;
-      }
-      break;
-    case 128:
-      switch (v) {
-        case 1: return f.template operator()<128, 2, true, 1, KNT, 4, 1, 36>();
-        case 2: return f.template operator()<128, 1, true, 2, KNT, 4, 2, 24>();
-        case 4: return f.template operator()<128, 2, true, 2, KNT, 4, 2, 24>();
-        case 7: return f.template operator()<128, 2, false, 1, KNT, 8, 1, 24>();
-        case 9: return f.template operator()<128, 2, false, 2, KNT, 4, 2, 24>();
-        case 10: return f.template operator()<128, 2, false, 1, KNT, 4, 1, 36>();
-        default: break;
-      }
-      break;
-    case 256:
-      if (v == 4) return f.template operator()<256, 1, true, 1, KNT, 4, 1, 24>();
-      break;
-    default: break;
-  }
-  return default_shape<KNT>(D, f);
 }
 
 }  // namespace

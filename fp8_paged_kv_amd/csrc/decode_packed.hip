@@ -9,10 +9,7 @@ namespace fp8pa {
 
 hipError_t launch_decode_packed(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                                 hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  auto l = [&]<int DD, int NS, bool PF, int OCC, bool KNT, int NW, int WPC, int SCD>() {
-    return launch_d<DD, NS, PF, OCC, KNT, NW, false, false, false, true>(a, scale_kind, W, lds, st, e0, e1);
-  };
-  return k_whole_lines ? default_shape<true>(D, l) : default_shape<false>(D, l);
+  return launch_family<false, false, false, true>(a, D, scale_kind, k_whole_lines, W, lds, st, e0, e1);
 }
 
 }  // namespace fp8pa

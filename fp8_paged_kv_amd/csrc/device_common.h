@@ -37,6 +37,22 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1, flo
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Eight E4M3 codes (element i from byte i of w0:w1) times an fp32 scale:
+// v[i] = fp32(code_i * s), one rounding of the exact product (the code's
+// fp32 value is exact).
+__device__ __forceinline__ void scaled_e4m3x8(uint32_t w0, uint32_t w1, float s, float (&v)[8]) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  v[0] = a[0] * s;
+  v[1] = a[1] * s;
+  v[2] = b[0] * s;
+  v[3] = b[1] * s;
+  v[4] = c[0] * s;
+  v[5] = c[1] * s;
+  v[6] = d[0] * s;
+  v[7] = d[1] * s;
+}
+
 // fp32 operand carrying an E8M0 scale byte in its exponent field.
 __device__ __forceinline__ float e8m0_as_scale_operand(uint32_t u) {
   return __builtin_bit_cast(float, u << 23);

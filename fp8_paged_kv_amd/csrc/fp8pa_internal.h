@@ -56,8 +56,10 @@ struct DecodeArgs {
   float* part_o;           // [W][2][G][D] partial outputs (first / last segment of a workgroup)
   float* part_lse;         // [W][2][G] base-2 log-sum-exp of each partial
   uint32_t* flags;         // [W][2] a slot's flag holds the call's epoch once its partial is complete
-  uint32_t epoch;          // distinct per call
-  int32_t tile_variant;    // kernel shape (tuning; 0 = default)
+  uint32_t epoch;          // distinct per call, never 0 (cleared flags hold 0)
+  uint32_t wait_epoch;     // the flag value a merger waits for (= epoch)
+  int32_t spin_limit;      // sleeps after which a merger's wait for a flag gives up
+  uint32_t* status;        // device status words: [0] counts merges whose wait gave up
   int32_t min_tiles;       // fewest tiles per active workgroup (>= 1)
   int32_t seg_cost;        // fixed cost of a unit in the share balance, in quarter tiles (>= 0)
   PoolGeom kg, vg;
@@ -95,33 +97,95 @@ struct AppendArgs {
   int32_t dbg_rows;
 };
 
-// Tokens per decode tile (one tile = one MFMA round of one wave).
-inline int decode_tile_tokens(int D, int tile_variant = 0) {
-  return (D <= 128 && !(D == 128 && tile_variant == 2)) ? 64 : 32;
+// Kernel shape of each head dim: NS (a tile is 32*NS positions), the
+// occupancy the kernel is compiled for (OCC waves per SIMD), waves per
+// workgroup (NW), workgroups launched per CU (WPC), and a unit's fixed cost in
+// the share balance, in quarter tiles (SC).  At head dim 128 one four-wave
+// workgroup per CU streams as fast as two and cuts half as many units.
+template <int D>
+struct Shape;
+template <>
+struct Shape<64> { static constexpr int NS = 2, OCC = 2, NW = 4, WPC = 2, SC = 24; };
+template <>
+struct Shape<128> { static constexpr int NS = 2, OCC = 2, NW = 4, WPC = 1, SC = 36; };
+template <>
+struct Shape<256> { static constexpr int NS = 1, OCC = 1, NW = 4, WPC = 1, SC = 24; };
+template <>
+struct Shape<512> { static constexpr int NS = 1, OCC = 1, NW = 4, WPC = 1, SC = 24; };
+
+// f.template operator()<D>() for a supported head dim D (64, 128, 256, 512).
+template <typename F>
+auto with_head_dim(int D, F&& f) {
+  switch (D) {
+    case 64: return f.template operator()<64>();
+    case 128: return f.template operator()<128>();
+    case 256: return f.template operator()<256>();
+    default: return f.template operator()<512>();
+  }
+}
+
+// Tokens per decode tile (one tile = one MFMA round of one wave), wave64s per
+// decode workgroup, and a unit's default fixed cost in the share balance.
+inline int decode_tile_tokens(int D) {
+  return with_head_dim(D, []<int DD>() { return 32 * Shape<DD>::NS; });
+}
+inline int decode_waves(int D) {
+  return with_head_dim(D, []<int DD>() { return Shape<DD>::NW; });
+}
+inline int decode_seg_cost(int D) {
+  return with_head_dim(D, []<int DD>() { return Shape<DD>::SC; });
+}
+inline int decode_wg_per_cu(int D) {
+  return with_head_dim(D, []<int DD>() { return Shape<DD>::WPC; });
 }
 
 // Positions whose page rows a workgroup stages in LDS at once.
 constexpr int kMaxSplitTokens = 16384;
 
+// V token-major (VT): the stage of a wave holds a tile's positions as rows of
+// VH dims, RS bytes apart (16 bytes of padding spread the 8 rows of a
+// transpose read over distinct banks); D > VH takes D/VH passes.
+template <int D>
+struct VStage {
+  static constexpr int VH = D < 128 ? D : 128;   // dims per pass
+  static constexpr int RS = VH + 16;             // stage row stride, bytes
+};
+
+// Dynamic LDS of a decode launch: the tile and non-empty prefixes and the
+// lengths (3 words per sequence), then the larger of the page-row stage and
+// the wave-combine buffer.
+inline size_t decode_lds_bytes(int D, int B, int G, int P) {
+  const int TT = decode_tile_tokens(D);
+  const size_t pre = (size_t)3 * (((int64_t)B + 4) & ~int64_t(3)) * 4;
+  const size_t stage = (size_t)(kMaxSplitTokens / TT * TT / P + 2) * 4;
+  const size_t combine = (size_t)(decode_waves(D) / 2) * G * (D + 4) * 4;
+  return pre + (stage > combine ? stage : combine);
+}
+
+// The per-wave V stages a token-major V pool adds (+ slack to align them to
+// 16 bytes).
+inline size_t decode_vstage_bytes(int D) {
+  return with_head_dim(D, []<int DD>() -> size_t {
+    return (size_t)Shape<DD>::NW * 32 * Shape<DD>::NS * VStage<DD>::RS + 16;
+  });
+}
+
 // Dynamic LDS of a decode launch, resident workgroups per CU, and the launch
 // itself (start/stop: optional events that time the decode kernel alone;
 // k_whole_lines: the K layout lets every 16-byte K load of a wave cover whole
 // 128-byte lines, so non-temporal loads are used).
-int decode_waves(int D, int tile_variant);   // wave64s per decode workgroup
-int decode_seg_cost(int D, int tile_variant);   // default unit cost in the share balance
-size_t decode_lds_bytes(int D, int tile_variant, int B, int G, int P);
-int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, int tile_variant, size_t lds);
+int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, size_t lds);
+// Device address of the current device's status words (see DecodeArgs::status),
+// or null if it cannot be resolved.
+uint32_t* device_status_words();
 hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                          hipStream_t st, hipEvent_t start, hipEvent_t stop);
-// The same with the new tokens appended in-kernel (a.k_new, a.v_new), default
-// kernel shape only (tile_variant 0).
+// The same with the new tokens appended in-kernel (a.k_new, a.v_new).
 hipError_t launch_decode_fused(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                                hipStream_t st, hipEvent_t start, hipEvent_t stop);
-// V in a token-major layout (HEADS or TOKENS), staged through LDS: the
-// decode with default kernel shapes, and the dynamic LDS its V stages add.
+// V in a token-major layout (HEADS or TOKENS), staged through LDS.
 hipError_t launch_decode_vtok(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                               hipStream_t st, hipEvent_t start, hipEvent_t stop);
-size_t decode_vstage_bytes(int D);
 // The fp8 compute mode (fp8 MFMA for QK^T over E4M3-rounded queries), default
 // kernel shapes, fp32 scales only.
 hipError_t launch_decode_fp8q(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,

@@ -41,13 +41,20 @@ class Counters(ctypes.Structure):
                                               "decode_packed_split")]
 
 
+class DeviceStatus(ctypes.Structure):
+    _fields_ = [("merge_timeouts", ctypes.c_uint64), ("reserved", ctypes.c_uint64 * 3)]
+
+
 _lib = None
 _P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
 SIGNATURES = {
     "fp8pa_version": ([], ctypes.c_char_p),
     "fp8pa_last_error": ([], ctypes.c_char_p),
-    "fp8pa_decode_plan": ([_I, _I, ctypes.POINTER(PoolDesc), _I, _I, _I, _I, ctypes.POINTER(Plan)], _I),
+    "fp8pa_decode_plan": ([_I, _I, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _I, _I, _I, _I,
+                           ctypes.POINTER(Plan)], _I),
+    "fp8pa_decode_workspace_bytes": ([_I, _I, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _I, _I, _I, _I],
+                                     _I64),
     "fp8pa_decode": ([_P, _P, _P, _P, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _P, _I64, _P, _I, _I, _I,
                       _P, _F, _I, _I, _I, _P, _SZ, _P], _I),
     "fp8pa_append_decode": ([_P, _P, _P, _P, _P, _P, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _P, _I64,
@@ -61,6 +68,8 @@ SIGNATURES = {
     "fp8pa_set_debug_checks": ([_P], _I),
     "fp8pa_set_decode_events": ([_P, _P], _I),
     "fp8pa_stream_read": ([_P, _SZ, _P, _P], _I),
+    "fp8pa_get_device_status": ([ctypes.POINTER(DeviceStatus), _I], _I),
+    "fp8pa_debug_force_merge_timeout": ([_I], _I),
 }
 
 
@@ -125,11 +134,21 @@ def _need(t, name, dtype=None, device=True):
         raise ValueError(f"{name} must be contiguous")
 
 
-def decode_plan(B, Hq, kd, max_seq_len, window=0, workgroups=0, variant="auto"):
+def decode_plan(B, Hq, kd, vd, max_seq_len, window=0, workgroups=0, variant="auto"):
+    """The variant, grid and workspace an fp8pa_decode call with these
+    arguments launches (raises what that call would)."""
     p = Plan()
-    _check(lib().fp8pa_decode_plan(B, Hq, ctypes.byref(kd), max_seq_len, window, workgroups,
+    _check(lib().fp8pa_decode_plan(B, Hq, ctypes.byref(kd), ctypes.byref(vd), max_seq_len, window, workgroups,
                                    VARIANTS.get(variant, variant), ctypes.byref(p)))
     return p
+
+
+def decode_workspace_bytes(B, Hq, kd, vd, max_seq_len, window=0, workgroups=0, variant="auto"):
+    n = lib().fp8pa_decode_workspace_bytes(B, Hq, ctypes.byref(kd), ctypes.byref(vd), max_seq_len, window,
+                                           workgroups, VARIANTS.get(variant, variant))
+    if n < 0:
+        raise Fp8paError(n, last_error())
+    return n
 
 
 def decode(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window=0, sinks=None, sm_scale=None,
@@ -153,7 +172,7 @@ def decode(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window
     _need(out, "out", torch.bfloat16)
     scale = D ** -0.5 if sm_scale is None else float(sm_scale)
     if workspace is None:   # (a given workspace is checked by the library)
-        plan = decode_plan(B, Hq, kd, max_seq_len, window, workgroups, variant)
+        plan = decode_plan(B, Hq, kd, vd, max_seq_len, window, workgroups, variant)
         if plan.workspace_bytes > 0:
             workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -187,7 +206,7 @@ def append_decode(q, k_new, v_new, k_pool, v_pool, kd, vd, block_table, seq_lens
     _need(out, "out", torch.bfloat16)
     scale = D ** -0.5 if sm_scale is None else float(sm_scale)
     if workspace is None:   # (a given workspace is checked by the library)
-        plan = decode_plan(B, Hq, kd, max_seq_len, window, workgroups, variant)
+        plan = decode_plan(B, Hq, kd, vd, max_seq_len, window, workgroups, variant)
         if plan.workspace_bytes > 0:
             workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -254,6 +273,19 @@ def set_debug_checks(err=None):
 def stream_read(buf, sink, stream=None):
     """Measurement helper: one streaming read of the whole of `buf`."""
     _check(lib().fp8pa_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def device_status(reset=False):
+    """The current device's status words (synchronizes the device):
+    {"merge_timeouts": n}; reset clears them."""
+    st = DeviceStatus()
+    _check(lib().fp8pa_get_device_status(ctypes.byref(st), 1 if reset else 0))
+    return {"merge_timeouts": int(st.merge_timeouts)}
+
+
+def force_merge_timeout(on):
+    """Test hook: while on (this thread), split merges give up waiting."""
+    _check(lib().fp8pa_debug_force_merge_timeout(1 if on else 0))
 
 
 def set_decode_events(start, stop):

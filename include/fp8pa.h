@@ -96,12 +96,16 @@ enum {
                                    serving", "Two compute paths": the fp8 dot rounds q to
                                    E4M3): each query row (sequence, query head) is
                                    quantized with one fp32 scale fp32(amax/448) (1 for a
-                                   zero row) and codes e4m3(fp32(q/scale)); QK^T takes the
-                                   K codes unconverted on the fp8 MFMA; PV and the softmax
-                                   as in MFMA_BF16.  Only on explicit request; pools with
-                                   fp32 scales and V in HEADS_DMAJOR, not with the fused
-                                   append (else FP8PA_EUNSUPPORTED); fp8pa_append_decode
-                                   runs it after the append kernel. */
+                                   zero row) and codes e4m3(fp32(q/scale)) with the IEEE
+                                   quotient (the KV quantizer's rule); QK^T takes the K
+                                   codes unconverted on the fp8 MFMA; PV and the softmax as
+                                   in MFMA_BF16.  Only on explicit request; pools with fp32
+                                   scales and V in HEADS_DMAJOR, |sm_scale| <= D^-0.5 (the
+                                   page's fp8 tolerance class, rtol = atol = 1.5e-1, holds
+                                   at the default score scale; larger scales spread the
+                                   logits so that q's rounding exceeds it), not with the
+                                   fused append (else FP8PA_EUNSUPPORTED);
+                                   fp8pa_append_decode runs it after the append kernel. */
   FP8PA_VARIANT_PACKED_HEADS = 3  /* packed heads (page "fp8 paged attention for MoE
                                    serving", pack_heads): one workgroup per (sequence,
                                    group of KV heads), one KV head per wave, no split and
@@ -114,9 +118,7 @@ enum {
                                    fp8pa_decode runs it instead of the split kernel when V
                                    is in HEADS_DMAJOR, D <= 128 and the B * ceil(Hkv / 4) units alone
                                    fill every resident workgroup slot of the device (the
-                                   plan still reports the split kernel's grid and
-                                   workspace, which then go unused; the counters record
-                                   what ran). */,
+                                   plan, given the same pools, reports it). */,
   FP8PA_VARIANT_PACKED_SPLIT = 4  /* packed heads with splits: a unit is (sequence, 4
                                    consecutive KV heads), one KV head per wave, so a
                                    workgroup reads whole groups of heads of each page row
@@ -161,27 +163,44 @@ typedef struct fp8pa_pool_desc {
  * is balanced however uneven the sequence lengths are.  Units cut between
  * workgroups are merged by log-sum-exp inside the same launch. */
 typedef struct fp8pa_plan {
-  int32_t workgroups;       /* W (auto: all resident at once on this device) */
+  int32_t workgroups;       /* W launched (auto: all resident at once on this device) */
   int32_t tile_tokens;      /* positions per tile */
-  int32_t variant;          /* FP8PA_VARIANT_* that will run */
+  int32_t variant;          /* FP8PA_VARIANT_* that fp8pa_decode runs with these arguments */
   int32_t reserved;
-  int64_t workspace_bytes;  /* needed by fp8pa_decode (0 when W == 1) */
+  int64_t workspace_bytes;  /* needed by fp8pa_decode (0 when nothing is split) */
 } fp8pa_plan;
 
 /* Library version string; never NULL. */
 const char* fp8pa_version(void);
 
-/* Message of the last error on the calling thread ("" if none). */
+/* Message of the last error on the calling thread ("" if none).  Every
+ * refusal is reported, as the page "fp8 paged attention for MoE serving"
+ * ("Two compute paths") asks of an explicit request that cannot be served:
+ * it is refused with a reason, never silently replaced. */
 const char* fp8pa_last_error(void);
 
-/* Plan a decode call.  B sequences, Hq query heads, K pool `kd`; every
- * seq_lens[b] must be <= max_seq_len; window <= 0 means none; workgroups 0
- * lets the library choose, else it is used as given (>= 1).  Refuses
- * (FP8PA_EUNSUPPORTED) shapes whose LDS needs exceed 64 KiB: 12 bytes per
- * sequence plus the larger of the page-row stage and the wave combine, i.e.
- * B above about 5000 (head dim 128) or 2700 (head dim 512 with G = 8). */
-int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, int max_seq_len,
-                      int window, int workgroups, int variant, fp8pa_plan* out);
+/* Plan a decode call (the split grid of page "fp8 paged attention for MoE
+ * serving", section "Why it happens": the grid runs over sequence, KV head
+ * and split, and an unsplit grid leaves most of the device idle).  B
+ * sequences, Hq query heads, pools `kd` and `vd` as they will be passed to
+ * fp8pa_decode; every seq_lens[b] must be <= max_seq_len; window <= 0 means
+ * none (the grid does not depend on it); workgroups 0 lets the library
+ * choose, else it is used as given (>= 1).  Validates the geometry exactly as
+ * fp8pa_decode does (same refusals) and reports the variant, grid and
+ * workspace that call launches.  Refuses (FP8PA_EUNSUPPORTED) shapes whose
+ * LDS needs exceed 64 KiB: 12 bytes per sequence plus the larger of the
+ * page-row stage and the wave combine, i.e. B above about 5000 (head dim 128)
+ * or 2700 (head dim 512 with G = 8). */
+int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
+                      int max_seq_len, int window, int workgroups, int variant, fp8pa_plan* out);
+
+/* Workspace bytes fp8pa_decode needs for these arguments (plan.workspace_bytes):
+ * >= 0, or a negative status (and fp8pa_last_error) when fp8pa_decode_plan
+ * would refuse.  The workspace holds the split partials [W][2][G][D] fp32,
+ * their log-sum-exp [W][2][G] and a flag per partial [W][2], each piece
+ * 256-byte aligned. */
+int64_t fp8pa_decode_workspace_bytes(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
+                                     int max_seq_len, int window, int workgroups, int variant);
 
 /*
  * Decode attention (the hot path).
@@ -290,8 +309,17 @@ int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, ui
 
 /*
  * Test hook: dequantize n codes with the device conversion the decode kernel
- * uses.  scales: device fp32 [n] (F32 kinds) or uint8 E8M0 [n] (E8M0_G32).
- * out: device fp32 [n].  Exact for all finite codes (E8M0 codes 10..245).
+ * uses, so that it can be compared bit for bit with code x scale (page "fp8
+ * paged attention for MoE serving", "Smallest correct example": the reference
+ * dequantizes with the code and its scale).  scales: device fp32 [n] (F32
+ * kinds) or uint8 E8M0 [n] (E8M0_G32).  out: device fp32 [n]:
+ *   F32_PAGE_HEAD, F32_TOKEN_HEAD: the E4M3 -> bf16 operand conversion, then
+ *     the product with the scale (the decode applies fp32 scales to the score
+ *     or the probability, the same product up to association);
+ *   E8M0_G32: the scaled conversion, exact for all finite codes (E8M0 codes
+ *     10..245);
+ *   F32_G<S>: fp32(code x scale) as the sub-row key path forms it before
+ *     splitting it into a hi/lo pair of bf16 operands.
  */
 int fp8pa_debug_dequant(const uint8_t* codes, const void* scales, int scale_kind, int n,
                         float* out, void* stream);
@@ -302,7 +330,9 @@ int fp8pa_debug_dequant(const uint8_t* codes, const void* scales, int scale_kind
  * device uint32 that the kernel may write. */
 int fp8pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
-/* Launch counters: what actually ran, not what was requested. */
+/* Launch counters: what actually ran, not what was requested (the page "fp8
+ * paged attention for MoE serving", "Two compute paths", reports which path
+ * served a call through compute_counts(); these are this library's). */
 typedef struct fp8pa_counters {
   int64_t decode_calls;     /* successful fp8pa_decode calls */
   int64_t decode_mfma_bf16; /* decode kernels launched, MFMA bf16 variant */
@@ -334,6 +364,26 @@ int fp8pa_get_counters(fp8pa_counters* out);
  * num_rows >= 1 (else FP8PA_EINVAL).  err NULL turns the checks off. */
 int fp8pa_set_debug_checks(uint32_t* err);
 int fp8pa_reset_counters(void);
+
+/* Device status of the current device.  merge_timeouts counts the split
+ * merges whose bounded wait for another workgroup's partial gave up since the
+ * library was loaded or last reset (a unit whose merge gave up has NaN
+ * outputs; the wait only gives up if a workgroup that holds an earlier piece
+ * never publishes it).  After a timeout the workspace's flags are in an
+ * unknown state: clear the workspace (zeros) before replaying a captured
+ * graph with it.  This query synchronizes the device (hipDeviceSynchronize)
+ * and is not for use under graph capture; reset != 0 clears the words. */
+typedef struct fp8pa_device_status {
+  uint64_t merge_timeouts;
+  uint64_t reserved[3];
+} fp8pa_device_status;
+int fp8pa_get_device_status(fp8pa_device_status* out, int reset);
+
+/* Test hook (calling thread only): while on, decode merges wait for a flag
+ * value that no workgroup writes, with a short bound, so every cut unit's
+ * merge gives up (NaN outputs, counted in merge_timeouts) and every kernel
+ * still ends.  For testing the timeout report; off by default. */
+int fp8pa_debug_force_merge_timeout(int on);
 
 /* Profiling hook (calling thread only): while set, every fp8pa_decode records
  * `start` on its stream just before the decode kernel and `stop` just after

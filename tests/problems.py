@@ -80,3 +80,15 @@ def permute_rows(prob: Problem, seed=1):
     table = np.where(prob.table >= 0, perm[np.maximum(prob.table, 0)], -1).astype(np.int32)
     from dataclasses import replace
     return replace(prob, k_pool=move(prob.k_pool, prob.kdesc), v_pool=move(prob.v_pool, prob.vdesc), table=table)
+
+
+def add_guard_rows(prob: Problem, n=2):
+    """The same problem with n poisoned rows appended to both pools, outside
+    the descriptors' num_rows: table entries planted there are invalid rows
+    that still lie inside the allocation, so a read or write through one
+    shows up in the results instead of faulting.  Returns (problem, rows)."""
+    from dataclasses import replace
+    k = np.concatenate([prob.k_pool, np.full(n * prob.kdesc.row_bytes, POISON, np.uint8)])
+    v = np.concatenate([prob.v_pool, np.full(n * prob.vdesc.row_bytes, POISON, np.uint8)])
+    first = prob.kdesc.num_rows
+    return replace(prob, k_pool=k, v_pool=v), list(range(first, first + n))

@@ -93,6 +93,8 @@ def call_decode(k=None, v=None, **kw):
     (dict(variant=2, k=kd(scale_kind="e8m0_32", row_bytes=16384 + 4096),
           v=vd(scale_kind="e8m0_32", row_bytes=16384 + 4096)), ops.EUNSUPPORTED),   # fp8 mode: fp32 scales only
     (dict(variant=2, v=vd(layout="tokens")), ops.EUNSUPPORTED),                    # fp8 mode: V d-major only
+    (dict(variant=2, sm_scale=0.09), ops.EUNSUPPORTED),                             # fp8 mode: sm_scale > D^-0.5
+    (dict(variant=2, sm_scale=-1.0), ops.EUNSUPPORTED),
     (dict(variant=3, workgroups=4, ws=F, ws_bytes=1 << 20), ops.EUNSUPPORTED),      # packed heads fix the grid
     (dict(variant=4, workgroups=0, v=vd(layout="heads")), ops.EUNSUPPORTED),        # packed splits: V d-major only
     (dict(variant=4, workgroups=0, Hq=64), ops.EUNSUPPORTED),                       # packed splits: G <= 4
@@ -182,22 +184,23 @@ def test_empty_batch_is_a_no_op():
 
 def test_plan_is_host_only_and_sane():
     k = kd()
-    p = ops.decode_plan(32, 32, k, 8192)
+    p = ops.decode_plan(32, 32, k, vd(), 8192)
     assert p.workgroups >= 1 and p.tile_tokens == 64
     G, D = 4, 128
     if p.workgroups > 1:
         assert p.workspace_bytes >= p.workgroups * 2 * G * (D + 1) * 4 + 32 * 8 * 8
     # explicit workgroup counts are honoured
-    p1 = ops.decode_plan(32, 32, k, 8192, workgroups=1)
+    p1 = ops.decode_plan(32, 32, k, vd(), 8192, workgroups=1)
     assert p1.workgroups == 1 and p1.workspace_bytes == 0
-    p7 = ops.decode_plan(4, 32, k, 8192, workgroups=7)
+    p7 = ops.decode_plan(4, 32, k, vd(), 8192, workgroups=7)
     assert p7.workgroups == 7 and p7.workspace_bytes >= 7 * 2 * G * (D + 1) * 4
     # the plan depends on host values only: same answer twice, any seq_lens
-    assert ops.decode_plan(32, 32, k, 8192).workgroups == p.workgroups
+    assert ops.decode_plan(32, 32, k, vd(), 8192).workgroups == p.workgroups
     # head dims 256 and 512 use 32-position tiles
-    assert ops.decode_plan(16, 16, kd(head_dim=512, num_kv_heads=2, page_size=32, row_bytes=65568), 16384).tile_tokens == 32
+    assert ops.decode_plan(16, 16, kd(head_dim=512, num_kv_heads=2, page_size=32, row_bytes=65568),
+                           vd(head_dim=512, num_kv_heads=2, page_size=32, row_bytes=65568), 16384).tile_tokens == 32
     with pytest.raises(ops.Fp8paError):
-        ops.decode_plan(1, 8, kd(head_dim=80), 100)
+        ops.decode_plan(1, 8, kd(head_dim=80), vd(head_dim=80), 100)
 
 
 def call_append(**kw):
@@ -240,15 +243,15 @@ def test_plan_of_the_variants():
     workspace; packed splits need partials for 4 * G query heads per unit;
     the fp8 mode plans like the default; the plan reports the variant."""
     k = kd()                                   # Hkv 8, D 128
-    pk = ops.decode_plan(5, 32, k, 8192, variant="packed_heads")
+    pk = ops.decode_plan(5, 32, k, vd(), 8192, variant="packed_heads")
     assert pk.workgroups == 10 and pk.workspace_bytes == 0 and pk.variant == ops.VARIANTS["packed_heads"]
     k6 = kd(num_kv_heads=6, row_bytes=12320)
-    assert ops.decode_plan(3, 24, k6, 8192, variant="packed_heads").workgroups == 6
-    ps = ops.decode_plan(4, 32, k, 8192, workgroups=7, variant="packed_split")
-    df = ops.decode_plan(4, 32, k, 8192, workgroups=7)
+    assert ops.decode_plan(3, 24, k6, vd(num_kv_heads=6, row_bytes=12320), 8192, variant="packed_heads").workgroups == 6
+    ps = ops.decode_plan(4, 32, k, vd(), 8192, workgroups=7, variant="packed_split")
+    df = ops.decode_plan(4, 32, k, vd(), 8192, workgroups=7)
     assert ps.variant == ops.VARIANTS["packed_split"] and ps.workgroups == 7
     assert ps.workspace_bytes >= 7 * 2 * 16 * (128 + 1) * 4 > df.workspace_bytes
-    f8 = ops.decode_plan(4, 32, k, 8192, workgroups=7, variant="mfma_fp8")
+    f8 = ops.decode_plan(4, 32, k, vd(), 8192, workgroups=7, variant="mfma_fp8")
     assert f8.variant == ops.VARIANTS["mfma_fp8"] and f8.workspace_bytes == df.workspace_bytes
     assert df.variant == ops.VARIANTS["mfma_bf16"]
 
@@ -266,3 +269,28 @@ def test_debug_checks_setting():
     finally:
         assert ops.lib().fp8pa_set_debug_checks(None) == ops.OK
     assert call_decode(k=kd(num_rows=0), workgroups=4) == ops.EWORKSPACE   # checks off: the next check applies
+
+
+def test_plan_validates_like_decode_and_sizes_the_workspace():
+    """The plan refuses what fp8pa_decode refuses for the pools (V in
+    HEADS_D64, K/V geometry mismatch, V sub-row groups), and
+    fp8pa_decode_workspace_bytes equals plan.workspace_bytes or returns the
+    refusal's status."""
+    for v in (vd(layout="heads_d64"), vd(num_kv_heads=4, row_bytes=8208),
+              vd(scale_kind="f32_g32", row_bytes=16384 + 2048)):
+        with pytest.raises(ops.Fp8paError) as e:
+            ops.decode_plan(4, 32, kd(), v, 8192, workgroups=7)
+        assert e.value.code == ops.EUNSUPPORTED
+        with pytest.raises(ops.Fp8paError):
+            ops.decode_workspace_bytes(4, 32, kd(), v, 8192, workgroups=7)
+        assert ops.lib().fp8pa_decode_workspace_bytes(4, 32, ctypes.byref(kd()), ctypes.byref(v), 8192, 0, 7, 0) \
+            == ops.EUNSUPPORTED
+    for wg in (1, 7, 300):
+        p = ops.decode_plan(4, 32, kd(), vd(), 8192, workgroups=wg)
+        assert ops.decode_workspace_bytes(4, 32, kd(), vd(), 8192, workgroups=wg) == p.workspace_bytes
+    # V token-major: the same grid, more LDS; the split kernel's workspace
+    assert ops.decode_plan(4, 32, kd(), vd(layout="tokens"), 8192, workgroups=7).workspace_bytes == \
+        ops.decode_plan(4, 32, kd(), vd(), 8192, workgroups=7).workspace_bytes
+    # a call with fewer bytes than the plan's is refused; exactly the plan's is accepted by validation
+    n = ops.decode_workspace_bytes(2, 32, kd(), vd(), 8192, workgroups=4)
+    assert call_decode(workgroups=4, ws=F, ws_bytes=n - 1) == ops.EWORKSPACE

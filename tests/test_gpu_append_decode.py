@@ -121,7 +121,7 @@ def test_append_decode_graph_replays_match_eager():
     tk = torch.from_numpy(xk).to(torch.bfloat16).to(DEV)
     tv = torch.from_numpy(xv).to(torch.bfloat16).to(DEV)
     msl = int(p.seq_lens.max())
-    plan = ops.decode_plan(p.B, p.Hq, kd, msl)
+    plan = ops.decode_plan(p.B, p.Hq, kd, vd, msl)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
     k_e, v_e = torch.from_numpy(k0).to(DEV), torch.from_numpy(v0).to(DEV)
     out_e = ops.append_decode(q, tk, tv, k_e, v_e, kd, vd, table, sl, msl, workspace=ws)

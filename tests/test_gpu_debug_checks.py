@@ -12,7 +12,7 @@ import torch
 from fp8_paged_kv_amd import ops
 from oracle import attention as oatt
 from tests.gpu_util import DEV, assert_parity, desc_of, device_problem, gpu_decode, say, to_np
-from tests.problems import make_problem
+from tests.problems import add_guard_rows, make_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -58,17 +58,22 @@ def test_checks_pass_valid_inputs_unchanged(err, name, kw, extra):
     assert torch.equal(got.view(torch.int16), want.view(torch.int16)), name
 
 
-@pytest.mark.parametrize("bad", [10 ** 6, -5])
-def test_bad_table_entry_is_flagged_and_contained(err, bad):
-    say("debug checks table", bad)
-    p = make_problem(802, B=3, Hq=16, Hkv=4, D=128, P=16, lens=[700, 90, 33])
+@pytest.mark.parametrize("guard", [0, 1])
+def test_bad_table_entry_is_flagged_and_contained(err, guard):
+    """An attended page's entry points at a row past num_rows (a poisoned
+    guard row inside the allocation): flagged, read as row 0 instead."""
+    say("debug checks table", guard)
+    p0 = make_problem(802, B=3, Hq=16, Hkv=4, D=128, P=16, lens=[700, 90, 33])
+    p, rows = add_guard_rows(p0)
     from dataclasses import replace
     t = p.table.copy()
-    t[1, 2] = bad                                         # an attended page of sequence 1
+    t[1, 2] = rows[guard]                                 # an attended page of sequence 1
     got = to_np(gpu_decode(replace(p, table=t), workgroups=5))
     assert err.tolist() == [1, 0]
-    assert np.all(np.isfinite(got[[0, 2]]))   # sequence 1 read row 0 (any bytes) in place of the bad entry
-    want = oracle(p, seqs=[0, 2])
+    assert np.all(np.isfinite(got[[0, 2]]))
+    if 0 in set(p.table[p.table >= 0].tolist()):          # row 0 holds data: sequence 1 stays finite
+        assert np.all(np.isfinite(got[1])), "a guard row was read"
+    want = oracle(p0, seqs=[0, 2])
     for b in (0, 2):
         assert_parity(got[b], want[b], f"sequence {b}")
 
@@ -92,10 +97,10 @@ def test_bad_length_is_flagged_and_zeroed(err):
 
 def test_append_skips_a_bad_row(err):
     say("debug checks append")
-    p = make_problem(804, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[40, 20])
+    p, rows = add_guard_rows(make_problem(804, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[40, 20]))
     kd, vd = desc_of(p.kdesc), desc_of(p.vdesc)
     t = p.table.copy()
-    t[1, 1] = 10 ** 7                                     # the page of position 20
+    t[1, 1] = rows[0]                                     # the page of position 20: a guard row
     ka, va = torch.from_numpy(p.k_pool).to(DEV), torch.from_numpy(p.v_pool).to(DEV)
     k0, v0 = ka.clone(), va.clone()
     x = torch.randn((2, 1, 2, 64), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).to(DEV)

@@ -11,7 +11,7 @@ import torch
 from fp8_paged_kv_amd import ops
 from oracle import attention as oatt
 from tests.gpu_util import assert_parity, device_problem, gpu_decode, say, to_np
-from tests.problems import make_problem, permute_rows
+from tests.problems import add_guard_rows, make_problem, permute_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -86,13 +86,15 @@ def test_poison_outside_attended_positions_never_leaks():
     """Slots past L, pages before the window and spare rows hold NaN codes and
     NaN scales; table entries past the last page are -1 or out of range."""
     p = make_problem(105, B=3, Hq=8, Hkv=2, D=64, P=16, lens=[37, 16, 250], window=50, sinks=True)
-    t = p.table.copy()
+    pg, guard = add_guard_rows(p)
+    t = pg.table.copy()
     for b in range(3):
         used = -(-int(p.seq_lens[b]) // 16)
-        t[b, used:] = 10 ** 8 if b == 0 else -1
-    # pages entirely before the window: point them at garbage rows too
+        t[b, used:] = guard[0] if b == 0 else -1          # past the last page: a poisoned guard row, or -1
+    # pages entirely before the window: point them at the other guard row and -7
     t[2, : (250 - 50) // 16] = -7
-    p2 = replace(p, table=t)
+    t[2, 0] = guard[1]
+    p2 = replace(pg, table=t)
     got = to_np(gpu_decode(p2))
     assert np.all(np.isfinite(got))
     assert_parity(got, oracle(p), "poison")
@@ -153,7 +155,7 @@ def test_split_merge_many_calls_one_workspace():
     p = make_problem(110, B=4, Hq=16, Hkv=2, D=128, P=16, lens=[3000, 1500, 64, 2500], sinks=True)
     dev = device_problem(p)
     msl = int(p.seq_lens.max())
-    plan = ops.decode_plan(p.B, p.Hq, dev["kd"], msl, workgroups=8)
+    plan = ops.decode_plan(p.B, p.Hq, dev["kd"], dev["vd"], msl, workgroups=8)
     assert plan.workgroups == 8
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda:0")
     rng = np.random.default_rng(0)
@@ -173,3 +175,60 @@ def test_split_merge_many_calls_one_workspace():
 def inputs_round(x):
     from fp8_paged_kv_amd.inputs import round_to_bf16
     return round_to_bf16(x)
+
+
+MANY = [
+    # (B, D, Hq, Hkv, window, sinks): batches above 64 take the four-wave startup scan
+    (65, 128, 16, 4, 0, True),
+    (96, 64, 16, 2, 200, False),
+    (200, 128, 16, 4, 300, True),
+]
+
+
+@pytest.mark.parametrize("B,D,Hq,Hkv,window,sinks", MANY, ids=[f"B{m[0]}-D{m[1]}" for m in MANY])
+@pytest.mark.parametrize("workgroups", [0, 3, 131])
+def test_many_sequences_default_kernel(B, D, Hq, Hkv, window, sinks, workgroups):
+    """The default d-major split kernel at batches above 64 (LDS prefix scan by
+    all waves, share bounds per thread, a binary search per segment), mixed
+    lengths with empty and one-position sequences, against the oracle."""
+    say("many sequences", B, D, "workgroups", workgroups)
+    rng = np.random.default_rng(B * 7 + D)
+    lens = rng.integers(1, 700, size=B)
+    lens[::9] = 0
+    lens[1] = 1
+    lens[2] = 64
+    lens[3] = 1500
+    p = make_problem(120 + B, B=B, Hq=Hq, Hkv=Hkv, D=D, P=16, lens=lens.tolist(), window=window, sinks=sinks)
+    dev = device_problem(p)
+    plan = ops.decode_plan(p.B, p.Hq, dev["kd"], dev["vd"], int(lens.max()), window, workgroups)
+    assert plan.variant == ops.VARIANTS["mfma_bf16"]
+    ops.reset_counters()
+    got = to_np(gpu_decode(p, dev=dev, workgroups=workgroups))
+    assert ops.counters()["decode_packed_heads"] == 0
+    assert_parity(got, oracle(p), f"B={B}")
+    assert np.all(got[lens == 0] == 0)
+
+
+def test_forced_merge_timeout_is_reported():
+    """A merge whose wait for another workgroup's partial gives up (forced
+    from the host: merges wait for a flag value no workgroup writes, with a
+    short bound) writes NaN for its unit and counts itself in the device
+    status; every kernel ends, and later calls are correct again."""
+    say("forced merge timeout")
+    p = make_problem(130, B=2, Hq=16, Hkv=4, D=128, P=16, lens=[3000, 2000], sinks=True)
+    dev = device_problem(p)
+    ops.device_status(reset=True)
+    good = to_np(gpu_decode(p, dev=dev, workgroups=7))
+    assert ops.device_status()["merge_timeouts"] == 0
+    assert_parity(good, oracle(p), "before")
+    ops.force_merge_timeout(True)
+    try:
+        bad = to_np(gpu_decode(p, dev=dev, workgroups=7))
+    finally:
+        ops.force_merge_timeout(False)
+    st = ops.device_status(reset=True)
+    assert st["merge_timeouts"] >= 1
+    assert np.isnan(bad).any()
+    again = to_np(gpu_decode(p, dev=dev, workgroups=7))
+    assert ops.device_status()["merge_timeouts"] == 0
+    assert np.array_equal(again, good)

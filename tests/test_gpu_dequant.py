@@ -35,3 +35,17 @@ def test_dequant_e8m0_bit_exact():
     want = fp8.dequant_fp32(codes, fp8.E8M0_TABLE[u]).astype(np.float32)
     assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32))
     assert ops.counters()["debug_launches"] >= 1
+
+
+def test_dequant_sub_row_key_conversion_bit_exact():
+    """The sub-row key path's fp32(code x scale), formed before its hi/lo bf16
+    split: every finite code times fp32 scales including subnormal products."""
+    say("dequant sub-row key conversion")
+    scales = np.array([1.0, 2.0 ** -7, 0.0123, 3.7, 1e-3, 250.0, 1e-38, 3e-39, 2.0 ** -140, 1e30, 7.1e-6,
+                       0.1, 1.0 / 448.0], dtype=np.float32)
+    codes = np.tile(CODES, len(scales))
+    sc = np.repeat(scales, len(CODES))
+    for kind in ("f32_g32", "f32_g64", "f32_g128", "f32_g256"):
+        got = ops.debug_dequant(torch.from_numpy(codes).to(DEV), torch.from_numpy(sc).to(DEV), kind)
+        want = fp8.dequant_fp32(codes, sc.astype(np.float64)).astype(np.float32)
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32)), kind

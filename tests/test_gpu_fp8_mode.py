@@ -1,9 +1,10 @@
 """The fp8 compute mode (FP8PA_VARIANT_MFMA_FP8) on the GPU: QK^T on the fp8
-MFMA with each query row rounded to E4M3.  Against the oracle that models that
-one rounding (decode of ``fp8_query(q)``) it meets the default parity bound;
-against the exact oracle it meets the page's fp8 tolerance class (1.5e-1); the
-counter records the mode; requests it cannot serve are refused, never
-downgraded."""
+MFMA with each query row rounded to E4M3 like a KV block (codes of q / s).
+Against the oracle that models that one rounding (decode of ``fp8_query(q)``)
+it meets the default parity bound; against the exact oracle it meets the
+page's fp8 tolerance class (1.5e-1) on every served case (the mode serves
+|sm_scale| <= D^-0.5 only); the counter records the mode; requests it cannot
+serve are refused, never downgraded."""
 import numpy as np
 import pytest
 import torch
@@ -32,8 +33,9 @@ CASES = [
     ("d128-aligned-rows", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[700, 65, 300], row_pad=32, align64=True)),
     ("d128-ktokens", dict(B=2, Hq=8, Hkv=2, D=128, P=16, lens=[260, 5], k_layout="tokens")),
     ("d128-kheads-p32", dict(B=2, Hq=8, Hkv=2, D=128, P=32, lens=[260, 77], k_layout="heads")),
-    ("d256-window-scale1", dict(B=2, Hq=4, Hkv=2, D=256, P=32, lens=[700, 33], window=100, sm_scale=1.0)),
-    ("d512-scale1", dict(B=2, Hq=8, Hkv=1, D=512, P=32, lens=[333, 64], sm_scale=1.0)),
+    ("d256-window", dict(B=2, Hq=4, Hkv=2, D=256, P=32, lens=[700, 33], window=100)),
+    ("d512-g8", dict(B=2, Hq=8, Hkv=1, D=512, P=32, lens=[333, 64])),
+    ("d256-p16-small-scale", dict(B=2, Hq=8, Hkv=2, D=256, P=16, lens=[300, 41], sm_scale=0.03)),
     ("empty-and-short", dict(B=4, Hq=8, Hkv=2, D=64, P=16, lens=[0, 1, 15, 65])),
 ]
 
@@ -49,14 +51,9 @@ def test_fp8_mode_parity(name, kw, workgroups):
     assert c["decode_mfma_fp8"] == 1 and c["decode_mfma_bf16"] == 0
     # the one rounding the mode adds, modelled exactly: the default bound
     assert_parity(got, oracle(p, oatt.fp8_query(p.q)), name)
-    # the exact result: the page's fp8 tolerance class, at the default score
-    # scale D**-0.5 (with sm_scale = 1 and D >= 256 the logits spread over
-    # tens of units and the E4M3 rounding of q moves them by tenths: the
-    # mode is outside that class there, which is why it is never chosen
-    # automatically)
-    if p.scale <= p.D ** -0.5 * (1 + 1e-6):
-        want = oracle(p)
-        assert np.all(np.abs(got - want) <= FP8_TOL + FP8_TOL * np.abs(want)), name
+    # the exact result: the page's fp8 tolerance class
+    want = oracle(p)
+    assert np.all(np.abs(got - want) <= FP8_TOL + FP8_TOL * np.abs(want)), name
 
 
 def test_fp8_mode_rounds_q_and_keeps_query_range():
@@ -84,8 +81,13 @@ def test_fp8_mode_refusals():
     p = make_problem(403, B=2, Hq=16, Hkv=2, D=128, P=16, lens=[300, 90], v_layout="tokens")
     with pytest.raises(RuntimeError):
         gpu_decode(p, variant="mfma_fp8")
+    # score scales above D^-0.5 (sm_scale = 1 at D = 256 and at D = 64)
+    for D, P in ((256, 32), (64, 16)):
+        p = make_problem(403, B=2, Hq=8, Hkv=2, D=D, P=P, lens=[300, 90], sm_scale=1.0)
+        with pytest.raises(RuntimeError):
+            gpu_decode(p, variant="mfma_fp8")
     c = ops.counters()
-    assert c["decode_calls"] == 0 and c["decode_mfma_fp8"] == 0 and c["errors"] == 2
+    assert c["decode_calls"] == 0 and c["decode_mfma_fp8"] == 0 and c["errors"] == 4
 
 
 def test_fp8_mode_append_decode_takes_two_launches():

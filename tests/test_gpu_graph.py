@@ -27,7 +27,7 @@ def test_graph_replays_match_eager(workgroups):
     say(f"graph capture: workgroups={workgroups}")
     p = make_problem(131, B=3, Hq=16, Hkv=2, D=128, P=16, lens=[900, 333, 40], window=512, sinks=True)
     dev = device_problem(p)
-    plan = ops.decode_plan(3, 16, dev["kd"], int(p.seq_lens.max()), p.window, workgroups)
+    plan = ops.decode_plan(3, 16, dev["kd"], dev["vd"], int(p.seq_lens.max()), p.window, workgroups)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0")
     out = torch.empty_like(dev["q"])
     eager = run(p, dev, None, ws, workgroups).clone()

@@ -13,7 +13,7 @@ import torch
 from fp8_paged_kv_amd import ops
 from oracle import attention as oatt
 from tests.gpu_util import DEV, assert_parity, desc_of, gpu_decode, say, to_np
-from tests.problems import make_problem
+from tests.problems import add_guard_rows, make_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,7 @@ CASES = [
 def test_packed_heads_parity(name, kw):
     say("packed heads parity", name)
     p = make_problem(501, **kw)
-    plan = ops.decode_plan(p.B, p.Hq, desc_of(p.kdesc), int(p.seq_lens.max()), p.window, variant="packed_heads")
+    plan = ops.decode_plan(p.B, p.Hq, desc_of(p.kdesc), desc_of(p.vdesc), int(p.seq_lens.max()), p.window, variant="packed_heads")
     assert plan.workgroups == p.B * -(-p.Hkv // 4) and plan.workspace_bytes == 0
     ops.reset_counters()
     got = to_np(gpu_decode(p, variant="packed_heads"))
@@ -55,11 +55,13 @@ def test_packed_heads_parity(name, kw):
 
 def test_packed_heads_poison_never_leaks():
     p = make_problem(502, B=3, Hq=8, Hkv=2, D=64, P=16, lens=[37, 16, 250], window=50, sinks=True)
+    p, guard = add_guard_rows(p)
     t = p.table.copy()
     for b in range(3):
         used = -(-int(p.seq_lens[b]) // 16)
         t[b, used:] = -1
     t[2, : (250 - 50) // 16] = -7
+    t[2, 0], t[0, -1] = guard      # never-read entries on poisoned guard rows
     got = to_np(gpu_decode(replace(p, table=t), variant="packed_heads"))
     assert np.all(np.isfinite(got))
     assert_parity(got, oracle(p), "poison")
@@ -122,6 +124,9 @@ def test_auto_takes_packed_heads_when_units_fill_the_device():
     say("auto packed")
     p = make_problem(506, B=320, Hq=32, Hkv=8, D=64, P=16, lens=list(range(1, 321)), sinks=True)
     kd = desc_of(p.kdesc)
+    plan = ops.decode_plan(p.B, p.Hq, kd, desc_of(p.vdesc), int(p.seq_lens.max()))
+    assert plan.variant == ops.VARIANTS["packed_heads"] and plan.workspace_bytes == 0
+    assert plan.workgroups == p.B * 2
     ops.reset_counters()
     got = gpu_decode(p)
     c = ops.counters()
@@ -129,6 +134,7 @@ def test_auto_takes_packed_heads_when_units_fill_the_device():
     assert_parity(to_np(got), oracle(p), "auto packed")
     # V token-major, or a small batch: the split kernel
     pv = make_problem(506, B=320, Hq=32, Hkv=8, D=64, P=16, lens=list(range(1, 321)), v_layout="tokens")
+    assert ops.decode_plan(pv.B, pv.Hq, kd, desc_of(pv.vdesc), 320).variant == ops.VARIANTS["mfma_bf16"]
     ops.reset_counters()
     assert_parity(to_np(gpu_decode(pv)), oracle(pv), "auto V tokens")
     assert ops.counters()["decode_packed_heads"] == 0

@@ -13,7 +13,7 @@ import torch
 from fp8_paged_kv_amd import ops
 from oracle import attention as oatt
 from tests.gpu_util import assert_parity, gpu_decode, say, to_np
-from tests.problems import make_problem
+from tests.problems import add_guard_rows, make_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -64,11 +64,13 @@ def test_packed_split_many_pieces_and_repeats():
 
 def test_packed_split_poison_never_leaks():
     p = make_problem(603, B=3, Hq=16, Hkv=4, D=64, P=16, lens=[37, 16, 250], window=50, sinks=True)
+    p, guard = add_guard_rows(p)
     t = p.table.copy()
     for b in range(3):
         used = -(-int(p.seq_lens[b]) // 16)
         t[b, used:] = -1
     t[2, : (250 - 50) // 16] = -7
+    t[2, 0], t[0, -1] = guard      # never-read entries on poisoned guard rows
     for w in (0, 5):
         got = to_np(gpu_decode(replace(p, table=t), workgroups=w, variant="packed_split"))
         assert np.all(np.isfinite(got))

@@ -15,7 +15,7 @@ from fp8_paged_kv_amd import ops
 from oracle import attention as oatt
 from oracle import pool as opool
 from tests.gpu_util import DEV, assert_parity, desc_of, gpu_decode, say, to_np
-from tests.problems import POISON, make_problem
+from tests.problems import add_guard_rows, POISON, make_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -85,11 +85,13 @@ def test_same_output_as_d_major(v_layout, D):
 def test_poison_outside_attended_positions_never_leaks():
     p = make_problem(303, B=3, Hq=8, Hkv=2, D=64, P=16, lens=[37, 16, 250], window=50, sinks=True,
                      v_layout="tokens", scale_kind="token_head")
+    p, guard = add_guard_rows(p)
     t = p.table.copy()
     for b in range(3):
         used = -(-int(p.seq_lens[b]) // 16)
         t[b, used:] = -1
     t[2, : (250 - 50) // 16] = -7
+    t[2, 0], t[0, -1] = guard      # never-read entries on poisoned guard rows
     got = to_np(gpu_decode(replace(p, table=t)))
     assert np.all(np.isfinite(got))
     assert_parity(got, oracle(p), "poison")
