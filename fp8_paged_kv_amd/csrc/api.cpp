@@ -489,6 +489,27 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
                      window, sinks, sm_scale, max_seq_len, workgroups, variant, workspace, workspace_bytes, stream);
 }
 
+int fp8pa_decode_noalloc(const void* q, void* out, const uint8_t* k_pool, const uint8_t* v_pool,
+                         const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, const int32_t* block_table,
+                         int64_t bt_stride, const int32_t* seq_lens, int B, int Hq, int window, const float* sinks,
+                         float sm_scale, int max_seq_len, int workgroups, int variant, void* stream) {
+  Resolved r{};
+  if (int rc = resolve(B, Hq, kd, vd, max_seq_len, workgroups, variant, false, &r)) return rc;
+  if (r.workspace_bytes > FP8PA_NOALLOC_SCRATCH_BYTES)
+    return fail(FP8PA_EWORKSPACE,
+                "this call needs %lld bytes of split scratch, more than the %d the allocation-free decode holds "
+                "(use fp8pa_decode with a workspace, or fewer workgroups)",
+                (long long)r.workspace_bytes, (int)FP8PA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (r.workspace_bytes > 0 && B > 0) {
+    ws = fp8pa::device_scratch();
+    if (!ws) return fail(FP8PA_EHIP, "the scratch of the allocation-free decode cannot be resolved on this device");
+  }
+  return decode_impl(nullptr, nullptr, q, out, k_pool, v_pool, kd, vd, block_table, bt_stride, seq_lens, B, Hq,
+                     window, sinks, sm_scale, max_seq_len, workgroups, variant, ws,
+                     ws ? (size_t)FP8PA_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
+
 // Longest attended span (max_seq_len, or the window) for which
 // fp8pa_append_decode appends inside the decode kernel.
 constexpr int kFusedMaxSpan = 2048;

@@ -5,6 +5,7 @@
 #include <unordered_map>
 
 #include "decode_kernel.h"
+#include "fp8pa.h"
 
 namespace fp8pa {
 
@@ -27,24 +28,42 @@ int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, size_t lds) 
 }
 
 namespace {
-// Status words of each device (DecodeArgs::status): one copy per device,
-// which holds it until the process ends.
+// Status words of each device (DecodeArgs::status), and the scratch of the
+// allocation-free decode (fp8pa_decode_noalloc: its split partials, their
+// log-sum-exp and flags).  Each device holds its own copy of both until the
+// process ends.  In host code these names are host-side stand-ins, not device
+// addresses: the addresses come from hipGetSymbolAddress, once per device.
 __device__ __align__(16) uint32_t status_words[4];
-}  // namespace
+__device__ __align__(256) uint8_t scratch[FP8PA_NOALLOC_SCRATCH_BYTES];
 
-uint32_t* device_status_words() {
-  constexpr int kMaxDevices = 64;
-  static std::mutex mu;
-  static uint32_t* addr[kMaxDevices] = {};
+constexpr int kMaxDevices = 64;
+
+// The current device's address of a device symbol, resolved on the first
+// call per device (with that device current) and remembered.
+template <typename T>
+T* symbol_address(const void* symbol, T* (&cache)[kMaxDevices], std::mutex& mu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
-  if (!addr[dev]) {
+  if (!cache[dev]) {
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(status_words)) != hipSuccess) return nullptr;
-    addr[dev] = static_cast<uint32_t*>(p);
+    if (hipGetSymbolAddress(&p, symbol) != hipSuccess || !p) return nullptr;
+    cache[dev] = static_cast<T*>(p);
   }
-  return addr[dev];
+  return cache[dev];
+}
+}  // namespace
+
+uint32_t* device_status_words() {
+  static std::mutex mu;
+  static uint32_t* addr[kMaxDevices] = {};
+  return symbol_address(HIP_SYMBOL(status_words), addr, mu);
+}
+
+uint8_t* device_scratch() {
+  static std::mutex mu;
+  static uint8_t* addr[kMaxDevices] = {};
+  return symbol_address(HIP_SYMBOL(scratch), addr, mu);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,

@@ -178,6 +178,10 @@ int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, size_t lds);
 // Device address of the current device's status words (see DecodeArgs::status),
 // or null if it cannot be resolved.
 uint32_t* device_status_words();
+// Device address of the current device's copy of the allocation-free decode's
+// scratch (FP8PA_NOALLOC_SCRATCH_BYTES, 256-byte aligned), or null if it
+// cannot be resolved.
+uint8_t* device_scratch();
 hipError_t launch_decode(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                          hipStream_t st, hipEvent_t start, hipEvent_t stop);
 // The same with the new tokens appended in-kernel (a.k_new, a.v_new).

@@ -57,6 +57,8 @@ SIGNATURES = {
                                      _I64),
     "fp8pa_decode": ([_P, _P, _P, _P, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _P, _I64, _P, _I, _I, _I,
                       _P, _F, _I, _I, _I, _P, _SZ, _P], _I),
+    "fp8pa_decode_noalloc": ([_P, _P, _P, _P, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _P, _I64, _P, _I,
+                              _I, _I, _P, _F, _I, _I, _I, _P], _I),
     "fp8pa_append_decode": ([_P, _P, _P, _P, _P, _P, ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _P, _I64,
                              _P, _I, _I, _I, _P, _F, _I, _I, _I, _P, _SZ, _P], _I),
     "fp8pa_merge_splits": ([_P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
@@ -180,6 +182,33 @@ def decode(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window
                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, Hq, window, _ptr(sinks),
                               scale, max_seq_len, workgroups, VARIANTS.get(variant, variant), _ptr(workspace),
                               ws_bytes, _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_noalloc(q, k_pool, v_pool, kd, vd, block_table, seq_lens, max_seq_len, window=0, sinks=None,
+                   sm_scale=None, workgroups=0, variant="auto", out=None, stream=None):
+    """decode() through the allocation-free entry point: the library's
+    per-device scratch holds the split partials (no workspace; calls that
+    overlap on one device race).  `out` is allocated here only when not given."""
+    _need(q, "q", torch.bfloat16)
+    _need(k_pool, "k_pool", torch.uint8)
+    _need(v_pool, "v_pool", torch.uint8)
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16)
+    scale = D ** -0.5 if sm_scale is None else float(sm_scale)
+    _check(lib().fp8pa_decode_noalloc(_ptr(q), _ptr(out), _ptr(k_pool), _ptr(v_pool), ctypes.byref(kd),
+                                      ctypes.byref(vd), _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, Hq,
+                                      window, _ptr(sinks), scale, max_seq_len, workgroups,
+                                      VARIANTS.get(variant, variant), _stream(stream)))
     return out
 
 

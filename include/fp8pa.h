@@ -241,6 +241,28 @@ int fp8pa_decode(const void* q, void* out, const uint8_t* k_pool, const uint8_t*
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): fp8pa_decode without the workspace arguments.  The split
+ * partials, their log-sum-exp and flags go to a scratch array the library
+ * holds per device, FP8PA_NOALLOC_SCRATCH_BYTES long, resolved on the first
+ * call on each device (with that device current) and held until the process
+ * ends.  The call allocates nothing.  Calls whose plan needs more workspace
+ * than that (plan.workspace_bytes) are refused with FP8PA_EWORKSPACE before
+ * anything is launched; every other argument, check and result is exactly
+ * fp8pa_decode's (same kernels, same plan, bit-identical output).  The
+ * scratch needs no clearing: flags carry the call's epoch.  Every call on one
+ * device shares that device's scratch: calls that overlap in time on one
+ * device (different streams, or threads) race and must not be issued.
+ */
+#define FP8PA_NOALLOC_SCRATCH_BYTES (16 << 20)
+int fp8pa_decode_noalloc(const void* q, void* out, const uint8_t* k_pool, const uint8_t* v_pool,
+                         const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
+                         const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                         int B, int Hq, int window, const float* sinks, float sm_scale,
+                         int max_seq_len, int workgroups, int variant, void* stream);
+
+/*
  * Append + decode (page "Lecture 8 — Inference Path: KV Cache, Decode, RoPE,
  * GQA, Paged KV" of the FlashAttention course, section "In-kernel KV cache
  * update": the attention kernel itself writes the new token's K and V,

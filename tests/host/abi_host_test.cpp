@@ -42,10 +42,13 @@ struct Launch {
 };
 static std::vector<Launch> g_launches;
 static uint32_t g_status_stub[4];
+alignas(256) static uint8_t g_scratch_stub[FP8PA_NOALLOC_SCRATCH_BYTES];
+uint8_t* fp8pa::device_scratch() { return g_scratch_stub; }
 
 namespace fp8pa {
 int decode_blocks_per_cu(int D, int, bool, size_t lds) { return lds <= 65536 ? decode_wg_per_cu(D) : 0; }
 uint32_t* device_status_words() { return g_status_stub; }
+uint8_t* device_scratch();
 #define STUB_DECODE(name, k)                                                                                   \
   hipError_t name(const DecodeArgs& a, int, int, bool, int W, size_t lds, hipStream_t, hipEvent_t, hipEvent_t) { \
     g_launches.push_back({k, a, W, lds});                                                                      \
@@ -293,6 +296,39 @@ int main() {
     LAUNCH(c);
     // empty batch: nothing launched
     c = Call(); c.B = 0; c.q = c.out = 0; g_launches.clear(); CHECK(c.run() == 0 && g_launches.empty());
+  }
+
+  // ---- the allocation-free decode: its partials inside the scratch, or a refusal
+  {
+    Call c;
+    c.workgroups = 7;
+    fp8pa_plan p{};
+    CHECK(c.plan(&p) == 0 && p.workspace_bytes > 0);
+    g_launches.clear();
+    auto noalloc = [](const Call& c) {
+      return fp8pa_decode_noalloc(fake(c.q), fake(c.out), fake(c.kp), fake(c.vp), &c.kd, &c.vd,
+                                  reinterpret_cast<const int32_t*>(c.bt), c.bt_stride,
+                                  reinterpret_cast<const int32_t*>(c.sl), c.B, c.Hq, c.window,
+                                  reinterpret_cast<const float*>(c.sinks), c.sm_scale, c.msl, c.workgroups,
+                                  c.variant, nullptr);
+    };
+    CHECK(noalloc(c) == 0 && g_launches.size() == 1);
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(g_scratch_stub), end = lo + sizeof(g_scratch_stub);
+    const uintptr_t po = reinterpret_cast<uintptr_t>(g_launches[0].a.part_o),
+                    pf = reinterpret_cast<uintptr_t>(g_launches[0].a.flags);
+    CHECK(po == lo && pf > po && pf + 7 * 2 * 4 <= end);
+    Call d;                                    // 600 x 2 x 8 x 512 x 4 bytes of partials > 16 MiB
+    d.kd = d.vd = desc(2, 512, 32, FP8PA_LAYOUT_HEADS, FP8PA_SCALE_F32_PAGE_HEAD, 65568);
+    d.vd.layout = FP8PA_LAYOUT_HEADS_DMAJOR;
+    d.Hq = 16; d.workgroups = 600; d.sm_scale = 1.0f;
+    g_launches.clear();
+    CHECK(noalloc(d) == FP8PA_EWORKSPACE && g_launches.empty() && fp8pa_last_error()[0]);
+    d.workgroups = 1;                          // no split: no scratch needed
+    CHECK(noalloc(d) == 0 && g_launches.size() == 1 && g_launches[0].a.part_o == nullptr);
+    Call e;
+    e.Hq = 30;
+    g_launches.clear();
+    CHECK(noalloc(e) == FP8PA_EINVAL && g_launches.empty());
   }
 
   // ---- forced merge timeout: the merger waits for a value no holder writes
