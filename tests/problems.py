@@ -92,3 +92,28 @@ def add_guard_rows(prob: Problem, n=2):
     v = np.concatenate([prob.v_pool, np.full(n * prob.vdesc.row_bytes, POISON, np.uint8)])
     first = prob.kdesc.num_rows
     return replace(prob, k_pool=k, v_pool=v), list(range(first, first + n))
+
+
+def swap_rows(prob: Problem, r1, r2):
+    """The same logical data with physical rows r1 and r2 exchanged in both
+    pools (and the table updated to match)."""
+    from dataclasses import replace
+    def move(pool, desc):
+        rows = pool[:desc.num_rows * desc.row_bytes].reshape(desc.num_rows, desc.row_bytes).copy()
+        rows[[r1, r2]] = rows[[r2, r1]]
+        out = pool.copy()
+        out[:desc.num_rows * desc.row_bytes] = rows.reshape(-1)
+        return out
+    t = prob.table.copy()
+    m1, m2 = t == r1, t == r2
+    t[m1], t[m2] = r2, r1
+    return replace(prob, k_pool=move(prob.k_pool, prob.kdesc), v_pool=move(prob.v_pool, prob.vdesc), table=t)
+
+
+def full_page_row(prob: Problem):
+    """A physical row holding a page whose every slot is attended data."""
+    for b in range(prob.B):
+        for pg in range(int(prob.seq_lens[b]) // prob.P):
+            if prob.table[b, pg] >= 0:
+                return int(prob.table[b, pg])
+    raise ValueError("no full page")
