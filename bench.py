@@ -157,6 +157,17 @@ def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgr
         hip.destroy(ev)
         return wall, ms / 1e3
 
+    # Settle: untimed steps for SETTLE_S seconds of wall time, so that the
+    # device's clocks have ramped up (measured: the first ~20 ms of sustained
+    # decode run up to 12% slower, then the step time is flat), then the
+    # `warmup` steps, then the timed region.
+    torch.cuda.synchronize()
+    t_settle, k = time.perf_counter(), 0
+    while time.perf_counter() - t_settle < SETTLE_S:
+        step(k)
+        k += 1
+        if k % 8 == 0:
+            torch.cuda.synchronize()
     for k in range(warmup):
         step(k)
     wall, ev_s = region(step, steps)
@@ -165,8 +176,12 @@ def time_layers(layers_copies, steps, warmup, hip, ops, workloads, torch, workgr
         def one(k, j=j):
             l = layers_copies[k % R][j]
             workloads.decode_layer(l, out=outs[j], workspace=ws[j], workgroups=workgroups, variant=variant)
-        for k in range(3):
+        t_settle, k = time.perf_counter(), 0
+        while time.perf_counter() - t_settle < SETTLE_S / 2:
             one(k)
+            k += 1
+            if k % 8 == 0:
+                torch.cuda.synchronize()
         kw, ke = region(one, steps)
         kern.append({"wall_s": kw, "event_s": ke})
     step_ev = hip.events(steps + 1)
@@ -535,6 +550,7 @@ def run_graph(args, wl, torch, np, ops, workloads, hip):
 
 
 HEADLINE = "gpt-oss-decode"   # the largest single-GPU config (most KV bytes per step)
+SETTLE_S = 0.2                 # untimed decode before each timed region (clock ramp-up)
 GATED = {"llama3-8b-decode", "gpt-oss-decode", "gemma4-mixed-pool", "long-context-mxfp8"}
 
 
@@ -645,7 +661,9 @@ def main():
                    "scales": head.scale_kind, "layers": [l["name"] for l in hrec["layers"]],
                    "kv_bytes_per_step": hrec["kv_bytes_per_step"], "parallelism": "single GPU",
                    "step": "one decode call per layer of the workload (window-128 layer and full layer), split "
-                           "merges inside the decode launch"},
+                           "merges inside the decode launch",
+                   "settle": f"{SETTLE_S} s of untimed decode steps, then the warm-up steps, before each timed "
+                             f"region"},
         "pct_of_peak": round(100 * hrec["gbps"] / PEAK_GBPS, 2),
         "us_per_step_events": hrec["us_per_step_events"],
         "roofline": {"bound": "hbm", "achieved": dl["kernel_gbps"], "peak": PEAK_GBPS, "unit": "GB/s",

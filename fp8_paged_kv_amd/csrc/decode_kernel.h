@@ -223,6 +223,16 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
   const int G = PS ? a.G * NW : a.G, P = a.P, log2P = a.log2P, B = a.B, Hkv = PS ? a.Hkv / NW : a.Hkv;
   int W = gridDim.x;
   const int w = blockIdx.x;
+  // XCD-blocked shares.  The dispatcher hands workgroups to the eight XCDs in
+  // turn (workgroup w runs on XCD w mod 8), and each XCD has its own L2.
+  // Workgroup w takes share sw = (w mod 8) * G8 + w / 8 (G8 = W / 8), so each
+  // XCD works through one contiguous block of the share list: whole runs of
+  // units, i.e. the KV heads of the same page rows.  The scale footer lines
+  // and the lines at head boundaries that neighbouring heads' shares touch
+  // are then fetched once into one L2 instead of into several.  A launch
+  // whose grid is not a multiple of 8 keeps sw = w.
+  const int G8 = (gridDim.x % 8 == 0 && gridDim.x >= 16) ? (int)gridDim.x / 8 : 0;
+  const int sw = G8 ? (w % 8) * G8 + w / 8 : w;
   const bool col = n < (PS ? a.G : G);
 
   // Debug checks (a.dbg set): a length outside [0, dbg_max_len] counts as 0
@@ -337,13 +347,13 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       }
       set_costs(tot, tot_ne);
       cap_W();
-      if (w < W) {
+      if (sw < W) {
         const int64_t lo = SC * Hkv * nep + TC * (int64_t)Hkv * pre;
         const int64_t hiw = lo + (int64_t)Hkv * (SC * ne + TC * nt);
         int64_t bnd[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int64_t c = floordiv((int64_t)(w + e) * Ct, W);
+          const int64_t c = floordiv((int64_t)(sw + e) * Ct, W);
           const bool hit = lane < B && c >= lo && c < hiw;
           const int64_t v = hit ? bound_in(c, lo, pre, nt) : 0;
           const uint64_t mask = __ballot(hit);
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       uint16_t* o = a.out + (size_t)bb * a.Hq * D;
       for (int i = threadIdx.x; i < a.Hq * D; i += NT) o[i] = 0;
     }
-    if (w >= W) return;
+    if (sw >= W) return;
   }
   auto cpre = [&](int bb) -> int64_t { return SC * Hkv * s_nep[bb] + TC * (int64_t)Hkv * s_pre[bb]; };
   // Cost start of tile i of unit (bb, gg).
@@ -452,13 +462,25 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     const int nbb = s_pre[bb + 1] - s_pre[bb];
     return cpre(bb) + (int64_t)gg * (SC + TC * nbb) + SC + TC * i;
   };
-  // Workgroup holding a tile of cost start c: the largest w with floor(w*Ct/W) <= c.
-  auto wg_of_cost = [&](int64_t c) -> int { return (int)(floordiv((c + 1) * W + Ct - 1, Ct) - 1); };
+  // Share holding a tile of cost start c: the largest sh with floor(sh*Ct/W) <= c.
+  auto share_of_cost = [&](int64_t c) -> int { return (int)(floordiv((c + 1) * W + Ct - 1, Ct) - 1); };
+  // The holder of a cut unit's pieces (shares sa..sb) that merges them: the
+  // one with the highest workgroup index, so that it waits only on workgroups
+  // dispatched before it.  Within an XCD block the workgroup index grows with
+  // the share; the last share of a block outranks every share of the next
+  // blocks but that block's own last one.  So: sb, unless the unit crosses
+  // into sb's block from an earlier one and sb does not end its block, in
+  // which case the end of the block before sb's.
+  auto merger_share = [&](int sa, int sb) -> int {
+    if (!G8 || sb % G8 == G8 - 1) return sb;
+    const int e = (sb / G8) * G8 - 1;
+    return e >= sa ? e : sb;
+  };
   if (!fast) {
     // The share's first and end tiles: the first tile whose cost start is >=
     // floor(w*Ct/W), resp. floor((w+1)*Ct/W), found by the thread whose
     // sequence's cost range holds that point (T past the end).
-    const int64_t cb[2] = {floordiv((int64_t)w * Ct, W), floordiv((int64_t)(w + 1) * Ct, W)};
+    const int64_t cb[2] = {floordiv((int64_t)sw * Ct, W), floordiv((int64_t)(sw + 1) * Ct, W)};
     if (threadIdx.x < 2) s_bnd[threadIdx.x] = T;
     __syncthreads();
     const int per = (B + NT - 1) / NT;
@@ -891,8 +913,10 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
   int64_t cur = s_bnd[0];
   const int64_t hi = s_bnd[1];
   int slot = 0;
-  // Unit to merge at the end of the share (uniform across the workgroup).
-  int pend = 0, pend_b = 0, pend_g = 0, pend_wa = 0, pend_first_slot_a = 0;
+  // Units to merge at the end of the share (uniform across the workgroup):
+  // at most two, the share's first and last segments.
+  int npend = 0;
+  int pend_b[2] = {0, 0}, pend_g[2] = {0, 0}, pend_sa[2] = {0, 0}, pend_sb[2] = {0, 0}, pend_fsa[2] = {0, 0};
   // Wave 0 located the first segment and staged its first page rows.
   bool staged = fast;
   int seg_no = 0;
@@ -1085,7 +1109,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       // read with sc1 (agent-coherent) accesses, which on this multi-XCD part
       // are coherent across the per-XCD L2 caches without a cache write-back
       // or invalidate.
-      const size_t pbase = ((size_t)w * 2 + slot) * G;
+      const size_t pbase = ((size_t)sw * 2 + slot) * G;
       const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
       if ((PS || wave == 0) && col) {
         // Lane (head n, quad) holds dims 16c + 4quad .. +3: one 16-byte store per c.
@@ -1104,22 +1128,23 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
-      const int w_a = wg_of_cost(tile_cost(b, g, 0)), w_b = wg_of_cost(tile_cost(b, g, nb - 1));
-      if (w == w_b) {
-        // This is the unit's last piece: merge the unit at the end of the share.
-        pend = 1;
-        pend_b = b;
-        pend_g = g;
-        // w_a's share holds an earlier segment (so this unit sits in its
+      const int s_a = share_of_cost(tile_cost(b, g, 0)), s_b = share_of_cost(tile_cost(b, g, nb - 1));
+      if (sw == merger_share(s_a, s_b)) {
+        // This share merges the unit, at its end.
+        pend_b[npend] = b;
+        pend_g[npend] = g;
+        pend_sa[npend] = s_a;
+        pend_sb[npend] = s_b;
+        // s_a's share holds an earlier segment (so this unit sits in its
         // last slot) iff it starts at or before the previous unit's last
-        // tile, whose cost start is 4 below this unit's.
-        pend_first_slot_a = floordiv((int64_t)w_a * Ct, W) <= tile_cost(b, g, 0) - SC - TC ? 1 : 0;
-        pend_wa = w_a;
+        // tile, whose cost start is SC + TC below this unit's first.
+        pend_fsa[npend] = floordiv((int64_t)s_a * Ct, W) <= tile_cost(b, g, 0) - SC - TC ? 1 : 0;
+        ++npend;
       } else if (threadIdx.x == 0) {
         // Wave 0 wrote the partial; once its stores have completed at the
         // coherence point, publish the slot.
         __builtin_amdgcn_s_waitcnt(0);
-        __hip_atomic_store(a.flags + 2 * w + slot, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.flags + 2 * sw + slot, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();   // LDS is reused by the next segment
@@ -1127,25 +1152,26 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     slot = 1;
   }
 
-  if (pend) {
-    // ---- merge the unit whose last piece was this share's first segment.
-    // Its pieces are held by workgroups w_a..w; w_a holds it in its last
-    // slot when its share began before the unit, every other one in its
-    // first slot.
-    const int w_a = pend_wa;
-    const int nseg = w - w_a + 1;
-    const int first_slot_a = pend_first_slot_a;
+  for (int pi = 0; pi < npend; ++pi) {
+    // ---- merge a unit whose pieces are held by shares w_a..s_b (this share
+    // among them); w_a holds it in its last slot when its share began before
+    // the unit, every other one in its first slot.
+    const int w_a = pend_sa[pi];
+    const int nseg = pend_sb[pi] - w_a + 1;
+    const int first_slot_a = pend_fsa[pi];
     auto slot_of = [&](int wi) -> int { return wi == w_a ? first_slot_a : 0; };
     auto part_row = [&](int wi) -> uint32_t { return (uint32_t)(((size_t)wi * 2 + slot_of(wi)) * G); };
     if (threadIdx.x == 0) {
       __builtin_amdgcn_s_waitcnt(0);   // this workgroup's own partial (wave 0) is complete
       s_timeout = 0;
     }
-    // Wait for the other holders' flags.  They have lower indices, so they
-    // were dispatched first and never wait on this workgroup; the wait is
-    // bounded all the same: a merge that gives up writes NaN outputs and
-    // counts itself in the device status word.
-    for (int i = threadIdx.x; i < nseg - 1; i += NT) {
+    __syncthreads();
+    // Wait for the other holders' flags.  Their workgroups have lower
+    // indices, so they were dispatched first and never wait on this
+    // workgroup; the wait is bounded all the same: a merge that gives up
+    // writes NaN outputs and counts itself in the device status word.
+    for (int i = threadIdx.x; i < nseg; i += NT) {
+      if (w_a + i == sw) continue;
       const uint32_t* f = a.flags + 2 * (w_a + i) + slot_of(w_a + i);
       int spins = 0;
       while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.wait_epoch) {
@@ -1159,7 +1185,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     __syncthreads();
     if (threadIdx.x == 0 && s_timeout)
       __hip_atomic_fetch_add(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int bq = pend_b, gq = pend_g;
+    const int bq = pend_b[pi], gq = pend_g[pi];
     const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
     // Merged 64 partials at a time with a running maximum per head (the sink
     // is the initial maximum, with weight 1): per chunk the weights go to LDS
@@ -1311,8 +1337,11 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       }
     }
     // Clear the consumed flags (a replayed graph reuses the epoch).
-    for (int i = threadIdx.x; i < nseg - 1; i += NT)
-      __hip_atomic_store(a.flags + 2 * (w_a + i) + slot_of(w_a + i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < nseg; i += NT)
+      if (w_a + i != sw)
+        __hip_atomic_store(a.flags + 2 * (w_a + i) + slot_of(w_a + i), 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();   // s_timeout and the LDS weights are reused by the next merge
   }
 }
 
