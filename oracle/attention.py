@@ -69,6 +69,24 @@ def fp8_query(q):
     return out
 
 
+def fp8_query_mx(q):
+    """The query of the fp8 compute mode over pools with E8M0 (MXFP8) scales,
+    as exact float64 values.
+
+    The fp8 path of page "fp8 paged attention for MoE serving" (section "Two
+    compute paths") adds one E4M3 rounding of q; with keys in the MXFP8 format
+    of page "Attention MXFP8 TKG Kernel API Reference" (E4M3 codes, one E8M0
+    scale per 32 elements), the reading taken is that q is rounded to the same
+    format: each (sequence, query head) row is cut into 32-element groups along
+    D and each group is quantized exactly like a 32-element KV group (the
+    smallest power of two s with amax <= 448 s, codes e4m3(q / s)).  The
+    fp8-mode output on such pools is ``decode_ref(fp8_query_mx(q), ...)``."""
+    q = np.asarray(q, dtype=np.float64)
+    codes, u = fp8mod.quantize_e8m0_g32(q)
+    scale = np.repeat(fp8mod.E8M0_TABLE[u], 32, axis=-1)
+    return fp8mod.dequant(codes, scale)
+
+
 def decode_ref(q, k_pool, v_pool, kdesc, vdesc, block_table, seq_lens,
                window=0, sinks=None, sm_scale=None, heads=None, seqs=None):
     """float64 [B, H_q, D] attention output (rows not in ``seqs``/``heads`` are 0).

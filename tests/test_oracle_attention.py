@@ -307,3 +307,40 @@ def test_fp8_query_divides_by_the_row_scale():
         y_mul = (row.astype(np.float32) * (np.float32(1.0) / s32)).astype(np.float64)
         alt = np.array([fp8.e4m3_value(int(c)) for c in _nearest_e4m3_brute(y_mul)]) * float(s32)
         assert not np.array_equal(got[r], alt), "the row does not separate the two rules"
+
+
+def test_fp8_query_mx_pins():
+    """The MXFP8 query: every 32-element group is code x 2**k with k the
+    smallest exponent whose 448 x 2**k covers the group's amax (checked by
+    search), each code the nearest E4M3 value of q / 2**k (exhaustive search);
+    groups are independent (scaling one group by 2**j scales only it); an
+    all-zero group stays zero; values already on the grid come back
+    unchanged."""
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((2, 3, 128)) * np.repeat(2.0 ** rng.integers(-6, 6, size=(2, 3, 4)), 32, axis=-1)
+    q[1, 2, 32:64] = 0.0
+    got = oatt.fp8_query_mx(q)
+    for idx in np.ndindex(q.shape[:-1]):
+        for gi in range(4):
+            x = q[idx][32 * gi:32 * gi + 32]
+            amax = np.abs(x).max()
+            if amax == 0.0:
+                assert np.all(got[idx][32 * gi:32 * gi + 32] == 0.0)
+                continue
+            k = -140
+            while 448.0 * 2.0 ** k < amax:
+                k += 1
+            y = (x.astype(np.float32) / np.float32(2.0 ** k)).astype(np.float64)   # exact: a power of two
+            want = np.array([fp8.e4m3_value(int(c)) for c in _nearest_e4m3_brute(y)]) * 2.0 ** k
+            np.testing.assert_array_equal(got[idx][32 * gi:32 * gi + 32], want)
+    # groups are independent
+    q2 = q.copy()
+    q2[0, 1, 64:96] *= 2.0 ** 5
+    g2 = oatt.fp8_query_mx(q2)
+    np.testing.assert_array_equal(g2[0, 1, 64:96], got[0, 1, 64:96] * 2.0 ** 5)
+    np.testing.assert_array_equal(np.delete(g2, np.s_[64:96], axis=-1)[0, 1], np.delete(got, np.s_[64:96], axis=-1)[0, 1])
+    # values on the grid come back unchanged
+    codes = rng.integers(0, 0x7F, size=(4, 64)).astype(np.uint8)
+    codes[:, 0] = codes[:, 32] = 0x7E
+    on = fp8.E4M3_TABLE[codes] * 2.0 ** -3
+    np.testing.assert_array_equal(oatt.fp8_query_mx(on), on)
