@@ -25,7 +25,7 @@ thread_local bool g_force_timeout = false;   // test hook: merges give up waitin
 
 struct Counters {
   std::atomic<int64_t> decode_calls{0}, decode_mfma{0}, decode_split{0}, merge{0}, append{0}, debug{0}, fused_append{0},
-      decode_vtok{0}, decode_fp8{0}, decode_packed{0}, decode_psplit{0}, errors{0};
+      decode_vtok{0}, decode_fp8{0}, decode_mx{0}, decode_packed{0}, decode_psplit{0}, errors{0};
 };
 Counters g_cnt;
 std::atomic<uint32_t> g_epoch{0};
@@ -252,9 +252,13 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
   const bool vt = vd->layout == FP8PA_LAYOUT_HEADS || vd->layout == FP8PA_LAYOUT_TOKENS;
   if (vt && fused) return fail(FP8PA_EUNSUPPORTED, "the one-launch append reads V in the HEADS_DMAJOR layout");
   const bool f8 = variant == FP8PA_VARIANT_MFMA_FP8;
-  if (f8 && (kd->scale_kind == FP8PA_SCALE_E8M0_G32 || grouped(kd->scale_kind) || vt || fused))
+  if (f8 && (grouped(kd->scale_kind) || vt || fused))
     return fail(FP8PA_EUNSUPPORTED,
-                "the fp8 compute mode takes fp32 page or token scales, V in HEADS_DMAJOR and no fused append");
+                "the fp8 compute mode takes page, token or E8M0 scales, V in HEADS_DMAJOR and no fused append");
+  // With E8M0 pools the fp8 mode runs the MX-scaled fp8 MFMA, 128 dims each.
+  if (f8 && kd->scale_kind == FP8PA_SCALE_E8M0_G32 && kd->head_dim % 128)
+    return fail(FP8PA_EUNSUPPORTED, "the fp8 mode over E8M0 pools needs a head_dim multiple of 128 (got %d)",
+                kd->head_dim);
   // fp32 sub-row K scales: K pieces are scaled before the MFMA (plain,
   // token-major-V and split kernels only).
   const bool kgroups = grouped(kd->scale_kind);
@@ -468,6 +472,7 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
   if (f8) g_cnt.decode_fp8.fetch_add(1);
   else g_cnt.decode_mfma.fetch_add(1);
+  if (f8 && kd->scale_kind == FP8PA_SCALE_E8M0_G32) g_cnt.decode_mx.fetch_add(1);
   if (W > 1 && !packed) g_cnt.decode_split.fetch_add(1);
   if (packed) g_cnt.decode_packed.fetch_add(1);
   if (psplit) g_cnt.decode_psplit.fetch_add(1);
@@ -699,6 +704,7 @@ int fp8pa_get_counters(fp8pa_counters* c) {
   c->decode_mfma_fp8 = g_cnt.decode_fp8.load();
   c->decode_packed_heads = g_cnt.decode_packed.load();
   c->decode_packed_split = g_cnt.decode_psplit.load();
+  c->decode_mfma_mxfp8 = g_cnt.decode_mx.load();
   return FP8PA_OK;
 }
 
@@ -754,6 +760,7 @@ int fp8pa_reset_counters(void) {
   g_cnt.decode_fp8 = 0;
   g_cnt.decode_packed = 0;
   g_cnt.decode_psplit = 0;
+  g_cnt.decode_mx = 0;
   return FP8PA_OK;
 }
 

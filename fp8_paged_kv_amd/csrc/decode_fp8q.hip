@@ -9,7 +9,7 @@ namespace fp8pa {
 
 hipError_t launch_decode_fp8q(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                               hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  if (scale_kind == 2) return hipErrorNotSupported;
+  if (scale_kind == 2 && D % 128) return hipErrorNotSupported;
   return launch_family<false, false, true>(a, D, scale_kind, k_whole_lines, W, lds, st, e0, e1);
 }
 

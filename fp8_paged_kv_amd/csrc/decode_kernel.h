@@ -190,7 +190,11 @@ struct Tile {
 template <int D, int SK, bool KNT, bool FUSED, bool VT, bool F8 = false, bool PK = false, bool PS = false>
 __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kernel(const DecodeArgs a) {
   static_assert(!(PS && (FUSED || PK)), "packed splits: plain kernels");
-  static_assert(!(F8 && SK >= 2), "E8M0 and sub-row K scales vary inside one fp8 MFMA");
+  static_assert(!(F8 && SK == 3), "sub-row fp32 K scales vary inside one fp8 MFMA");
+  static_assert(!(F8 && SK == 2 && D % 128), "the MX-scaled fp8 MFMA contracts 128 dims at a time");
+  // MX: the fp8 mode over E8M0 pools: QK^T on the MX-scaled fp8 MFMA, which
+  // applies the keys' E8M0 scales and the query's own (MXFP8) scales itself.
+  constexpr bool MX = F8 && SK == 2;
   static_assert(!(SK == 3 && (FUSED || PK || PS)), "sub-row K scales: split kernels without the fused append");
   static_assert(!(PK && (FUSED || F8)), "packed heads: plain bf16 kernels");
   constexpr int NS = Shape<D>::NS;
@@ -506,6 +510,15 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
   bf16x8 qop[NQ];
   uint64_t qop8[NQ];   // F8: E4M3 codes of the same dims
   float qsc = 1.0f;    // F8: scale of the lane's query row
+  // MX: the 16x16x128 MFMA takes, from lane (quad, n), bytes 0-15 as
+  // contraction elements 16quad.. and bytes 16-31 as 64 + 16quad.., and the
+  // lane's scale byte for elements 32quad .. 32quad + 31.  With element k =
+  // dim 128x + k, a lane's K bytes are exactly the two 16-byte pieces the
+  // bf16 path loads (t.k[s][aa][2x], [2x + 1]) and its key scale is the E8M0
+  // byte of dims 128x + 32quad .. +31 of its row.
+  constexpr int NX = D / 128;   // MX: MFMAs of 128 dims per 16 positions
+  v8i32 qmx[MX ? NX : 1];       // MX: E4M3 codes of the lane's query head, same dims as its K bytes
+  uint32_t qmxs[MX ? NX : 1];   // MX: E8M0 scale of dims 128x + 32quad .. +31 of that head
 
   // Row of a page of the current chunk.  A group with no attended position
   // reads a clamped (attended) page instead: its scores are masked to -inf and
@@ -626,18 +639,20 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
           t.ke8[s][aa] = load_e8_row<NG>(kf);
         }
     }
-    const uint8_t* krow = kpool + rk.code + 16 * quad;
+    {
+      const uint8_t* krow = kpool + rk.code + 16 * quad;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int aa = 0; aa < 2; ++aa) {
-        const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
+        for (int aa = 0; aa < 2; ++aa) {
+          const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const uint8_t* src = krow + tp * a.kg.tok_stride + m * a.kg.dchunk_stride;
-          t.k[s][aa][m] = KNT ? ld_stream<u32x4>(src) : ld_global<u32x4>(src);
+          for (int m = 0; m < NM; ++m) {
+            const uint8_t* src = krow + tp * a.kg.tok_stride + m * a.kg.dchunk_stride;
+            t.k[s][aa][m] = KNT ? ld_stream<u32x4>(src) : ld_global<u32x4>(src);
+          }
         }
-      }
+    }
     if constexpr (VT) {
       // Whole 16-byte pieces of NIV consecutive position rows (NIV <= 16
       // divides P, so they share a page).
@@ -710,8 +725,19 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
 #pragma unroll
       for (int aa = 0; aa < 2; ++aa) {
         f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (MX) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
+          for (int x = 0; x < NX; ++x) {
+            const u32x4 lo = t.k[s][aa][2 * x], hi = t.k[s][aa][2 * x + 1];
+            const v8i32 kx = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            // Formats 0, 0: E4M3 for both operands; scale bytes in bits 0-7.
+            s4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                kx, qmx[x], s4, 0, 0, 0, (int)byte_of(t.ke8[s][aa], 4 * x + quad), 0, (int)qmxs[x]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < (MX ? 0 : NM); ++m) {
           float cvt = 1.0f;
           if constexpr (SK == 2) {
             const uint32_t e = byte_of(t.ke8[s][aa], 2 * m + (quad >> 1));
@@ -740,7 +766,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float f = a.qk_scale;
-          if constexpr (F8) f *= qsc;
+          if constexpr (F8 && !MX) f *= qsc;
           if constexpr (SK == 0) f *= t.ks;
           if constexpr (SK == 1) f *= t.kst[s][4 * aa + j];
           sc[s][aa][j] = s4[j] * f;
@@ -952,14 +978,65 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     {
       // Q operand (B of QK): lane (head n, quad) holds dims 64m + 16quad + 8h2 + i.
       const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G + (col ? n : 0)) * D;
+      if constexpr (MX) {
+        // MXFP8 query: each 32-dim group of the head gets the E8M0 scale 2^k
+        // of the KV quantizer (the smallest with amax <= 448 * 2^k) and codes
+        // e4m3(q * 2^-k) (an exact scaling).  The lane holds dims 128x +
+        // 16quad .. +15 (bytes 0-15) and 128x + 64 + 16quad .. +15 (bytes
+        // 16-31): halves of groups 4x + quad/2 and 4x + 2 + quad/2, whose
+        // other halves sit in the lane 16 apart (quad ^ 1).  Its scale operand
+        // is group 4x + quad's, found in lane n + 32 * (quad & 1).
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+        for (int x = 0; x < NX; ++x) {
+          uint32_t wv[16];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          u32x4 v = col ? ld_global<u32x4>(qrow + 64 * m + 16 * quad + 8 * h2) : u32x4{0, 0, 0, 0};
-          qop[2 * m + h2] = __builtin_bit_cast(bf16x8, v);
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const u32x4 v =
+                  col ? ld_global<u32x4>(qrow + 128 * x + 64 * h + 16 * quad + 8 * c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+              for (int j = 0; j < 4; ++j) wv[8 * h + 4 * c + j] = v[j];
+            }
+          float am[2] = {0.0f, 0.0f};
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              am[h] = fmaxf(am[h], fmaxf(fabsf(bf16_to_f32((uint16_t)wv[8 * h + j])),
+                                         fabsf(bf16_to_f32((uint16_t)(wv[8 * h + j] >> 16)))));
+            am[h] = fmaxf(am[h], __shfl_xor(am[h], 16));
+          }
+          const uint32_t u0 = e8m0_code(am[0]), u1 = e8m0_code(am[1]);
+          v8i32 codes;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int sh = 127 - (int)(h ? u1 : u0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t w0 = wv[8 * h + 2 * j], w1 = wv[8 * h + 2 * j + 1];
+              const uint32_t c0 = f32_to_e4m3(__builtin_amdgcn_ldexpf(bf16_to_f32((uint16_t)w0), sh));
+              const uint32_t c1 = f32_to_e4m3(__builtin_amdgcn_ldexpf(bf16_to_f32((uint16_t)(w0 >> 16)), sh));
+              const uint32_t c2 = f32_to_e4m3(__builtin_amdgcn_ldexpf(bf16_to_f32((uint16_t)w1), sh));
+              const uint32_t c3 = f32_to_e4m3(__builtin_amdgcn_ldexpf(bf16_to_f32((uint16_t)(w1 >> 16)), sh));
+              codes[4 * h + j] = (int)(c0 | (c1 << 8) | (c2 << 16) | (c3 << 24));
+            }
+          }
+          qmx[x] = codes;
+          const int src = n + 32 * (quad & 1);
+          const uint32_t g0 = (uint32_t)__shfl((int)u0, src), g1 = (uint32_t)__shfl((int)u1, src);
+          qmxs[x] = quad >= 2 ? g1 : g0;
         }
-      if constexpr (F8) {
+      } else {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            u32x4 v = col ? ld_global<u32x4>(qrow + 64 * m + 16 * quad + 8 * h2) : u32x4{0, 0, 0, 0};
+            qop[2 * m + h2] = __builtin_bit_cast(bf16x8, v);
+          }
+      }
+      if constexpr (F8 && !MX) {
         // The row's amax (the four quads of a head column hold its dims),
         // its scale fp32(amax / 448) (1 for a zero row), and the codes
         // e4m3(fp32(q / scale)) with the IEEE-rounded quotient (the rule of
@@ -1356,7 +1433,7 @@ hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t 
       hipExtLaunchKernelGGL((decode_kernel<D, 1, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
     case 2:
-      if constexpr (F8) return hipErrorNotSupported;
+      if constexpr (F8 && D % 128) return hipErrorNotSupported;
       else hipExtLaunchKernelGGL((decode_kernel<D, 2, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
     default:   // fp32 sub-row K scales

@@ -38,7 +38,7 @@ class Counters(ctypes.Structure):
                                               "append_launches", "debug_launches", "errors", "fused_appends",
                                               "decode_v_token_major", "decode_mfma_fp8",
                                               "decode_packed_heads",
-                                              "decode_packed_split")]
+                                              "decode_packed_split", "decode_mfma_mxfp8")]
 
 
 class DeviceStatus(ctypes.Structure):

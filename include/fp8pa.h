@@ -99,8 +99,13 @@ enum {
                                    zero row) and codes e4m3(fp32(q/scale)) with the IEEE
                                    quotient (the KV quantizer's rule); QK^T takes the K
                                    codes unconverted on the fp8 MFMA; PV and the softmax as
-                                   in MFMA_BF16.  Only on explicit request; pools with fp32
-                                   scales and V in HEADS_DMAJOR, |sm_scale| <= D^-0.5 (the
+                                   in MFMA_BF16.  With E8M0 pools (head_dim a multiple of
+                                   128) q is rounded to the keys' own MXFP8 format instead:
+                                   one E8M0 scale per 32 dims (the KV quantizer's rule) and
+                                   codes e4m3(q / scale); QK^T then runs on the MX-scaled
+                                   fp8 MFMA, which applies both operands' E8M0 scales
+                                   itself (counted in decode_mfma_mxfp8).  Only on explicit
+                                   request; V in HEADS_DMAJOR, |sm_scale| <= D^-0.5 (the
                                    page's fp8 tolerance class, rtol = atol = 1.5e-1, holds
                                    at the default score scale; larger scales spread the
                                    logits so that q's rounding exceeds it), not with the
@@ -368,6 +373,7 @@ typedef struct fp8pa_counters {
   int64_t decode_mfma_fp8;  /* decode kernels launched, fp8 compute mode */
   int64_t decode_packed_heads; /* decode kernels launched, packed heads */
   int64_t decode_packed_split;  /* decode kernels launched, packed heads with splits */
+  int64_t decode_mfma_mxfp8;  /* of decode_mfma_fp8: over E8M0 pools, on the MX-scaled fp8 MFMA */
 } fp8pa_counters;
 
 int fp8pa_get_counters(fp8pa_counters* out);

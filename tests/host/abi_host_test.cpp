@@ -258,7 +258,8 @@ int main() {
     c = Call(); c.variant = FP8PA_VARIANT_MFMA_FP8; c.sm_scale = 0.09f; REFUSE(c, FP8PA_EUNSUPPORTED);
     c = Call(); c.variant = FP8PA_VARIANT_MFMA_FP8; c.vd.layout = FP8PA_LAYOUT_TOKENS; REFUSE(c, FP8PA_EUNSUPPORTED);
     c = Call(); c.variant = FP8PA_VARIANT_MFMA_FP8; c.kd.scale_kind = c.vd.scale_kind = FP8PA_SCALE_E8M0_G32;
-    c.kd.row_bytes = c.vd.row_bytes = 16384 + 4096; REFUSE(c, FP8PA_EUNSUPPORTED);
+    c.kd.head_dim = c.vd.head_dim = 64; c.kd.row_bytes = c.vd.row_bytes = 8192 + 4096; c.sm_scale = 0.125f;
+    REFUSE(c, FP8PA_EUNSUPPORTED);   // the MX-scaled MFMA contracts 128 dims
     // packed variants
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_HEADS; c.workgroups = 3; REFUSE(c, FP8PA_EUNSUPPORTED);
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_HEADS; c.vd.layout = FP8PA_LAYOUT_HEADS; REFUSE(c, FP8PA_EUNSUPPORTED);
@@ -283,6 +284,16 @@ int main() {
     c = Call(); c.vd.layout = FP8PA_LAYOUT_TOKENS; c.workgroups = 5; LAUNCH(c);
     c = Call(); c.variant = FP8PA_VARIANT_MFMA_FP8; LAUNCH(c);
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_HEADS; LAUNCH(c);
+    c = Call(); c.variant = FP8PA_VARIANT_MFMA_FP8; c.kd.scale_kind = c.vd.scale_kind = FP8PA_SCALE_E8M0_G32;
+    c.kd.row_bytes = c.vd.row_bytes = 16384 + 4096;
+    {
+      fp8pa_counters c0{}, c1{};
+      fp8pa_get_counters(&c0);
+      LAUNCH(c);   // MX-scaled fp8 MFMA
+      fp8pa_get_counters(&c1);
+      CHECK(c1.decode_mfma_fp8 == c0.decode_mfma_fp8 + 1 && c1.decode_mfma_mxfp8 == c0.decode_mfma_mxfp8 + 1 &&
+            c1.decode_mfma_bf16 == c0.decode_mfma_bf16);
+    }
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_SPLIT; c.workgroups = 9; LAUNCH(c);
     c = Call(); c.kd.scale_kind = FP8PA_SCALE_F32_G32; c.kd.row_bytes = 16384 + 2048;
     c.vd.scale_kind = FP8PA_SCALE_F32_TOKEN_HEAD; c.vd.row_bytes = 16384 + 2048; c.workgroups = 3; LAUNCH(c);

@@ -33,7 +33,7 @@ def test_version_and_struct_sizes():
     assert b"gfx950" in ops.lib().fp8pa_version()
     assert ctypes.sizeof(ops.PoolDesc) == 48
     assert ctypes.sizeof(ops.Plan) == 24
-    assert ctypes.sizeof(ops.Counters) == 96
+    assert ctypes.sizeof(ops.Counters) == 104
 
 
 def kd(**kw):
@@ -90,8 +90,8 @@ def call_decode(k=None, v=None, **kw):
     (dict(sm_scale=float("nan")), ops.EINVAL),
     (dict(sm_scale=float("inf")), ops.EINVAL),
     (dict(variant=7), ops.EUNSUPPORTED),
-    (dict(variant=2, k=kd(scale_kind="e8m0_32", row_bytes=16384 + 4096),
-          v=vd(scale_kind="e8m0_32", row_bytes=16384 + 4096)), ops.EUNSUPPORTED),   # fp8 mode: fp32 scales only
+    (dict(variant=2, k=kd(scale_kind="e8m0_32", head_dim=64, row_bytes=8192 + 4096),
+          v=vd(scale_kind="e8m0_32", head_dim=64, row_bytes=8192 + 4096)), ops.EUNSUPPORTED),  # MX fp8: D % 128
     (dict(variant=2, v=vd(layout="tokens")), ops.EUNSUPPORTED),                    # fp8 mode: V d-major only
     (dict(variant=2, sm_scale=0.09), ops.EUNSUPPORTED),                             # fp8 mode: sm_scale > D^-0.5
     (dict(variant=2, sm_scale=-1.0), ops.EUNSUPPORTED),

@@ -74,9 +74,9 @@ def test_fp8_mode_rounds_q_and_keeps_query_range():
 
 
 def test_fp8_mode_refusals():
-    p = make_problem(403, B=2, Hq=16, Hkv=2, D=128, P=128, lens=[300, 90], scale_kind="e8m0_32")
+    p = make_problem(403, B=2, Hq=16, Hkv=2, D=64, P=128, lens=[300, 90], scale_kind="e8m0_32")
     ops.reset_counters()
-    with pytest.raises(RuntimeError):
+    with pytest.raises(RuntimeError):                  # E8M0 at 64 dims: the MX MFMA contracts 128
         gpu_decode(p, variant="mfma_fp8")
     p = make_problem(403, B=2, Hq=16, Hkv=2, D=128, P=16, lens=[300, 90], v_layout="tokens")
     with pytest.raises(RuntimeError):
@@ -115,3 +115,45 @@ def test_fp8_mode_append_decode_takes_two_launches():
     assert c["append_launches"] == 1 and c["fused_appends"] == 0 and c["decode_mfma_fp8"] == 1
     assert torch.equal(kb, ka) and torch.equal(vb, va)
     assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
+MX_CASES = [
+    ("d128-p128", dict(B=2, Hq=16, Hkv=2, D=128, P=128, lens=[1000, 130])),
+    ("d128-p16-sinks", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[513, 64, 1], sinks=True)),
+    ("d128-window", dict(B=2, Hq=16, Hkv=2, D=128, P=32, lens=[900, 77], window=200)),
+    ("d128-kheads", dict(B=2, Hq=8, Hkv=2, D=128, P=32, lens=[260, 77], k_layout="heads")),
+    ("d128-ktokens", dict(B=2, Hq=8, Hkv=2, D=128, P=16, lens=[260, 5], k_layout="tokens")),
+    ("d256", dict(B=2, Hq=8, Hkv=2, D=256, P=32, lens=[300, 41])),
+    ("d512-g8", dict(B=2, Hq=8, Hkv=1, D=512, P=32, lens=[333, 64])),
+    ("empty-and-short", dict(B=4, Hq=8, Hkv=2, D=128, P=16, lens=[0, 1, 15, 65])),
+]
+
+
+@pytest.mark.parametrize("name,kw", MX_CASES, ids=[c[0] for c in MX_CASES])
+@pytest.mark.parametrize("workgroups", [1, 0, 3])
+def test_mx_fp8_mode_parity(name, kw, workgroups):
+    """The fp8 mode over E8M0 pools: q rounded to MXFP8 (E8M0 per 32 dims),
+    QK^T on the MX-scaled fp8 MFMA.  Within the default bound of the oracle
+    decoding fp8_query_mx(q), and within the page's fp8 class of the exact
+    oracle; the MX counter records it."""
+    say("mx fp8 mode parity", name, "workgroups", workgroups)
+    p = make_problem(411, scale_kind="e8m0_32", **kw)
+    ops.reset_counters()
+    got = to_np(gpu_decode(p, workgroups=workgroups, variant="mfma_fp8"))
+    c = ops.counters()
+    assert c["decode_mfma_fp8"] == 1 and c["decode_mfma_mxfp8"] == 1 and c["decode_mfma_bf16"] == 0
+    assert_parity(got, oracle(p, oatt.fp8_query_mx(p.q)), name)
+    want = oracle(p)
+    assert np.all(np.abs(got - want) <= FP8_TOL + FP8_TOL * np.abs(want)), name
+
+
+def test_mx_fp8_mode_refusals():
+    p = make_problem(412, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[300, 90], scale_kind="e8m0_32")
+    ops.reset_counters()
+    with pytest.raises(RuntimeError):                  # 64 dims: the MX MFMA contracts 128
+        gpu_decode(p, variant="mfma_fp8")
+    p = make_problem(412, B=2, Hq=8, Hkv=2, D=128, P=16, lens=[300, 90], scale_kind="e8m0_32", v_layout="tokens")
+    with pytest.raises(RuntimeError):
+        gpu_decode(p, variant="mfma_fp8")
+    c = ops.counters()
+    assert c["decode_calls"] == 0 and c["decode_mfma_mxfp8"] == 0 and c["errors"] == 2

@@ -325,3 +325,31 @@ def test_llama_full_size_sub_row_key_scales():
                  (int(rng.integers(len(layer.lens))), int(rng.integers(layer.Hkv)))]:
         err, frac = check_panel(configs.LLAMA3_8B, layer, out_np, b, g)
         say(f"  f32_g32 b={b} g={g}: max err {err:.2e} ({frac:.2f} of bound)")
+
+
+def test_long_context_full_size_mx_fp8_mode():
+    """The long-context MXFP8 call at full size in the fp8 mode (the MX-scaled
+    fp8 MFMA): sampled panels within the default bound of the oracle decoding
+    the MXFP8-rounded query, and within the page's fp8 class of the exact
+    oracle."""
+    say("workload mx fp8")
+    wl = configs.LONG_MXFP8
+    layer = workloads.build_workload(wl)[0]
+    ops.reset_counters()
+    out = workloads.decode_layer(layer, variant="mfma_fp8")
+    torch.cuda.synchronize()
+    assert ops.counters()["decode_mfma_mxfp8"] == 1
+    out_np = to_np(out)
+    assert np.all(np.isfinite(out_np))
+    q = inputs.normal_bf16(configs.SEED, wl.index, "q", 0, (len(layer.lens), layer.Hq, layer.D))
+    qmx = oatt.fp8_query_mx(q)
+    G = layer.Hq // layer.Hkv
+    for b, g in [(0, 3), (2, 7)]:
+        kd, vd, hk, hv = oracle_panel(wl, layer, b, g)
+        want = oatt.decode_ref(qmx, hk, hv, kd, vd, layer.table_np, layer.lens, sm_scale=layer.sm_scale,
+                               seqs=[b], heads=[g])
+        err, frac = assert_parity(out_np[b, g * G:(g + 1) * G], want[b, g * G:(g + 1) * G], f"mx b={b} g={g}")
+        exact = oatt.decode_ref(q, hk, hv, kd, vd, layer.table_np, layer.lens, sm_scale=layer.sm_scale,
+                                seqs=[b], heads=[g])[b, g * G:(g + 1) * G]
+        assert np.all(np.abs(out_np[b, g * G:(g + 1) * G] - exact) <= 0.15 + 0.15 * np.abs(exact))
+        say(f"  mx b={b} g={g}: max err {err:.2e} ({frac:.2f} of bound)")
