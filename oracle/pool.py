@@ -34,8 +34,8 @@ Scale footer (byte offset from the scale block's start):
   "token_head" fp32 per (token, head): 4*(h*P + t), or 4*(t*H + h) for "tokens"
   "e8m0_32"    one E8M0 byte per (token, head, 32 dims along D):
                (h*P + t)*(D/32) + d//32, or (t*H + h)*(D/32) + d//32 for "tokens"
-  "f32_g<S>"   fp32 per (token, head, S dims along D), S in 32, 64, 128, 256 (the
-               page's sub-row key groups, k_groups = D/S):
+  "f32_g<S>"   fp32 per (token, head, S dims along D), S in 8, 16, 32, 64, 128,
+               256 (the page's sub-row groups, k_groups or v_groups = D/S):
                4*((h*P + t)*(D/S) + d//S), or 4*((t*H + h)*(D/S) + d//S) for "tokens"
 """
 from dataclasses import dataclass, replace
@@ -46,7 +46,7 @@ import numpy as np
 from . import fp8
 
 LAYOUTS = ("heads", "tokens", "heads_d64", "heads_dmajor")
-GROUP_KINDS = {"f32_g32": 32, "f32_g64": 64, "f32_g128": 128, "f32_g256": 256}
+GROUP_KINDS = {"f32_g8": 8, "f32_g16": 16, "f32_g32": 32, "f32_g64": 64, "f32_g128": 128, "f32_g256": 256}
 SCALE_KINDS = ("page_head", "token_head", "e8m0_32") + tuple(GROUP_KINDS)
 
 

@@ -28,7 +28,7 @@ def test_group_as_wide_as_the_head_is_the_token_kind(layout, D, kind):
     assert np.array_equal(a.k_pool, b.k_pool)
 
 
-@pytest.mark.parametrize("kind", ["f32_g32", "f32_g64"])
+@pytest.mark.parametrize("kind", ["f32_g8", "f32_g16", "f32_g32", "f32_g64"])
 @pytest.mark.parametrize("layout", ["heads", "tokens", "heads_d64", "heads_dmajor"])
 def test_each_group_reads_back_as_its_own_token_scaled_row(kind, layout):
     """Group g of head h holds exactly what a "token_head" pool built from the
