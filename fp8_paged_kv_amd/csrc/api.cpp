@@ -49,9 +49,11 @@ int ilog2(int64_t v) {
   return r;
 }
 
-// Dims per scale of the fp32 sub-row kinds (FP8PA_SCALE_F32_G32..G256).
-int group_dims(int kind) { return 32 << (kind - FP8PA_SCALE_F32_G32); }
-bool grouped(int kind) { return kind >= FP8PA_SCALE_F32_G32 && kind <= FP8PA_SCALE_F32_G256; }
+// Dims per scale of the fp32 sub-row kinds (FP8PA_SCALE_F32_G8..G256).
+bool grouped(int kind) { return kind >= FP8PA_SCALE_F32_G32 && kind <= FP8PA_SCALE_F32_G16; }
+int group_dims(int kind) {
+  return kind == FP8PA_SCALE_F32_G8 ? 8 : kind == FP8PA_SCALE_F32_G16 ? 16 : 32 << (kind - FP8PA_SCALE_F32_G32);
+}
 
 int64_t scale_bytes(const fp8pa_pool_desc& d) {
   const int64_t H = d.num_kv_heads, P = d.page_size, D = d.head_dim;
@@ -78,7 +80,7 @@ int check_desc(const fp8pa_pool_desc* d, const char* name) {
     return fail(FP8PA_EUNSUPPORTED, "%s: page_size %d is not a power of two in [16,1024]", name, d->page_size);
   if (d->layout < FP8PA_LAYOUT_HEADS || d->layout > FP8PA_LAYOUT_HEADS_D64)
     return fail(FP8PA_EINVAL, "%s: unknown layout %d", name, d->layout);
-  if (d->scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || d->scale_kind > FP8PA_SCALE_F32_G256)
+  if (d->scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || d->scale_kind > FP8PA_SCALE_F32_G16)
     return fail(FP8PA_EINVAL, "%s: unknown scale_kind %d", name, d->scale_kind);
   if (grouped(d->scale_kind) && group_dims(d->scale_kind) > d->head_dim)
     return fail(FP8PA_EINVAL, "%s: %d dims per scale exceed head_dim %d", name, group_dims(d->scale_kind),
@@ -206,6 +208,8 @@ struct Resolved {
   int Gu;                  // query heads per unit (packed splits: NW * G)
   size_t lds;              // dynamic LDS bytes
   size_t vstage_off;       // V token-major: offset of the per-wave V stages
+  size_t vgstage_off;      // V sub-row scales: offset of the per-wave scale stages
+  int sk;                  // kernel scale code: the K kind 0-2, 3 (K groups, V per token), 4 (K and V groups)
   int64_t part_o_bytes, part_lse_bytes, flag_bytes;   // workspace pieces, 256-byte aligned
   int64_t workspace_bytes; // 0 when nothing is split
 };
@@ -242,8 +246,14 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
   if (int rc = check_desc(vd, "vd")) return rc;
   if (kd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
     return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS_D64, HEADS or TOKENS layout");
-  if (grouped(vd->scale_kind))
-    return fail(FP8PA_EUNSUPPORTED, "vd: decode reads fp32 sub-row scales for K only");
+  // fp32 sub-row V scales: with K in sub-row groups too; one PV MFMA covers 16
+  // dims, so V groups span at least 16; the per-wave stage holds 16 groups.
+  const bool vgroups = grouped(vd->scale_kind);
+  if (vgroups && (!grouped(kd->scale_kind) || group_dims(vd->scale_kind) < 16 ||
+                  vd->head_dim / group_dims(vd->scale_kind) > 16))
+    return fail(FP8PA_EUNSUPPORTED,
+                "vd: decode reads fp32 sub-row V scales with K in sub-row scales, groups of 16 to head_dim dims and "
+                "at most 16 groups per head");
   if (g_dbg && (kd->num_rows < 1 || vd->num_rows < 1))
     return fail(FP8PA_EINVAL, "debug checks need num_rows >= 1 in both descriptors");
   if (vd->layout == FP8PA_LAYOUT_HEADS_D64)
@@ -275,10 +285,20 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
                   B, D, lds);
   }
   if (vd->num_kv_heads != kd->num_kv_heads || vd->head_dim != kd->head_dim || vd->page_size != kd->page_size ||
-      (vd->scale_kind != kd->scale_kind && !(kgroups && vd->scale_kind == FP8PA_SCALE_F32_TOKEN_HEAD)))
+      (vd->scale_kind != kd->scale_kind &&
+       !(kgroups && (vd->scale_kind == FP8PA_SCALE_F32_TOKEN_HEAD || vgroups))))
     return fail(FP8PA_EUNSUPPORTED,
                 "K and V pools must share num_kv_heads, head_dim, page_size and scale_kind (or K in fp32 "
-                "sub-row scales with V in F32_TOKEN_HEAD)");
+                "sub-row scales with V in F32_TOKEN_HEAD or fp32 sub-row scales)");
+  // V sub-row scales: a per-wave LDS stage of the tile's (position, group) scales.
+  size_t vgstage_off = 0;
+  if (vgroups) {
+    vgstage_off = (lds + 15) / 16 * 16;
+    lds = vgstage_off + (size_t)nw * fp8pa::decode_tile_tokens(D) * (D / group_dims(vd->scale_kind)) * 4 + 16;
+    if (lds > 65536)
+      return fail(FP8PA_EUNSUPPORTED, "B=%d, head_dim %d with V sub-row scales need %zu bytes of LDS (> 64 KiB)", B,
+                  D, lds);
+  }
   // Packed heads: requested, or taken automatically when the units fill the
   // device (V d-major, no fused append).
   const bool packed = packed_req || (!vt && !fused && !kgroups && auto_packs(B, Hq, kd, workgroups, variant));
@@ -292,7 +312,8 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
     // One resident generation: every workgroup gets an equal share of the
     // tiles and all of them run at once.
     const int cus = device_cus();
-    const int per_cu = cus > 0 ? fp8pa::decode_blocks_per_cu(D, kd->scale_kind, k_whole, lds) : 0;
+    const int per_cu = cus > 0 ? fp8pa::decode_blocks_per_cu(D, kgroups ? (vgroups ? 4 : 3) : kd->scale_kind,
+                                                             k_whole, lds) : 0;
     W = (cus > 0 && per_cu > 0) ? cus * per_cu : 1024;
   }
   r->variant = f8 ? FP8PA_VARIANT_MFMA_FP8
@@ -309,6 +330,8 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
   r->Gu = Gu;
   r->lds = lds;
   r->vstage_off = vstage_off;
+  r->vgstage_off = vgstage_off;
+  r->sk = kgroups ? (vgroups ? 4 : 3) : kd->scale_kind;
   if (W > 1 && !packed) {
     r->part_o_bytes = round256((int64_t)W * 2 * Gu * D * 4);
     r->part_lse_bytes = round256((int64_t)W * 2 * Gu * 4);
@@ -436,6 +459,7 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   a.window = window > 0 ? window : 0;
   a.qk_scale = (float)((double)sm_scale * 1.4426950408889634);
   a.vstage_off = (int32_t)r.vstage_off;
+  a.vgstage_off = (int32_t)r.vgstage_off;
   a.dbg = g_dbg;
   a.dbg_rows = (int32_t)std::min<int64_t>(std::min(kd->num_rows, vd->num_rows), INT32_MAX);
   a.dbg_max_len = max_seq_len;
@@ -461,14 +485,14 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   // A wave's 16-byte K loads cover 64 bytes of each of 16 tokens: whole lines
   // when the 64-byte pieces of consecutive tokens are adjacent.
   const bool k_whole = r.k_whole;
-  hipError_t e = fused ? fp8pa::launch_decode_fused(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
-                 : vt  ? fp8pa::launch_decode_vtok(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
-                 : f8  ? fp8pa::launch_decode_fp8q(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop)
-                 : packed ? fp8pa::launch_decode_packed(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start,
+  hipError_t e = fused ? fp8pa::launch_decode_fused(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                 : vt  ? fp8pa::launch_decode_vtok(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                 : f8  ? fp8pa::launch_decode_fp8q(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                 : packed ? fp8pa::launch_decode_packed(a, D, r.sk, k_whole, W, lds, st, g_ev_start,
                                                         g_ev_stop)
-                 : psplit ? fp8pa::launch_decode_pksplit(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start,
+                 : psplit ? fp8pa::launch_decode_pksplit(a, D, r.sk, k_whole, W, lds, st, g_ev_start,
                                                          g_ev_stop)
-                       : fp8pa::launch_decode(a, D, kd->scale_kind, k_whole, W, lds, st, g_ev_start, g_ev_stop);
+                       : fp8pa::launch_decode(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
   if (f8) g_cnt.decode_fp8.fetch_add(1);
   else g_cnt.decode_mfma.fetch_add(1);
@@ -661,7 +685,7 @@ int fp8pa_append_quant(const void* k_new, const void* v_new, uint8_t* k_pool, ui
 int fp8pa_debug_dequant(const uint8_t* codes, const void* scales, int scale_kind, int n, float* out,
                         void* stream) {
   if (n < 0) return fail(FP8PA_EINVAL, "n must be >= 0");
-  if (scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || scale_kind > FP8PA_SCALE_F32_G256)
+  if (scale_kind < FP8PA_SCALE_F32_PAGE_HEAD || scale_kind > FP8PA_SCALE_F32_G16)
     return fail(FP8PA_EINVAL, "unknown scale_kind %d", scale_kind);
   if (n == 0) {
     ok();

@@ -169,7 +169,8 @@ struct Tile {
   float vst[NS][8];
   u32x4 ke8[NS][2];     // E8M0 bytes of the lane's K rows
   u32x4 ve8[NS][NE];    // E8M0 bytes of the lane's 8 score positions, all groups
-  float kgs[NS][2][NM]; // fp32 sub-row scales of the lane's K pieces
+  float kgs[NS][2][NM][2];   // fp32 sub-row scales of the two 8-dim halves of the lane's K pieces
+  float vgs[SK == 4 ? 8 * NS : 1];   // SK = 4: the lane's share of the tile's fp32 sub-row V scales
 };
 
 // FUSED: also append each sequence's new token (DecodeArgs::k_new / v_new)
@@ -190,12 +191,12 @@ struct Tile {
 template <int D, int SK, bool KNT, bool FUSED, bool VT, bool F8 = false, bool PK = false, bool PS = false>
 __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kernel(const DecodeArgs a) {
   static_assert(!(PS && (FUSED || PK)), "packed splits: plain kernels");
-  static_assert(!(F8 && SK == 3), "sub-row fp32 K scales vary inside one fp8 MFMA");
+  static_assert(!(F8 && SK >= 3), "sub-row fp32 K scales vary inside one fp8 MFMA");
   static_assert(!(F8 && SK == 2 && D % 128), "the MX-scaled fp8 MFMA contracts 128 dims at a time");
   // MX: the fp8 mode over E8M0 pools: QK^T on the MX-scaled fp8 MFMA, which
   // applies the keys' E8M0 scales and the query's own (MXFP8) scales itself.
   constexpr bool MX = F8 && SK == 2;
-  static_assert(!(SK == 3 && (FUSED || PK || PS)), "sub-row K scales: split kernels without the fused append");
+  static_assert(!(SK >= 3 && (FUSED || PK || PS)), "sub-row scales: split kernels without the fused append");
   static_assert(!(PK && (FUSED || F8)), "packed heads: plain bf16 kernels");
   constexpr int NS = Shape<D>::NS;
   constexpr int NW = Shape<D>::NW;
@@ -581,10 +582,11 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
         scales8(t.kst[s], ksc, tpq + 8 * s, a.kg.sc_tok_stride);
         scales8(t.vst[s], vsc, tpq + 8 * s, a.vg.sc_tok_stride);
       }
-    } else if constexpr (SK == 3) {
-      // K: the scale of each of the lane's 16-dim pieces (position row tk +
-      // 8s + 4aa + kslot, dims 64m + 16*quad..: one group, as groups span
-      // at least 32 dims).  V: per (token, head), as for SK = 1.
+    } else if constexpr (SK >= 3) {
+      // K: the scales of the two 8-dim halves of each of the lane's 16-dim
+      // pieces (position row tk + 8s + 4aa + kslot, dims 64m + 16*quad.. and
+      // +8..: one group each, as groups span at least 8 dims; the same one
+      // when they span 16 or more).
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -592,12 +594,32 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
           const int tp = (tk + 8 * s + 4 * aa + kslot) & (P - 1);
           const uint8_t* kf = a.kp + rk.scale + kvh * a.kg.sc_head_stride + tp * a.kg.sc_tok_stride;
 #pragma unroll
-          for (int m = 0; m < NM; ++m) t.kgs[s][aa][m] = ld_global<float>(kf + 4 * ((64 * m + 16 * quad) >> a.kg.sc_gshift));
+          for (int m = 0; m < NM; ++m) {
+            t.kgs[s][aa][m][0] = ld_global<float>(kf + 4 * ((64 * m + 16 * quad) >> a.kg.sc_gshift));
+            t.kgs[s][aa][m][1] = a.kg.sc_gshift < 4
+                                     ? ld_global<float>(kf + 4 * ((64 * m + 16 * quad + 8) >> a.kg.sc_gshift))
+                                     : t.kgs[s][aa][m][0];
+          }
         }
+      if constexpr (SK == 3) {
+        // V: per (token, head), as for SK = 1.
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) t.vst[s][i] = ld_global<float>(vsc + (tpq + 8 * s + i) * a.vg.sc_tok_stride);
+          for (int i = 0; i < 8; ++i) t.vst[s][i] = ld_global<float>(vsc + (tpq + 8 * s + i) * a.vg.sc_tok_stride);
+      } else {
+        // V in sub-row groups: lane l loads the groups gh, gh + LP, ... of
+        // tile position l % TT (gh = l / TT, LP = 64 / TT lanes per position).
+        constexpr int LP = 64 / TT;
+        const int pos = T0 + lane % TT, gh = lane / TT, ngv = D >> a.vg.sc_gshift;
+        const RowBases rvg = row_bases(a.vg, row_of(pos >> log2P));
+        const uint8_t* vf = a.vp + rvg.scale + kvh * a.vg.sc_head_stride + (pos & (P - 1)) * a.vg.sc_tok_stride;
+#pragma unroll
+        for (int i = 0; i < 8 * NS; ++i) {
+          const int gg = gh + LP * i;
+          t.vgs[i] = gg < ngv ? ld_global<float>(vf + 4 * gg) : 0.0f;
+        }
+      }
     } else {
       if constexpr (VT) {
         // One position's NG bytes at a time: in the TOKENS layout consecutive
@@ -685,6 +707,10 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
   // (vstage_off leaves 16 bytes of slack to round the stage up to 16 bytes.)
   uint8_t* const vstage = reinterpret_cast<uint8_t*>(s_dyn) + a.vstage_off +
                           ((0u - (uint32_t)reinterpret_cast<uintptr_t>(s_dyn)) & 15u) + wave * (TT * VStage<D>::RS);
+  // SK = 4: the wave's stage of the tile's V group scales, [group][position].
+  float* const vgstage = reinterpret_cast<float*>(
+      reinterpret_cast<uint8_t*>(s_dyn) + a.vgstage_off + ((0u - (uint32_t)reinterpret_cast<uintptr_t>(s_dyn)) & 15u) +
+      wave * (TT * (D >> a.vg.sc_gshift) * 4));
   auto stage_v = [&](TileT& t) {
     constexpr int VH = VStage<D>::VH, RS = VStage<D>::RS, NIV = TileT::NIV, LPP = D / 16, CPP = VH / 16;
     const int prow = (lane / LPP) * NIV, pc = lane % LPP;
@@ -749,13 +775,12 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
                                                             s4, 0, 0, 0);
             s4 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)(((uint64_t)w[3] << 32) | w[2]),
                                                             (long)qop8[2 * m + 1], s4, 0, 0, 0);
-          } else if constexpr (SK == 3) {
-            const float ks = t.kgs[s][aa][m];
+          } else if constexpr (SK >= 3) {
             bf16x8 hi, lo;
-            scaled_e4m3x8_hilo(w[0], w[1], ks, hi, lo);
+            scaled_e4m3x8_hilo(w[0], w[1], t.kgs[s][aa][m][0], hi, lo);
             s4 = mfma_16x16x32_bf16(hi, qop[2 * m], s4);
             s4 = mfma_16x16x32_bf16(lo, qop[2 * m], s4);
-            scaled_e4m3x8_hilo(w[2], w[3], ks, hi, lo);
+            scaled_e4m3x8_hilo(w[2], w[3], t.kgs[s][aa][m][1], hi, lo);
             s4 = mfma_16x16x32_bf16(hi, qop[2 * m + 1], s4);
             s4 = mfma_16x16x32_bf16(lo, qop[2 * m + 1], s4);
           } else {
@@ -829,9 +854,46 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
         for (int c = 0; c < NC; ++c) t.v[c][k] &= mk;
       }
     }
+    if constexpr (SK == 4) {
+      // The lane's V group scales to the wave's stage, [group][tile position].
+      constexpr int LP = 64 / TT;
+      const int ngv = D >> a.vg.sc_gshift;
+#pragma unroll
+      for (int i = 0; i < 8 * NS; ++i) {
+        const int gg = lane / TT + LP * i;
+        if (gg < ngv) vgstage[gg * TT + lane % TT] = t.vgs[i];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if constexpr (SK == 2) {
+      if constexpr (SK == 4) {
+        // One probability operand (hi/lo pair) per V group: p x the group
+        // scale of each of the lane's 8 positions; a 16-dim chunk lies in one
+        // group, so chunk c uses group 16c / S.
+        int gprev = -1;
+        bf16x8 pop, pol;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int gg = (16 * c) >> a.vg.sc_gshift;
+          if (gg != gprev) {
+            const float* sp = vgstage + gg * TT + GT * quad + 8 * s;
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(sp), s1 = *reinterpret_cast<const f32x4*>(sp + 4);
+            float pv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float sv = i < 4 ? s0[i] : s1[i - 4];
+              pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * sv;
+            }
+            split_bf16x8(pv, pop, pol);
+            gprev = gg;
+          }
+          const bf16x8 vop = e4m3x8_to_bf16x8(t.v[c][2 * s], t.v[c][2 * s + 1], 1.0f);
+          acc[c] = mfma_16x16x32_bf16(vop, pop, acc[c]);
+          acc[c] = mfma_16x16x32_bf16(vop, pol, acc[c]);
+        }
+      } else if constexpr (SK == 2) {
         bf16x8 pop[NG], pol[NG];
 #pragma unroll
         for (int gq = 0; gq < NG; ++gq) {
@@ -870,6 +932,11 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
           acc[c] = mfma_16x16x32_bf16(vop, pol, acc[c]);
         }
       }
+    }
+    if constexpr (SK == 4) {
+      // The next tile rewrites the stage only after these reads.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   };
 
@@ -1436,9 +1503,13 @@ hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t 
       if constexpr (F8 && D % 128) return hipErrorNotSupported;
       else hipExtLaunchKernelGGL((decode_kernel<D, 2, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
-    default:   // fp32 sub-row K scales
+    case 3:    // fp32 sub-row K scales, V per (token, head)
       if constexpr (F8 || FUSED || PK || PS) return hipErrorNotSupported;
       else hipExtLaunchKernelGGL((decode_kernel<D, 3, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
+      break;
+    default:   // fp32 sub-row K and V scales
+      if constexpr (F8 || FUSED || PK || PS) return hipErrorNotSupported;
+      else hipExtLaunchKernelGGL((decode_kernel<D, 4, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
   }
   return hipGetLastError();
@@ -1464,7 +1535,8 @@ int occupancy_d(int sk, size_t lds) {
     case 0: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 0, KNT, false, false>, NT, lds); break;
     case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 1, KNT, false, false>, NT, lds); break;
     case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 2, KNT, false, false>, NT, lds); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 3, KNT, false, false>, NT, lds); break;
+    case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 3, KNT, false, false>, NT, lds); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 4, KNT, false, false>, NT, lds); break;
   }
   return e == hipSuccess ? nb : -1;
 }

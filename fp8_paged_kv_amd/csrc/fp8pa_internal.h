@@ -66,6 +66,7 @@ struct DecodeArgs {
   int32_t P, log2P, B, Hq, Hkv, G, window;
   float qk_scale;          // sm_scale * log2(e)
   int32_t vstage_off;      // V token-major: byte offset of the per-wave V stages in dynamic LDS
+  int32_t vgstage_off;     // V sub-row scales: byte offset of the per-wave scale stages in dynamic LDS
   uint32_t* dbg;           // debug checks: error words [2] (table, lengths), or null (no checks)
   int32_t dbg_rows;        // rows of the smaller pool (debug checks)
   int32_t dbg_max_len;     // largest valid seq_lens[b] (debug checks)

@@ -10,7 +10,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8pa.so")
 
 LAYOUTS = {"heads": 0, "tokens": 1, "heads_dmajor": 2, "heads_d64": 3}
-SCALE_KINDS = {"page_head": 0, "token_head": 1, "e8m0_32": 2, "f32_g32": 3, "f32_g64": 4, "f32_g128": 5, "f32_g256": 6}
+SCALE_KINDS = {"page_head": 0, "token_head": 1, "e8m0_32": 2, "f32_g32": 3, "f32_g64": 4, "f32_g128": 5, "f32_g256": 6,
+               "f32_g8": 7, "f32_g16": 8}
 VARIANTS = {"auto": 0, "mfma_bf16": 1, "mfma_fp8": 2, "packed_heads": 3, "packed_split": 4}
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4

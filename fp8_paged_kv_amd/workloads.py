@@ -56,7 +56,7 @@ def raw_kv(seed, wl, layer_index, b, tensor, n_pos, Hkv, D):
     return inputs.normal_bf16(seed, wl.index, tensor, layer_index * 4096 + b, (n_pos, Hkv, D))
 
 
-GROUP_DIMS = {"f32_g32": 32, "f32_g64": 64, "f32_g128": 128, "f32_g256": 256}
+GROUP_DIMS = {"f32_g8": 8, "f32_g16": 16, "f32_g32": 32, "f32_g64": 64, "f32_g128": 128, "f32_g256": 256}
 
 
 def scale_block_bytes(scale_kind, Hkv, P, D):

@@ -71,12 +71,14 @@ enum {
  *   E8M0_G32        E8M0 per (token, head, 32 dims along D), the MXFP8 scale
  *                   of page "Attention MXFP8 TKG Kernel API Reference":
  *                   slot*(D/32) + d/32.  Value 2**(u-127).
- *   F32_G<S>        fp32 per (token, head, S dims along D), S = 32, 64, 128 or
- *                   256 dividing D: the sub-row key scales of page "fp8 paged
- *                   attention for MoE serving" ("Supported scope", k_groups =
- *                   D/S): 4*(slot*(D/S) + d/S).  Written by fp8pa_append_quant
- *                   for K or V; fp8pa_decode reads them for K, with V in
- *                   F32_TOKEN_HEAD (else FP8PA_EUNSUPPORTED).              */
+ *   F32_G<S>        fp32 per (token, head, S dims along D), S = 8, 16, 32, 64,
+ *                   128 or 256 dividing D: the sub-row scales of page "fp8 paged
+ *                   attention for MoE serving" ("Supported scope", k_groups or
+ *                   v_groups = D/S): 4*(slot*(D/S) + d/S).  Written by
+ *                   fp8pa_append_quant for K or V.  fp8pa_decode reads them for
+ *                   K with V in F32_TOKEN_HEAD, or for K and V together (V
+ *                   groups of at least 16 dims and at most 16 groups per head);
+ *                   other pairings are refused with FP8PA_EUNSUPPORTED.     */
 enum {
   FP8PA_SCALE_F32_PAGE_HEAD = 0,
   FP8PA_SCALE_F32_TOKEN_HEAD = 1,
@@ -84,7 +86,9 @@ enum {
   FP8PA_SCALE_F32_G32 = 3,
   FP8PA_SCALE_F32_G64 = 4,
   FP8PA_SCALE_F32_G128 = 5,
-  FP8PA_SCALE_F32_G256 = 6
+  FP8PA_SCALE_F32_G256 = 6,
+  FP8PA_SCALE_F32_G8 = 7,
+  FP8PA_SCALE_F32_G16 = 8
 };
 
 /* ---- decode variants.  An explicit request is honoured or refused with

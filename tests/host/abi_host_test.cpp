@@ -246,7 +246,7 @@ int main() {
     c = Call(); c.kd.layout = 7; REFUSE(c, FP8PA_EINVAL);
     c = Call(); c.kd.layout = FP8PA_LAYOUT_HEADS_DMAJOR; REFUSE(c, FP8PA_EUNSUPPORTED);
     c = Call(); c.vd.layout = FP8PA_LAYOUT_HEADS_D64; REFUSE(c, FP8PA_EUNSUPPORTED);
-    c = Call(); c.kd.scale_kind = 7; REFUSE(c, FP8PA_EINVAL);
+    c = Call(); c.kd.scale_kind = 9; REFUSE(c, FP8PA_EINVAL);
     c = Call(); c.kd.scale_kind = -1; REFUSE(c, FP8PA_EINVAL);
     c = Call(); c.kd.flags = 2; REFUSE(c, FP8PA_EINVAL);
     c = Call(); c.kd.num_kv_heads = 0; REFUSE(c, FP8PA_EINVAL);
@@ -297,6 +297,12 @@ int main() {
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_SPLIT; c.workgroups = 9; LAUNCH(c);
     c = Call(); c.kd.scale_kind = FP8PA_SCALE_F32_G32; c.kd.row_bytes = 16384 + 2048;
     c.vd.scale_kind = FP8PA_SCALE_F32_TOKEN_HEAD; c.vd.row_bytes = 16384 + 2048; c.workgroups = 3; LAUNCH(c);
+    c = Call(); c.kd.scale_kind = FP8PA_SCALE_F32_G8; c.vd.scale_kind = FP8PA_SCALE_F32_G16;   // K and V groups
+    c.kd.row_bytes = c.vd.row_bytes = 16384 + 8192; c.workgroups = 3; LAUNCH(c);
+    c.workgroups = 1;
+    g_launches.clear();
+    CHECK(c.run() == 0 && g_launches.size() == 1 && g_launches[0].lds > (size_t)4 * 64 * 8 * 4 &&
+          g_launches[0].a.vgstage_off > 0);   // a stage of 8 V groups x 64 positions per wave
     c = Call(); c.kd.head_dim = c.vd.head_dim = 512; c.kd.num_kv_heads = c.vd.num_kv_heads = 2; c.Hq = 16;
     c.kd.page_size = c.vd.page_size = 32; c.kd.row_bytes = c.vd.row_bytes = 65568; c.sm_scale = 1.0f; LAUNCH(c);
     c = Call(); c.kd.flags = c.vd.flags = FP8PA_POOL_ALIGN64; c.kd.row_bytes = c.vd.row_bytes = 16448; LAUNCH(c);
@@ -381,7 +387,7 @@ int main() {
     CHECK(fp8pa_merge_splits(Ff, Ff, nullptr, fake(F), 2, 8, 4, 80, nullptr) == FP8PA_EUNSUPPORTED);
     CHECK(fp8pa_merge_splits(nullptr, Ff, nullptr, fake(F), 2, 8, 4, 64, nullptr) == FP8PA_EINVAL);
     CHECK(fp8pa_merge_splits(Ff, Ff, nullptr, fake(F), 2, 0, 4, 64, nullptr) == FP8PA_EINVAL);
-    CHECK(fp8pa_debug_dequant(fake(F), Ff, 7, 16, reinterpret_cast<float*>(F), nullptr) == FP8PA_EINVAL);
+    CHECK(fp8pa_debug_dequant(fake(F), Ff, 9, 16, reinterpret_cast<float*>(F), nullptr) == FP8PA_EINVAL);
     CHECK(fp8pa_debug_dequant(fake(F), Ff, 0, -1, reinterpret_cast<float*>(F), nullptr) == FP8PA_EINVAL);
     CHECK(fp8pa_stream_read(fake(F + 4), 64, reinterpret_cast<uint32_t*>(F), nullptr) == FP8PA_EINVAL);
     CHECK(fp8pa_stream_read(fake(F), 60, reinterpret_cast<uint32_t*>(F), nullptr) == FP8PA_EINVAL);
@@ -445,7 +451,7 @@ int main() {
         d->head_dim = (int)pick({0, 32, 64, 96, 128, 256, 512, 1024, -64});
         d->page_size = (int)pick({0, 1, 8, 16, 24, 32, 128, 1024, 4096, -16});
         d->layout = (int)pick({-1, 0, 1, 2, 3, 4});
-        d->scale_kind = (int)pick({-1, 0, 1, 2, 3, 4, 5, 6, 7});
+        d->scale_kind = (int)pick({-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9});
         d->flags = (int)pick({0, 0, 1, 2});
         d->row_bytes = pick({0, 16, 2064, 8224, 16416, 65568, 135168, int64_t(1) << 31, INT64_MAX, -16, 16448});
         d->scale_offset = pick({-1, -1, 0, 16384, 65536, INT64_MAX});

@@ -98,8 +98,10 @@ def call_decode(k=None, v=None, **kw):
     (dict(variant=3, workgroups=4, ws=F, ws_bytes=1 << 20), ops.EUNSUPPORTED),      # packed heads fix the grid
     (dict(variant=4, workgroups=0, v=vd(layout="heads")), ops.EUNSUPPORTED),        # packed splits: V d-major only
     (dict(variant=4, workgroups=0, Hq=64), ops.EUNSUPPORTED),                       # packed splits: G <= 4
-    (dict(k=kd(scale_kind="f32_g32", row_bytes=16384 + 2048),
-          v=vd(scale_kind="f32_g32", row_bytes=16384 + 2048)), ops.EUNSUPPORTED),   # V sub-row groups: not read
+    (dict(k=kd(scale_kind="f32_g32", row_bytes=16384 + 8192),
+          v=vd(scale_kind="f32_g8", row_bytes=16384 + 8192)), ops.EUNSUPPORTED),    # V groups under 16 dims
+    (dict(k=kd(scale_kind="token_head", row_bytes=16384 + 2048),
+          v=vd(scale_kind="f32_g32", row_bytes=16384 + 2048)), ops.EUNSUPPORTED),   # V groups need K groups
     (dict(k=kd(scale_kind="f32_g32", row_bytes=16384 + 2048)), ops.EUNSUPPORTED),   # K groups with V page scales
     (dict(k=kd(scale_kind="f32_g32", row_bytes=16384 + 1024)), ops.EINVAL),         # group scales do not fit
     (dict(k=kd(scale_kind="f32_g256", row_bytes=16384 + 512),
@@ -110,7 +112,7 @@ def call_decode(k=None, v=None, **kw):
           v=vd(scale_kind="token_head", row_bytes=16384 + 512)), ops.EUNSUPPORTED),  # packed heads: none either
     (dict(variant=4, workgroups=0, k=kd(scale_kind="f32_g64", row_bytes=16384 + 1024),
           v=vd(scale_kind="token_head", row_bytes=16384 + 512)), ops.EUNSUPPORTED),
-    (dict(k=kd(scale_kind=7)), ops.EINVAL),
+    (dict(k=kd(scale_kind=9)), ops.EINVAL),
     (dict(max_seq_len=-1), ops.EINVAL),
     (dict(workgroups=-2), ops.EINVAL),
     (dict(workgroups=4), ops.EWORKSPACE),                       # cut units need a workspace
@@ -232,7 +234,7 @@ def test_merge_and_debug_refuse_before_launch():
     assert ops.lib().fp8pa_merge_splits(P(F), P(F), None, P(F), 2, 8, 4, 80, None) == ops.EUNSUPPORTED
     assert ops.lib().fp8pa_merge_splits(None, P(F), None, P(F), 2, 8, 4, 64, None) == ops.EINVAL
     assert ops.lib().fp8pa_merge_splits(P(F), P(F), None, P(F), 2, 0, 4, 64, None) == ops.EINVAL
-    assert ops.lib().fp8pa_debug_dequant(P(F), P(F), 7, 16, P(F), None) == ops.EINVAL
+    assert ops.lib().fp8pa_debug_dequant(P(F), P(F), 9, 16, P(F), None) == ops.EINVAL
     assert ops.lib().fp8pa_debug_dequant(None, P(F), 0, 16, P(F), None) == ops.EINVAL
     c = ops.counters()
     assert c["merge_launches"] == 0 and c["debug_launches"] == 0 and c["errors"] == 5

@@ -1,10 +1,10 @@
-"""fp32 sub-row key scales (FP8PA_SCALE_F32_G32..G256, the page's k_groups) on
-the GPU: decode parity against the float64 oracle over head dims 64-512,
-every group width a head dim takes, K in HEADS_D64 / HEADS / TOKENS, V
-d-major and token-major, windows, sinks, split counts, empty and short
-sequences; groups of very different ranges (the reason for the format); the
-append + decode call; and the refusals of the variants that do not read
-them."""
+"""fp32 sub-row scales (FP8PA_SCALE_F32_G8..G256, the page's k_groups and
+v_groups) on the GPU: decode parity against the float64 oracle over head dims
+64-512, every group width a head dim takes (8-dim key groups included), K in
+HEADS_D64 / HEADS / TOKENS, V d-major and token-major, V per token or in its
+own sub-row groups, windows, sinks, split counts, empty and short sequences;
+groups of very different ranges (the reason for the format); the append +
+decode call; and the refusals of the variants that do not read them."""
 from dataclasses import replace
 
 import numpy as np
@@ -44,6 +44,12 @@ CASES = [
     ("g1-hkv8", dict(B=2, Hq=8, Hkv=8, D=64, P=16, lens=[90, 3], scale_kind="f32_g32")),
     ("empty-and-short", dict(B=4, Hq=8, Hkv=2, D=64, P=16, lens=[0, 1, 15, 65], scale_kind="f32_g32",
                              sinks=True)),
+    # key groups narrower than 32 dims (k_groups 8 and 16 at head dim 128)
+    ("d128-g16", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[700, 65, 9], scale_kind="f32_g16", sinks=True)),
+    ("d128-g8-window", dict(B=2, Hq=16, Hkv=2, D=128, P=32, lens=[900, 77], scale_kind="f32_g8", window=200)),
+    ("d64-g8-ktokens", dict(B=2, Hq=8, Hkv=2, D=64, P=16, lens=[300, 31], scale_kind="f32_g8", k_layout="tokens")),
+    ("d256-g16-kheads", dict(B=2, Hq=8, Hkv=2, D=256, P=32, lens=[500, 40], scale_kind="f32_g16",
+                             k_layout="heads")),
 ]
 
 
@@ -130,8 +136,72 @@ def test_kgroups_refusals(variant):
     with pytest.raises(RuntimeError):
         gpu_decode(p, variant=variant)
     assert ops.counters()["decode_calls"] == 0
-    # V in sub-row groups is not read by decode
+    # V in sub-row groups: refused with the packed variants and the fp8 mode too,
+    # and for V groups narrower than a 16-dim PV chunk, or V groups with K per token
     pv = make_problem(705, B=2, Hq=16, Hkv=4, D=128, P=16, lens=[100, 30], scale_kind="f32_g32",
                       v_scale_kind="f32_g32")
     with pytest.raises(RuntimeError):
-        gpu_decode(pv)
+        gpu_decode(pv, variant=variant)
+    for kk, vk in (("f32_g32", "f32_g8"), ("token_head", "f32_g32")):
+        pb = make_problem(705, B=2, Hq=16, Hkv=4, D=128, P=16, lens=[100, 30], scale_kind=kk, v_scale_kind=vk)
+        with pytest.raises(RuntimeError):
+            gpu_decode(pb)
+    assert ops.counters()["decode_calls"] == 0
+
+
+VG_CASES = [
+    # (name, kwargs): K and V both in fp32 sub-row groups (k_groups, v_groups)
+    ("d64-k32-v32", dict(B=3, Hq=8, Hkv=2, D=64, P=16, lens=[300, 17, 129], scale_kind="f32_g32",
+                         v_scale_kind="f32_g32")),
+    ("d64-k8-v16-sinks", dict(B=2, Hq=8, Hkv=2, D=64, P=16, lens=[200, 33], scale_kind="f32_g8",
+                              v_scale_kind="f32_g16", sinks=True)),
+    ("d128-k32-v16", dict(B=3, Hq=32, Hkv=8, D=128, P=16, lens=[1500, 64, 700], scale_kind="f32_g32",
+                          v_scale_kind="f32_g16")),
+    ("d128-k16-v64-window", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[900, 100, 20], scale_kind="f32_g16",
+                                 v_scale_kind="f32_g64", window=300)),
+    ("d128-k64-v128-p128", dict(B=2, Hq=16, Hkv=4, D=128, P=128, lens=[1000, 130], scale_kind="f32_g64",
+                                v_scale_kind="f32_g128", k_layout="tokens")),
+    ("d256-k32-v32-window", dict(B=2, Hq=16, Hkv=8, D=256, P=32, lens=[1500, 33], scale_kind="f32_g32",
+                                 v_scale_kind="f32_g32", window=1024, sm_scale=1.0)),
+    ("d512-k64-v32", dict(B=2, Hq=16, Hkv=2, D=512, P=32, lens=[333, 64], scale_kind="f32_g64",
+                          v_scale_kind="f32_g32", sm_scale=1.0)),
+    ("empty-and-short", dict(B=4, Hq=8, Hkv=2, D=128, P=16, lens=[0, 1, 15, 65], scale_kind="f32_g32",
+                             v_scale_kind="f32_g32", sinks=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", VG_CASES, ids=[c[0] for c in VG_CASES])
+@pytest.mark.parametrize("workgroups", [1, 0, 5])
+def test_vgroups_parity(name, kw, workgroups):
+    say("v groups parity", name, "workgroups", workgroups)
+    p = make_problem(706, **kw)
+    got = to_np(gpu_decode(p, workgroups=workgroups))
+    assert_parity(got, oracle(p), name)
+
+
+@pytest.mark.parametrize("v_layout", ["heads", "tokens"])
+def test_vgroups_token_major_v(v_layout):
+    say("v groups V", v_layout)
+    p = make_problem(707, B=3, Hq=16, Hkv=4, D=128, P=16, lens=[300, 65, 7], scale_kind="f32_g32",
+                     v_scale_kind="f32_g32", v_layout=v_layout, sinks=True)
+    ops.reset_counters()
+    got = to_np(gpu_decode(p, workgroups=3))
+    assert ops.counters()["decode_v_token_major"] == 1
+    assert_parity(got, oracle(p), f"V groups {v_layout}")
+
+
+def test_vgroups_of_very_different_ranges_and_poison():
+    """One 16-dim V group 2**10 times larger than the rest, and NaN scales and
+    codes in every unattended slot: the result matches the oracle."""
+    say("v groups ranges")
+    p = make_problem(708, B=2, Hq=16, Hkv=4, D=128, P=16, lens=[500, 70], scale_kind="f32_g32",
+                     v_scale_kind="f32_g16", window=333)
+    from oracle import pool as _pool
+    vs = []
+    for x in p.raw_v:
+        x = x.astype(np.float32).copy()
+        x[:, :, 48:64] *= np.float32(1024.0)
+        vs.append(x)
+    v_pool = _pool.pack_sequences(np.full_like(p.v_pool, 0xFF), p.vdesc, p.table, vs)
+    p2 = replace(p, v_pool=v_pool, raw_v=vs)
+    assert_parity(to_np(gpu_decode(p2, workgroups=3)), oracle(p2), "ranges")
