@@ -274,8 +274,8 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
   const bool kgroups = grouped(kd->scale_kind);
   if (kgroups && (fused || packed_req || psplit))
     return fail(FP8PA_EUNSUPPORTED, "sub-row K scales take the split kernels and no fused append");
-  if ((packed_req || psplit) && (vt || fused))
-    return fail(FP8PA_EUNSUPPORTED, "packed heads read V in HEADS_DMAJOR and take no fused append");
+  if ((packed_req || psplit) && fused) return fail(FP8PA_EUNSUPPORTED, "packed heads take no fused append");
+  if (psplit && vt) return fail(FP8PA_EUNSUPPORTED, "packed splits read V in HEADS_DMAJOR");
   size_t vstage_off = 0;
   if (vt) {
     vstage_off = (lds + 15) / 16 * 16;
@@ -485,14 +485,17 @@ int decode_impl(const void* k_new, const void* v_new, const void* q, void* out, 
   // A wave's 16-byte K loads cover 64 bytes of each of 16 tokens: whole lines
   // when the 64-byte pieces of consecutive tokens are adjacent.
   const bool k_whole = r.k_whole;
-  hipError_t e = fused ? fp8pa::launch_decode_fused(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
-                 : vt  ? fp8pa::launch_decode_vtok(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
-                 : f8  ? fp8pa::launch_decode_fp8q(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
-                 : packed ? fp8pa::launch_decode_packed(a, D, r.sk, k_whole, W, lds, st, g_ev_start,
-                                                        g_ev_stop)
-                 : psplit ? fp8pa::launch_decode_pksplit(a, D, r.sk, k_whole, W, lds, st, g_ev_start,
-                                                         g_ev_stop)
-                       : fp8pa::launch_decode(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop);
+  // The kernel family: packed heads (which take no workspace) first, then the
+  // split kernels, which must have their partials and flags.
+  if (!packed && W > 1 && (!a.part_o || !a.part_lse || !a.flags))
+    return fail(FP8PA_EWORKSPACE, "internal: a split launch without its workspace");
+  hipError_t e = packed ? (vt ? fp8pa::launch_decode_packed_vt(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                              : fp8pa::launch_decode_packed(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop))
+                 : psplit ? fp8pa::launch_decode_pksplit(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                 : fused  ? fp8pa::launch_decode_fused(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                 : vt     ? fp8pa::launch_decode_vtok(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                 : f8     ? fp8pa::launch_decode_fp8q(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop)
+                          : fp8pa::launch_decode(a, D, r.sk, k_whole, W, lds, st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(FP8PA_EHIP, "decode launch: %s", hipGetErrorString(e));
   if (f8) g_cnt.decode_fp8.fetch_add(1);
   else g_cnt.decode_mfma.fetch_add(1);

@@ -199,6 +199,9 @@ hipError_t launch_decode_fp8q(const DecodeArgs& a, int D, int scale_kind, bool k
 // kernel shapes.
 hipError_t launch_decode_packed(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
                                 hipStream_t st, hipEvent_t start, hipEvent_t stop);
+// Packed heads with V in a token-major layout (a.vstage_off set).
+hipError_t launch_decode_packed_vt(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,
+                                   hipStream_t st, hipEvent_t start, hipEvent_t stop);
 // Packed heads with splits: units of decode_waves(D, 0) KV heads (a.G and
 // a.Hkv are the per-KV-head values), default kernel shapes.
 hipError_t launch_decode_pksplit(const DecodeArgs& a, int D, int scale_kind, bool k_whole_lines, int W, size_t lds,

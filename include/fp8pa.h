@@ -122,7 +122,9 @@ enum {
                                    windowed calls and for large batches.  The grid is fixed
                                    (workgroups must be 0; the plan reports B * ceil(Hkv / 4),
                                    no workspace); no fused append (fp8pa_append_decode runs
-                                   it after the append kernel); V in HEADS_DMAJOR (else
+                                   it after the append kernel); V in HEADS_DMAJOR, HEADS or
+                                   TOKENS (each wave stages its V rows in LDS, as the split
+                                   kernel does); no sub-row fp32 scales (else
                                    FP8PA_EUNSUPPORTED).  With AUTO and workgroups 0,
                                    fp8pa_decode runs it instead of the split kernel when V
                                    is in HEADS_DMAJOR, D <= 128 and the B * ceil(Hkv / 4) units alone

@@ -35,7 +35,8 @@ hipError_t hipMemcpy(void* dst, const void* src, size_t n, hipMemcpyKind) {
 
 // ---- stub launchers: record the launch
 struct Launch {
-  int kind;   // 0 decode, 1 fused, 2 vtok, 3 fp8, 4 packed, 5 psplit, 6 merge, 7 append, 8 read, 9 dequant
+  int kind;   // 0 decode, 1 fused, 2 vtok, 3 fp8, 4 packed, 5 psplit, 6 merge, 7 append, 8 read, 9 dequant,
+             // 10 packed with token-major V
   fp8pa::DecodeArgs a;
   int W;
   size_t lds;
@@ -60,6 +61,7 @@ STUB_DECODE(launch_decode_vtok, 2)
 STUB_DECODE(launch_decode_fp8q, 3)
 STUB_DECODE(launch_decode_packed, 4)
 STUB_DECODE(launch_decode_pksplit, 5)
+STUB_DECODE(launch_decode_packed_vt, 10)
 hipError_t launch_merge(const MergeArgs&, int, hipStream_t) {
   g_launches.push_back({6, {}, 0, 0});
   return hipSuccess;
@@ -165,7 +167,14 @@ static void expect_launch(Call c, int line) {
   CHECK(l.a.epoch != 0 && l.a.wait_epoch == l.a.epoch && l.a.status != nullptr);
   const int kinds[] = {0, 0, 4, 5};   // what each plan variant launches (bf16 may be plain, fused or vtok)
   (void)kinds;
-  if (p.variant == FP8PA_VARIANT_PACKED_HEADS) CHECK(l.kind == 4);
+  const bool vt = c.vd.layout == FP8PA_LAYOUT_HEADS || c.vd.layout == FP8PA_LAYOUT_TOKENS;
+  if (p.variant == FP8PA_VARIANT_PACKED_HEADS) CHECK(l.kind == (vt ? 10 : 4));
+  if (vt) CHECK(l.kind == 2 || l.kind == 10);
+  if (vt) CHECK(l.a.vstage_off > 0 && l.lds >= (size_t)l.a.vstage_off + fp8pa::decode_vstage_bytes(c.kd.head_dim));
+  // Every kernel but packed heads cuts units when W > 1 and then stores
+  // partials and flags: they must point into the workspace.
+  if (l.kind != 4 && l.kind != 10 && l.W > 1) CHECK(l.a.part_o && l.a.part_lse && l.a.flags);
+  if (l.kind == 4 || l.kind == 10) CHECK(p.workspace_bytes == 0 && l.W == c.B * ((c.kd.num_kv_heads + 3) / 4));
   if (p.variant == FP8PA_VARIANT_PACKED_SPLIT) CHECK(l.kind == 5);
   if (p.variant == FP8PA_VARIANT_MFMA_FP8) CHECK(l.kind == 3);
   if (p.workspace_bytes > 0) {
@@ -262,7 +271,9 @@ int main() {
     REFUSE(c, FP8PA_EUNSUPPORTED);   // the MX-scaled MFMA contracts 128 dims
     // packed variants
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_HEADS; c.workgroups = 3; REFUSE(c, FP8PA_EUNSUPPORTED);
-    c = Call(); c.variant = FP8PA_VARIANT_PACKED_HEADS; c.vd.layout = FP8PA_LAYOUT_HEADS; REFUSE(c, FP8PA_EUNSUPPORTED);
+    c = Call(); c.variant = FP8PA_VARIANT_PACKED_SPLIT; c.vd.layout = FP8PA_LAYOUT_HEADS; REFUSE(c, FP8PA_EUNSUPPORTED);
+    c = Call(); c.variant = FP8PA_VARIANT_PACKED_HEADS; c.kd.scale_kind = c.vd.scale_kind = FP8PA_SCALE_F32_G32;
+    c.kd.row_bytes = c.vd.row_bytes = 16 * 1024 + 8 * 16 * 4 * 4; REFUSE(c, FP8PA_EUNSUPPORTED);
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_SPLIT; c.Hq = 64; REFUSE(c, FP8PA_EUNSUPPORTED);
     // sub-row K scales
     c = Call(); c.kd.scale_kind = FP8PA_SCALE_F32_G32; c.kd.row_bytes = 16384 + 2048; REFUSE(c, FP8PA_EUNSUPPORTED);
@@ -284,6 +295,19 @@ int main() {
     c = Call(); c.vd.layout = FP8PA_LAYOUT_TOKENS; c.workgroups = 5; LAUNCH(c);
     c = Call(); c.variant = FP8PA_VARIANT_MFMA_FP8; LAUNCH(c);
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_HEADS; LAUNCH(c);
+    // Packed heads with V token-major: the packed kernel with its V stage,
+    // the packed grid and no workspace (not the split kernel for token-major
+    // V, which would cut units with no partials to store into), e.g. head dim
+    // 256, P 16, 3 sequences x 4 KV heads.
+    for (int lay : {FP8PA_LAYOUT_HEADS, FP8PA_LAYOUT_TOKENS})
+      for (int D : {64, 128, 256, 512}) {
+        c = Call(); c.variant = FP8PA_VARIANT_PACKED_HEADS; c.B = 3; c.Hq = 16; c.msl = 300;
+        c.kd = desc(4, D, 16, FP8PA_LAYOUT_HEADS_D64, FP8PA_SCALE_F32_PAGE_HEAD, (int64_t)4 * 16 * D + 16);
+        c.vd = desc(4, D, 16, lay, FP8PA_SCALE_F32_PAGE_HEAD, (int64_t)4 * 16 * D + 16);
+        LAUNCH(c);
+        CHECK(g_launches.size() == 1 && g_launches[0].kind == 10 && g_launches[0].W == 3 &&
+              g_launches[0].a.part_o == nullptr);
+      }
     c = Call(); c.variant = FP8PA_VARIANT_MFMA_FP8; c.kd.scale_kind = c.vd.scale_kind = FP8PA_SCALE_E8M0_G32;
     c.kd.row_bytes = c.vd.row_bytes = 16384 + 4096;
     {

@@ -22,6 +22,7 @@ CASES = [
     ("d64-window-sinks", dict(B=3, Hq=16, Hkv=2, D=64, P=16, lens=[500, 100, 33], window=128, sinks=True)),
     ("d128-aligned-rows", dict(B=2, Hq=16, Hkv=4, D=128, P=16, lens=[700, 65], row_pad=32, align64=True)),
     ("d256-window", dict(B=2, Hq=4, Hkv=2, D=256, P=32, lens=[700, 33], window=100, sm_scale=1.0)),
+    ("d256-p16", dict(B=3, Hq=16, Hkv=4, D=256, P=16, lens=[300, 65, 7], sm_scale=1.0)),
     ("d512", dict(B=2, Hq=8, Hkv=1, D=512, P=32, lens=[333, 65], sm_scale=1.0)),
     ("d128-e8m0-p128", dict(B=2, Hq=16, Hkv=2, D=128, P=128, lens=[1000, 129], scale_kind="e8m0_32")),
     ("d64-token-scales", dict(B=2, Hq=8, Hkv=2, D=64, P=16, lens=[250, 31], scale_kind="token_head")),

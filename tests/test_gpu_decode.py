@@ -42,6 +42,7 @@ CASES = [
     ("d128-kheads", dict(B=2, Hq=8, Hkv=2, D=128, P=32, lens=[260, 77], k_layout="heads")),
     ("d64-kheads-p128", dict(B=1, Hq=8, Hkv=2, D=64, P=128, lens=[700], k_layout="heads", sinks=True)),
     ("d256-p256-vblocks", dict(B=1, Hq=8, Hkv=2, D=256, P=256, lens=[900], window=300)),
+    ("d256-p16", dict(B=3, Hq=16, Hkv=4, D=256, P=16, lens=[300, 65, 7], sinks=True, sm_scale=1.0)),
     ("g1-mqa-like", dict(B=2, Hq=2, Hkv=2, D=64, P=16, lens=[90, 3])),
     ("g16", dict(B=1, Hq=16, Hkv=1, D=64, P=64, lens=[450])),
     ("wide-rows", dict(B=2, Hq=8, Hkv=2, D=64, P=16, lens=[100, 50], row_pad=4096)),

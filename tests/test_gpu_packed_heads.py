@@ -33,6 +33,7 @@ CASES = [
     ("d128-aligned-rows", dict(B=3, Hq=16, Hkv=4, D=128, P=16, lens=[700, 65, 300], row_pad=32, align64=True)),
     ("d128-e8m0-p128", dict(B=2, Hq=16, Hkv=2, D=128, P=128, lens=[1000, 130], scale_kind="e8m0_32")),
     ("d256-hkv8-window", dict(B=2, Hq=16, Hkv=8, D=256, P=32, lens=[1500, 33], window=1024, sm_scale=1.0)),
+    ("d256-p16", dict(B=3, Hq=16, Hkv=4, D=256, P=16, lens=[300, 65, 7], sinks=True, sm_scale=1.0)),
     ("d512-g8", dict(B=2, Hq=16, Hkv=2, D=512, P=32, lens=[333, 64], sm_scale=1.0)),
     ("g16-hkv1", dict(B=1, Hq=16, Hkv=1, D=64, P=64, lens=[450])),
     ("empty-and-short", dict(B=4, Hq=8, Hkv=2, D=64, P=16, lens=[0, 1, 15, 65], sinks=True)),
@@ -67,22 +68,27 @@ def test_packed_heads_poison_never_leaks():
     assert_parity(got, oracle(p), "poison")
 
 
-@pytest.mark.skip(reason="packed heads with V in a token-major order took a GPU memory fault at head dim 256 "
-                         "(P 16, tokens) whose cause was not found; the combination is refused")
 @pytest.mark.parametrize("v_layout,D", [("tokens", 64), ("heads", 128), ("tokens", 256), ("heads", 512)])
 def test_packed_heads_token_major_v(v_layout, D):
+    """Packed heads with V in the page's token-major orders: the packed kernel
+    with a per-wave V stage, its fixed grid and no workspace.  (These calls
+    once went to the split kernel for token-major V, handed the packed grid
+    and no partial buffers; at head dim 256 that kernel cut a unit and stored
+    its partial through a null pointer.)"""
     say("packed heads V", v_layout, D)
     p = make_problem(505, B=3, Hq=16, Hkv=4, D=D, P=16, lens=[300, 65, 7], v_layout=v_layout, sinks=True,
                      sm_scale=1.0 if D >= 256 else None)
+    plan = ops.decode_plan(p.B, p.Hq, desc_of(p.kdesc), desc_of(p.vdesc), 300, variant="packed_heads")
+    assert plan.variant == ops.VARIANTS["packed_heads"] and plan.workgroups == 3 and plan.workspace_bytes == 0
     ops.reset_counters()
     got = to_np(gpu_decode(p, variant="packed_heads"))
     c = ops.counters()
-    assert c["decode_packed_heads"] == 1 and c["decode_v_token_major"] == 1
+    assert c["decode_packed_heads"] == 1 and c["decode_v_token_major"] == 1 and c["decode_split"] == 0
     assert_parity(got, oracle(p), f"V {v_layout}")
 
 
 def test_packed_heads_refusals():
-    p = make_problem(503, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[100, 30], v_layout="tokens")
+    p = make_problem(503, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[100, 30], scale_kind="f32_g32")
     with pytest.raises(RuntimeError):
         gpu_decode(p, variant="packed_heads")
     p = make_problem(503, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[100, 30])

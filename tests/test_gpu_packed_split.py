@@ -33,6 +33,7 @@ CASES = [
                                  k_layout="heads")),
     ("d128-e8m0-p128", dict(B=2, Hq=16, Hkv=4, D=128, P=128, lens=[1000, 130], scale_kind="e8m0_32")),
     ("d256-hkv8-g2-window", dict(B=2, Hq=16, Hkv=8, D=256, P=32, lens=[1500, 33], window=1024, sm_scale=1.0)),
+    ("d256-p16", dict(B=3, Hq=16, Hkv=4, D=256, P=16, lens=[300, 65, 7], sinks=True, sm_scale=1.0)),
     ("d512-hkv4-g1", dict(B=2, Hq=4, Hkv=4, D=512, P=32, lens=[333, 64], sm_scale=1.0)),
     ("g1-hkv8", dict(B=2, Hq=8, Hkv=8, D=64, P=16, lens=[90, 3])),
     ("empty-and-short", dict(B=4, Hq=16, Hkv=4, D=64, P=16, lens=[0, 1, 15, 65], sinks=True)),

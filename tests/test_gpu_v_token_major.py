@@ -45,6 +45,9 @@ CASES = [
                                  v_layout="tokens")),
     ("d256-vheads-e8m0", dict(B=1, Hq=8, Hkv=2, D=256, P=32, lens=[300], scale_kind="e8m0_32", sinks=True,
                               v_layout="heads")),
+    ("d256-p16-vtokens", dict(B=3, Hq=16, Hkv=4, D=256, P=16, lens=[300, 65, 7], sinks=True, sm_scale=1.0,
+                              v_layout="tokens")),
+    ("d256-p16-vheads", dict(B=3, Hq=16, Hkv=4, D=256, P=16, lens=[300, 65, 7], window=100, v_layout="heads")),
     ("d512-vtokens", dict(B=2, Hq=8, Hkv=1, D=512, P=32, lens=[333, 64], sm_scale=1.0, v_layout="tokens")),
     ("d512-vheads-token-scales", dict(B=2, Hq=16, Hkv=2, D=512, P=16, lens=[260, 97], sm_scale=1.0,
                                       scale_kind="token_head", k_layout="heads", v_layout="heads")),
