@@ -240,9 +240,12 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
   if (psplit && (kd->num_kv_heads % nw || G * nw > 16))
     return fail(FP8PA_EUNSUPPORTED, "packed splits need Hkv %% %d == 0 and G <= %d", nw, 16 / nw);
   const int Gu = psplit ? G * nw : G;
-  size_t lds = fp8pa::decode_lds_bytes(D, B, Gu, kd->page_size);
-  if (lds > 65536)
-    return fail(FP8PA_EUNSUPPORTED, "B=%d, G=%d, head_dim %d need %zu bytes of LDS (> 64 KiB)", B, G, D, lds);
+  // The stages end at decode_stage_end; the combine buffer may overlap them,
+  // so the launch takes the larger of the stages' end and decode_lds_bytes.
+  const size_t lds_min = fp8pa::decode_lds_bytes(D, B, Gu, kd->page_size);
+  size_t lds = fp8pa::decode_stage_end(D, B, kd->page_size);
+  if (lds_min > 65536)
+    return fail(FP8PA_EUNSUPPORTED, "B=%d, G=%d, head_dim %d need %zu bytes of LDS (> 64 KiB)", B, G, D, lds_min);
   if (int rc = check_desc(vd, "vd")) return rc;
   if (kd->layout == FP8PA_LAYOUT_HEADS_DMAJOR)
     return fail(FP8PA_EUNSUPPORTED, "kd: decode reads K in the HEADS_D64, HEADS or TOKENS layout");
@@ -299,6 +302,7 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
       return fail(FP8PA_EUNSUPPORTED, "B=%d, head_dim %d with V sub-row scales need %zu bytes of LDS (> 64 KiB)", B,
                   D, lds);
   }
+  if (lds < lds_min) lds = lds_min;   // the wave-combine buffer
   // Packed heads: requested, or taken automatically when the units fill the
   // device (V d-major, no fused append).
   const bool packed = packed_req || (!vt && !fused && !kgroups && auto_packs(B, Hq, kd, workgroups, variant));

@@ -1186,8 +1186,20 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     float lsum = l_run;
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
-    float* s_o = s_work;   // [NW / 2][G][D + 4]
-    constexpr int OS = D + 4;
+    // Wave combine, in the order ((w0 + w2) + (w1 + w3)).  The combine
+    // buffer s_o may overlap the page-row and V stages, all read for the last
+    // time before the barrier below.
+    //  - Head dims up to 128, sliced: the waves' rescaled accumulators go to
+    //    LDS ([NW][NC][G][16]) and each wave sums its NC/4 16-dim chunks over
+    //    the four waves, then stores those chunks of the output or partial.
+    //  - Larger head dims, a pairwise tree ([NW/2][G][D+4]): waves 2, 3 hand
+    //    their accumulators to waves 0, 1, then wave 1 to wave 0, which
+    //    stores everything (the sliced form spills registers there).
+    float* s_o = s_work;
+    constexpr bool SLICED = D <= 128;
+    constexpr int CPW = NC / NW;   // chunks each wave sums (sliced)
+    static_assert(NW == 4 && CPW >= 1, "four-wave combine");
+    auto owned = [&](int c) { return SLICED ? c / CPW == wave : wave == 0; };
     if (quad == 0) {
       s_m[wave][n] = m_run;
       s_l[wave][n] = lsum;
@@ -1213,36 +1225,58 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[c] *= f;
       }
-      // Pairwise tree: at each level the upper half of the remaining waves
-      // hands its accumulators to the lower half through LDS.
+      if constexpr (SLICED) {
+        if (col) {
 #pragma unroll
-      for (int half = NW / 2; half >= 1; half >>= 1) {
-        if (wave >= half && wave < 2 * half && col) {
-          float* dst = s_o + ((wave - half) * G + n) * OS + 4 * quad;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
+          for (int c = 0; c < NC; ++c)
+            *reinterpret_cast<f32x4*>(s_o + ((wave * NC + c) * G + n) * 16 + 4 * quad) = acc[c];
         }
         __syncthreads();
-        if (wave < half && col) {
-          const float* src = s_o + (wave * G + n) * OS + 4 * quad;
+        if (col) {
 #pragma unroll
-          for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
+          for (int c = 0; c < NC; ++c) {
+            if (!owned(c)) continue;
+            const float* src = s_o + (c * G + n) * 16 + 4 * quad;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + NC * G * 16);
+            const f32x4 v2 = *reinterpret_cast<const f32x4*>(src + 2 * NC * G * 16);
+            const f32x4 v3 = *reinterpret_cast<const f32x4*>(src + 3 * NC * G * 16);
+            acc[c] = (v0 + v2) + (v1 + v3);
+          }
         }
-        if (half > 1) __syncthreads();
+      } else {
+        constexpr int OS = D + 4;
+#pragma unroll
+        for (int half = NW / 2; half >= 1; half >>= 1) {
+          if (wave >= half && wave < 2 * half && col) {
+            float* dst = s_o + ((wave - half) * G + n) * OS + 4 * quad;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4*>(dst + 16 * c) = acc[c];
+          }
+          __syncthreads();
+          if (wave < half && col) {
+            const float* src = s_o + (wave * G + n) * OS + 4 * quad;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
+          }
+          if (half > 1) __syncthreads();
+        }
       }
     }
 
     const int h = PS ? kvh * a.G + n : g * G + n;   // the lane's query head
     const int prow = PS ? wave * a.G + n : n;         // its row among the unit's G
     if (ta == 0 && tc == nb) {
-      // The segment is the whole unit: o = acc / (sum + e^(sink - max)).
-      if ((PS || wave == 0) && col) {
+      // The segment is the whole unit: o = acc / (sum + e^(sink - max)),
+      // each wave its own chunks (packed splits: each wave its own rows).
+      if (col) {
         float den = Ltot;
         if (a.sinks) den += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - M_ref);
         const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
         uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * D + 4 * quad;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
+          if (!PS && !owned(c)) continue;
           u32x2 pk = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv), pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
           *reinterpret_cast<u32x2*>(orow + 16 * c) = pk;
         }
@@ -1255,22 +1289,18 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       // or invalidate.
       const size_t pbase = ((size_t)sw * 2 + slot) * G;
       const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(a.part_o, (uint32_t)((size_t)gridDim.x * 2 * G * D * 4));
-      if ((PS || wave == 0) && col) {
-        // Lane (head n, quad) holds dims 16c + 4quad .. +3: one 16-byte store per c.
+      if (col) {
+        // Lane (head n, quad) holds dims 16c + 4quad .. +3: one 16-byte store
+        // per c, each wave its own chunks (packed splits: its own rows).
         const float inv = (Ltot > 0.0f) ? __builtin_amdgcn_rcpf(Ltot) : 0.0f;
         const uint32_t row = (uint32_t)((pbase + prow) * D * 4) + 16 * quad;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) st_coherent4(prs, row + 64 * c, acc[c] * inv);
-        if (quad == 0)
+        for (int c = 0; c < NC; ++c)
+          if (PS || owned(c)) st_coherent4(prs, row + 64 * c, acc[c] * inv);
+        if (quad == 0 && (PS || wave == 0))
           __hip_atomic_store(a.part_lse + pbase + prow,
                              (M == kNegInf || !(Ltot > 0.0f)) ? kNegInf : M + __builtin_amdgcn_logf(Ltot),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if constexpr (PS) {
-        // Every wave wrote its rows: all stores complete before the slot is
-        // published (or merged by this workgroup).
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
       }
       const int s_a = share_of_cost(tile_cost(b, g, 0)), s_b = share_of_cost(tile_cost(b, g, nb - 1));
       if (sw == merger_share(s_a, s_b)) {
@@ -1284,11 +1314,14 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
         // tile, whose cost start is SC + TC below this unit's first.
         pend_fsa[npend] = floordiv((int64_t)s_a * Ct, W) <= tile_cost(b, g, 0) - SC - TC ? 1 : 0;
         ++npend;
-      } else if (threadIdx.x == 0) {
-        // Wave 0 wrote the partial; once its stores have completed at the
-        // coherence point, publish the slot.
+      } else {
+        // Every wave wrote part of the partial: once all its stores have
+        // completed at the coherence point, the slot is published.  (A merger
+        // waits for its own stores when its merge begins.)
         __builtin_amdgcn_s_waitcnt(0);
-        __hip_atomic_store(a.flags + 2 * sw + slot, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (threadIdx.x == 0)
+          __hip_atomic_store(a.flags + 2 * sw + slot, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();   // LDS is reused by the next segment
@@ -1305,10 +1338,8 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     const int first_slot_a = pend_fsa[pi];
     auto slot_of = [&](int wi) -> int { return wi == w_a ? first_slot_a : 0; };
     auto part_row = [&](int wi) -> uint32_t { return (uint32_t)(((size_t)wi * 2 + slot_of(wi)) * G); };
-    if (threadIdx.x == 0) {
-      __builtin_amdgcn_s_waitcnt(0);   // this workgroup's own partial (wave 0) is complete
-      s_timeout = 0;
-    }
+    __builtin_amdgcn_s_waitcnt(0);   // every wave's part of this workgroup's own partial is complete
+    if (threadIdx.x == 0) s_timeout = 0;
     __syncthreads();
     // Wait for the other holders' flags.  Their workgroups have lower
     // indices, so they were dispatched first and never wait on this

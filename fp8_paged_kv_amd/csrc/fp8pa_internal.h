@@ -153,14 +153,23 @@ struct VStage {
 };
 
 // Dynamic LDS of a decode launch: the tile and non-empty prefixes and the
-// lengths (3 words per sequence), then the larger of the page-row stage and
-// the wave-combine buffer.
-inline size_t decode_lds_bytes(int D, int B, int G, int P) {
+// lengths (3 words per sequence), then the page-row stage (decode_stage_end),
+// after which the token-major V and V-scale stages go; the wave-combine
+// buffer starts after the prefixes too and may overlap all three stages (they
+// are dead while the waves combine), so the launch needs at least
+// decode_lds_bytes.  The combine holds the four waves' accumulators of G
+// rows up to head dim 128, and two waves' rows of D + 4 floats above.
+inline size_t decode_prefix_bytes(int64_t B) { return (size_t)3 * ((B + 4) & ~int64_t(3)) * 4; }
+inline size_t decode_stage_end(int D, int64_t B, int P) {
   const int TT = decode_tile_tokens(D);
-  const size_t pre = (size_t)3 * (((int64_t)B + 4) & ~int64_t(3)) * 4;
-  const size_t stage = (size_t)(kMaxSplitTokens / TT * TT / P + 2) * 4;
-  const size_t combine = (size_t)(decode_waves(D) / 2) * G * (D + 4) * 4;
-  return pre + (stage > combine ? stage : combine);
+  return decode_prefix_bytes(B) + (size_t)(kMaxSplitTokens / TT * TT / P + 2) * 4;
+}
+inline size_t decode_combine_bytes(int D, int G) {
+  return D <= 128 ? (size_t)decode_waves(D) * G * D * 4 : (size_t)(decode_waves(D) / 2) * G * (D + 4) * 4;
+}
+inline size_t decode_lds_bytes(int D, int B, int G, int P) {
+  const size_t st = decode_stage_end(D, B, P), cb = decode_prefix_bytes(B) + decode_combine_bytes(D, G);
+  return st > cb ? st : cb;
 }
 
 // The per-wave V stages a token-major V pool adds (+ slack to align them to

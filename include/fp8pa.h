@@ -200,8 +200,8 @@ const char* fp8pa_last_error(void);
  * fp8pa_decode does (same refusals) and reports the variant, grid and
  * workspace that call launches.  Refuses (FP8PA_EUNSUPPORTED) shapes whose
  * LDS needs exceed 64 KiB: 12 bytes per sequence plus the larger of the
- * page-row stage and the wave combine, i.e. B above about 5000 (head dim 128)
- * or 2700 (head dim 512 with G = 8). */
+ * page-row stage and the wave combine, i.e. B above about 4700 (head dim 128,
+ * G = 4) or 2700 (head dim 512 with G = 8). */
 int fp8pa_decode_plan(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
                       int max_seq_len, int window, int workgroups, int variant, fp8pa_plan* out);
 

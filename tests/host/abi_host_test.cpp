@@ -164,6 +164,11 @@ static void expect_launch(Call c, int line) {
   const Launch& l = g_launches[0];
   CHECK(l.W == p.workgroups);
   CHECK(l.lds <= 65536);
+  {
+    // The wave-combine buffer (which may overlap the stages) fits the launch's LDS.
+    const int Gu = c.Hq / c.kd.num_kv_heads * (p.variant == FP8PA_VARIANT_PACKED_SPLIT ? 4 : 1);
+    CHECK(l.lds >= fp8pa::decode_lds_bytes(c.kd.head_dim, c.B, Gu, c.kd.page_size));
+  }
   CHECK(l.a.epoch != 0 && l.a.wait_epoch == l.a.epoch && l.a.status != nullptr);
   const int kinds[] = {0, 0, 4, 5};   // what each plan variant launches (bf16 may be plain, fused or vtok)
   (void)kinds;
