@@ -209,7 +209,8 @@ struct Resolved {
   size_t lds;              // dynamic LDS bytes
   size_t vstage_off;       // V token-major: offset of the per-wave V stages
   size_t vgstage_off;      // V sub-row scales: offset of the per-wave scale stages
-  int sk;                  // kernel scale code: the K kind 0-2, 3 (K groups, V per token), 4 (K and V groups)
+  int sk;                  // kernel scale class: the K kind 0-2; K groups of 16+ dims with V per token (3)
+                           // or V groups (4); K groups of 8 dims with V per token (5) or V groups (6)
   int64_t part_o_bytes, part_lse_bytes, flag_bytes;   // workspace pieces, 256-byte aligned
   int64_t workspace_bytes; // 0 when nothing is split
 };
@@ -307,6 +308,9 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
   // device (V d-major, no fused append).
   const bool packed = packed_req || (!vt && !fused && !kgroups && auto_packs(B, Hq, kd, workgroups, variant));
   const bool k_whole = kd->layout == FP8PA_LAYOUT_HEADS_D64 || (D == 64 && kd->layout == FP8PA_LAYOUT_HEADS);
+  const int sk = !kgroups ? kd->scale_kind
+                 : group_dims(kd->scale_kind) == 8 ? (vgroups ? 6 : 5)
+                                                   : (vgroups ? 4 : 3);
   int W = workgroups;
   if (packed) {
     const int64_t Wp = (int64_t)B * ((kd->num_kv_heads + nw - 1) / nw);
@@ -316,8 +320,7 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
     // One resident generation: every workgroup gets an equal share of the
     // tiles and all of them run at once.
     const int cus = device_cus();
-    const int per_cu = cus > 0 ? fp8pa::decode_blocks_per_cu(D, kgroups ? (vgroups ? 4 : 3) : kd->scale_kind,
-                                                             k_whole, lds) : 0;
+    const int per_cu = cus > 0 ? fp8pa::decode_blocks_per_cu(D, sk, k_whole, lds) : 0;
     W = (cus > 0 && per_cu > 0) ? cus * per_cu : 1024;
   }
   r->variant = f8 ? FP8PA_VARIANT_MFMA_FP8
@@ -335,7 +338,7 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
   r->lds = lds;
   r->vstage_off = vstage_off;
   r->vgstage_off = vgstage_off;
-  r->sk = kgroups ? (vgroups ? 4 : 3) : kd->scale_kind;
+  r->sk = sk;
   if (W > 1 && !packed) {
     r->part_o_bytes = round256((int64_t)W * 2 * Gu * D * 4);
     r->part_lse_bytes = round256((int64_t)W * 2 * Gu * 4);

@@ -15,7 +15,7 @@ int decode_blocks_per_cu(int D, int scale_kind, bool k_whole_lines, size_t lds) 
   // (they depend only on the kernel and its LDS, the same on every device
   // of this architecture).
   thread_local std::unordered_map<uint64_t, int> memo;
-  const uint64_t key = (uint64_t)D | ((uint64_t)scale_kind << 12) | ((uint64_t)k_whole_lines << 14) |
+  const uint64_t key = (uint64_t)D | ((uint64_t)scale_kind << 12) | ((uint64_t)k_whole_lines << 16) |
                        ((uint64_t)lds << 24);
   const auto it = memo.find(key);
   if (it != memo.end()) return it->second;

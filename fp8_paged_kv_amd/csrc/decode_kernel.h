@@ -169,8 +169,10 @@ struct Tile {
   float vst[NS][8];
   u32x4 ke8[NS][2];     // E8M0 bytes of the lane's K rows
   u32x4 ve8[NS][NE];    // E8M0 bytes of the lane's 8 score positions, all groups
-  float kgs[NS][2][NM][2];   // fp32 sub-row scales of the two 8-dim halves of the lane's K pieces
-  float vgs[SK == 4 ? 8 * NS : 1];   // SK = 4: the lane's share of the tile's fp32 sub-row V scales
+  // fp32 sub-row K scales of the lane's 16-dim K pieces (SK >= 5: of their
+  // two 8-dim halves)
+  float kgs[NS][2][NM][SK >= 5 ? 2 : 1];
+  float vgs[SK == 4 || SK == 6 ? 8 * NS : 1];   // V in groups: the lane's share of the tile's V scales
 };
 
 // FUSED: also append each sequence's new token (DecodeArgs::k_new / v_new)
@@ -191,12 +193,18 @@ struct Tile {
 template <int D, int SK, bool KNT, bool FUSED, bool VT, bool F8 = false, bool PK = false, bool PS = false>
 __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kernel(const DecodeArgs a) {
   static_assert(!(PS && (FUSED || PK)), "packed splits: plain kernels");
-  static_assert(!(F8 && SK >= 3), "sub-row fp32 K scales vary inside one fp8 MFMA");
+  // Scale classes: 0 page, 1 token, 2 E8M0 (K and V alike); fp32 sub-row K
+  // groups with V per (token, head) (3: groups of 16 dims or more, 5: of 8)
+  // or V in groups too (4, 6).
+  constexpr bool KG = SK >= 3;                // K in fp32 sub-row groups
+  constexpr bool VG = SK == 4 || SK == 6;     // V in fp32 sub-row groups
+  constexpr bool K8 = SK >= 5;                // K groups of 8 dims: two scales per 16-dim piece
+  static_assert(!(F8 && KG), "sub-row fp32 K scales vary inside one fp8 MFMA");
   static_assert(!(F8 && SK == 2 && D % 128), "the MX-scaled fp8 MFMA contracts 128 dims at a time");
   // MX: the fp8 mode over E8M0 pools: QK^T on the MX-scaled fp8 MFMA, which
   // applies the keys' E8M0 scales and the query's own (MXFP8) scales itself.
   constexpr bool MX = F8 && SK == 2;
-  static_assert(!(SK >= 3 && (FUSED || PK || PS)), "sub-row scales: split kernels without the fused append");
+  static_assert(!(KG && (FUSED || PK || PS)), "sub-row scales: split kernels without the fused append");
   static_assert(!(PK && (FUSED || F8)), "packed heads: plain bf16 kernels");
   constexpr int NS = Shape<D>::NS;
   constexpr int NW = Shape<D>::NW;
@@ -582,11 +590,10 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
         scales8(t.kst[s], ksc, tpq + 8 * s, a.kg.sc_tok_stride);
         scales8(t.vst[s], vsc, tpq + 8 * s, a.vg.sc_tok_stride);
       }
-    } else if constexpr (SK >= 3) {
-      // K: the scales of the two 8-dim halves of each of the lane's 16-dim
-      // pieces (position row tk + 8s + 4aa + kslot, dims 64m + 16*quad.. and
-      // +8..: one group each, as groups span at least 8 dims; the same one
-      // when they span 16 or more).
+    } else if constexpr (KG) {
+      // K: the scale of each of the lane's 16-dim pieces (position row tk +
+      // 8s + 4aa + kslot, dims 64m + 16*quad..: one group, as groups span 16
+      // dims or more), or of its two 8-dim halves (K8).
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -596,12 +603,10 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
             t.kgs[s][aa][m][0] = ld_global<float>(kf + 4 * ((64 * m + 16 * quad) >> a.kg.sc_gshift));
-            t.kgs[s][aa][m][1] = a.kg.sc_gshift < 4
-                                     ? ld_global<float>(kf + 4 * ((64 * m + 16 * quad + 8) >> a.kg.sc_gshift))
-                                     : t.kgs[s][aa][m][0];
+            if constexpr (K8) t.kgs[s][aa][m][K8 ? 1 : 0] = ld_global<float>(kf + 4 * ((64 * m + 16 * quad + 8) >> 3));
           }
         }
-      if constexpr (SK == 3) {
+      if constexpr (!VG) {
         // V: per (token, head), as for SK = 1.
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -616,8 +621,10 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
         const uint8_t* vf = a.vp + rvg.scale + kvh * a.vg.sc_head_stride + (pos & (P - 1)) * a.vg.sc_tok_stride;
 #pragma unroll
         for (int i = 0; i < 8 * NS; ++i) {
+          // (Unconditional loads, clamped into the head's groups.)
           const int gg = gh + LP * i;
-          t.vgs[i] = gg < ngv ? ld_global<float>(vf + 4 * gg) : 0.0f;
+          const float v = ld_global<float>(vf + 4 * (gg < ngv ? gg : ngv - 1));
+          t.vgs[i] = gg < ngv ? v : 0.0f;
         }
       }
     } else {
@@ -775,12 +782,12 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
                                                             s4, 0, 0, 0);
             s4 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)(((uint64_t)w[3] << 32) | w[2]),
                                                             (long)qop8[2 * m + 1], s4, 0, 0, 0);
-          } else if constexpr (SK >= 3) {
+          } else if constexpr (KG) {
             bf16x8 hi, lo;
             scaled_e4m3x8_hilo(w[0], w[1], t.kgs[s][aa][m][0], hi, lo);
             s4 = mfma_16x16x32_bf16(hi, qop[2 * m], s4);
             s4 = mfma_16x16x32_bf16(lo, qop[2 * m], s4);
-            scaled_e4m3x8_hilo(w[2], w[3], t.kgs[s][aa][m][1], hi, lo);
+            scaled_e4m3x8_hilo(w[2], w[3], t.kgs[s][aa][m][K8 ? 1 : 0], hi, lo);
             s4 = mfma_16x16x32_bf16(hi, qop[2 * m + 1], s4);
             s4 = mfma_16x16x32_bf16(lo, qop[2 * m + 1], s4);
           } else {
@@ -854,7 +861,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
         for (int c = 0; c < NC; ++c) t.v[c][k] &= mk;
       }
     }
-    if constexpr (SK == 4) {
+    if constexpr (VG) {
       // The lane's V group scales to the wave's stage, [group][tile position].
       constexpr int LP = 64 / TT;
       const int ngv = D >> a.vg.sc_gshift;
@@ -868,7 +875,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if constexpr (SK == 4) {
+      if constexpr (VG) {
         // One probability operand (hi/lo pair) per V group: p x the group
         // scale of each of the lane's 8 positions; a 16-dim chunk lies in one
         // group, so chunk c uses group 16c / S.
@@ -921,7 +928,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
           // L) read a clamped attended one), so p * scale is 0 where p is;
           // a token scale of a masked position may be anything.
           if constexpr (SK == 0) pv[i] = p[s][i] * t.vs;
-          if constexpr (SK == 1 || SK == 3) pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * t.vst[s][i];
+          if constexpr (SK == 1 || (KG && !VG)) pv[i] = (p[s][i] == 0.0f) ? 0.0f : p[s][i] * t.vst[s][i];
         }
         bf16x8 pop, pol;
         split_bf16x8(pv, pop, pol);
@@ -933,7 +940,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
         }
       }
     }
-    if constexpr (SK == 4) {
+    if constexpr (VG) {
       // The next tile rewrites the stage only after these reads.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1189,14 +1196,15 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     // Wave combine, in the order ((w0 + w2) + (w1 + w3)).  The combine
     // buffer s_o may overlap the page-row and V stages, all read for the last
     // time before the barrier below.
-    //  - Head dims up to 128, sliced: the waves' rescaled accumulators go to
-    //    LDS ([NW][NC][G][16]) and each wave sums its NC/4 16-dim chunks over
-    //    the four waves, then stores those chunks of the output or partial.
-    //  - Larger head dims, a pairwise tree ([NW/2][G][D+4]): waves 2, 3 hand
-    //    their accumulators to waves 0, 1, then wave 1 to wave 0, which
-    //    stores everything (the sliced form spills registers there).
+    //  - Sliced (head dim 64, and 128 with page or E8M0 scales): the waves'
+    //    rescaled accumulators go to LDS ([NW][NC][G][16]) and each wave sums
+    //    its NC/4 16-dim chunks over the four waves, then stores those chunks
+    //    of the output or partial.
+    //  - Otherwise a pairwise tree ([NW/2][G][D+4]): waves 2, 3 hand their
+    //    accumulators to waves 0, 1, then wave 1 to wave 0, which stores
+    //    everything (the sliced form spills registers in those kernels).
     float* s_o = s_work;
-    constexpr bool SLICED = D <= 128;
+    constexpr bool SLICED = D == 64 || (D == 128 && (SK == 0 || SK == 2));
     constexpr int CPW = NC / NW;   // chunks each wave sums (sliced)
     static_assert(NW == 4 && CPW >= 1, "four-wave combine");
     auto owned = [&](int c) { return SLICED ? c / CPW == wave : wave == 0; };
@@ -1534,13 +1542,21 @@ hipError_t launch_d(const DecodeArgs& a, int sk, int W, size_t lds, hipStream_t 
       if constexpr (F8 && D % 128) return hipErrorNotSupported;
       else hipExtLaunchKernelGGL((decode_kernel<D, 2, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
-    case 3:    // fp32 sub-row K scales, V per (token, head)
+    case 3:    // fp32 sub-row K scales (groups of 16 dims or more), V per (token, head)
       if constexpr (F8 || FUSED || PK || PS) return hipErrorNotSupported;
       else hipExtLaunchKernelGGL((decode_kernel<D, 3, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
-    default:   // fp32 sub-row K and V scales
+    case 4:    // fp32 sub-row K and V scales
       if constexpr (F8 || FUSED || PK || PS) return hipErrorNotSupported;
       else hipExtLaunchKernelGGL((decode_kernel<D, 4, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
+      break;
+    case 5:    // K groups of 8 dims, V per (token, head)
+      if constexpr (F8 || FUSED || PK || PS) return hipErrorNotSupported;
+      else hipExtLaunchKernelGGL((decode_kernel<D, 5, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
+      break;
+    default:   // K groups of 8 dims, V in groups
+      if constexpr (F8 || FUSED || PK || PS) return hipErrorNotSupported;
+      else hipExtLaunchKernelGGL((decode_kernel<D, 6, KNT, FUSED, VT, F8, PK, PS>), grid, block, lds, st, e0, e1, 0, a);
       break;
   }
   return hipGetLastError();
@@ -1567,7 +1583,9 @@ int occupancy_d(int sk, size_t lds) {
     case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 1, KNT, false, false>, NT, lds); break;
     case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 2, KNT, false, false>, NT, lds); break;
     case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 3, KNT, false, false>, NT, lds); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 4, KNT, false, false>, NT, lds); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 4, KNT, false, false>, NT, lds); break;
+    case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 5, KNT, false, false>, NT, lds); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<D, 6, KNT, false, false>, NT, lds); break;
   }
   return e == hipSuccess ? nb : -1;
 }

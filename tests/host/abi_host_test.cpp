@@ -40,8 +40,10 @@ struct Launch {
   fp8pa::DecodeArgs a;
   int W;
   size_t lds;
+  int sk;     // the kernel scale class the launcher was given
 };
 static std::vector<Launch> g_launches;
+static int g_last_sk = -1;   // scale class of the last launch expect_launch made
 static uint32_t g_status_stub[4];
 alignas(256) static uint8_t g_scratch_stub[FP8PA_NOALLOC_SCRATCH_BYTES];
 uint8_t* fp8pa::device_scratch() { return g_scratch_stub; }
@@ -50,10 +52,10 @@ namespace fp8pa {
 int decode_blocks_per_cu(int D, int, bool, size_t lds) { return lds <= 65536 ? decode_wg_per_cu(D) : 0; }
 uint32_t* device_status_words() { return g_status_stub; }
 uint8_t* device_scratch();
-#define STUB_DECODE(name, k)                                                                                   \
-  hipError_t name(const DecodeArgs& a, int, int, bool, int W, size_t lds, hipStream_t, hipEvent_t, hipEvent_t) { \
-    g_launches.push_back({k, a, W, lds});                                                                      \
-    return hipSuccess;                                                                                         \
+#define STUB_DECODE(name, k)                                                                                      \
+  hipError_t name(const DecodeArgs& a, int, int sk, bool, int W, size_t lds, hipStream_t, hipEvent_t, hipEvent_t) { \
+    g_launches.push_back({k, a, W, lds, sk});                                                                     \
+    return hipSuccess;                                                                                            \
   }
 STUB_DECODE(launch_decode, 0)
 STUB_DECODE(launch_decode_fused, 1)
@@ -162,6 +164,7 @@ static void expect_launch(Call c, int line) {
     return;
   }
   const Launch& l = g_launches[0];
+  g_last_sk = l.sk;
   CHECK(l.W == p.workgroups);
   CHECK(l.lds <= 65536);
   {
@@ -326,8 +329,15 @@ int main() {
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_SPLIT; c.workgroups = 9; LAUNCH(c);
     c = Call(); c.kd.scale_kind = FP8PA_SCALE_F32_G32; c.kd.row_bytes = 16384 + 2048;
     c.vd.scale_kind = FP8PA_SCALE_F32_TOKEN_HEAD; c.vd.row_bytes = 16384 + 2048; c.workgroups = 3; LAUNCH(c);
+    CHECK(g_last_sk == 3);   // K groups of 16+ dims, V per token
+    c.kd.scale_kind = FP8PA_SCALE_F32_G8; c.kd.row_bytes = c.vd.row_bytes = 16384 + 8192; LAUNCH(c);
+    CHECK(g_last_sk == 5);   // K groups of 8 dims, V per token
+    c = Call(); c.kd.scale_kind = c.vd.scale_kind = FP8PA_SCALE_F32_G32; c.kd.row_bytes = c.vd.row_bytes = 16384 + 2048;
+    c.workgroups = 3; LAUNCH(c);
+    CHECK(g_last_sk == 4);   // K and V groups of 16+ dims
     c = Call(); c.kd.scale_kind = FP8PA_SCALE_F32_G8; c.vd.scale_kind = FP8PA_SCALE_F32_G16;   // K and V groups
     c.kd.row_bytes = c.vd.row_bytes = 16384 + 8192; c.workgroups = 3; LAUNCH(c);
+    CHECK(g_last_sk == 6);   // K groups of 8 dims, V groups
     c.workgroups = 1;
     g_launches.clear();
     CHECK(c.run() == 0 && g_launches.size() == 1 && g_launches[0].lds > (size_t)4 * 64 * 8 * 4 &&
