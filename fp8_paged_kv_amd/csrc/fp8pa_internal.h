@@ -108,7 +108,7 @@ struct Shape;
 template <>
 struct Shape<64> { static constexpr int NS = 2, OCC = 2, NW = 4, WPC = 2, SC = 24; };
 template <>
-struct Shape<128> { static constexpr int NS = 2, OCC = 2, NW = 4, WPC = 1, SC = 36; };
+struct Shape<128> { static constexpr int NS = 2, OCC = 2, NW = 4, WPC = 1, SC = 48; };
 template <>
 struct Shape<256> { static constexpr int NS = 1, OCC = 1, NW = 4, WPC = 1, SC = 24; };
 template <>
