@@ -429,6 +429,11 @@ FORMATS = (("heads_d64", "heads_dmajor", None), ("heads", "heads_dmajor", None),
            ("heads", "heads", "token_head"), ("tokens", "tokens", "token_head"),
            ("heads_d64", "heads_dmajor", "f32_g32"), ("heads_d64", "heads_dmajor", "f32_g64"),
            ("tokens", "tokens", "f32_g32"))
+# The same formats with rows on 128-byte lines (row width a multiple of 128):
+# token-major pools then load whole lines.
+FORMATS_ROW128 = (("heads_d64", "heads_dmajor", None), ("heads", "heads_dmajor", None),
+                  ("tokens", "heads_dmajor", None), ("heads", "heads", None), ("tokens", "tokens", None),
+                  ("tokens", "tokens", "token_head"))
 
 
 def copies_of(layers, wl, R, torch):
@@ -454,12 +459,12 @@ def run_formats(args, wl, torch, np, ops, workloads, hip):
     library's append in that format.  Formats that share a scale kind hold the
     same codes and scales, so their outputs must agree bit for bit."""
     first = {}
-    for kl, vl, sk in FORMATS:
+    for kl, vl, sk, ra in [f + (16,) for f in FORMATS] + [f + (128,) for f in FORMATS_ROW128]:
         if args.variant in ("mfma_fp8", "packed_heads", "packed_split") and (vl != "heads_dmajor" or
                                                                               (sk or "").startswith("f32_g")):
             continue   # these variants read V d-major only, and no sub-row K scales
         sk = wl.scale_kind if sk is None else sk
-        layers = workloads.build_workload(wl, k_layout=kl, v_layout=vl, scale_kind=sk)
+        layers = workloads.build_workload(wl, k_layout=kl, v_layout=vl, scale_kind=sk, row_align=ra)
         R = args.copies or rotation(layers, wl, np)
         copies = copies_of(layers, wl, R, torch)
         outs = [workloads.decode_layer(l, variant=args.variant).clone() for l in layers]
@@ -479,7 +484,7 @@ def run_formats(args, wl, torch, np, ops, workloads, hip):
                          "kernel_gbps": round(b / (km * 1e-3) / 1e9, 1),
                          "pct_peak": round(100 * b / (km * 1e-3) / 1e9 / PEAK_GBPS, 1)})
         print(json.dumps({"format": {"k_layout": kl, "v_layout": vl, "scale_kind": sk,
-                                     "row_bytes": layers[0].row_bytes}, "variant": args.variant,
+                                     "row_bytes": layers[0].row_bytes, "row_align": ra}, "variant": args.variant,
                           "workload": wl.name, "layers": rows,
                           "timing": f"hipEvents around {args.steps} back-to-back launches per layer, "
                                     f"{R} pool copies rotated"}), flush=True)

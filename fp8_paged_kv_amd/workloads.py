@@ -87,13 +87,15 @@ def first_attended_page(L, window, P):
 
 
 def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", layers=None, verbose=False,
-                   k_layout="heads_d64", v_layout="heads_dmajor", scale_kind=None):
+                   k_layout="heads_d64", v_layout="heads_dmajor", scale_kind=None, row_align=16):
     """Build the device pools of the workload's layers (all, or the indices in
     ``layers``).  Layers of a shared-pool workload index disjoint rows of one
     K pool and one V pool.  ``k_layout``, ``v_layout`` and ``scale_kind``
     replace the defaults (the workload's own scale kind); a scale block that
     does not fit the layer's row width widens the rows to the natural row,
-    rounded up to 16 bytes."""
+    rounded up to 16 bytes.  ``row_align`` > 16 rounds the row width up to a
+    multiple of it (128: every row starts on a 128-byte line, as token-major
+    pools need for whole-line loads)."""
     scale_kind = wl.scale_kind if scale_kind is None else scale_kind
     lens = inputs.seq_lens(seed, wl.index, wl.B, wl.L_lo, wl.L_hi)
     P = wl.P
@@ -121,6 +123,7 @@ def build_workload(wl: configs.Workload, seed=configs.SEED, device="cuda:0", lay
         natural = P * lay.Hkv * lay.D + max(scale_block_bytes(scale_kind, lay.Hkv, P, lay.D),
                                             scale_block_bytes(v_kind_of(scale_kind), lay.Hkv, P, lay.D))
         row_width[li] = max(lay.row_bytes, -(-natural // 16) * 16)
+        row_width[li] = -(-row_width[li] // row_align) * row_align
     if wl.shared_pool:   # one row width for the layers of a shared pool
         row_width = {li: max(row_width.values()) for li in row_width}
     sinks_np = inputs.sinks(seed, wl.index, wl.layers[0].Hq) if wl.sinks else None
