@@ -602,6 +602,27 @@ def measure(wl, args, hip, torch, np, ops, workloads):
     return rec, layers, copies
 
 
+def copy_probe(torch, hip):
+    """A plain 1 GiB device copy: its counters scale the PMC byte counts of
+    a profiled run."""
+    n = 1 << 30
+    stream = torch.cuda.current_stream().cuda_stream
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    ev = hip.events(2)
+    for _ in range(3):
+        b.copy_(a)
+    hip.record(ev[0], stream)
+    for _ in range(5):
+        b.copy_(a)
+    hip.record(ev[1], stream)
+    ms = hip.elapsed_ms(ev[0], ev[1]) / 5
+    hip.destroy(ev)
+    del a, b
+    return {"bytes_read": n, "bytes_written": n, "us": round(ms * 1e3, 2),
+            "read_plus_write_gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -622,6 +643,8 @@ def main():
     by_name = {w.name: w for w in configs.ALL}
     if args.formats:
         run_formats(args, by_name[args.workload or "llama3-8b-decode"], torch, np, ops, workloads, hip)
+        if args.copy_probe:
+            print(json.dumps({"copy_probe": copy_probe(torch, hip)}), flush=True)
         return
     if args.graph:
         run_graph(args, by_name[args.workload or "llama3-8b-decode"], torch, np, ops, workloads, hip)
@@ -698,23 +721,7 @@ def main():
     out["roofline"]["frac_of_measured_read"] = round(dl["kernel_gbps"] / out["read_probe"]["gbps"], 4)
     del x
     if args.copy_probe:
-        # A plain device copy of known size: its counters scale the PMC byte
-        # counts of a profiled run.
-        n = 1 << 30
-        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
-        b = torch.empty_like(a)
-        ev = hip.events(2)
-        for _ in range(3):
-            b.copy_(a)
-        hip.record(ev[0], stream)
-        for _ in range(5):
-            b.copy_(a)
-        hip.record(ev[1], stream)
-        ms = hip.elapsed_ms(ev[0], ev[1]) / 5
-        hip.destroy(ev)
-        out["copy_probe"] = {"bytes_read": n, "bytes_written": n, "us": round(ms * 1e3, 2),
-                             "read_plus_write_gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
-        del a, b
+        out["copy_probe"] = copy_probe(torch, hip)
     out["fused_append_decode"] = fused
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(head, args.cpu_budget)
     print(json.dumps(out), flush=True)
