@@ -219,6 +219,20 @@ int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 
 // Validates a decode request (everything but pointers and scalars of the
 // call) and resolves what it launches.  fused: the one-launch append.
+// An upper bound on the shares the split kernel keeps for a call whose
+// lengths are at most max_seq_len: its own cap, floor(cost / (unit cost + one
+// tile per wave)), at the most tiles a unit can have (a window only lowers
+// it).  Workgroups beyond it would start, find no share and exit.
+int64_t share_bound(int B, int Hkv, int D, int max_seq_len) {
+  const int TT = fp8pa::decode_tile_tokens(D), NW = fp8pa::decode_waves(D);
+  const int64_t nt = ((int64_t)max_seq_len + TT - 1) / TT;
+  const int64_t U = (int64_t)B * Hkv, T = U * nt;
+  if (T == 0) return 1;
+  const bool unit_mode = T <= (int64_t)NW * U;
+  const int64_t TC = unit_mode ? 0 : 4, SC = unit_mode ? 1 : fp8pa::decode_seg_cost(D);
+  return std::max<int64_t>(1, (SC * U + TC * T) / (SC + TC * NW));
+}
+
 int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, int max_seq_len, int workgroups,
             int variant, bool fused, Resolved* r) {
   if (int rc = check_desc(kd, "kd")) return rc;
@@ -322,6 +336,15 @@ int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd,
     const int cus = device_cus();
     const int per_cu = cus > 0 ? fp8pa::decode_blocks_per_cu(D, sk, k_whole, lds) : 0;
     W = (cus > 0 && per_cu > 0) ? cus * per_cu : 1024;
+    // Small calls: about as many workgroups as the kernel can give shares
+    // to (rounded up to a multiple of 8 from 16 on, so that the shares form
+    // one block per XCD), instead of a full grid whose first XCD blocks take
+    // all the shares (workgroup w runs on XCD w mod 8).
+    if (!psplit) {
+      int64_t cap = share_bound(B, kd->num_kv_heads, D, max_seq_len);
+      if (cap >= 16) cap = (cap + 7) / 8 * 8;
+      if (cap < W) W = (int)cap;
+    }
   }
   r->variant = f8 ? FP8PA_VARIANT_MFMA_FP8
                : packed ? FP8PA_VARIANT_PACKED_HEADS
