@@ -1263,9 +1263,18 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
           }
           __syncthreads();
           if (wave < half && col) {
+            // Reads in groups of eight, each group one LDS round trip (read
+            // one at a time, the adds waited on every read).
             const float* src = s_o + (wave * G + n) * OS + 4 * quad;
+            static_assert(NC % 8 == 0, "whole groups of chunks");
 #pragma unroll
-            for (int c = 0; c < NC; ++c) acc[c] += *reinterpret_cast<const f32x4*>(src + 16 * c);
+            for (int c0 = 0; c0 < NC; c0 += 8) {
+              f32x4 t[8];
+#pragma unroll
+              for (int c = 0; c < 8; ++c) t[c] = *reinterpret_cast<const f32x4*>(src + 16 * (c0 + c));
+#pragma unroll
+              for (int c = 0; c < 8; ++c) acc[c0 + c] += t[c];
+            }
           }
           if (half > 1) __syncthreads();
         }
@@ -1441,8 +1450,30 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
           s_M[threadIdx.x] = sk;
           s_den[threadIdx.x] = (sk != kNegInf) ? 1.0f : 0.0f;
         }
+        // Loads of KB partials x NJ groups are issued together; absent ones
+        // use an offset past the buffer's range, which reads zero.
+        constexpr uint32_t kNone = 0xFFFFFFF0u;
+        int hhj[NJ];
+        uint32_t offj[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int gi = pass0 + threadIdx.x + NT * j;
+          hhj[j] = gi < ngrp ? (4 * gi) / D : 0;
+          offj[j] = gi < ngrp ? (uint32_t)(16 * gi) : kNone;
+        }
+        f32x4 ov[NJ][KB];
+        auto issue = [&](int c0, int k0, int nc) {
+#pragma unroll
+          for (int kk = 0; kk < KB; ++kk) {
+            const bool ok = k0 + kk < nc;
+            const uint32_t rb = ok ? part_row(w_a + c0 + k0 + kk) * (uint32_t)D * 4u : 0u;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ov[j][kk] = ld_coherent4(prs, (ok && offj[j] != kNone) ? rb + offj[j] : kNone);
+          }
+        };
         for (int c0 = 0; c0 < nseg; c0 += CHS) {
           const int nc = nseg - c0 < CHS ? nseg - c0 : CHS;
+          issue(c0, 0, nc);   // the first partials' loads overlap the round trip of the weights
           for (int i = threadIdx.x; i < G * CHS; i += NT) {
             const int hh = i / CHS, k = i - hh * CHS;
             s_wt[i] = k < nc ? __hip_atomic_load(a.part_lse + part_row(w_a + c0 + k) + hh, __ATOMIC_RELAXED,
@@ -1469,27 +1500,10 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
           }
           __syncthreads();
           {
-            // Loads of KB partials x NJ groups are issued together; absent
-            // ones use an offset past the buffer's range, which reads zero.
-            constexpr uint32_t kNone = 0xFFFFFFF0u;
-            int hhj[NJ];
-            uint32_t offj[NJ];
   #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-              const int gi = pass0 + threadIdx.x + NT * j;
-              hhj[j] = gi < ngrp ? (4 * gi) / D : 0;
-              offj[j] = gi < ngrp ? (uint32_t)(16 * gi) : kNone;
-              num[j] *= s_sc[hhj[j]];
-            }
+            for (int j = 0; j < NJ; ++j) num[j] *= s_sc[hhj[j]];
             for (int k0 = 0; k0 < nc; k0 += KB) {
-              f32x4 ov[NJ][KB];
-  #pragma unroll
-              for (int kk = 0; kk < KB; ++kk) {
-                const bool ok = k0 + kk < nc;
-                const uint32_t rb = ok ? part_row(w_a + c0 + k0 + kk) * (uint32_t)D * 4u : 0u;
-  #pragma unroll
-                for (int j = 0; j < NJ; ++j) ov[j][kk] = ld_coherent4(prs, (ok && offj[j] != kNone) ? rb + offj[j] : kNone);
-              }
+              if (k0 > 0) issue(c0, k0, nc);
   #pragma unroll
               for (int kk = 0; kk < KB; ++kk) {
                 const int kx = k0 + kk < CHS ? k0 + kk : CHS - 1;
