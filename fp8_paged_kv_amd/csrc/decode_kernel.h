@@ -1388,57 +1388,116 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     constexpr int KB = 8;     // partials whose loads are in flight together
     const int ngrp = G * D / 4;
     float* s_wt = s_work;     // [G][CHS]
-    constexpr int KF = NJ == 1 ? 16 : 4;   // partials merged in registers
+    constexpr int KF = NJ == 1 ? 32 : 4;   // most partials merged in registers
     if (NJ <= 2 && nseg <= KF && ngrp <= NT * NJ) {
       // Few partials, one pass, head dim <= 256: every thread issues the lse
       // values and the float4 groups of its heads together (one round trip)
       // and merges them in registers, in the same order and arithmetic as the
       // chunked path.  (At head dim 512 the chunked path measured faster.)
-      constexpr uint32_t kNone = 0xFFFFFFF0u;   // past the buffer: reads zero
-      int hhj[NJ];
-      bool okj[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int gi = threadIdx.x + NT * j;
-        okj[j] = gi < ngrp;
-        hhj[j] = okj[j] ? (4 * gi) / D : 0;
-      }
-      f32x4 ov[NJ][KF];
-      float lv[NJ][KF];
-#pragma unroll
-      for (int k = 0; k < KF; ++k) {
-        const bool ok = k < nseg;
-        const uint32_t row = ok ? part_row(w_a + k) : 0u;
-#pragma unroll
+      // KFv loads per group are issued whatever nseg is, so up to 16 partials
+      // take the shorter form.
+      auto reg_merge = [&]<int KFv>() {
+        constexpr uint32_t kNone = 0xFFFFFFF0u;   // past the buffer: reads zero
+        int hhj[NJ];
+        bool okj[NJ];
+  #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const uint32_t gi = threadIdx.x + (uint32_t)NT * j;
-          ov[j][k] = ld_coherent4(prs, (ok && okj[j]) ? row * (uint32_t)D * 4u + 16u * gi : kNone);
-          lv[j][k] = ok ? __hip_atomic_load(a.part_lse + row + hhj[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                        : kNegInf;
+          const int gi = threadIdx.x + NT * j;
+          okj[j] = gi < ngrp;
+          hhj[j] = okj[j] ? (4 * gi) / D : 0;
         }
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (!okj[j]) continue;
-        const int gi = threadIdx.x + NT * j;
-        const int hh = hhj[j], d = 4 * gi - hh * D;
-        const float sk = a.sinks ? a.sinks[gq * G + hh] * kLog2e : kNegInf;
-        float M = sk;
-#pragma unroll
-        for (int k = 0; k < KF; ++k) M = fmaxf(M, lv[j][k]);
-        float den = (sk != kNegInf) ? __builtin_amdgcn_exp2f(sk - M) : 0.0f;
-        f32x4 num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+        f32x4 ov[NJ][KFv];
+        float lv[NJ][KFv];
+  #pragma unroll
+        for (int k = 0; k < KFv; ++k) {
+          const bool ok = k < nseg;
+          const uint32_t row = ok ? part_row(w_a + k) : 0u;
+  #pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const uint32_t gi = threadIdx.x + (uint32_t)NT * j;
+            ov[j][k] = ld_coherent4(prs, (ok && okj[j]) ? row * (uint32_t)D * 4u + 16u * gi : kNone);
+            lv[j][k] = ok ? __hip_atomic_load(a.part_lse + row + hhj[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : kNegInf;
+          }
+        }
+  #pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (!okj[j]) continue;
+          const int gi = threadIdx.x + NT * j;
+          const int hh = hhj[j], d = 4 * gi - hh * D;
+          const float sk = a.sinks ? a.sinks[gq * G + hh] * kLog2e : kNegInf;
+          float M = sk;
+  #pragma unroll
+          for (int k = 0; k < KFv; ++k) M = fmaxf(M, lv[j][k]);
+          float den = (sk != kNegInf) ? __builtin_amdgcn_exp2f(sk - M) : 0.0f;
+          f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int k = 0; k < KFv; ++k) {
+            const float wv = (lv[j][k] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(lv[j][k] - M);
+            den += wv;
+            num += ov[j][k] * wv;
+          }
+          const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
+          const f32x4 o = num * inv;
+          u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+          *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
+        }
+      };
+      if constexpr (NJ == 1) {
+        if (nseg <= 16)
+          reg_merge.template operator()<16>();
+        else
+          reg_merge.template operator()<KF>();
+      } else {
+        // The same steps written out at KF = 4 (head dim 256): called through
+        // the lambda, that kernel's main loop compiled to slower code.
+        constexpr uint32_t kNone = 0xFFFFFFF0u;   // past the buffer: reads zero
+        int hhj[NJ];
+        bool okj[NJ];
+  #pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int gi = threadIdx.x + NT * j;
+          okj[j] = gi < ngrp;
+          hhj[j] = okj[j] ? (4 * gi) / D : 0;
+        }
+        f32x4 ov[NJ][KF];
+        float lv[NJ][KF];
+  #pragma unroll
         for (int k = 0; k < KF; ++k) {
-          const float wv = (lv[j][k] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(lv[j][k] - M);
-          den += wv;
-          num += ov[j][k] * wv;
+          const bool ok = k < nseg;
+          const uint32_t row = ok ? part_row(w_a + k) : 0u;
+  #pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const uint32_t gi = threadIdx.x + (uint32_t)NT * j;
+            ov[j][k] = ld_coherent4(prs, (ok && okj[j]) ? row * (uint32_t)D * 4u + 16u * gi : kNone);
+            lv[j][k] = ok ? __hip_atomic_load(a.part_lse + row + hhj[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : kNegInf;
+          }
         }
-        const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
-        const f32x4 o = num * inv;
-        u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
-        *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
+  #pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (!okj[j]) continue;
+          const int gi = threadIdx.x + NT * j;
+          const int hh = hhj[j], d = 4 * gi - hh * D;
+          const float sk = a.sinks ? a.sinks[gq * G + hh] * kLog2e : kNegInf;
+          float M = sk;
+  #pragma unroll
+          for (int k = 0; k < KF; ++k) M = fmaxf(M, lv[j][k]);
+          float den = (sk != kNegInf) ? __builtin_amdgcn_exp2f(sk - M) : 0.0f;
+          f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int k = 0; k < KF; ++k) {
+            const float wv = (lv[j][k] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(lv[j][k] - M);
+            den += wv;
+            num += ov[j][k] * wv;
+          }
+          const float inv = (M == kNegInf || !(den > 0.0f)) ? 0.0f : __builtin_amdgcn_rcpf(den);
+          const f32x4 o = num * inv;
+          u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          if (s_timeout) pk = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+          *reinterpret_cast<u32x2*>(a.out + ((size_t)bq * a.Hq + gq * G + hh) * D + d) = pk;
+        }
       }
     } else {
       for (int pass0 = 0; pass0 < ngrp; pass0 += NT * NJ) {
