@@ -338,22 +338,14 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       const int len = lane < B ? chk_len(a.seq_lens[lane], bad_len) : 0;
       flag(bad_len, 1);
       const int nt = tiles_of(len), ne = nt > 0 ? 1 : 0;
-      int incl = nt, incl_ne = ne;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off), v2 = __shfl_up(incl_ne, off);
-        if (lane >= off) {
-          incl += v;
-          incl_ne += v2;
-        }
-      }
+      const int incl = wave_incl_sum(nt), incl_ne = wave_incl_sum(ne);
       const int pre = incl - nt, nep = incl_ne - ne;
       if (lane < B) {
         s_len[lane] = len;
         s_pre[lane] = pre;
         s_nep[lane] = nep;
       }
-      const int tot = __shfl(incl, 63), tot_ne = __shfl(incl_ne, 63);
+      const int tot = __builtin_amdgcn_readlane(incl, 63), tot_ne = __builtin_amdgcn_readlane(incl_ne, 63);
       if (lane == 0) {
         s_pre[B] = tot;
         s_nep[B] = tot_ne;
@@ -418,15 +410,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
         lne += nt > 0;
       }
     flag(bad_len, 1);
-    int incl = local, incl_ne = lne;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off), v2 = __shfl_up(incl_ne, off);
-      if (lane >= off) {
-        incl += v;
-        incl_ne += v2;
-      }
-    }
+    const int incl = wave_incl_sum(local), incl_ne = wave_incl_sum(lne);
     if (lane == 63) {
       s_wsum[wave] = incl;
       s_wsum_ne[wave] = incl_ne;
@@ -822,8 +806,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
         for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sc[s][aa][j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = pair_max32(pair_max16(tmax));
     const float m_new = fmaxf(m_run, tmax);
     const float m_ref = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
@@ -992,8 +975,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     }
     // The wave's head is complete: o = acc / (sum + e^(sink - max)).
     float lsum = l_run;
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    lsum = pair_sum32(pair_sum16(lsum));
     if (active && col) {
       const int h = g * G + n;
       const float m_ref = (m_run == kNegInf) ? 0.0f : m_run;
@@ -1079,7 +1061,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
             for (int j = 0; j < 8; ++j)
               am[h] = fmaxf(am[h], fmaxf(fabsf(bf16_to_f32((uint16_t)wv[8 * h + j])),
                                          fabsf(bf16_to_f32((uint16_t)(wv[8 * h + j] >> 16)))));
-            am[h] = fmaxf(am[h], __shfl_xor(am[h], 16));
+            am[h] = pair_max16(am[h]);
           }
           const uint32_t u0 = e8m0_code(am[0]), u1 = e8m0_code(am[1]);
           v8i32 codes;
@@ -1123,8 +1105,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
           for (int j = 0; j < 4; ++j)
             am = fmaxf(am, fmaxf(fabsf(bf16_to_f32((uint16_t)v[j])), fabsf(bf16_to_f32((uint16_t)(v[j] >> 16)))));
         }
-        am = fmaxf(am, __shfl_xor(am, 16));
-        am = fmaxf(am, __shfl_xor(am, 32));
+        am = pair_max32(pair_max16(am));
         qsc = am > 0.0f ? am / 448.0f : 1.0f;
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
@@ -1191,8 +1172,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
 
     // ---- combine the waves' states in LDS.
     float lsum = l_run;
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    lsum = pair_sum32(pair_sum16(lsum));
     // Wave combine, in the order ((w0 + w2) + (w1 + w3)).  The combine
     // buffer s_o may overlap the page-row and V stages, all read for the last
     // time before the barrier below.
