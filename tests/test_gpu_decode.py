@@ -131,6 +131,21 @@ def test_workgroup_counts_agree():
         assert np.max(np.abs(o - outs[0])) < 2e-2
 
 
+@pytest.mark.parametrize("D,Hq,L,pieces", [(64, 4, 15000, 24), (64, 4, 30400, 48), (128, 8, 24000, 24),
+                                             (128, 8, 48400, 48)])
+def test_one_unit_in_many_pieces(D, Hq, L, pieces):
+    """A single long (sequence, KV head) unit cut into 24 or 48 pieces: the
+    merge takes its 32-partial register form, resp. its chunked form (the
+    lengths make each share hold at least a round of tiles, so the kernel
+    keeps every requested workgroup)."""
+    say("one unit in pieces", D, L, pieces)
+    p = make_problem(111, B=1, Hq=Hq, Hkv=1, D=D, P=16, lens=[L], sinks=True)
+    dev = device_problem(p)
+    want = oracle(p)
+    for w in (pieces, 0):
+        assert_parity(to_np(gpu_decode(p, dev=dev, workgroups=w)), want, f"workgroups={w}")
+
+
 def test_more_workgroups_than_tiles():
     """Workgroups with an empty share exit; units are still complete."""
     p = make_problem(108, B=2, Hq=8, Hkv=2, D=64, P=16, lens=[130, 64])
