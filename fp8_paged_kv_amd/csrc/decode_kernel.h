@@ -14,8 +14,10 @@
 // Work decomposition.  A unit is one (sequence, KV head): the G query heads
 // of the unit share every K/V read (page section "Why it happens": the grid
 // runs over sequence, KV head and split).  A unit's attended positions form a
-// run of tiles; the tiles of all units, sequence by sequence, make one global
-// list, and workgroup w of W takes the w-th equal share of it, so every
+// run of tiles; the tiles of all units, sequence by sequence (or KV head by
+// KV head, so that the heads' shares of the same pages run side by side on
+// one XCD), make one global list, and workgroup w of W takes an equal share
+// of it, so every
 // workgroup streams the same number of bytes however uneven the sequence
 // lengths are, and W is chosen so that all workgroups are resident at once.
 // A call with few tiles uses only the first ceil(T / min_tiles) workgroups
@@ -244,8 +246,37 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
   // and the lines at head boundaries that neighbouring heads' shares touch
   // are then fetched once into one L2 instead of into several.  A launch
   // whose grid is not a multiple of 8 keeps sw = w.
+  //
+  // Head-major order.  When the grid is not capped and W is a multiple of
+  // 8 * Hkv, units are ordered KV head first (all sequences of head 0, then
+  // of head 1, ...).  Every head's run then costs Ct / Hkv, a whole number of
+  // shares, so shares j, W/Hkv + j, 2W/Hkv + j, ... cover the same positions
+  // of the same sequences, one KV head each.  Those Hkv shares go to Hkv
+  // consecutive workgroups of one XCD (its k-th workgroup takes head k mod
+  // Hkv of share group x * G8h + k / Hkv, G8h = W / (8 Hkv)), which start
+  // together and walk the same page rows in step: the scale-footer lines and
+  // the lines that straddle two heads' payloads are fetched into that L2 once
+  // for all the heads.  A share then lies inside one head's run, so its
+  // head and its place in the run are known without a division (Hkv a power
+  // of two).  Otherwise units are ordered sequence first.  (Head dims 128
+  // and 512 keep the sequence-first order: the extra set-up state made them
+  // spill.)
+  constexpr bool HMK = D == 64 || D == 256;
   const int G8 = (gridDim.x % 8 == 0 && gridDim.x >= 16) ? (int)gridDim.x / 8 : 0;
-  const int sw = G8 ? (w % 8) * G8 + w / 8 : w;
+  int sw = 0;         // this workgroup's share
+  bool hm = false;    // head-major unit order
+  int G8m = 0;        // shares per XCD block (of one head's run in head-major order)
+  int hgh = 0, hj = 0, hlog = 0;   // head-major: the share's head, its share in that head's run, log2 Hkv
+  // Every value is assigned from uniform ones (W, w, Hkv), whatever ran
+  // before, so that they stay in scalar registers.
+  auto set_order = [&]() {
+    hm = HMK && G8 && W == (int)gridDim.x && (Hkv & (Hkv - 1)) == 0 && W % (8 * Hkv) == 0;
+    hlog = hm ? __builtin_ctz((unsigned)Hkv) : 0;
+    G8m = hm ? W >> (3 + hlog) : G8;
+    hgh = hm ? (w >> 3) & (Hkv - 1) : 0;
+    hj = hm ? (w & 7) * G8m + (w >> (3 + hlog)) : 0;
+    sw = hm ? hgh * (W >> hlog) + hj : (G8 ? (w % 8) * G8 + w / 8 : w);
+  };
   const bool col = n < (PS ? a.G : G);
 
   // Debug checks (a.dbg set): a length outside [0, dbg_max_len] counts as 0
@@ -285,7 +316,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
   // non-empty (at least min_tiles tiles' worth).  When units average at most
   // one tile per wave, a split would only add merges: tiles then cost 0 and a
   // unit 1, so shares are whole units (unit-aligned mode).
-  int64_t T = 0, U = 0, TC = 0, SC = 0, Ct = 0;
+  int64_t T = 0, U = 0, TC = 0, SC = 0, Ct = 0, T1 = 0, Ct1 = 0;
   auto set_costs = [&](int tiles, int nonempty) {
     T = (int64_t)tiles * Hkv;
     U = (int64_t)nonempty * Hkv;
@@ -293,6 +324,8 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     TC = unit_mode ? 0 : 4;
     SC = unit_mode ? 1 : a.seg_cost;
     Ct = SC * U + TC * T;
+    T1 = tiles;                           // tiles of one KV head's run (head-major order)
+    Ct1 = SC * nonempty + TC * T1;        // and its cost: Ct = Hkv * Ct1
   };
   auto cap_W = [&]() {
     int64_t want = floordiv(Ct, SC + TC * a.min_tiles);
@@ -302,9 +335,10 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
   };
   // A share bound as a global tile index: the first tile whose cost start is
   // >= c, for c inside the cost range of sequence bb (which starts at lo,
-  // after pre tiles, and has nbb tiles per unit); past a unit's last tile
-  // that is the next unit's first.
-  auto bound_in = [&](int64_t c, int64_t lo, int pre, int nbb) -> int64_t {
+  // after pre tiles, and has nbb tiles per unit, hk units); past a unit's
+  // last tile that is the next unit's first.  In head-major order the range
+  // is one head's (hk = 1) and the caller adds the head run's offset.
+  auto bound_in = [&](int64_t c, int64_t lo, int pre, int nbb, int hk) -> int64_t {
     const int64_t span = SC + TC * nbb;
     int64_t gg = floordiv(c - lo, span);
     const int64_t r = c - lo - gg * span;
@@ -313,7 +347,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       t = 0;
       ++gg;
     }
-    return (int64_t)Hkv * pre + gg * nbb + t;
+    return (int64_t)hk * pre + gg * nbb + t;
   };
   // Page rows of the chunk [ca, cb) of the current segment's tiles.
   int b = 0, g = 0, L = 0, start = 0, tbeg = 0, p_first = 0, nstaged = 1;
@@ -352,27 +386,33 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       }
       set_costs(tot, tot_ne);
       cap_W();
+      set_order();
       if (sw < W) {
-        const int64_t lo = SC * Hkv * nep + TC * (int64_t)Hkv * pre;
-        const int64_t hiw = lo + (int64_t)Hkv * (SC * ne + TC * nt);
+        const int hk = hm ? 1 : Hkv;   // units of a sequence inside one cost range
+        const int64_t lo = SC * hk * nep + TC * (int64_t)hk * pre;
+        const int64_t hiw = lo + (int64_t)hk * (SC * ne + TC * nt);
+        const int64_t gofs = hm ? (int64_t)hgh * T1 : 0;   // head-major: first tile of the share's head run
         int64_t bnd[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int64_t c = floordiv((int64_t)(sw + e) * Ct, W);
+          // head-major: the bound inside the head's run (cost Ct1, W >> hlog shares)
+          const int64_t c = hm ? floordiv((int64_t)(hj + e) * Ct1, W >> hlog) : floordiv((int64_t)(sw + e) * Ct, W);
           const bool hit = lane < B && c >= lo && c < hiw;
-          const int64_t v = hit ? bound_in(c, lo, pre, nt) : 0;
+          const int64_t v = hit ? gofs + bound_in(c, lo, pre, nt, hk) : 0;
           const uint64_t mask = __ballot(hit);
-          bnd[e] = mask ? readlane64(v, (int)__builtin_ctzll(mask)) : T;
+          bnd[e] = mask ? readlane64(v, (int)__builtin_ctzll(mask)) : (hm ? gofs + T1 : T);
         }
         if (bnd[0] < bnd[1]) {
           // The first segment's unit: b is the last sequence whose tiles start
-          // at or before bnd[0] (a non-empty one, as bnd[0] < T).
-          const int bl = 63 - (int)__builtin_clzll(__ballot(lane < B && (int64_t)Hkv * pre <= bnd[0]));
+          // at or before bnd[0] (a non-empty one, as bnd[0] < T), within the
+          // share's head run in head-major order.
+          const int64_t r0 = bnd[0] - gofs;
+          const int bl = 63 - (int)__builtin_clzll(__ballot(lane < B && (int64_t)hk * pre <= r0));
           b = bl;
           const int nb = __builtin_amdgcn_readlane(nt, bl);
-          const int64_t ubase = (int64_t)Hkv * __builtin_amdgcn_readlane(pre, bl);
-          g = (int)floordiv(bnd[0] - ubase, nb);
-          const int64_t ustart = ubase + (int64_t)g * nb;
+          const int64_t ubase = gofs + (int64_t)hk * __builtin_amdgcn_readlane(pre, bl);
+          g = hm ? hgh : (int)floordiv(bnd[0] - ubase, nb);
+          const int64_t ustart = hm ? ubase : ubase + (int64_t)g * nb;
           const int ta = (int)(bnd[0] - ustart);
           const int tc = (int)((bnd[1] < ustart + nb ? bnd[1] : ustart + nb) - ustart);
           L = __builtin_amdgcn_readlane(len, bl);
@@ -396,6 +436,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     __syncthreads();
     W = s_first[0];
     set_costs(s_pre[B], s_nep[B]);
+    set_order();
   } else {
     const int per = (B + NT - 1) / NT;
     const int bb0 = threadIdx.x * per;
@@ -441,6 +482,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     __syncthreads();
     set_costs(s_pre[B], s_nep[B]);
     cap_W();
+    set_order();
   }
 
   // Sequences with nothing to attend get a zero output (packed heads: each
@@ -453,11 +495,15 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     }
     if (sw >= W) return;
   }
-  auto cpre = [&](int bb) -> int64_t { return SC * Hkv * s_nep[bb] + TC * (int64_t)Hkv * s_pre[bb]; };
+  // Cost start of sequence bb's units (of one head's run in head-major order).
+  auto cpre = [&](int bb) -> int64_t {
+    const int hk = hm ? 1 : Hkv;
+    return SC * hk * s_nep[bb] + TC * (int64_t)hk * s_pre[bb];
+  };
   // Cost start of tile i of unit (bb, gg).
   auto tile_cost = [&](int bb, int gg, int i) -> int64_t {
     const int nbb = s_pre[bb + 1] - s_pre[bb];
-    return cpre(bb) + (int64_t)gg * (SC + TC * nbb) + SC + TC * i;
+    return hm ? (int64_t)gg * Ct1 + cpre(bb) + SC + TC * i : cpre(bb) + (int64_t)gg * (SC + TC * nbb) + SC + TC * i;
   };
   // Share holding a tile of cost start c: the largest sh with floor(sh*Ct/W) <= c.
   auto share_of_cost = [&](int64_t c) -> int { return (int)(floordiv((c + 1) * W + Ct - 1, Ct) - 1); };
@@ -468,19 +514,25 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
   // blocks but that block's own last one.  So: sb, unless the unit crosses
   // into sb's block from an earlier one and sb does not end its block, in
   // which case the end of the block before sb's.
+  // (In head-major order a unit's pieces lie in one head's run, whose XCD
+  // blocks are G8m shares long, and the same holds.)
   auto merger_share = [&](int sa, int sb) -> int {
-    if (!G8 || sb % G8 == G8 - 1) return sb;
-    const int e = (sb / G8) * G8 - 1;
+    if (!G8m || sb % G8m == G8m - 1) return sb;
+    const int e = (sb / G8m) * G8m - 1;
     return e >= sa ? e : sb;
   };
   if (!fast) {
     // The share's first and end tiles: the first tile whose cost start is >=
     // floor(w*Ct/W), resp. floor((w+1)*Ct/W), found by the thread whose
     // sequence's cost range holds that point (T past the end).
-    const int64_t cb[2] = {floordiv((int64_t)sw * Ct, W), floordiv((int64_t)(sw + 1) * Ct, W)};
-    if (threadIdx.x < 2) s_bnd[threadIdx.x] = T;
+    // (head-major: inside the share's head run, of cost Ct1 and W >> hlog shares)
+    const int64_t gofs = hm ? (int64_t)hgh * T1 : 0;
+    const int64_t cb[2] = {hm ? floordiv((int64_t)hj * Ct1, W >> hlog) : floordiv((int64_t)sw * Ct, W),
+                           hm ? floordiv((int64_t)(hj + 1) * Ct1, W >> hlog) : floordiv((int64_t)(sw + 1) * Ct, W)};
+    if (threadIdx.x < 2) s_bnd[threadIdx.x] = hm ? gofs + T1 : T;
     __syncthreads();
     const int per = (B + NT - 1) / NT;
+    const int hk = hm ? 1 : Hkv;
     for (int i = 0; i < per; ++i) {
       const int bb = threadIdx.x * per + i;
       if (bb >= B) break;
@@ -488,7 +540,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int64_t c = cb[e];
-        if (c >= lo && c < hiw) s_bnd[e] = bound_in(c, lo, s_pre[bb], s_pre[bb + 1] - s_pre[bb]);
+        if (c >= lo && c < hiw) s_bnd[e] = gofs + bound_in(c, lo, s_pre[bb], s_pre[bb + 1] - s_pre[bb], hk);
       }
     }
     __syncthreads();
@@ -1008,6 +1060,16 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     if (staged) {
       b = s_first[1];
       g = s_first[2];
+    } else if (hm) {
+      g = hgh;   // the share's head run, then the sequence inside it
+      const int64_t r = cur - (int64_t)g * T1;
+      int lo_b = 0, hi_b = B - 1;   // largest b with s_pre[b] <= r (a non-empty sequence)
+      while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if ((int64_t)s_pre[mid] <= r) lo_b = mid;
+        else hi_b = mid - 1;
+      }
+      b = lo_b;
     } else {
       int lo_b = 0, hi_b = B - 1;   // largest b with s_pre[b] * Hkv <= cur (a non-empty sequence)
       while (lo_b < hi_b) {
@@ -1019,8 +1081,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
       g = (int)floordiv(cur - (int64_t)s_pre[b] * Hkv, s_pre[b + 1] - s_pre[b]);
     }
     const int nb = s_pre[b + 1] - s_pre[b];
-    const int64_t ubase = (int64_t)s_pre[b] * Hkv;
-    const int64_t ustart = ubase + (int64_t)g * nb;
+    const int64_t ustart = hm ? (int64_t)g * T1 + s_pre[b] : (int64_t)s_pre[b] * Hkv + (int64_t)g * nb;
     const int64_t uend = ustart + nb;
     const int64_t send = hi < uend ? hi : uend;
     const int ta = (int)(cur - ustart), tc = (int)(send - ustart);
