@@ -220,9 +220,10 @@ int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 // Validates a decode request (everything but pointers and scalars of the
 // call) and resolves what it launches.  fused: the one-launch append.
 // An upper bound on the shares the split kernel keeps for a call whose
-// lengths are at most max_seq_len: its own cap, floor(cost / (unit cost + one
-// tile per wave)), at the most tiles a unit can have (a window only lowers
-// it).  Workgroups beyond it would start, find no share and exit.
+// lengths are at most max_seq_len: its own cap, the larger of floor(cost /
+// (unit cost + one tile per wave)) and floor(tiles / waves), at the most tiles
+// a unit can have (a window only lowers it).  Workgroups beyond it would
+// start, find no share and exit.
 int64_t share_bound(int B, int Hkv, int D, int max_seq_len) {
   const int TT = fp8pa::decode_tile_tokens(D), NW = fp8pa::decode_waves(D);
   const int64_t nt = ((int64_t)max_seq_len + TT - 1) / TT;
@@ -230,7 +231,8 @@ int64_t share_bound(int B, int Hkv, int D, int max_seq_len) {
   if (T == 0) return 1;
   const bool unit_mode = T <= (int64_t)NW * U;
   const int64_t TC = unit_mode ? 0 : 4, SC = unit_mode ? 1 : fp8pa::decode_seg_cost(D);
-  return std::max<int64_t>(1, (SC * U + TC * T) / (SC + TC * NW));
+  const int64_t by_cost = (SC * U + TC * T) / (SC + TC * NW), by_tiles = unit_mode ? 0 : T / NW;
+  return std::max<int64_t>(1, std::max(by_cost, by_tiles));
 }
 
 int resolve(int B, int Hq, const fp8pa_pool_desc* kd, const fp8pa_pool_desc* vd, int max_seq_len, int workgroups,

@@ -20,9 +20,10 @@
 // of it, so every
 // workgroup streams the same number of bytes however uneven the sequence
 // lengths are, and W is chosen so that all workgroups are resident at once.
-// A call with few tiles uses only the first ceil(T / min_tiles) workgroups
-// (at least one tile per wave), so every active workgroup's share is
-// non-empty.
+// A call with few tiles uses only as many workgroups as give each at least
+// one tile per wave (counting the units' fixed costs, or, for a call with few
+// units, on average), so the shares stay worth a launch; a share that falls
+// inside a unit's fixed cost is empty and simply ends.
 // Every workgroup builds the list itself from seq_lens (a prefix sum in LDS),
 // so the grid depends on host values only.  A workgroup's share cuts units
 // into segments; a workgroup is NW wave64s (four by default), each wave walks
@@ -327,8 +328,14 @@ __global__ __launch_bounds__(64 * Shape<D>::NW, Shape<D>::OCC) void decode_kerne
     T1 = tiles;                           // tiles of one KV head's run (head-major order)
     Ct1 = SC * nonempty + TC * T1;        // and its cost: Ct = Hkv * Ct1
   };
+  // A call with few units (single long sequences) may also take up to one
+  // share per NW tiles (min_tiles = NW outside packed splits), ignoring the
+  // units' fixed costs: every share then costs at least 4 * NW, so it holds a
+  // tile of any unit whose tiles it overlaps; a share that holds only part of
+  // a unit's fixed cost is empty, holds no unit and merges nothing.
   auto cap_W = [&]() {
     int64_t want = floordiv(Ct, SC + TC * a.min_tiles);
+    if (!PS && TC > 0 && T / NW > want) want = T / NW;
     if (want < 1) want = 1;
     if (T == 0) want = 0;
     if (want < W) W = (int)want;

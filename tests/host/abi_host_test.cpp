@@ -329,17 +329,21 @@ int main() {
     c = Call(); c.variant = FP8PA_VARIANT_PACKED_SPLIT; c.workgroups = 9; LAUNCH(c);
     {
       // Automatic grids of small calls stop at the shares the kernel can
-      // form: 2 units of 4 tiles are 2 shares; 8 units of 256 tiles give 134,
-      // rounded up to 136 (a multiple of 8); a large call keeps one workgroup
-      // per CU (256 stub CUs).
+      // form: 2 units of 4 tiles are 2 shares (whole units); 8 units of 30
+      // tiles give 60 (one tile per wave), rounded up to 64 (a multiple of 8);
+      // 8 units of 256 tiles give 512 shares, so a full grid; a large call
+      // keeps one workgroup per CU (256 stub CUs).
       fp8pa_plan p{};
       c = Call(); c.B = 1; c.Hq = 8; c.msl = 256;
       c.kd = desc(2, 64, 16, FP8PA_LAYOUT_HEADS_D64, FP8PA_SCALE_F32_PAGE_HEAD, 2064);
       c.vd = desc(2, 64, 16, FP8PA_LAYOUT_HEADS_DMAJOR, FP8PA_SCALE_F32_PAGE_HEAD, 2064);
       CHECK(c.plan(&p) == 0 && p.workgroups == 2);
       LAUNCH(c);
+      c = Call(); c.B = 1; c.msl = 1900;
+      CHECK(c.plan(&p) == 0 && p.workgroups == 64);
+      LAUNCH(c);
       c = Call(); c.B = 1; c.msl = 16384; c.bt_stride = 1024;
-      CHECK(c.plan(&p) == 0 && p.workgroups == 136);
+      CHECK(c.plan(&p) == 0 && p.workgroups == 256);
       LAUNCH(c);
       c = Call(); c.B = 32; c.msl = 8192;
       CHECK(c.plan(&p) == 0 && p.workgroups == 256);
